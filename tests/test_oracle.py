@@ -1,0 +1,406 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test checks the f64 oracle against something other than itself: a
+closed form, an invariant of softmax attention, a special case, brute force
+(the O(n^2) full-causal re-prefill route), a library routine (scipy softmax,
+torch SDPA in float64 on the CPU), or the worked example printed on the
+franken_ocr 0.8.0 decoder_qwen2.rs page (tests/golden).  Together they are
+chosen so that a plausible slip in the oracle -- a dropped max shift, a wrong
+scale, a wrong GQA index, K and V swapped, an off-by-one in the attended
+length -- fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from kv_cached_decode_kvdec_amd import inputs as gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+D = 64
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _cache(rng, B, Hkv, cap, d=D, dtype=np.float32):
+    K = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32)
+    return K, V
+
+
+def test_scale_is_one_over_sqrt_64():
+    # franken_ocr config tests pin 1/sqrt(head_dim) = 1/8 at head_dim 64.
+    assert oracle.SCALE_HEAD_DIM_64 == 1.0 / math.sqrt(64) == 0.125
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 64, 300])
+def test_weights_sum_to_one(n):
+    rng = _rng(n)
+    q = rng.standard_normal((2, 3, D)).astype(np.float32)
+    K, _ = _cache(rng, 2, 3, n)
+    V = np.ones_like(K)
+    out = oracle.attend(q, K, V, np.array([n, n], np.int32))
+    np.testing.assert_allclose(out, 1.0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [1, 5, 33, 64])
+def test_weights_equal_library_softmax(n):
+    # V = first n rows of the identity: out[h][j] is the weight of row j.
+    rng = _rng(100 + n)
+    Hq = 4
+    q = rng.standard_normal((1, Hq, D)).astype(np.float32)
+    K, _ = _cache(rng, 1, Hq, n)
+    V = np.zeros_like(K)
+    for j in range(n):
+        V[0, :, j, j] = 1.0
+    out = oracle.attend(q, K, V, np.array([n], np.int32))
+    for h in range(Hq):
+        scores = (q[0, h].astype(np.float64) @ K[0, h].astype(np.float64).T) * 0.125
+        w = scipy.special.softmax(scores)
+        np.testing.assert_allclose(out[0, h, :n], w, rtol=1e-12, atol=1e-15)
+        assert abs(out[0, h, :n].sum() - 1.0) < 1e-12
+        assert np.all(out[0, h, n:] == 0.0)
+
+
+def test_large_scores_need_the_max_shift():
+    # Scores of order 1e3 overflow exp() in f64 unless the max is subtracted.
+    rng = _rng(7)
+    q = (rng.standard_normal((1, 2, D)) * 60.0).astype(np.float32)
+    K, V = _cache(rng, 1, 2, 40)
+    K *= 60.0
+    out = oracle.attend(q, K, V, np.array([40], np.int32))
+    assert np.all(np.isfinite(out))
+    for h in range(2):
+        s = (q[0, h].astype(np.float64) @ K[0, h].astype(np.float64).T) * 0.125
+        assert np.abs(s).max() > 800.0
+        w = scipy.special.softmax(s)
+        np.testing.assert_allclose(out[0, h], w @ V[0, h].astype(np.float64), rtol=1e-10, atol=1e-12)
+
+
+def test_identical_keys_give_mean_of_v():
+    rng = _rng(11)
+    n = 37
+    q = rng.standard_normal((3, 2, D)).astype(np.float32)
+    K, V = _cache(rng, 3, 2, n)
+    K[:] = K[:, :, :1, :]            # every row equal to row 0
+    out = oracle.attend(q, K, V, np.full(3, n, np.int32))
+    mean = V.astype(np.float64).mean(axis=2)
+    np.testing.assert_allclose(out, mean, rtol=1e-12, atol=1e-13)
+
+
+def test_dominant_key_selects_its_value_row():
+    rng = _rng(12)
+    n, jstar = 50, 17
+    q = rng.standard_normal((1, 1, D)).astype(np.float32)
+    K, V = _cache(rng, 1, 1, n)
+    qq = q[0, 0].astype(np.float64)
+    others = np.max(K[0, 0].astype(np.float64) @ qq) * 0.125
+    alpha = (others + 80.0) / (0.125 * qq @ qq)       # dominant score beats the rest by >= 80
+    K[0, 0, jstar] = (alpha * qq).astype(np.float32)
+    out = oracle.attend(q, K, V, np.array([n], np.int32))
+    np.testing.assert_allclose(out[0, 0], V[0, 0, jstar].astype(np.float64), rtol=1e-12, atol=1e-14)
+
+
+def test_single_row_returns_that_row_exactly():
+    rng = _rng(13)
+    q = rng.standard_normal((4, 5, D)).astype(np.float32)
+    K, V = _cache(rng, 4, 5, 8)
+    out = oracle.attend(q, K, V, np.ones(4, np.int32))
+    assert np.array_equal(out, V[:, :, 0, :].astype(np.float64))
+
+
+def test_shift_of_all_keys_leaves_output_unchanged():
+    rng = _rng(14)
+    n = 29
+    q = rng.standard_normal((2, 3, D)).astype(np.float32)
+    K, V = _cache(rng, 2, 3, n)
+    u = rng.standard_normal(D).astype(np.float32) * 0.5
+    K2 = (K.astype(np.float64) + u).astype(np.float32)
+    a = oracle.attend(q, K, V, np.full(2, n, np.int32))
+    b = oracle.attend(q, K2, V, np.full(2, n, np.int32))
+    # the shift is exact in f64 only up to the f32 storage of K + u
+    np.testing.assert_allclose(a, b, rtol=1e-5, atol=1e-6)
+    # exact version: shift along a direction orthogonal to q leaves scores untouched
+    qv = q[0, 0].astype(np.float64)
+    w = np.zeros(D)
+    w[0], w[1] = qv[1], -qv[0]            # q . w = 0 exactly in f64
+    Kd = K[:1, :1].astype(np.float64) + w
+    s1 = (Kd[0, 0] @ qv) * 0.125
+    s0 = (K[0, 0].astype(np.float64) @ qv) * 0.125
+    np.testing.assert_allclose(s1, s0, rtol=0, atol=1e-12)
+
+
+def test_row_permutation_invariance():
+    rng = _rng(15)
+    n = 45
+    q = rng.standard_normal((1, 2, D)).astype(np.float32)
+    K, V = _cache(rng, 1, 2, n)
+    perm = rng.permutation(n)
+    a = oracle.attend(q, K, V, np.array([n], np.int32))
+    b = oracle.attend(q, np.ascontiguousarray(K[:, :, perm]), np.ascontiguousarray(V[:, :, perm]),
+                      np.array([n], np.int32))
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
+def test_rows_beyond_length_are_never_read():
+    rng = _rng(16)
+    q = rng.standard_normal((3, 2, D)).astype(np.float32)
+    K, V = _cache(rng, 3, 2, 64)
+    lens = np.array([1, 17, 63], np.int32)
+    ref = oracle.attend(q, K, V, lens)
+    for b, n in enumerate(lens):
+        K[b, :, n:] = np.nan
+        V[b, :, n:] = np.nan
+    out = oracle.attend(q, K, V, lens)
+    assert np.array_equal(out, ref)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (6, 2), (16, 4)])
+def test_incremental_decode_equals_last_row_of_reprefill(Hq, Hkv):
+    """Decode with append over T steps == last row of a full-causal re-prefill.
+
+    The re-prefill route is the O(n^2) parity path of franken_ocr's
+    `generate_greedy`; the decode route appends then attends every cached row.
+    """
+    rng = _rng(17 + Hq)
+    T, cap = 12, 64
+    Q = rng.standard_normal((T, Hq, D)).astype(np.float32)
+    Kt = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    Vt = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    Kc = np.full((1, Hkv, cap, D), np.nan, np.float32)
+    Vc = np.full((1, Hkv, cap, D), np.nan, np.float32)
+    lens = np.zeros(1, np.int32)
+    full = oracle.prefill_causal(Q, Kt, Vt)
+    for t in range(T):
+        lens = oracle.append(Kc, Vc, Kt[None, t], Vt[None, t], lens)
+        step = oracle.attend(Q[None, t], Kc, Vc, lens)
+        np.testing.assert_allclose(step[0], full[t], rtol=1e-12, atol=1e-14)
+    # and the re-prefill's last row, recomputed from scratch over all T positions
+    last = oracle.prefill_causal(Q, Kt, Vt)[-1]
+    np.testing.assert_allclose(oracle.attend(Q[None, T - 1], Kc, Vc, lens)[0], last,
+                               rtol=1e-12, atol=1e-14)
+
+
+def test_reprefill_rows_are_causal():
+    # Row i of the prefill must not change when later positions change.
+    rng = _rng(18)
+    n = 9
+    Q = rng.standard_normal((n, 2, D))
+    K = rng.standard_normal((n, 2, D))
+    V = rng.standard_normal((n, 2, D))
+    a = oracle.prefill_causal(Q, K, V)
+    K2, V2 = K.copy(), V.copy()
+    K2[5:] += 3.0
+    V2[5:] -= 1.0
+    b = oracle.prefill_causal(Q, K2, V2)
+    assert np.array_equal(a[:5], b[:5])
+    assert not np.allclose(a[5:], b[5:])
+
+
+def test_gqa_equals_broadcast_mha_bitwise():
+    # franken_ocr `gqa_decode_attention_matches_broadcast_mha_reference` idea, at head_dim 64.
+    rng = _rng(19)
+    B, Hq, Hkv, cap = 3, 16, 4, 40
+    group = Hq // Hkv
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    K, V = _cache(rng, B, Hkv, cap)
+    lens = np.array([1, 23, 40], np.int32)
+    gqa = oracle.attend(q, K, V, lens)
+    Kb = np.repeat(K, group, axis=1)
+    Vb = np.repeat(V, group, axis=1)
+    mha = oracle.attend(q, Kb, Vb, lens)
+    assert np.array_equal(gqa, mha)
+
+
+def test_golden_gqa_head_mapping():
+    with open(os.path.join(GOLDEN, "gqa_broadcast_mapping.json")) as f:
+        g = json.load(f)
+    Hq, Hkv, d = g["n_q_heads"], g["n_kv_heads"], g["head_dim"]
+    rng = _rng(20)
+    for row, expect in zip(g["kv_rows"], g["broadcast_rows"]):
+        # one cached position: attention returns that position's V for every head
+        V = np.array(row, np.float32).reshape(1, Hkv, 1, d)
+        K = rng.standard_normal((1, Hkv, 1, d)).astype(np.float32)
+        q = rng.standard_normal((1, Hq, d)).astype(np.float32)
+        out = oracle.attend(q, K, V, np.array([1], np.int32))
+        assert out.reshape(-1).tolist() == expect
+
+
+def test_matches_torch_sdpa_float64():
+    rng = _rng(21)
+    B, Hq, Hkv, cap = 2, 8, 2, 70
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    K, V = _cache(rng, B, Hkv, cap)
+    lens = np.array([70, 31], np.int32)
+    out = oracle.attend(q, K, V, lens)
+    g = Hq // Hkv
+    for b in range(B):
+        n = lens[b]
+        qt = torch.from_numpy(q[b].astype(np.float64))[:, None, :]                # [Hq,1,D]
+        kt = torch.from_numpy(np.repeat(K[b, :, :n], g, 0).astype(np.float64))    # [Hq,n,D]
+        vt = torch.from_numpy(np.repeat(V[b, :, :n], g, 0).astype(np.float64))
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=0.125)
+        np.testing.assert_allclose(out[b], ref[:, 0].numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_bf16_storage_is_read_exactly():
+    # bf16 bit patterns with known values: 0x3F80 = 1, 0xC000 = -2, 0x3E00 = 0.125,
+    # 0x4049 = 3.140625 (pi truncated to 8 mantissa bits).
+    bits = np.array([0x3F80, 0xC000, 0x3E00, 0x4049], np.uint16)
+    assert oracle.bf16_to_f32(bits).tolist() == [1.0, -2.0, 0.125, 3.140625]
+    # n = 1 returns V[0] exactly, also through the bf16 reader
+    V = np.zeros((1, 1, 1, D), np.uint16)
+    V[0, 0, 0, :4] = bits
+    K = np.zeros((1, 1, 1, D), np.uint16)
+    q = np.ones((1, 1, D), np.float32)
+    out = oracle.attend(q, K, V, np.array([1], np.int32))
+    assert out[0, 0, :4].tolist() == [1.0, -2.0, 0.125, 3.140625]
+
+
+def test_bf16_cache_equals_f32_cache_of_the_widened_values():
+    rng = _rng(22)
+    q = rng.standard_normal((2, 4, D)).astype(np.float32)
+    K, V = _cache(rng, 2, 2, 33)
+    Kb, Vb = gen.f32_to_bf16_bits(K), gen.f32_to_bf16_bits(V)
+    lens = np.array([33, 5], np.int32)
+    a = oracle.attend(q, Kb, Vb, lens)
+    b = oracle.attend(q, oracle.bf16_to_f32(Kb), oracle.bf16_to_f32(Vb), lens)
+    assert np.array_equal(a, b)
+
+
+def test_fail_closed_nan_and_empty():
+    # lattice-inference `full_attention_step_q8`: a non-finite score row gives zeros.
+    rng = _rng(23)
+    q = rng.standard_normal((3, 2, D)).astype(np.float32)
+    K, V = _cache(rng, 3, 2, 16)
+    q[1, 0, 5] = np.nan
+    q[2, 1, 0] = np.inf
+    lens = np.array([0, 16, 16], np.int32)
+    out = oracle.attend(q, K, V, lens)
+    assert np.all(out[0] == 0.0)          # empty key set
+    assert np.all(out[1, 0] == 0.0)       # NaN score row
+    assert np.all(np.isfinite(out[1, 1])) and np.any(out[1, 1] != 0.0)
+    # q with +inf: scores are +/-inf or NaN; the row must come out finite (zeros)
+    assert np.all(np.isfinite(out[2, 1]))
+
+
+def test_oracle_rejects_bad_grouping():
+    q = np.zeros((1, 6, D), np.float32)
+    K = np.zeros((1, 4, 1, D), np.float32)
+    with pytest.raises(ValueError):
+        oracle.attend(q, K, K, np.array([1], np.int32))
+
+
+def test_append_writes_exactly_one_row_per_head():
+    rng = _rng(24)
+    B, Hkv, cap = 3, 2, 64
+    for dt in (np.float32, np.uint16):
+        if dt == np.float32:
+            Kc = rng.standard_normal((B, Hkv, cap, D)).astype(dt)
+            kn = rng.standard_normal((B, Hkv, D)).astype(dt)
+        else:
+            Kc = rng.integers(0, 2**16, (B, Hkv, cap, D)).astype(dt)
+            kn = rng.integers(0, 2**16, (B, Hkv, D)).astype(dt)
+        Vc = Kc[::-1].copy()
+        vn = kn[::-1].copy()
+        K0, V0 = Kc.copy(), Vc.copy()
+        lens = np.array([0, 5, 63], np.int32)
+        new = oracle.append(Kc, Vc, kn, vn, lens)
+        assert new.tolist() == [1, 6, 64]
+        for b in range(B):
+            changed = np.argwhere(np.any(Kc[b].view(np.uint8) != K0[b].view(np.uint8), axis=-1))
+            assert all(r == lens[b] for _, r in changed)
+            assert Kc[b, :, lens[b]].tobytes() == kn[b].tobytes()
+            assert Vc[b, :, lens[b]].tobytes() == vn[b].tobytes()
+            mask = np.ones(cap, bool)
+            mask[lens[b]] = False
+            assert Kc[b][:, mask].tobytes() == K0[b][:, mask].tobytes()
+            assert Vc[b][:, mask].tobytes() == V0[b][:, mask].tobytes()
+
+
+def test_append_overflow_writes_nothing():
+    Kc = np.zeros((2, 1, 4, D), np.float32)
+    Vc = np.zeros_like(Kc)
+    kn = np.ones((2, 1, D), np.float32)
+    with pytest.raises(ValueError):
+        oracle.append(Kc, Vc, kn, kn, np.array([1, 4], np.int32))
+    assert not Kc.any() and not Vc.any()
+
+
+def test_seed_is_the_head_first_permute():
+    # token-major [B][rows][H*D] -> head-major [B][H][cap][D]; tiny hand-checked case
+    B, rows, H, d, cap = 1, 3, 2, 2, 4
+    src = np.arange(B * rows * H * d, dtype=np.float32).reshape(B, rows, H * d)
+    dst = np.full((B, H, cap, d), -1.0, np.float32)
+    oracle.load()
+    import ctypes
+    rc = oracle.oracle.load().kvdec_oracle_seed(dst.ctypes.data_as(ctypes.c_void_p),
+                                                src.ctypes.data_as(ctypes.c_void_p),
+                                                4, B, rows, H, d, cap)
+    assert rc == 0
+    # head 0 takes lanes [0,1] of every token row, head 1 lanes [2,3]
+    assert dst[0, 0, :3].tolist() == [[0, 1], [4, 5], [8, 9]]
+    assert dst[0, 1, :3].tolist() == [[2, 3], [6, 7], [10, 11]]
+    assert dst[0, :, 3].tolist() == [[-1, -1], [-1, -1]]
+
+
+# ---- pins of the seeded input generator (shared by both sides) -----------------
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, 1.0 + 2**-9, -2.5, np.nan], np.float32)
+    bits = gen.f32_to_bf16_bits(x)
+    # 1+2^-8 is a tie between 1 and 1+2^-7 -> even (1.0); 1+3*2^-8 ties up to 1+2^-6
+    assert oracle.bf16_to_f32(bits[:5]).tolist() == [1.0, 1.0, 1.0 + 2**-6, 1.0, -2.5]
+    assert np.isnan(oracle.bf16_to_f32(bits[5:])[0])
+
+
+def test_rope_is_stride_half_and_relative():
+    rng = _rng(25)
+    x = rng.standard_normal((5, D)).astype(np.float32)
+    # position 0 is the identity
+    assert np.allclose(gen.rope_rotate(x, np.zeros(5), 1e6), x, atol=0)
+    # each pair (i, i+32) keeps its norm
+    y = gen.rope_rotate(x, np.arange(5) * 100 + 7, 1e6).astype(np.float64)
+    xd = x.astype(np.float64)
+    np.testing.assert_allclose(y[:, :32] ** 2 + y[:, 32:] ** 2, xd[:, :32] ** 2 + xd[:, 32:] ** 2,
+                               rtol=1e-5)
+    # pair (0, 32) rotates by the position itself (inv_freq_0 = 1): e_0 -> cos p e_0 + sin p e_32
+    e0 = np.zeros((1, D), np.float32)
+    e0[0, 0] = 1.0
+    r = gen.rope_rotate(e0, np.array([1.0]), 1e6)[0]
+    assert abs(r[0] - math.cos(1.0)) < 1e-7 and abs(r[32] - math.sin(1.0)) < 1e-7
+    assert np.all(r[1:32] == 0) and np.all(r[33:] == 0)
+    # scores depend on relative position only
+    q, k = x[0], x[1]
+    def s(m, n):
+        return float(gen.rope_rotate(q[None], np.array([m]), 1e6)[0].astype(np.float64)
+                     @ gen.rope_rotate(k[None], np.array([n]), 1e6)[0].astype(np.float64))
+    assert abs(s(10, 3) - s(110, 103)) < 1e-4
+    assert abs(s(10, 3) - s(10, 4)) > 1e-3
+
+
+def test_generator_is_deterministic_and_canaried():
+    wl = gen.WORKLOADS["qwen2-0.5b"]
+    a = gen.make_inputs(wl, batch=3, lens=np.array([1, 70, 5], np.int32))
+    b = gen.make_inputs(wl, batch=3, lens=np.array([1, 70, 5], np.int32))
+    assert a.k_cache.tobytes() == b.k_cache.tobytes()
+    assert a.cap == 128
+    assert np.isnan(a.k_cache[0, :, 1:]).all() and not np.isnan(a.k_cache[0, :, :1]).any()
+    assert np.isnan(a.v_cache[2, :, 5:]).all() and not np.isnan(a.v_cache[2, :, :5]).any()
+
+
+def test_workload_lengths_follow_their_laws():
+    rng = _rng(26)
+    x = gen.draw_lens(rng, "loguniform:16:8192", 20000)
+    assert x.min() >= 16 and x.max() <= 8192
+    # log-uniform on [16, 8192]: mean = (8192 - 16) / ln(512)
+    assert abs(x.mean() - (8192 - 16) / math.log(512)) < 40
+    u = gen.draw_lens(rng, "uniform:1:4096", 20000)
+    assert u.min() >= 1 and u.max() <= 4096 and abs(u.mean() - 2048.5) < 30
