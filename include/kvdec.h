@@ -1,0 +1,186 @@
+/*
+ * kvdec.h -- C ABI of libkvdec.so: the single-token KV-cached decode step
+ * (append the new token's K/V rows, then attend one query per head over the
+ * cached rows and, for encoder-decoder models, over static encoder K/V) on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (docs.rs source pages; cited by page and item):
+ *   [WA-DEC]  whisper-apr 0.3.3, src/model/decoder_generated.rs
+ *   [WA-CUDA] whisper-apr 0.3.0, src/cuda/impl_generated.rs
+ *   [FO-Q2]   franken_ocr 0.8.0, src/native_engine/decoder_qwen2.rs
+ *   [CERA]    cera 0.5.4, src/model/whisper.rs
+ *   [LAT-Q8]  lattice-inference 0.4.0, src/forward/cpu_q8.rs
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked (device) are HIP device pointers; (host) are host
+ *     pointers.  All device memory (caches, lengths, q, out, workspace) is
+ *     owned by the caller; the library never allocates, frees or keeps
+ *     device memory, never synchronises and never creates streams.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *     Work is enqueued asynchronously on it, in call order.
+ *   - Device pointers must be non-NULL and 16-byte aligned.
+ *   - Return value: KVDEC_OK or a kvdec_status error code.  On error nothing
+ *     has been enqueued and no device or host state has changed;
+ *     kvdec_last_error() describes the failure (thread-local string).
+ *   - head_dim is 64.  K/V elements are IEEE binary32 (KVDEC_F32) or
+ *     bfloat16 bit patterns (KVDEC_BF16); q and out are always binary32.
+ */
+#ifndef KVDEC_H
+#define KVDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVDEC_OK = 0,
+    KVDEC_E_INVALID = 1,   /* NULL / misaligned pointer, non-positive size, unknown dtype */
+    KVDEC_E_SHAPE = 2,     /* head_dim != 64, heads not a multiple of KV heads, rows > capacity */
+    KVDEC_E_OVERFLOW = 3,  /* an append would exceed a sequence's capacity */
+    KVDEC_E_STATIC = 4,    /* append/self-attend on a static (encoder) cache, or cross on a dynamic one */
+    KVDEC_E_WORKSPACE = 5, /* workspace smaller than kvdec_workspace_bytes() */
+    KVDEC_E_HIP = 6        /* a HIP launch failed; see kvdec_last_error() */
+} kvdec_status;
+
+typedef enum { KVDEC_F32 = 0, KVDEC_BF16 = 1 } kvdec_dtype;
+
+#define KVDEC_HEAD_DIM 64
+#define KVDEC_ROW_ALIGN 64     /* padded capacity granule, rows */
+#define KVDEC_MIN_CHUNK 64     /* smallest split-sequence chunk, rows */
+#define KVDEC_MAX_CHUNK 4096   /* largest split-sequence chunk, rows */
+#define KVDEC_MAX_GROUP 8      /* query heads per KV head supported */
+
+/* Opaque host-side handle: the cache description plus a host mirror of the
+ * per-sequence lengths (used for validation and launch sizing, so no call
+ * ever reads the lengths back from the device). */
+typedef struct kvdec_cache kvdec_cache;
+
+/*
+ * Cache description.  Layout is head-major and padded:
+ *   k, v : (device) [batch][n_kv_heads][kvdec_padded_capacity(capacity)][64]
+ *          elements of `dtype`.  One row is 256 B (f32) or 128 B (bf16), so a
+ *          (sequence, KV head) pair is one contiguous run of rows.
+ *   lens : (device) int32[batch], rows currently held per sequence.
+ * This is the head-first GPU cache of [WA-CUDA]
+ * `init_gpu_decoder_kv_cache_head_first` ([n_heads, max_seq_len, head_dim] per
+ * layer) extended by a batch axis and row padding; one handle is one layer's
+ * self-attention cache (is_static = 0) or one layer's encoder cross-attention
+ * cache (is_static = 1; [CERA] `WhisperCrossAttentionCache`, computed once per
+ * audio and never appended to).
+ */
+typedef struct {
+    int32_t batch;       /* sequences, >= 1 */
+    int32_t n_kv_heads;  /* KV heads, >= 1 */
+    int32_t head_dim;    /* must be 64 */
+    int32_t capacity;    /* rows each sequence may hold, >= 1 */
+    int32_t dtype;       /* kvdec_dtype */
+    int32_t is_static;   /* 0: self cache (appendable); 1: static encoder cache */
+    void* k;             /* (device) */
+    void* v;             /* (device) */
+    int32_t* lens;       /* (device) */
+} kvdec_cache_desc;
+
+/* Rows per (sequence, KV head) actually laid out for `capacity`: capacity
+ * rounded up to a multiple of KVDEC_ROW_ALIGN.  Returns 0 for capacity < 1. */
+int32_t kvdec_padded_capacity(int32_t capacity);
+
+/* Create a handle over caller-owned memory and write the initial lengths
+ * lens_host[batch] (host) to desc->lens on `stream`.  Cache contents are not
+ * touched.  Errors: KVDEC_E_INVALID (NULL/misaligned pointers, batch < 1,
+ * unknown dtype), KVDEC_E_SHAPE (head_dim != 64, a length outside
+ * [0, capacity]).  *out receives the handle (host). */
+int32_t kvdec_cache_create(const kvdec_cache_desc* desc, const int32_t* lens_host,
+                           void* stream, kvdec_cache** out);
+
+/* Release the handle (host memory only; the caller's device memory is not freed). */
+void kvdec_cache_destroy(kvdec_cache* cache);
+
+/* Set every sequence's length from lens_host[batch] (host), device and mirror,
+ * leaving cache rows untouched ([WA-DEC] `LayerKVCache::reset` keeps the
+ * storage).  Errors: KVDEC_E_INVALID, KVDEC_E_SHAPE (length outside
+ * [0, capacity]). */
+int32_t kvdec_reset_lens(kvdec_cache* cache, const int32_t* lens_host, void* stream);
+
+/* Copy the host mirror of the lengths into lens_out[batch] (host).  No device access. */
+int32_t kvdec_get_lens(const kvdec_cache* cache, int32_t* lens_out);
+
+/*
+ * Seed rows [0, rows) of every sequence from token-major data and set every
+ * length to `rows`: the interleaved-to-head-first permute [L, H*64] ->
+ * [H, L, 64] of [WA-CUDA] `populate_cross_kv_caches_gpu` (encoder K/V), also
+ * usable for a prefill of the self cache ([FO-Q2] `Qwen2KvCache::seed`).
+ *   k_tok, v_tok : (device) [batch][rows][n_kv_heads*64] elements of dtype.
+ * Allowed on static and dynamic caches.  Errors: KVDEC_E_INVALID,
+ * KVDEC_E_SHAPE (rows < 0 or rows > capacity).
+ */
+int32_t kvdec_seed(kvdec_cache* cache, const void* k_tok, const void* v_tok, int32_t rows,
+                   void* stream);
+
+/*
+ * Append one token: for every sequence b and KV head g, copy k_new[b][g][:]
+ * and v_new[b][g][:] into row lens[b] of the cache, then lens[b] += 1.
+ *   k_new, v_new : (device) [batch][n_kv_heads][64] elements of the cache dtype.
+ * A pure byte copy (bit-exact, no conversion): [WA-DEC]
+ * `LayerKVCache::append`, [FO-Q2] `Qwen2KvCache::append`, and the head-first
+ * scatter at row `pos` of [WA-CUDA] `kv_cache_scatter_gpu`.
+ * Errors: KVDEC_E_OVERFLOW when any lens[b] + 1 > capacity -- checked before
+ * anything is enqueued, like the "cache overflow" check of
+ * `LayerKVCache::append`; KVDEC_E_STATIC on a static cache; KVDEC_E_INVALID.
+ */
+int32_t kvdec_append(kvdec_cache* cache, const void* k_new, const void* v_new, void* stream);
+
+/* Workspace bytes any attend call on `cache` with n_q_heads query heads may
+ * need (split-sequence partial results).  0 on invalid arguments. */
+size_t kvdec_workspace_bytes(const kvdec_cache* cache, int32_t n_q_heads);
+
+/*
+ * Decode attention of one query per head over the cached rows of each
+ * sequence (self-attention; the cache must be dynamic):
+ *   out[b][h][:] = sum_j softmax_j(scale * q[b][h] . K[b][g][j]) * V[b][g][j][:]
+ * for j < lens[b], g = h / (n_q_heads / n_kv_heads).
+ *   q   : (device) float [batch][n_q_heads][64]
+ *   out : (device) float [batch][n_q_heads][64]
+ *   ws  : (device) workspace of ws_bytes >= kvdec_workspace_bytes(cache, n_q_heads)
+ * Semantics follow [FO-Q2] `decode_attn_head` / `qwen2_decode_attention`
+ * (every cached row attended, no mask: causality is implicit because the
+ * cache holds only positions <= the current one, the current one included
+ * after kvdec_append), [LAT-Q8] `full_attention_step_q8` (GQA mapping
+ * kvh = qh / groups; a softmax denominator that is not > 0, e.g. from a NaN
+ * score, yields a zero output row) and [CERA] `multi_head_attention`.
+ * A sequence with length 0 yields a zero row.  scale is usually 1/sqrt(64).
+ * chunk_rows: rows per split-sequence chunk; 0 picks automatically, else a
+ * multiple of 64 in [KVDEC_MIN_CHUNK, KVDEC_MAX_CHUNK].  The result for a
+ * sequence does not depend on the other sequences in the batch.
+ * Errors: KVDEC_E_SHAPE (n_q_heads not a positive multiple of n_kv_heads, or
+ * group > KVDEC_MAX_GROUP), KVDEC_E_STATIC, KVDEC_E_WORKSPACE, KVDEC_E_INVALID,
+ * KVDEC_E_HIP.
+ */
+int32_t kvdec_attend_self(const kvdec_cache* cache, const float* q, int32_t n_q_heads,
+                          float scale, int32_t chunk_rows, float* out, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * Cross-attention over a static encoder cache: the same computation as
+ * kvdec_attend_self over every seeded row (1500 for Whisper's 30 s window),
+ * with the decoder's cross query: [CERA] `decode_step_into` cross block and
+ * [WA-CUDA] `forward_decoder_block_gpu_stream` (incremental attention with
+ * seq_len = encoder length).  The cache must be static (KVDEC_E_STATIC otherwise).
+ */
+int32_t kvdec_attend_cross(const kvdec_cache* cache, const float* q, int32_t n_q_heads,
+                           float scale, int32_t chunk_rows, float* out, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* kvdec_status_str(int32_t status);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* kvdec_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVDEC_H */

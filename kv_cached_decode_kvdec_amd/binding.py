@@ -1,0 +1,145 @@
+"""ctypes binding of libkvdec.so (include/kvdec.h), same names as the C ABI.
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of libkvdec.so.  If the library is missing, load() raises -- there
+is no fallback path of any kind.  PyTorch is used for device memory and the
+current HIP stream.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvdec.so")
+
+KVDEC_OK = 0
+KVDEC_E_INVALID = 1
+KVDEC_E_SHAPE = 2
+KVDEC_E_OVERFLOW = 3
+KVDEC_E_STATIC = 4
+KVDEC_E_WORKSPACE = 5
+KVDEC_E_HIP = 6
+KVDEC_F32 = 0
+KVDEC_BF16 = 1
+HEAD_DIM = 64
+MIN_CHUNK = 64
+MAX_CHUNK = 4096
+MAX_GROUP = 8
+
+EXPORTED = [
+    "kvdec_padded_capacity", "kvdec_cache_create", "kvdec_cache_destroy", "kvdec_reset_lens",
+    "kvdec_get_lens", "kvdec_seed", "kvdec_append", "kvdec_workspace_bytes",
+    "kvdec_attend_self", "kvdec_attend_cross", "kvdec_status_str", "kvdec_last_error",
+]
+
+
+class KvdecError(RuntimeError):
+    def __init__(self, code, where, detail):
+        super().__init__(f"{where}: {detail} (status {code})")
+        self.code = code
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("is_static", ctypes.c_int32),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("lens", ctypes.c_void_p)]
+
+
+_lib = None
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+
+
+def load():
+    """Load libkvdec.so; raises ImportError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import "
+                          f"__graft_entry__ as g; g.build()'` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "kvdec_padded_capacity": (_i32, [_i32]),
+        "kvdec_cache_create": (_i32, [ctypes.POINTER(CacheDesc), _vp, _vp, ctypes.POINTER(_vp)]),
+        "kvdec_cache_destroy": (None, [_vp]),
+        "kvdec_reset_lens": (_i32, [_vp, _vp, _vp]),
+        "kvdec_get_lens": (_i32, [_vp, _vp]),
+        "kvdec_seed": (_i32, [_vp, _vp, _vp, _i32, _vp]),
+        "kvdec_append": (_i32, [_vp, _vp, _vp, _vp]),
+        "kvdec_workspace_bytes": (_sz, [_vp, _i32]),
+        "kvdec_attend_self": (_i32, [_vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz, _vp]),
+        "kvdec_attend_cross": (_i32, [_vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz, _vp]),
+        "kvdec_status_str": (ctypes.c_char_p, [_i32]),
+        "kvdec_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(code, where):
+    if code != KVDEC_OK:
+        lib = load()
+        raise KvdecError(code, where, lib.kvdec_last_error().decode() or
+                         lib.kvdec_status_str(code).decode())
+
+
+def _int_array(vals):
+    arr = (ctypes.c_int32 * len(vals))(*[int(v) for v in vals])
+    return arr
+
+
+# --- thin wrappers, one per C entry point --------------------------------------
+
+def kvdec_padded_capacity(capacity):
+    return load().kvdec_padded_capacity(int(capacity))
+
+
+def kvdec_cache_create(desc, lens_host, stream=None):
+    h = _vp()
+    arr = _int_array(lens_host)
+    _check(load().kvdec_cache_create(ctypes.byref(desc), arr, stream, ctypes.byref(h)),
+           "kvdec_cache_create")
+    return h
+
+
+def kvdec_cache_destroy(handle):
+    if handle:
+        load().kvdec_cache_destroy(handle)
+
+
+def kvdec_reset_lens(handle, lens_host, stream=None):
+    _check(load().kvdec_reset_lens(handle, _int_array(lens_host), stream), "kvdec_reset_lens")
+
+
+def kvdec_get_lens(handle, batch):
+    arr = (ctypes.c_int32 * batch)()
+    _check(load().kvdec_get_lens(handle, arr), "kvdec_get_lens")
+    return list(arr)
+
+
+def kvdec_seed(handle, k_tok_ptr, v_tok_ptr, rows, stream=None):
+    _check(load().kvdec_seed(handle, k_tok_ptr, v_tok_ptr, int(rows), stream), "kvdec_seed")
+
+
+def kvdec_append(handle, k_new_ptr, v_new_ptr, stream=None):
+    _check(load().kvdec_append(handle, k_new_ptr, v_new_ptr, stream), "kvdec_append")
+
+
+def kvdec_workspace_bytes(handle, n_q_heads):
+    return load().kvdec_workspace_bytes(handle, int(n_q_heads))
+
+
+def kvdec_attend_self(handle, q_ptr, n_q_heads, scale, chunk_rows, out_ptr, ws_ptr, ws_bytes,
+                      stream=None):
+    _check(load().kvdec_attend_self(handle, q_ptr, int(n_q_heads), float(scale), int(chunk_rows),
+                                    out_ptr, ws_ptr, int(ws_bytes), stream), "kvdec_attend_self")
+
+
+def kvdec_attend_cross(handle, q_ptr, n_q_heads, scale, chunk_rows, out_ptr, ws_ptr, ws_bytes,
+                       stream=None):
+    _check(load().kvdec_attend_cross(handle, q_ptr, int(n_q_heads), float(scale), int(chunk_rows),
+                                     out_ptr, ws_ptr, int(ws_bytes), stream), "kvdec_attend_cross")

@@ -1,0 +1,121 @@
+"""PyTorch-facing helpers over the C ABI: device tensors in, device tensors out.
+
+KVCache owns torch tensors for one layer's K/V cache and lengths and a
+libkvdec handle over them.  Every method only checks shapes/dtypes and
+passes pointers to libkvdec.so; all work is done by its HIP kernels on the
+current torch stream.
+"""
+import ctypes
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+_TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+_CODE = {"f32": B.KVDEC_F32, "bf16": B.KVDEC_BF16}
+
+
+def current_stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def to_device(x, device="cuda"):
+    """numpy f32 / uint16-as-bf16-bits / int32 array -> device tensor (bit-exact)."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(x).to(device)
+
+
+def to_host_bits(t):
+    """device tensor -> numpy with the same bits (bf16 comes back as uint16)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class KVCache:
+    def __init__(self, batch, n_kv_heads, capacity, dtype="f32", static=False, lens=None,
+                 device="cuda", k=None, v=None):
+        self.batch, self.n_kv_heads, self.capacity = int(batch), int(n_kv_heads), int(capacity)
+        self.dtype, self.static = dtype, bool(static)
+        self.cap_pad = B.kvdec_padded_capacity(capacity)
+        shape = (self.batch, self.n_kv_heads, self.cap_pad, B.HEAD_DIM)
+        tdt = _TORCH_DTYPE[dtype]
+        self.k = torch.zeros(shape, dtype=tdt, device=device) if k is None else k
+        self.v = torch.zeros(shape, dtype=tdt, device=device) if v is None else v
+        for t in (self.k, self.v):
+            if tuple(t.shape) != shape or t.dtype != tdt or not t.is_contiguous():
+                raise ValueError(f"cache tensor must be contiguous {shape} {tdt}")
+        self.lens_dev = torch.zeros(self.batch, dtype=torch.int32, device=device)
+        self.desc = B.CacheDesc(self.batch, self.n_kv_heads, B.HEAD_DIM, self.capacity,
+                                _CODE[dtype], int(self.static), self.k.data_ptr(),
+                                self.v.data_ptr(), self.lens_dev.data_ptr())
+        lens = [0] * self.batch if lens is None else [int(x) for x in lens]
+        self.handle = B.kvdec_cache_create(self.desc, lens, current_stream())
+        self._ws = {}
+
+    # --- state -------------------------------------------------------------
+    def lens(self):
+        return B.kvdec_get_lens(self.handle, self.batch)
+
+    def reset_lens(self, lens):
+        B.kvdec_reset_lens(self.handle, [int(x) for x in lens], current_stream())
+
+    def close(self):
+        if getattr(self, "handle", None):
+            B.kvdec_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # --- operations ---------------------------------------------------------
+    def _check_rows(self, t, shape, name):
+        if t.dtype != self.k.dtype or tuple(t.shape) != shape or not t.is_contiguous() \
+                or t.device != self.k.device:
+            raise ValueError(f"{name} must be a contiguous {shape} {self.k.dtype} tensor on "
+                             f"{self.k.device}")
+
+    def seed(self, k_tok, v_tok):
+        rows = k_tok.shape[1]
+        shape = (self.batch, rows, self.n_kv_heads * B.HEAD_DIM)
+        self._check_rows(k_tok, shape, "k_tok")
+        self._check_rows(v_tok, shape, "v_tok")
+        B.kvdec_seed(self.handle, _ptr(k_tok), _ptr(v_tok), rows, current_stream())
+
+    def append(self, k_new, v_new):
+        shape = (self.batch, self.n_kv_heads, B.HEAD_DIM)
+        self._check_rows(k_new, shape, "k_new")
+        self._check_rows(v_new, shape, "v_new")
+        B.kvdec_append(self.handle, _ptr(k_new), _ptr(v_new), current_stream())
+
+    def workspace(self, n_q_heads):
+        ws = self._ws.get(n_q_heads)
+        if ws is None:
+            nbytes = B.kvdec_workspace_bytes(self.handle, n_q_heads)
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=self.k.device)
+            self._ws[n_q_heads] = ws
+        return ws
+
+    def attend(self, q, scale=0.125, chunk_rows=0, out=None):
+        Hq = q.shape[1]
+        if q.dtype != torch.float32 or q.dim() != 3 or q.shape[0] != self.batch \
+                or q.shape[2] != B.HEAD_DIM or not q.is_contiguous() or q.device != self.k.device:
+            raise ValueError("q must be a contiguous float32 [batch, n_q_heads, 64] device tensor")
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self.workspace(Hq)
+        fn = B.kvdec_attend_cross if self.static else B.kvdec_attend_self
+        fn(self.handle, _ptr(q), Hq, scale, chunk_rows, _ptr(out), _ptr(ws), ws.numel(),
+           current_stream())
+        return out

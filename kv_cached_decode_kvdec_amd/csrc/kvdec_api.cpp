@@ -1,0 +1,274 @@
+// Host side of libkvdec.so: argument validation, the host mirror of the
+// per-sequence lengths, chunk-size choice and workspace sizing.  Every check
+// runs before anything is enqueued, so an error leaves device and host state
+// unchanged.  No device memory is allocated and no call synchronises.
+#include "../../include/kvdec.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kvdec_internal.h"
+
+struct kvdec_cache {
+    kvdec_cache_desc d;
+    int32_t cap_pad;
+    std::vector<int32_t> lens;   // host mirror of d.lens
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t esz_of(int32_t dtype) { return dtype == KVDEC_F32 ? 4 : 2; }
+
+int32_t hip_fail(hipError_t e, const char* what)
+{
+    return fail(KVDEC_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int32_t check_lens(const int32_t* lens_host, int32_t batch, int32_t capacity)
+{
+    if (!lens_host) return fail(KVDEC_E_INVALID, "lens_host is NULL");
+    for (int32_t b = 0; b < batch; ++b)
+        if (lens_host[b] < 0 || lens_host[b] > capacity)
+            return fail(KVDEC_E_SHAPE, "length %d of sequence %d outside [0, %d]", lens_host[b], b,
+                        capacity);
+    return KVDEC_OK;
+}
+
+int64_t chunks_for(const std::vector<int32_t>& lens, int32_t T)
+{
+    int64_t n = 0;
+    for (int32_t l : lens) n += (static_cast<int64_t>(l) + T - 1) / T;
+    return n;
+}
+
+// Automatic chunk size: the largest power-of-two chunk (64 .. 4096 rows)
+// that still gives at least kTargetBlocks workgroups, so every one of the
+// 256 compute units gets several chunks while partial traffic stays small.
+constexpr int64_t kTargetBlocks = 2048;
+
+int32_t auto_chunk(const std::vector<int32_t>& lens, int32_t n_kv_heads)
+{
+    for (int32_t T = KVDEC_MAX_CHUNK; T > KVDEC_MIN_CHUNK; T >>= 1)
+        if (chunks_for(lens, T) * n_kv_heads >= kTargetBlocks) return T;
+    return KVDEC_MIN_CHUNK;
+}
+
+int64_t max_chunks(const kvdec_cache* c)
+{
+    return static_cast<int64_t>(c->d.batch) * ((c->cap_pad + KVDEC_MIN_CHUNK - 1) / KVDEC_MIN_CHUNK);
+}
+
+int32_t attend_common(const kvdec_cache* c, const float* q, int32_t n_q_heads, float scale,
+                      int32_t chunk_rows, float* out, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
+    if (!aligned16(q) || !aligned16(out))
+        return fail(KVDEC_E_INVALID, "q and out must be non-NULL, 16-byte aligned device pointers");
+    if (n_q_heads <= 0 || n_q_heads % c->d.n_kv_heads != 0)
+        return fail(KVDEC_E_SHAPE, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                    n_q_heads, c->d.n_kv_heads);
+    const int32_t group = n_q_heads / c->d.n_kv_heads;
+    if (group > KVDEC_MAX_GROUP)
+        return fail(KVDEC_E_SHAPE, "group size %d exceeds %d", group, KVDEC_MAX_GROUP);
+    if (!std::isfinite(scale)) return fail(KVDEC_E_INVALID, "scale must be finite");
+    if (chunk_rows != 0 && (chunk_rows < KVDEC_MIN_CHUNK || chunk_rows > KVDEC_MAX_CHUNK ||
+                            chunk_rows % 64 != 0))
+        return fail(KVDEC_E_INVALID, "chunk_rows %d must be 0 or a multiple of 64 in [%d, %d]",
+                    chunk_rows, KVDEC_MIN_CHUNK, KVDEC_MAX_CHUNK);
+    const kvdec::PartialLayout part = kvdec::partial_layout(max_chunks(c), n_q_heads);
+    if (!aligned16(ws) || ws_bytes < part.bytes)
+        return fail(KVDEC_E_WORKSPACE, "workspace needs %zu bytes at a 16-byte aligned address, got %zu",
+                    part.bytes, ws_bytes);
+
+    kvdec::AttendArgs a;
+    a.q = q;
+    a.k = c->d.k;
+    a.v = c->d.v;
+    a.lens = c->d.lens;
+    a.batch = c->d.batch;
+    a.n_kv_heads = c->d.n_kv_heads;
+    a.group = group;
+    a.cap_pad = c->cap_pad;
+    a.chunk_rows = chunk_rows ? chunk_rows : auto_chunk(c->lens, c->d.n_kv_heads);
+    a.n_chunks = chunks_for(c->lens, a.chunk_rows);
+    a.need_merge = false;
+    for (int32_t l : c->lens)
+        if ((l + a.chunk_rows - 1) / a.chunk_rows != 1) a.need_merge = true;
+    a.qscale = scale * 1.4426950408889634f;
+    a.out = out;
+    a.ws = ws;
+    a.part = part;
+    const hipError_t e = kvdec::launch_attend(c->d.dtype, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "attend launch");
+    return KVDEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvdec_padded_capacity(int32_t capacity)
+{
+    if (capacity < 1) return 0;
+    const int64_t p = (static_cast<int64_t>(capacity) + KVDEC_ROW_ALIGN - 1) / KVDEC_ROW_ALIGN *
+                      KVDEC_ROW_ALIGN;
+    return p > INT32_MAX ? 0 : static_cast<int32_t>(p);
+}
+
+int32_t kvdec_cache_create(const kvdec_cache_desc* desc, const int32_t* lens_host, void* stream,
+                           kvdec_cache** out)
+{
+    g_err.clear();
+    if (!desc || !out) return fail(KVDEC_E_INVALID, "desc and out must not be NULL");
+    *out = nullptr;
+    const kvdec_cache_desc& d = *desc;
+    if (d.batch < 1 || d.n_kv_heads < 1 || d.capacity < 1)
+        return fail(KVDEC_E_INVALID, "batch, n_kv_heads and capacity must be >= 1");
+    if (d.head_dim != KVDEC_HEAD_DIM)
+        return fail(KVDEC_E_SHAPE, "head_dim must be %d, got %d", KVDEC_HEAD_DIM, d.head_dim);
+    if (d.dtype != KVDEC_F32 && d.dtype != KVDEC_BF16)
+        return fail(KVDEC_E_INVALID, "unknown dtype %d", d.dtype);
+    if (d.is_static != 0 && d.is_static != 1) return fail(KVDEC_E_INVALID, "is_static must be 0 or 1");
+    if (!aligned16(d.k) || !aligned16(d.v) || !aligned16(d.lens))
+        return fail(KVDEC_E_INVALID, "k, v and lens must be non-NULL, 16-byte aligned device pointers");
+    const int32_t cap_pad = kvdec_padded_capacity(d.capacity);
+    if (cap_pad == 0) return fail(KVDEC_E_SHAPE, "capacity %d too large", d.capacity);
+    int32_t rc = check_lens(lens_host, d.batch, d.capacity);
+    if (rc) return rc;
+    kvdec_cache* c = new kvdec_cache;
+    c->d = d;
+    c->cap_pad = cap_pad;
+    c->lens.assign(lens_host, lens_host + d.batch);
+    const hipError_t e = kvdec::launch_set_lens(d.lens, lens_host, d.batch,
+                                                static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        delete c;
+        return hip_fail(e, "set lengths");
+    }
+    *out = c;
+    return KVDEC_OK;
+}
+
+void kvdec_cache_destroy(kvdec_cache* cache) { delete cache; }
+
+int32_t kvdec_reset_lens(kvdec_cache* c, const int32_t* lens_host, void* stream)
+{
+    g_err.clear();
+    if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
+    int32_t rc = check_lens(lens_host, c->d.batch, c->d.capacity);
+    if (rc) return rc;
+    const hipError_t e = kvdec::launch_set_lens(c->d.lens, lens_host, c->d.batch,
+                                                static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "set lengths");
+    c->lens.assign(lens_host, lens_host + c->d.batch);
+    return KVDEC_OK;
+}
+
+int32_t kvdec_get_lens(const kvdec_cache* c, int32_t* lens_out)
+{
+    g_err.clear();
+    if (!c || !lens_out) return fail(KVDEC_E_INVALID, "cache and lens_out must not be NULL");
+    std::memcpy(lens_out, c->lens.data(), sizeof(int32_t) * c->lens.size());
+    return KVDEC_OK;
+}
+
+int32_t kvdec_seed(kvdec_cache* c, const void* k_tok, const void* v_tok, int32_t rows, void* stream)
+{
+    g_err.clear();
+    if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
+    if (rows < 0 || rows > c->d.capacity)
+        return fail(KVDEC_E_SHAPE, "rows %d outside [0, capacity %d]", rows, c->d.capacity);
+    if (rows > 0 && (!aligned16(k_tok) || !aligned16(v_tok)))
+        return fail(KVDEC_E_INVALID, "k_tok and v_tok must be non-NULL, 16-byte aligned device pointers");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = kvdec::launch_seed(c->d.dtype, c->d.k, c->d.v, k_tok, v_tok, c->d.batch, rows,
+                                      c->d.n_kv_heads, c->cap_pad, s);
+    if (e != hipSuccess) return hip_fail(e, "seed launch");
+    std::vector<int32_t> l(c->d.batch, rows);
+    e = kvdec::launch_set_lens(c->d.lens, l.data(), c->d.batch, s);
+    if (e != hipSuccess) return hip_fail(e, "set lengths");
+    c->lens = l;
+    return KVDEC_OK;
+}
+
+int32_t kvdec_append(kvdec_cache* c, const void* k_new, const void* v_new, void* stream)
+{
+    g_err.clear();
+    if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
+    if (c->d.is_static) return fail(KVDEC_E_STATIC, "append on a static (encoder) cache");
+    if (!aligned16(k_new) || !aligned16(v_new))
+        return fail(KVDEC_E_INVALID, "k_new and v_new must be non-NULL, 16-byte aligned device pointers");
+    for (int32_t b = 0; b < c->d.batch; ++b)
+        if (c->lens[b] + 1 > c->d.capacity)
+            return fail(KVDEC_E_OVERFLOW, "cache overflow: sequence %d holds %d + 1 > %d", b,
+                        c->lens[b], c->d.capacity);
+    const hipError_t e = kvdec::launch_append(c->d.dtype, c->d.k, c->d.v, k_new, v_new, c->d.lens,
+                                              c->d.batch, c->d.n_kv_heads, c->d.capacity,
+                                              c->cap_pad, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+    for (auto& l : c->lens) ++l;
+    return KVDEC_OK;
+}
+
+size_t kvdec_workspace_bytes(const kvdec_cache* c, int32_t n_q_heads)
+{
+    if (!c || n_q_heads <= 0) return 0;
+    return kvdec::partial_layout(max_chunks(c), n_q_heads).bytes;
+}
+
+int32_t kvdec_attend_self(const kvdec_cache* c, const float* q, int32_t n_q_heads, float scale,
+                          int32_t chunk_rows, float* out, void* ws, size_t ws_bytes, void* stream)
+{
+    g_err.clear();
+    if (c && c->d.is_static)
+        return fail(KVDEC_E_STATIC, "self-attention on a static (encoder) cache; use kvdec_attend_cross");
+    return attend_common(c, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
+}
+
+int32_t kvdec_attend_cross(const kvdec_cache* c, const float* q, int32_t n_q_heads, float scale,
+                           int32_t chunk_rows, float* out, void* ws, size_t ws_bytes, void* stream)
+{
+    g_err.clear();
+    if (c && !c->d.is_static)
+        return fail(KVDEC_E_STATIC, "cross-attention needs a static (encoder) cache");
+    return attend_common(c, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
+}
+
+const char* kvdec_status_str(int32_t s)
+{
+    switch (s) {
+        case KVDEC_OK: return "ok";
+        case KVDEC_E_INVALID: return "invalid argument";
+        case KVDEC_E_SHAPE: return "shape error";
+        case KVDEC_E_OVERFLOW: return "cache overflow";
+        case KVDEC_E_STATIC: return "static/dynamic cache mismatch";
+        case KVDEC_E_WORKSPACE: return "workspace too small";
+        case KVDEC_E_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char* kvdec_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

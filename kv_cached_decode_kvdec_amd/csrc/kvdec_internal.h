@@ -1,0 +1,55 @@
+// Internal interface between the host C-ABI layer (kvdec_api.cpp) and the
+// gfx950 kernels (kvdec_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvdec {
+
+constexpr int kHeadDim = 64;
+constexpr int kLensPerLaunch = 256;   // lengths carried by value in one set-lens launch
+
+struct LensBlock {
+    int32_t v[kLensPerLaunch];
+};
+
+// Partial results of the split-sequence attention, per (chunk, query head):
+// unnormalised o[64] and (m, l) with m in log2 units.
+struct PartialLayout {
+    size_t o_offset;    // float [slots][64]
+    size_t ml_offset;   // float2 [slots]
+    size_t bytes;
+};
+
+PartialLayout partial_layout(int64_t max_chunks, int32_t n_q_heads);
+
+struct AttendArgs {
+    const float* q;
+    const void* k;
+    const void* v;
+    const int32_t* lens;
+    int32_t batch;
+    int32_t n_kv_heads;
+    int32_t group;          // query heads per KV head
+    int32_t cap_pad;        // padded rows per (sequence, KV head)
+    int32_t chunk_rows;     // rows per split-sequence chunk
+    int64_t n_chunks;       // sum over sequences of ceil(len / chunk_rows)
+    bool need_merge;        // some sequence has != 1 chunk
+    float qscale;           // scale * log2(e)
+    float* out;
+    void* ws;
+    PartialLayout part;
+};
+
+hipError_t launch_set_lens(int32_t* lens, const int32_t* host, int32_t n, hipStream_t s);
+hipError_t launch_append(int dtype, void* k, void* v, const void* k_new, const void* v_new,
+                         int32_t* lens, int32_t batch, int32_t n_kv_heads, int32_t capacity,
+                         int32_t cap_pad, hipStream_t s);
+hipError_t launch_seed(int dtype, void* k, void* v, const void* k_tok, const void* v_tok,
+                       int32_t batch, int32_t rows, int32_t n_kv_heads, int32_t cap_pad,
+                       hipStream_t s);
+hipError_t launch_attend(int dtype, const AttendArgs& a, hipStream_t s);
+
+}  // namespace kvdec

@@ -1,0 +1,528 @@
+// gfx950 kernels of the single-token KV-cached decode step.
+//
+//   append  : scatter one new K/V row per (sequence, KV head) to row lens[b]
+//             of the head-major cache, then lens[b] += 1 (pure byte copy).
+//   seed    : token-major [B][rows][H*64] -> head-major [B][H][cap][64].
+//   attend  : split-sequence decode attention.  One workgroup owns one
+//             (sequence, chunk of rows, KV head) and all query heads that
+//             share that KV head, so every K/V byte is read from HBM once.
+//             Each 16-byte lane load covers 4 f32 / 8 bf16 dims of a row; a
+//             row's dot product is finished with DPP butterflies inside the
+//             16-lane (f32) or 8-lane (bf16) row group; softmax is online
+//             per row slot with exp2 (scale * log2 e folded into q).
+//   merge   : log-sum-exp merge of the chunk partials of every
+//             (sequence, query head) whose length spans more than one chunk.
+//
+// Arithmetic follows the per-head decode of franken_ocr 0.8.0
+// decoder_qwen2.rs (`decode_attn_head`: scores scaled by 1/sqrt(d), max-shifted
+// softmax, weighted V sum) with the online-softmax rescaling named in
+// whisper-apr 0.3.3 decoder_generated.rs (`compute_attention_cached_with_scratch`,
+// Milakov & Gimelshein 2018), and the fail-closed rule of lattice-inference
+// 0.4.0 cpu_q8.rs (`full_attention_step_q8`: a denominator that is not > 0
+// gives a zero row).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvdec_internal.h"
+
+namespace kvdec {
+
+namespace {
+
+constexpr float kNegBig = -1.0e30f;   // finite "no row seen yet" running max
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int ESZ>
+struct Lay {
+    static constexpr int kRowBytes = kHeadDim * ESZ;   // 256 (f32) / 128 (bf16)
+    static constexpr int kLPR = kRowBytes / 16;        // lanes per row: 16 / 8
+    static constexpr int kEPL = 16 / ESZ;              // elements per lane: 4 / 8
+    static constexpr int kRPI = 64 / kLPR;             // rows per wave load: 4 / 8
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// All-reduce (sum) over the LPR lanes that hold one row.  xor-1 and xor-2
+// via quad permutes, then the half-row and row mirrors; every lane of the
+// group ends with the same bits.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x)
+{
+    x += dpp<0xB1>(x);     // quad_perm [1,0,3,2]
+    x += dpp<0x4E>(x);     // quad_perm [2,3,0,1]
+    x += dpp<0x141>(x);    // row_half_mirror
+    if constexpr (LPR == 16) x += dpp<0x140>(x);   // row_mirror
+    return x;
+}
+
+template <int ESZ>
+__device__ __forceinline__ void unpack(const uint4 w, float (&f)[Lay<ESZ>::kEPL])
+{
+    if constexpr (ESZ == 4) {
+        f[0] = __uint_as_float(w.x);
+        f[1] = __uint_as_float(w.y);
+        f[2] = __uint_as_float(w.z);
+        f[3] = __uint_as_float(w.w);
+    } else {
+        // bf16 -> f32 is exact: the 16 bits become the high half.
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            f[2 * k] = __uint_as_float(u[k] << 16);
+            f[2 * k + 1] = __uint_as_float(u[k] & 0xFFFF0000u);
+        }
+    }
+}
+
+__device__ __forceinline__ uint4 load16(const char* p)
+{
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+// Map a flattened chunk index to its sequence.  Chunks are numbered
+// sequence by sequence: sequence b owns ceil(lens[b] / T) consecutive
+// indices starting at the exclusive prefix sum.  Done by one wave with a
+// 64-wide scan per group of 64 sequences; all lanes return the same values.
+struct Located {
+    int b, c, len, nch;
+};
+
+__device__ __forceinline__ bool locate(const int32_t* __restrict__ lens, int B, int T, int cap,
+                                       int blk, int lane, Located& r)
+{
+    int base = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+        const int bi = b0 + lane;
+        const int ln = bi < B ? min(max(lens[bi], 0), cap) : 0;
+        const int cnt = (ln + T - 1) / T;
+        int incl = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(incl, d);
+            if (lane >= d) incl += t;
+        }
+        const int total = __shfl(incl, 63);
+        if (blk < base + total) {
+            const unsigned long long m = __ballot(incl > blk - base);
+            const int first = __ffsll(static_cast<long long>(m)) - 1;
+            r.b = b0 + first;
+            r.c = blk - base - __shfl(incl - cnt, first);
+            r.len = __shfl(ln, first);
+            r.nch = __shfl(cnt, first);
+            return true;
+        }
+        base += total;
+    }
+    return false;
+}
+
+// Exclusive chunk prefix and chunk count of sequence b (one wave).
+__device__ __forceinline__ void chunks_of(const int32_t* __restrict__ lens, int b, int T, int cap,
+                                          int lane, int& excl, int& nch, int& len)
+{
+    int acc = 0;
+    for (int b0 = 0; b0 < b; b0 += 64) {
+        const int bi = b0 + lane;
+        const int ln = bi < b ? min(max(lens[bi], 0), cap) : 0;
+        acc += (ln + T - 1) / T;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
+    excl = acc;
+    len = min(max(lens[b], 0), cap);
+    nch = (len + T - 1) / T;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// set lengths (values carried by value; no host-to-device copy)
+// ---------------------------------------------------------------------------
+__global__ void set_lens_kernel(int32_t* __restrict__ lens, int32_t n, LensBlock vals)
+{
+    const int t = threadIdx.x;
+    if (t < n) lens[t] = vals.v[t];
+}
+
+// ---------------------------------------------------------------------------
+// append: one workgroup per sequence; 16-byte copies; the length is bumped
+// after the workgroup barrier so no thread reads the new value.
+// ---------------------------------------------------------------------------
+template <int ROW_BYTES>
+__global__ __launch_bounds__(256) void append_kernel(char* __restrict__ K, char* __restrict__ V,
+                                                     const char* __restrict__ kn,
+                                                     const char* __restrict__ vn,
+                                                     int32_t* __restrict__ lens, int Hkv,
+                                                     int capacity, int cap_pad)
+{
+    constexpr int VPR = ROW_BYTES / 16;
+    const int b = blockIdx.x;
+    const int len = lens[b];
+    if (len < 0 || len >= capacity) return;     // host already rejected this
+    const int n = Hkv * VPR;
+    for (int t = threadIdx.x; t < 2 * n; t += blockDim.x) {
+        const bool isv = t >= n;
+        const int tt = isv ? t - n : t;
+        const int g = tt / VPR, w = tt - g * VPR;
+        const size_t hg = static_cast<size_t>(b) * Hkv + g;
+        const uint4* src = reinterpret_cast<const uint4*>((isv ? vn : kn) + hg * ROW_BYTES) + w;
+        uint4* dst = reinterpret_cast<uint4*>((isv ? V : K) +
+                                              (hg * cap_pad + len) * ROW_BYTES) + w;
+        *dst = *src;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) lens[b] = len + 1;
+}
+
+// ---------------------------------------------------------------------------
+// seed: token-major -> head-major, grid-stride over 16-byte words.
+// ---------------------------------------------------------------------------
+template <int ROW_BYTES>
+__global__ __launch_bounds__(256) void seed_kernel(char* __restrict__ K, char* __restrict__ V,
+                                                   const char* __restrict__ kt,
+                                                   const char* __restrict__ vt, int B, int rows,
+                                                   int Hkv, int cap_pad)
+{
+    constexpr int VPR = ROW_BYTES / 16;
+    const size_t n = static_cast<size_t>(B) * rows * Hkv * VPR;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < 2 * n;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+        const bool isv = i >= n;
+        size_t j = isv ? i - n : i;
+        const int w = static_cast<int>(j % VPR);
+        j /= VPR;
+        const int g = static_cast<int>(j % Hkv);
+        j /= Hkv;
+        const int t = static_cast<int>(j % rows);
+        const size_t b = j / rows;
+        const uint4* src = reinterpret_cast<const uint4*>(isv ? vt : kt) +
+                           ((b * rows + t) * Hkv + g) * VPR + w;
+        uint4* dst = reinterpret_cast<uint4*>(isv ? V : K) +
+                     ((b * Hkv + g) * cap_pad + t) * VPR + w;
+        *dst = *src;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// attend
+// ---------------------------------------------------------------------------
+// Lane layout inside a wave: lane = sub * LPR + part.  `part` selects 16
+// bytes (EPL dims) of a row, `sub` the row slot (RPI slots per load).  One
+// wave iteration loads U rows per slot: rows r0 + u * RPI + sub.
+// WAVES waves interleave over the chunk in steps of U * RPI rows.
+template <int ESZ, int GROUP, int WAVES, int U>
+__global__ __launch_bounds__(WAVES * 64) void attend_kernel(
+    const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
+    const int32_t* __restrict__ lens, int B, int Hkv, int cap_pad, int T, float qscale,
+    float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml)
+{
+    using L = Lay<ESZ>;
+    constexpr int EPL = L::kEPL, LPR = L::kLPR, RPI = L::kRPI, RB = L::kRowBytes;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sub = lane / LPR;
+    const int part = lane - sub * LPR;
+    const int g = blockIdx.y;
+    const int Hq = Hkv * GROUP;
+
+    Located loc;
+    if (!locate(lens, B, T, cap_pad, blockIdx.x, lane, loc)) return;
+    const int row0 = loc.c * T;
+    const int row_end = min(loc.len, row0 + T);
+
+    // q for the GROUP heads sharing KV head g, this lane's dims, pre-scaled.
+    float qv[GROUP][EPL];
+#pragma unroll
+    for (int i = 0; i < GROUP; ++i) {
+        const float* qp = q + (static_cast<size_t>(loc.b) * Hq + g * GROUP + i) * kHeadDim + part * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) {
+            const float4 t = *reinterpret_cast<const float4*>(qp + e);
+            qv[i][e + 0] = t.x * qscale;
+            qv[i][e + 1] = t.y * qscale;
+            qv[i][e + 2] = t.z * qscale;
+            qv[i][e + 3] = t.w * qscale;
+        }
+    }
+
+    const size_t hoff = (static_cast<size_t>(loc.b) * Hkv + g) * cap_pad * RB + part * 16;
+    const char* Kb = K + hoff;
+    const char* Vb = V + hoff;
+
+    float m[GROUP], l[GROUP], o[GROUP][EPL];
+#pragma unroll
+    for (int i = 0; i < GROUP; ++i) {
+        m[i] = kNegBig;
+        l[i] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[i][e] = 0.f;
+    }
+
+    constexpr int kWaveRows = U * RPI;
+    for (int r0 = row0 + wave * kWaveRows; r0 < row_end; r0 += WAVES * kWaveRows) {
+        uint4 kr[U], vr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = min(r0 + u * RPI + sub, row_end - 1);
+            kr[u] = load16(Kb + static_cast<size_t>(r) * RB);
+            vr[u] = load16(Vb + static_cast<size_t>(r) * RB);
+        }
+        float s[U][GROUP];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float kf[EPL];
+            unpack<ESZ>(kr[u], kf);
+            const bool valid = r0 + u * RPI + sub < row_end;
+#pragma unroll
+            for (int i = 0; i < GROUP; ++i) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) d = fmaf(qv[i][e], kf[e], d);
+                d = row_sum<LPR>(d);
+                s[u][i] = valid ? d : -INFINITY;
+            }
+        }
+        float vf[U][EPL];
+#pragma unroll
+        for (int u = 0; u < U; ++u) unpack<ESZ>(vr[u], vf[u]);
+#pragma unroll
+        for (int i = 0; i < GROUP; ++i) {
+            float mx = s[0][i];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][i]);
+            const float mn = fmaxf(m[i], mx);
+            const float alpha = fast_exp2(m[i] - mn);
+            m[i] = mn;
+            float p[U];
+            float ps = 0.f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                p[u] = fast_exp2(s[u][i] - mn);
+                ps += p[u];
+            }
+            l[i] = fmaf(l[i], alpha, ps);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                float acc = o[i][e] * alpha;
+#pragma unroll
+                for (int u = 0; u < U; ++u) acc = fmaf(p[u], vf[u][e], acc);
+                o[i][e] = acc;
+            }
+        }
+    }
+
+    // Merge the RPI row slots of the wave (lanes with equal `part`).
+#pragma unroll
+    for (int msk = LPR; msk < 64; msk <<= 1) {
+#pragma unroll
+        for (int i = 0; i < GROUP; ++i) {
+            const float m2 = __shfl_xor(m[i], msk);
+            const float l2 = __shfl_xor(l[i], msk);
+            const float mn = fmaxf(m[i], m2);
+            const float a = fast_exp2(m[i] - mn), c2 = fast_exp2(m2 - mn);
+            l[i] = l[i] * a + l2 * c2;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const float o2 = __shfl_xor(o[i][e], msk);
+                o[i][e] = o[i][e] * a + o2 * c2;
+            }
+            m[i] = mn;
+        }
+    }
+
+    // Merge the waves through LDS, then write the output (single-chunk
+    // sequence) or the chunk partial.
+    __shared__ float sm_o[WAVES][GROUP][kHeadDim];
+    __shared__ float sm_m[WAVES][GROUP];
+    __shared__ float sm_l[WAVES][GROUP];
+    if (sub == 0) {
+#pragma unroll
+        for (int i = 0; i < GROUP; ++i) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) sm_o[wave][i][part * EPL + e] = o[i][e];
+            if (part == 0) {
+                sm_m[wave][i] = m[i];
+                sm_l[wave][i] = l[i];
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = wave; i < GROUP; i += WAVES) {
+        float M = sm_m[0][i];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) M = fmaxf(M, sm_m[w][i]);
+        float Lsum = 0.f, acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const float c = fast_exp2(sm_m[w][i] - M);
+            Lsum = fmaf(sm_l[w][i], c, Lsum);
+            acc = fmaf(sm_o[w][i][lane], c, acc);
+        }
+        const int h = g * GROUP + i;
+        if (loc.nch == 1) {
+            out[(static_cast<size_t>(loc.b) * Hq + h) * kHeadDim + lane] =
+                (Lsum > 0.f) ? acc / Lsum : 0.f;
+        } else {
+            const size_t slot = static_cast<size_t>(blockIdx.x) * Hq + h;
+            part_o[slot * kHeadDim + lane] = acc;
+            if (lane == 0) part_ml[slot] = make_float2(M, Lsum);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// merge: one wave per (sequence, query head); lane = output dim.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ lens, int B, int Hq,
+                                                    int T, int cap_pad,
+                                                    const float* __restrict__ part_o,
+                                                    const float2* __restrict__ part_ml,
+                                                    float* __restrict__ out)
+{
+    const int lane = threadIdx.x & 63;
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (w >= B * Hq) return;
+    const int b = w / Hq, h = w - b * Hq;
+    int excl, nch, len;
+    chunks_of(lens, b, T, cap_pad, lane, excl, nch, len);
+    if (nch == 1) return;     // written by the attend kernel
+    float* o = out + static_cast<size_t>(w) * kHeadDim;
+    if (nch == 0) {
+        o[lane] = 0.f;
+        return;
+    }
+    float M = kNegBig;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, part_ml[static_cast<size_t>(excl + c) * Hq + h].x);
+    float Lsum = 0.f, acc = 0.f;
+    for (int c = 0; c < nch; ++c) {
+        const size_t slot = static_cast<size_t>(excl + c) * Hq + h;
+        const float2 ml = part_ml[slot];
+        const float s = fast_exp2(ml.x - M);
+        Lsum = fmaf(ml.y, s, Lsum);
+        acc = fmaf(part_o[slot * kHeadDim + lane], s, acc);
+    }
+    o[lane] = (Lsum > 0.f) ? acc / Lsum : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// host-side launchers
+// ---------------------------------------------------------------------------
+PartialLayout partial_layout(int64_t max_chunks, int32_t n_q_heads)
+{
+    PartialLayout p;
+    const size_t slots = static_cast<size_t>(max_chunks) * static_cast<size_t>(n_q_heads);
+    p.o_offset = 0;
+    p.ml_offset = (slots * kHeadDim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+    p.bytes = p.ml_offset + slots * sizeof(float2) + 256;
+    return p;
+}
+
+hipError_t launch_set_lens(int32_t* lens, const int32_t* host, int32_t n, hipStream_t s)
+{
+    for (int32_t off = 0; off < n; off += kLensPerLaunch) {
+        LensBlock blk;
+        const int32_t cnt = (n - off) < kLensPerLaunch ? (n - off) : kLensPerLaunch;
+        for (int32_t i = 0; i < kLensPerLaunch; ++i) blk.v[i] = i < cnt ? host[off + i] : 0;
+        hipLaunchKernelGGL(set_lens_kernel, dim3(1), dim3(kLensPerLaunch), 0, s, lens + off, cnt,
+                           blk);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_append(int dtype, void* k, void* v, const void* k_new, const void* v_new,
+                         int32_t* lens, int32_t batch, int32_t n_kv_heads, int32_t capacity,
+                         int32_t cap_pad, hipStream_t s)
+{
+    const dim3 grid(batch), block(256);
+    if (dtype == 0)
+        hipLaunchKernelGGL(append_kernel<256>, grid, block, 0, s, static_cast<char*>(k),
+                           static_cast<char*>(v), static_cast<const char*>(k_new),
+                           static_cast<const char*>(v_new), lens, n_kv_heads, capacity, cap_pad);
+    else
+        hipLaunchKernelGGL(append_kernel<128>, grid, block, 0, s, static_cast<char*>(k),
+                           static_cast<char*>(v), static_cast<const char*>(k_new),
+                           static_cast<const char*>(v_new), lens, n_kv_heads, capacity, cap_pad);
+    return hipGetLastError();
+}
+
+hipError_t launch_seed(int dtype, void* k, void* v, const void* k_tok, const void* v_tok,
+                       int32_t batch, int32_t rows, int32_t n_kv_heads, int32_t cap_pad,
+                       hipStream_t s)
+{
+    if (rows == 0) return hipSuccess;
+    const size_t words = static_cast<size_t>(batch) * rows * n_kv_heads * (dtype == 0 ? 16 : 8) * 2;
+    size_t blocks = (words + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+    if (dtype == 0)
+        hipLaunchKernelGGL(seed_kernel<256>, grid, block, 0, s, static_cast<char*>(k),
+                           static_cast<char*>(v), static_cast<const char*>(k_tok),
+                           static_cast<const char*>(v_tok), batch, rows, n_kv_heads, cap_pad);
+    else
+        hipLaunchKernelGGL(seed_kernel<128>, grid, block, 0, s, static_cast<char*>(k),
+                           static_cast<char*>(v), static_cast<const char*>(k_tok),
+                           static_cast<const char*>(v_tok), batch, rows, n_kv_heads, cap_pad);
+    return hipGetLastError();
+}
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kUnroll = 4;
+
+template <int ESZ, int GROUP>
+hipError_t attend_t(const AttendArgs& a, hipStream_t s)
+{
+    float* po = reinterpret_cast<float*>(static_cast<char*>(a.ws) + a.part.o_offset);
+    float2* pml = reinterpret_cast<float2*>(static_cast<char*>(a.ws) + a.part.ml_offset);
+    if (a.n_chunks > 0) {
+        const dim3 grid(static_cast<unsigned>(a.n_chunks), a.n_kv_heads), block(kWaves * 64);
+        hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWaves, kUnroll>), grid, block, 0, s, a.q,
+                           static_cast<const char*>(a.k), static_cast<const char*>(a.v), a.lens,
+                           a.batch, a.n_kv_heads, a.cap_pad, a.chunk_rows, a.qscale, a.out, po,
+                           pml);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (a.need_merge) {
+        const int Hq = a.n_kv_heads * GROUP;
+        const int waves = a.batch * Hq;
+        hipLaunchKernelGGL(merge_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, a.lens, a.batch,
+                           Hq, a.chunk_rows, a.cap_pad, po, pml, a.out);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+template <int ESZ>
+hipError_t attend_dispatch_group(const AttendArgs& a, hipStream_t s)
+{
+    switch (a.group) {
+        case 1: return attend_t<ESZ, 1>(a, s);
+        case 2: return attend_t<ESZ, 2>(a, s);
+        case 3: return attend_t<ESZ, 3>(a, s);
+        case 4: return attend_t<ESZ, 4>(a, s);
+        case 5: return attend_t<ESZ, 5>(a, s);
+        case 6: return attend_t<ESZ, 6>(a, s);
+        case 7: return attend_t<ESZ, 7>(a, s);
+        case 8: return attend_t<ESZ, 8>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attend(int dtype, const AttendArgs& a, hipStream_t s)
+{
+    return dtype == 0 ? attend_dispatch_group<4>(a, s) : attend_dispatch_group<2>(a, s);
+}
+
+}  // namespace kvdec

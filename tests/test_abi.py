@@ -1,0 +1,95 @@
+"""The C-ABI library loads, exports every symbol include/kvdec.h declares, and
+its host-side validation rejects bad arguments before touching the device
+(no GPU needed: none of these calls reaches a HIP launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cached_decode_kvdec_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "kvdec.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvdec_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), f"libkvdec.so does not export {n}"
+    assert sorted(B.EXPORTED) == names
+
+
+def test_library_is_gfx950_native():
+    # the shared object carries a gfx950 code object bundle
+    with open(B.LIB_PATH, "rb") as f:
+        blob = f.read()
+    assert b"gfx950" in blob
+
+
+def test_padded_capacity():
+    assert B.kvdec_padded_capacity(0) == 0
+    assert B.kvdec_padded_capacity(1) == 64
+    assert B.kvdec_padded_capacity(64) == 64
+    assert B.kvdec_padded_capacity(65) == 128
+    assert B.kvdec_padded_capacity(449) == 512
+    assert B.kvdec_padded_capacity(4097) == 4160
+    assert B.kvdec_padded_capacity(8200) == 8256
+
+
+def _desc(**kw):
+    d = dict(batch=2, n_kv_heads=2, head_dim=64, capacity=10, dtype=0, is_static=0,
+             k=4096, v=8192, lens=12288)
+    d.update(kw)
+    return B.CacheDesc(**d)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=32), B.KVDEC_E_SHAPE),
+    (dict(head_dim=128), B.KVDEC_E_SHAPE),
+    (dict(batch=0), B.KVDEC_E_INVALID),
+    (dict(n_kv_heads=0), B.KVDEC_E_INVALID),
+    (dict(capacity=0), B.KVDEC_E_INVALID),
+    (dict(dtype=7), B.KVDEC_E_INVALID),
+    (dict(is_static=2), B.KVDEC_E_INVALID),
+    (dict(k=0), B.KVDEC_E_INVALID),
+    (dict(v=8200), B.KVDEC_E_INVALID),       # not 16-byte aligned
+    (dict(lens=0), B.KVDEC_E_INVALID),
+])
+def test_create_rejects_bad_descriptions(kw, code):
+    with pytest.raises(B.KvdecError) as e:
+        B.kvdec_cache_create(_desc(**kw), [0, 0])
+    assert e.value.code == code
+    assert B.load().kvdec_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("lens", [[0, 11], [-1, 0]])
+def test_create_rejects_lengths_outside_capacity(lens):
+    with pytest.raises(B.KvdecError) as e:
+        B.kvdec_cache_create(_desc(), lens)
+    assert e.value.code == B.KVDEC_E_SHAPE
+
+
+def test_null_handle_calls_fail_cleanly():
+    lib = B.load()
+    assert lib.kvdec_append(None, ctypes.c_void_p(16), ctypes.c_void_p(32), None) == B.KVDEC_E_INVALID
+    assert lib.kvdec_attend_self(None, ctypes.c_void_p(16), 4, 0.125, 0, ctypes.c_void_p(32),
+                                 ctypes.c_void_p(64), 1 << 20, None) == B.KVDEC_E_INVALID
+    assert lib.kvdec_workspace_bytes(None, 4) == 0
+    assert lib.kvdec_reset_lens(None, None, None) == B.KVDEC_E_INVALID
+    lib.kvdec_cache_destroy(None)
+
+
+def test_status_strings():
+    lib = B.load()
+    for code in range(7):
+        assert lib.kvdec_status_str(code).decode()
+    assert lib.kvdec_status_str(99).decode() == "unknown status"
