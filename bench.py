@@ -1,0 +1,364 @@
+"""Benchmark of the single-token KV-cached decode step on one MI355X.
+
+One step = one decode token for every sequence of one layer: append the new
+K/V row (kvdec_append), self-attention over the cached rows
+(kvdec_attend_self) and, for the Whisper-shaped workloads, cross-attention
+over the 1500 static encoder rows (kvdec_attend_cross).  Workloads with
+several consecutive steps (Whisper-large: 32, GQA: 8) cycle through them; the
+lengths are rolled back to the workload's starting lengths at the start of
+each cycle (one tiny kernel, counted inside the step time).
+
+Prints ONE JSON line on stdout (the headline workload, default
+whisper-large: batch 64, 20 heads, bf16 K/V, self 448 -> 480 over 32 steps
+plus cross-attention over 1500 rows) and a per-workload table on stderr.
+
+Inputs are seeded synthetic tensors resident in HBM before the timed region
+starts.  The timed region is K back-to-back steps bracketed by device
+synchronisation.  HIP events around every attend call inside the timed
+region give the attend kernel's average launch duration (one kernel per
+attend call) and its achieved algorithmic bandwidth.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention steps/sec + effective KV HBM GB/s (% of peak), batch 64"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+FLUSH_BYTES = 1 << 30           # > 256 MB Infinity Cache
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attend_bytes(wl, lens_post):
+    """Algorithmic bytes of one attend launch: each valid K and V row once, q in, out."""
+    s = 4 if wl.dtype == "f32" else 2
+    B = len(lens_post)
+    rows = int(np.sum(lens_post, dtype=np.int64))
+    return rows * wl.n_kv_heads * 64 * 2 * s + B * wl.n_q_heads * 64 * 4 * 2
+
+
+class Bench:
+    def __init__(self, name, torch, gen, B, KVCache, to_device):
+        wl = gen.WORKLOADS[name]
+        self.wl, self.torch, self.B = wl, torch, B
+        t0 = time.time()
+        inp = gen.make_inputs(wl, canary=False)
+        self.inp = inp
+        nb = wl.batch
+        self.lens0 = inp.lens.copy()
+        self.self_cache = KVCache(nb, wl.n_kv_heads, inp.cap, wl.dtype, lens=inp.lens,
+                                  k=to_device(inp.k_cache), v=to_device(inp.v_cache))
+        self.kn = [to_device(x) for x in inp.k_new]
+        self.vn = [to_device(x) for x in inp.v_new]
+        self.q = [to_device(x) for x in inp.q_self]
+        self.out = torch.empty_like(self.q[0])
+        self.cross = None
+        if wl.cross:
+            self.cross = KVCache(nb, wl.n_kv_heads, gen.ENC_LEN, wl.dtype, static=True,
+                                 lens=[0] * nb)
+            self.cross.seed(to_device(inp.cross_k_tok), to_device(inp.cross_v_tok))
+            self.qc = [to_device(x) for x in inp.q_cross]
+            self.cout = torch.empty_like(self.qc[0])
+        # free host copies of the big arrays
+        inp.k_cache = inp.v_cache = inp.cross_k_tok = inp.cross_v_tok = None
+        torch.cuda.synchronize()
+        self.S = wl.steps
+        # algorithmic bytes per step of the cycle
+        self.self_bytes, self.step_bytes = [], []
+        for s in range(self.S):
+            post = self.lens0 + s + 1
+            self.self_bytes.append(attend_bytes(wl, post))
+            self.step_bytes.append(gen.kv_bytes_per_step(wl, post))
+        self.cross_bytes = attend_bytes(wl, np.full(nb, gen.ENC_LEN)) if wl.cross else 0
+        self._prep_raw()
+        log(f"[{name}] inputs ready in {time.time() - t0:.1f}s: {wl.describe}")
+
+    def _prep_raw(self):
+        """Bind the C entry points and pointers once, so a step is 3-4 ctypes calls."""
+        import ctypes
+        from kv_cached_decode_kvdec_amd import binding as Bd
+        lib = Bd.load()
+        torch = self.torch
+        self.lib = lib
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        vp = ctypes.c_void_p
+        sc = self.self_cache
+        self.h_self = sc.handle
+        self.ws_self = sc.workspace(self.wl.n_q_heads)
+        self.p_kn = [vp(t.data_ptr()) for t in self.kn]
+        self.p_vn = [vp(t.data_ptr()) for t in self.vn]
+        self.p_q = [vp(t.data_ptr()) for t in self.q]
+        self.p_out = vp(self.out.data_ptr())
+        self.p_ws = vp(self.ws_self.data_ptr())
+        self.n_ws = self.ws_self.numel()
+        self.lens0_c = (ctypes.c_int32 * len(self.lens0))(*self.lens0.tolist())
+        if self.cross is not None:
+            self.h_cross = self.cross.handle
+            self.ws_cross = self.cross.workspace(self.wl.n_q_heads)
+            self.p_qc = [vp(t.data_ptr()) for t in self.qc]
+            self.p_cout = vp(self.cout.data_ptr())
+            self.p_wsc = vp(self.ws_cross.data_ptr())
+            self.n_wsc = self.ws_cross.numel()
+
+    def step(self, i, events=None):
+        lib, st, s, Hq = self.lib, self.stream, i % self.S, self.wl.n_q_heads
+        if s == 0:
+            rc = lib.kvdec_reset_lens(self.h_self, self.lens0_c, st)
+            assert rc == 0, lib.kvdec_last_error()
+        rc = lib.kvdec_append(self.h_self, self.p_kn[s], self.p_vn[s], st)
+        assert rc == 0, lib.kvdec_last_error()
+        if events is not None:
+            events[0].record()
+        rc = lib.kvdec_attend_self(self.h_self, self.p_q[s], Hq, 0.125, 0, self.p_out, self.p_ws,
+                                   self.n_ws, st)
+        assert rc == 0, lib.kvdec_last_error()
+        if events is not None:
+            events[1].record()
+        if self.cross is not None:
+            rc = lib.kvdec_attend_cross(self.h_cross, self.p_qc[s], Hq, 0.125, 0, self.p_cout,
+                                        self.p_wsc, self.n_wsc, st)
+            assert rc == 0, lib.kvdec_last_error()
+            if events is not None:
+                events[2].record()
+
+    def run(self, steps, warmup, cold_steps=0):
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        # timed region: K back-to-back steps, start index aligned to a cycle
+        n_ev = 3 if self.cross is not None else 2
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(i, evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        att_ms, att_bytes = [], []
+        for i in range(steps):
+            s = i % self.S
+            att_ms.append(evs[i][0].elapsed_time(evs[i][1]))
+            att_bytes.append(self.self_bytes[s])
+            if self.cross is not None:
+                att_ms.append(evs[i][1].elapsed_time(evs[i][2]))
+                att_bytes.append(self.cross_bytes)
+        step_bytes = sum(self.step_bytes[i % self.S] for i in range(steps))
+        res = {
+            "steps": steps,
+            "ms_per_step": wall * 1e3 / steps,
+            "steps_per_s": steps / wall,
+            "bytes_per_step": step_bytes / steps,
+            "effective_gbps": step_bytes / wall / 1e9,
+            "attend_launches": len(att_ms),
+            "attend_avg_us": 1e3 * float(np.mean(att_ms)),
+            "attend_gbps": float(np.sum(att_bytes)) / (float(np.sum(att_ms)) * 1e-3) / 1e9,
+            "attend_bytes_per_launch": float(np.mean(att_bytes)),
+        }
+        res["pct_of_hbm_peak"] = 100.0 * res["effective_gbps"] / HBM_PEAK_GBPS
+        res["attend_frac"] = res["attend_gbps"] / HBM_PEAK_GBPS
+        if cold_steps:
+            flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(cold_steps)]
+            for i in range(cold_steps):
+                flush.zero_()
+                ev[i][0].record()
+                self.step(i)
+                ev[i][1].record()
+            torch.cuda.synchronize()
+            ms = [a.elapsed_time(b) for a, b in ev]
+            cb = sum(self.step_bytes[i % self.S] for i in range(cold_steps))
+            res["cold_ms_per_step"] = float(np.mean(ms))
+            res["cold_gbps"] = cb / (float(np.sum(ms)) * 1e-3) / 1e9
+            res["cold_pct_of_hbm_peak"] = 100.0 * res["cold_gbps"] / HBM_PEAK_GBPS
+            del flush
+        return res
+
+    def close(self):
+        self.self_cache.close()
+        if self.cross is not None:
+            self.cross.close()
+
+
+def copy_bandwidth(torch, nbytes=2 << 30, reps=10):
+    """Plain device-to-device copy (read + write), the achievable-bandwidth probe."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(name, target_s=12.0):
+    """The f64 oracle, as it stands, timed on whole decode steps of the workload.
+
+    Steps of the workload's cycle (append + self [+ cross] attention for every
+    sequence) run back to back, single-threaded, until target_s has passed.
+    """
+    import oracle
+    from kv_cached_decode_kvdec_amd import inputs as gen
+    wl = gen.WORKLOADS[name]
+    inp = gen.make_inputs(wl, canary=False)
+    B = wl.batch
+    if wl.cross:
+        cK = np.zeros((B, wl.n_kv_heads, gen.padded_rows(gen.ENC_LEN), 64), inp.k_cache.dtype)
+        cV = np.zeros_like(cK)
+        oracle.seed(cK, inp.cross_k_tok)
+        oracle.seed(cV, inp.cross_v_tok)
+        clens = np.full(B, gen.ENC_LEN, np.int32)
+    Kh, Vh = inp.k_cache, inp.v_cache
+    lens = inp.lens.copy()
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        s = steps % wl.steps
+        if s == 0:
+            lens = inp.lens.copy()
+        lens = oracle.append(Kh, Vh, inp.k_new[s], inp.v_new[s], lens)
+        oracle.attend(inp.q_self[s], Kh, Vh, lens)
+        if wl.cross:
+            oracle.attend(inp.q_cross[s], cK, cV, clens)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": steps / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} whole decode steps of {name} (all {B} sequences: append + self"
+                      f"{' + cross' if wl.cross else ''} attention) through the f64 C oracle, "
+                      f"1 thread, {el:.1f} s",
+            "cpu_model": cpu, "machine": platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="whisper-large")
+    ap.add_argument("--per-workload", default="all",
+                    help="comma list of extra workloads to report on stderr/JSON, or 'none'")
+    ap.add_argument("--cold-steps", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run the plain copy kernel (for counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the decode step is data-parallel over sequences "
+              f"with no exchange between GPUs, and this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from kv_cached_decode_kvdec_amd import inputs as gen
+    from kv_cached_decode_kvdec_amd import binding as Bd
+    from kv_cached_decode_kvdec_amd.cache import KVCache, to_device
+    Bd.load()    # fails loudly if libkvdec.so is missing
+    torch.cuda.set_device(0)
+
+    if args.copy_probe:
+        gbps = copy_bandwidth(torch, reps=4)
+        log(f"copy probe: {gbps:.0f} GB/s")
+        return
+
+    head = args.workload
+    extra = [] if args.per_workload == "none" else (
+        gen.ORDER if args.per_workload == "all" else args.per_workload.split(","))
+    names = [head] + [n for n in extra if n != head]
+
+    results = {}
+    for name in names:
+        wl = gen.WORKLOADS[name]
+        bench = Bench(name, torch, gen, Bd, KVCache, to_device)
+        K = args.steps
+        if name == head:
+            res = bench.run(K, args.warmup, cold_steps=args.cold_steps)
+        else:
+            res = bench.run(max(K // 2, wl.steps), max(args.warmup // 2, 4),
+                            cold_steps=args.cold_steps)
+        bench.close()
+        del bench
+        torch.cuda.empty_cache()
+        results[name] = res
+        log(f"[{name}] {res['steps_per_s']:.0f} steps/s, {res['ms_per_step'] * 1e3:.1f} us/step, "
+            f"{res['effective_gbps']:.0f} GB/s ({res['pct_of_hbm_peak']:.1f}% of 8 TB/s); "
+            f"cold {res.get('cold_ms_per_step', 0) * 1e3:.1f} us/step "
+            f"({res.get('cold_pct_of_hbm_peak', 0):.1f}%); attend kernel "
+            f"{res['attend_avg_us']:.1f} us avg, {res['attend_gbps']:.0f} GB/s")
+
+    copy_gbps = copy_bandwidth(torch)
+    log(f"plain copy kernel: {copy_gbps:.0f} GB/s (read + write)")
+
+    h = results[head]
+    wl = gen.WORKLOADS[head]
+    line = {
+        "metric": METRIC,
+        "value": round(h["steps_per_s"], 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": head, "describe": wl.describe, "batch": wl.batch,
+                   "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads, "head_dim": 64,
+                   "kv_dtype": wl.dtype, "steps_per_cycle": wl.steps,
+                   "cross_len": gen.ENC_LEN if wl.cross else 0},
+        "effective_kv_gbps": round(h["effective_gbps"], 1),
+        "pct_of_hbm_peak": round(h["pct_of_hbm_peak"], 2),
+        "cold_ms_per_step": round(h.get("cold_ms_per_step", 0.0), 5),
+        "cold_pct_of_hbm_peak": round(h.get("cold_pct_of_hbm_peak", 0.0), 2),
+        "copy_kernel_gbps": round(copy_gbps, 1),
+        "roofline": {"bound": "hbm", "kernel": "attend_kernel (one launch per attend call)",
+                     "achieved": round(h["attend_gbps"], 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(h["attend_frac"], 4), "traffic": None,
+                     "avg_launch_us": round(h["attend_avg_us"], 2),
+                     "bytes_per_launch": int(h["attend_bytes_per_launch"])},
+        "per_workload": {n: {k: (round(v, 4) if isinstance(v, float) else v)
+                             for k, v in r.items()} for n, r in results.items()},
+    }
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        line["cpu_baseline"] = cpu_baseline(head)
+        log(f"cpu baseline: {line['cpu_baseline']['value']:.3f} steps/s "
+            f"({time.time() - t0:.0f}s incl. input generation)")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -133,7 +133,10 @@ int32_t kvdec_seed(kvdec_cache* cache, const void* k_tok, const void* v_tok, int
 int32_t kvdec_append(kvdec_cache* cache, const void* k_new, const void* v_new, void* stream);
 
 /* Workspace bytes any attend call on `cache` with n_q_heads query heads may
- * need (split-sequence partial results).  0 on invalid arguments. */
+ * need (split-sequence partial results).  Its contents need no
+ * initialisation and carry nothing between calls; calls sharing one
+ * workspace must not run concurrently (use one stream, or one workspace per
+ * stream).  0 on invalid arguments. */
 size_t kvdec_workspace_bytes(const kvdec_cache* cache, int32_t n_q_heads);
 
 /*
@@ -152,8 +155,10 @@ size_t kvdec_workspace_bytes(const kvdec_cache* cache, int32_t n_q_heads);
  * score, yields a zero output row) and [CERA] `multi_head_attention`.
  * A sequence with length 0 yields a zero row.  scale is usually 1/sqrt(64).
  * chunk_rows: rows per split-sequence chunk; 0 picks automatically, else a
- * multiple of 64 in [KVDEC_MIN_CHUNK, KVDEC_MAX_CHUNK].  The result for a
- * sequence does not depend on the other sequences in the batch.
+ * multiple of 64 in [KVDEC_MIN_CHUNK, KVDEC_MAX_CHUNK].  For a given
+ * chunk_rows the result for a sequence is bitwise independent of the other
+ * sequences in the batch.  One kernel launch per call, plus a log-sum-exp
+ * merge launch when some sequence spans more than one chunk.
  * Errors: KVDEC_E_SHAPE (n_q_heads not a positive multiple of n_kv_heads, or
  * group > KVDEC_MAX_GROUP), KVDEC_E_STATIC, KVDEC_E_WORKSPACE, KVDEC_E_INVALID,
  * KVDEC_E_HIP.

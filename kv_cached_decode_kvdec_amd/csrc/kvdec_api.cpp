@@ -58,7 +58,10 @@ int32_t check_lens(const int32_t* lens_host, int32_t batch, int32_t capacity)
 int64_t chunks_for(const std::vector<int32_t>& lens, int32_t T)
 {
     int64_t n = 0;
-    for (int32_t l : lens) n += (static_cast<int64_t>(l) + T - 1) / T;
+    for (int32_t l : lens) {
+        const int64_t c = (static_cast<int64_t>(l) + T - 1) / T;
+        n += c > 0 ? c : 1;
+    }
     return n;
 }
 
@@ -112,9 +115,7 @@ int32_t attend_common(const kvdec_cache* c, const float* q, int32_t n_q_heads, f
     a.cap_pad = c->cap_pad;
     a.chunk_rows = chunk_rows ? chunk_rows : auto_chunk(c->lens, c->d.n_kv_heads);
     a.n_chunks = chunks_for(c->lens, a.chunk_rows);
-    a.need_merge = false;
-    for (int32_t l : c->lens)
-        if ((l + a.chunk_rows - 1) / a.chunk_rows != 1) a.need_merge = true;
+    a.need_merge = a.n_chunks > c->d.batch;   // some sequence has more than one chunk
     a.qscale = scale * 1.4426950408889634f;
     a.out = out;
     a.ws = ws;

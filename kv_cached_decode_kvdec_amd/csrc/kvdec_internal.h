@@ -15,11 +15,11 @@ struct LensBlock {
     int32_t v[kLensPerLaunch];
 };
 
-// Partial results of the split-sequence attention, per (chunk, query head):
-// unnormalised o[64] and (m, l) with m in log2 units.
+// Workspace of the split-sequence attention: partial results per
+// (chunk, query head): unnormalised o[64] and (m, l) with m in log2 units.
 struct PartialLayout {
-    size_t o_offset;    // float [slots][64]
-    size_t ml_offset;   // float2 [slots]
+    size_t o_offset;        // float [slots][64]
+    size_t ml_offset;       // float2 [slots]
     size_t bytes;
 };
 
@@ -35,8 +35,8 @@ struct AttendArgs {
     int32_t group;          // query heads per KV head
     int32_t cap_pad;        // padded rows per (sequence, KV head)
     int32_t chunk_rows;     // rows per split-sequence chunk
-    int64_t n_chunks;       // sum over sequences of ceil(len / chunk_rows)
-    bool need_merge;        // some sequence has != 1 chunk
+    int64_t n_chunks;       // sum over sequences of max(1, ceil(len / chunk_rows))
+    bool need_merge;        // some sequence spans more than one chunk
     float qscale;           // scale * log2(e)
     float* out;
     void* ws;

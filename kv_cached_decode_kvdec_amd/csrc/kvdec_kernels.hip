@@ -9,9 +9,15 @@
 //             Each 16-byte lane load covers 4 f32 / 8 bf16 dims of a row; a
 //             row's dot product is finished with DPP butterflies inside the
 //             16-lane (f32) or 8-lane (bf16) row group; softmax is online
-//             per row slot with exp2 (scale * log2 e folded into q).
+//             per row slot with exp2 (scale * log2 e folded into q).  A
+//             sequence that fits one chunk is finished in place; otherwise
+//             each workgroup stores its partial (m, l, o[64]).
 //   merge   : log-sum-exp merge of the chunk partials of every
-//             (sequence, query head) whose length spans more than one chunk.
+//             (sequence, query head) whose length spans more than one chunk
+//             (a second launch, only when some sequence has several chunks:
+//             a last-block merge inside the attend kernel would need a
+//             device-scope release per workgroup, which on this chip writes
+//             back the XCD's L2 and serialises the chunks).
 //
 // Arithmetic follows the per-head decode of franken_ocr 0.8.0
 // decoder_qwen2.rs (`decode_attn_head`: scores scaled by 1/sqrt(d), max-shifted
@@ -86,8 +92,9 @@ __device__ __forceinline__ uint4 load16(const char* p)
 }
 
 // Map a flattened chunk index to its sequence.  Chunks are numbered
-// sequence by sequence: sequence b owns ceil(lens[b] / T) consecutive
-// indices starting at the exclusive prefix sum.  Done by one wave with a
+// sequence by sequence: sequence b owns max(1, ceil(lens[b] / T))
+// consecutive indices starting at the exclusive prefix sum (an empty
+// sequence keeps one chunk with no rows, which writes its zero row).  Done by one wave with a
 // 64-wide scan per group of 64 sequences; all lanes return the same values.
 struct Located {
     int b, c, len, nch;
@@ -100,7 +107,7 @@ __device__ __forceinline__ bool locate(const int32_t* __restrict__ lens, int B, 
     for (int b0 = 0; b0 < B; b0 += 64) {
         const int bi = b0 + lane;
         const int ln = bi < B ? min(max(lens[bi], 0), cap) : 0;
-        const int cnt = (ln + T - 1) / T;
+        const int cnt = bi < B ? max(1, (ln + T - 1) / T) : 0;
         int incl = cnt;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
@@ -120,23 +127,6 @@ __device__ __forceinline__ bool locate(const int32_t* __restrict__ lens, int B, 
         base += total;
     }
     return false;
-}
-
-// Exclusive chunk prefix and chunk count of sequence b (one wave).
-__device__ __forceinline__ void chunks_of(const int32_t* __restrict__ lens, int b, int T, int cap,
-                                          int lane, int& excl, int& nch, int& len)
-{
-    int acc = 0;
-    for (int b0 = 0; b0 < b; b0 += 64) {
-        const int bi = b0 + lane;
-        const int ln = bi < b ? min(max(lens[bi], 0), cap) : 0;
-        acc += (ln + T - 1) / T;
-    }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
-    excl = acc;
-    len = min(max(lens[b], 0), cap);
-    nch = (len + T - 1) / T;
 }
 
 }  // namespace
@@ -377,7 +367,8 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// merge: one wave per (sequence, query head); lane = output dim.
+// merge: one wave per (sequence, query head); lane = output dim.  Partials
+// are combined in chunk order, so the result does not depend on scheduling.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ lens, int B, int Hq,
                                                     int T, int cap_pad,
@@ -389,25 +380,28 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
     const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (w >= B * Hq) return;
     const int b = w / Hq, h = w - b * Hq;
-    int excl, nch, len;
-    chunks_of(lens, b, T, cap_pad, lane, excl, nch, len);
-    if (nch == 1) return;     // written by the attend kernel
-    float* o = out + static_cast<size_t>(w) * kHeadDim;
-    if (nch == 0) {
-        o[lane] = 0.f;
-        return;
+    // exclusive prefix of chunk counts over sequences < b
+    int acc = 0;
+    for (int b0 = 0; b0 < b; b0 += 64) {
+        const int bi = b0 + lane;
+        if (bi < b) acc += max(1, (min(max(lens[bi], 0), cap_pad) + T - 1) / T);
     }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
+    const int nch = max(1, (min(max(lens[b], 0), cap_pad) + T - 1) / T);
+    if (nch == 1) return;     // finished by the attend kernel
+    const size_t first = static_cast<size_t>(acc);
     float M = kNegBig;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, part_ml[static_cast<size_t>(excl + c) * Hq + h].x);
-    float Lsum = 0.f, acc = 0.f;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, part_ml[(first + c) * Hq + h].x);
+    float Lsum = 0.f, o = 0.f;
     for (int c = 0; c < nch; ++c) {
-        const size_t slot = static_cast<size_t>(excl + c) * Hq + h;
+        const size_t slot = (first + c) * Hq + h;
         const float2 ml = part_ml[slot];
-        const float s = fast_exp2(ml.x - M);
-        Lsum = fmaf(ml.y, s, Lsum);
-        acc = fmaf(part_o[slot * kHeadDim + lane], s, acc);
+        const float sc = fast_exp2(ml.x - M);
+        Lsum = fmaf(ml.y, sc, Lsum);
+        o = fmaf(part_o[slot * kHeadDim + lane], sc, o);
     }
-    o[lane] = (Lsum > 0.f) ? acc / Lsum : 0.f;
+    out[static_cast<size_t>(w) * kHeadDim + lane] = (Lsum > 0.f) ? o / Lsum : 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -415,11 +409,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
 // ---------------------------------------------------------------------------
 PartialLayout partial_layout(int64_t max_chunks, int32_t n_q_heads)
 {
+    auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
     PartialLayout p;
     const size_t slots = static_cast<size_t>(max_chunks) * static_cast<size_t>(n_q_heads);
     p.o_offset = 0;
-    p.ml_offset = (slots * kHeadDim * sizeof(float) + 255) & ~static_cast<size_t>(255);
-    p.bytes = p.ml_offset + slots * sizeof(float2) + 256;
+    p.ml_offset = up(slots * kHeadDim * sizeof(float));
+    p.bytes = p.ml_offset + up(slots * sizeof(float2));
     return p;
 }
 
@@ -481,25 +476,20 @@ constexpr int kUnroll = 4;
 template <int ESZ, int GROUP>
 hipError_t attend_t(const AttendArgs& a, hipStream_t s)
 {
-    float* po = reinterpret_cast<float*>(static_cast<char*>(a.ws) + a.part.o_offset);
-    float2* pml = reinterpret_cast<float2*>(static_cast<char*>(a.ws) + a.part.ml_offset);
-    if (a.n_chunks > 0) {
-        const dim3 grid(static_cast<unsigned>(a.n_chunks), a.n_kv_heads), block(kWaves * 64);
-        hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWaves, kUnroll>), grid, block, 0, s, a.q,
-                           static_cast<const char*>(a.k), static_cast<const char*>(a.v), a.lens,
-                           a.batch, a.n_kv_heads, a.cap_pad, a.chunk_rows, a.qscale, a.out, po,
-                           pml);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (a.need_merge) {
-        const int Hq = a.n_kv_heads * GROUP;
-        const int waves = a.batch * Hq;
-        hipLaunchKernelGGL(merge_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, a.lens, a.batch,
-                           Hq, a.chunk_rows, a.cap_pad, po, pml, a.out);
-        return hipGetLastError();
-    }
-    return hipSuccess;
+    char* ws = static_cast<char*>(a.ws);
+    float* po = reinterpret_cast<float*>(ws + a.part.o_offset);
+    float2* pml = reinterpret_cast<float2*>(ws + a.part.ml_offset);
+    const dim3 grid(static_cast<unsigned>(a.n_chunks), a.n_kv_heads), block(kWaves * 64);
+    hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWaves, kUnroll>), grid, block, 0, s, a.q,
+                       static_cast<const char*>(a.k), static_cast<const char*>(a.v), a.lens,
+                       a.batch, a.n_kv_heads, a.cap_pad, a.chunk_rows, a.qscale, a.out, po, pml);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.need_merge) return e;
+    const int Hq = a.n_kv_heads * GROUP;
+    const int waves = a.batch * Hq;
+    hipLaunchKernelGGL(merge_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, a.lens, a.batch, Hq,
+                       a.chunk_rows, a.cap_pad, po, pml, a.out);
+    return hipGetLastError();
 }
 
 template <int ESZ>

@@ -256,3 +256,35 @@ def test_full_size_parity(name):
     assert to_host_bits(run.self_cache.k).tobytes() == run.Kh.tobytes()
     assert to_host_bits(run.self_cache.v).tobytes() == run.Vh.tobytes()
     _log(f"full {name}: worst row-relative error {worst:.3e}")
+
+
+def test_workspace_reuse_is_stable_and_shareable():
+    wl = gen.WORKLOADS["gqa"]
+    lens = np.array([5000, 64, 0, 1300, 129], np.int32)
+    inp = gen.make_inputs(wl, batch=5, lens=lens, steps=1, seed=23)
+    run = Run(inp, 64)
+    out, _ = run.step(0)
+    first = out.clone()
+    ws = run.self_cache.workspace(wl.n_q_heads)
+    for _ in range(3):
+        again = run.self_cache.attend(to_device(inp.q_self[0]), chunk_rows=64)
+        torch.cuda.synchronize()
+        assert torch.equal(again, first)
+    _check_step(run, 0, first, None)
+    # the same workspace serves a different cache of a smaller size
+    other = KVCache(2, wl.n_kv_heads, 700, "bf16", lens=[700, 3],
+                    k=to_device(inp.k_cache[:2, :, :704]), v=to_device(inp.v_cache[:2, :, :704]))
+    q2 = to_device(inp.q_self[0][:2])
+    o2 = torch.empty_like(q2)
+    import ctypes
+    B.kvdec_attend_self(other.handle, ctypes.c_void_p(q2.data_ptr()), wl.n_q_heads, 0.125, 64,
+                        ctypes.c_void_p(o2.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel())
+    torch.cuda.synchronize()
+    ref = oracle.attend(inp.q_self[0][:2], inp.k_cache[:2, :, :704], inp.v_cache[:2, :, :704],
+                        np.array([700, 3], np.int32))
+    assert_attention_close(o2.cpu().numpy(), ref, "bf16", "shared workspace")
+    # garbage in the workspace does not matter: it holds nothing between calls
+    ws.fill_(255)
+    again = run.self_cache.attend(to_device(inp.q_self[0]), chunk_rows=64)
+    torch.cuda.synchronize()
+    assert torch.equal(again, first)
