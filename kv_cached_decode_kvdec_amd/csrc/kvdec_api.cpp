@@ -65,13 +65,31 @@ int64_t chunks_for(const std::vector<int32_t>& lens, int32_t T)
     return n;
 }
 
-// Automatic chunk size: the largest power-of-two chunk (64 .. 4096 rows)
-// that still gives at least kTargetBlocks workgroups, so every one of the
-// 256 compute units gets several chunks while partial traffic stays small.
-constexpr int64_t kTargetBlocks = 2048;
+// Automatic chunk size (rows per workgroup), measured on MI355X:
+//  - with at least kPairsOneChunk (sequence, KV head) pairs and lengths within
+//    2x of their mean, one chunk per sequence: enough workgroups to fill the
+//    256 CUs, even work per workgroup, and no merge launch;
+//  - otherwise the largest power of two in [64, 4096] that still gives at
+//    least kTargetBlocks workgroups (a few per CU, so ragged lengths balance)
+//    -- at this size the merge traffic is well under 1% of the K/V bytes.
+constexpr int64_t kPairsOneChunk = 1024;
+constexpr int64_t kTargetBlocks = 1536;
 
 int32_t auto_chunk(const std::vector<int32_t>& lens, int32_t n_kv_heads)
 {
+    int64_t total = 0;
+    int32_t longest = 0;
+    for (int32_t l : lens) {
+        total += l;
+        longest = l > longest ? l : longest;
+    }
+    const int64_t pairs = static_cast<int64_t>(lens.size()) * n_kv_heads;
+    if (pairs >= kPairsOneChunk && longest <= KVDEC_MAX_CHUNK &&
+        static_cast<int64_t>(longest) * static_cast<int64_t>(lens.size()) <= 2 * total) {
+        int32_t T = KVDEC_MIN_CHUNK;
+        while (T < longest) T <<= 1;
+        return T;
+    }
     for (int32_t T = KVDEC_MAX_CHUNK; T > KVDEC_MIN_CHUNK; T >>= 1)
         if (chunks_for(lens, T) * n_kv_heads >= kTargetBlocks) return T;
     return KVDEC_MIN_CHUNK;

@@ -67,6 +67,26 @@ __device__ __forceinline__ float row_sum(float x)
     return x;
 }
 
+__device__ __forceinline__ float row_max16(float x)
+{
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    x = fmaxf(x, dpp<0x141>(x));
+    x = fmaxf(x, dpp<0x140>(x));
+    return x;
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// float -> bfloat16 bits, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 template <int ESZ>
 __device__ __forceinline__ void unpack(const uint4 w, float (&f)[Lay<ESZ>::kEPL])
 {
@@ -86,9 +106,15 @@ __device__ __forceinline__ void unpack(const uint4 w, float (&f)[Lay<ESZ>::kEPL]
     }
 }
 
-__device__ __forceinline__ uint4 load16(const char* p)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// K/V rows are read exactly once per call: nontemporal 16-byte loads keep
+// them from displacing useful lines in L2 (measured on MI355X: a plain
+// streaming read reaches ~6.1 TB/s, ~7.0 TB/s with nontemporal loads).
+__device__ __forceinline__ uint4 load16_stream(const char* p)
 {
-    return *reinterpret_cast<const uint4*>(p);
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
 }
 
 // Map a flattened chunk index to its sequence.  Chunks are numbered
@@ -127,6 +153,41 @@ __device__ __forceinline__ bool locate(const int32_t* __restrict__ lens, int B, 
         base += total;
     }
     return false;
+}
+
+// Combine the WAVES per-wave states of a workgroup (staged in LDS) and
+// write either the normalised output row (sequence fits one chunk) or the
+// chunk partial (m, l, o[64]) for the merge launch.
+template <int WAVES, int GROUP>
+__device__ __forceinline__ void finish_block(const float (&sm_o)[WAVES][GROUP][kHeadDim],
+                                             const float (&sm_m)[WAVES][GROUP],
+                                             const float (&sm_l)[WAVES][GROUP], int wave, int lane,
+                                             const Located& loc, int g, int Hq,
+                                             float* __restrict__ out, float* __restrict__ part_o,
+                                             float2* __restrict__ part_ml)
+{
+    __syncthreads();
+    for (int i = wave; i < GROUP; i += WAVES) {
+        float M = sm_m[0][i];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) M = fmaxf(M, sm_m[w][i]);
+        float Lsum = 0.f, acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const float c = fast_exp2(sm_m[w][i] - M);
+            Lsum = fmaf(sm_l[w][i], c, Lsum);
+            acc = fmaf(sm_o[w][i][lane], c, acc);
+        }
+        const int h = g * GROUP + i;
+        if (loc.nch == 1) {
+            out[(static_cast<size_t>(loc.b) * Hq + h) * kHeadDim + lane] =
+                (Lsum > 0.f) ? acc / Lsum : 0.f;
+        } else {
+            const size_t slot = static_cast<size_t>(blockIdx.x) * Hq + h;
+            part_o[slot * kHeadDim + lane] = acc;
+            if (lane == 0) part_ml[slot] = make_float2(M, Lsum);
+        }
+    }
 }
 
 }  // namespace
@@ -260,8 +321,8 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = min(r0 + u * RPI + sub, row_end - 1);
-            kr[u] = load16(Kb + static_cast<size_t>(r) * RB);
-            vr[u] = load16(Vb + static_cast<size_t>(r) * RB);
+            kr[u] = load16_stream(Kb + static_cast<size_t>(r) * RB);
+            vr[u] = load16_stream(Vb + static_cast<size_t>(r) * RB);
         }
         float s[U][GROUP];
 #pragma unroll
@@ -342,33 +403,178 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
             }
         }
     }
-    __syncthreads();
-    for (int i = wave; i < GROUP; i += WAVES) {
-        float M = sm_m[0][i];
-#pragma unroll
-        for (int w = 1; w < WAVES; ++w) M = fmaxf(M, sm_m[w][i]);
-        float Lsum = 0.f, acc = 0.f;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) {
-            const float c = fast_exp2(sm_m[w][i] - M);
-            Lsum = fmaf(sm_l[w][i], c, Lsum);
-            acc = fmaf(sm_o[w][i][lane], c, acc);
-        }
-        const int h = g * GROUP + i;
-        if (loc.nch == 1) {
-            out[(static_cast<size_t>(loc.b) * Hq + h) * kHeadDim + lane] =
-                (Lsum > 0.f) ? acc / Lsum : 0.f;
-        } else {
-            const size_t slot = static_cast<size_t>(blockIdx.x) * Hq + h;
-            part_o[slot * kHeadDim + lane] = acc;
-            if (lane == 0) part_ml[slot] = make_float2(M, Lsum);
-        }
-    }
+    finish_block<WAVES, GROUP>(sm_o, sm_m, sm_l, wave, lane, loc, g, Hq, out, part_o, part_ml);
 }
 
 // ---------------------------------------------------------------------------
-// merge: one wave per (sequence, query head); lane = output dim.  Partials
-// are combined in chunk order, so the result does not depend on scheduling.
+// attend, grouped-query heads on MFMA (bf16 K/V, 4 query heads per KV
+// head).  Scores of a 16-row K tile for all heads of the group come from
+// v_mfma_f32_16x16x32_bf16: B = K^T (16 rows x 32 dims per instruction, two
+// instructions per 64-dim row), A = the group's q rows repeated to the 16
+// rows of the instruction, in bf16 as hi + lo parts (q = hi + lo to ~2^-16
+// relative), so the scores carry f32-level accuracy.  Lane l owns KV row
+// (l & 15) of the tile and, with j = l >> 4, dims 8j .. 8j+7 and
+// 32+8j .. 32+8j+7 of that row: each of the two 16-byte loads of a wave then
+// covers one contiguous 64-byte half of all 16 rows.  The MFMA output puts
+// every head's score of the lane's row in the lane, and the V sum is done on
+// the VALU from the same lane's 32 bytes of V.  Softmax is online per 16-row
+// tile (tile max over the 16 row slots with DPP).
+// ---------------------------------------------------------------------------
+template <int GROUP, int WAVES, int U>
+__global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
+    const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
+    const int32_t* __restrict__ lens, int B, int Hkv, int cap_pad, int T, float qscale,
+    float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml)
+{
+    static_assert(GROUP % 4 == 0, "MFMA path takes groups of 4 query heads");
+    constexpr int P = GROUP / 4;           // MFMA passes, 4 heads each
+    constexpr int RB = 128;                // bf16 row bytes
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int slot = lane & 15;            // KV row inside the 16-row tile
+    const int j = lane >> 4;               // dims 8j .. 8j+7 and 32+8j .. 32+8j+7
+    const int g = blockIdx.y;
+    const int Hq = Hkv * GROUP;
+
+    Located loc;
+    if (!locate(lens, B, T, cap_pad, blockIdx.x, lane, loc)) return;
+    const int row0 = loc.c * T;
+    const int row_end = min(loc.len, row0 + T);
+
+    // A operands.  Instruction t of a row covers k-slots 8j .. 8j+7 <-> dims
+    // 32t + 8j .. +8 (the lane's own 16 bytes of K); A row i is head 4p + (i & 3).
+    bf16x8 qa_hi[P][2], qa_lo[P][2];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const int head = g * GROUP + 4 * p + (slot & 3);
+        const float* qp = q + (static_cast<size_t>(loc.b) * Hq + head) * kHeadDim + 8 * j;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const float4 x0 = *reinterpret_cast<const float4*>(qp + 32 * t);
+            const float4 x1 = *reinterpret_cast<const float4*>(qp + 32 * t + 4);
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xv = xs[e] * qscale;
+                const uint32_t hb = bf16_rne(xv);
+                const float hf = __uint_as_float(hb << 16);
+                const uint32_t lb = bf16_rne(xv - hf);
+                qa_hi[p][t][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hb));
+                qa_lo[p][t][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lb));
+            }
+        }
+    }
+
+    const size_t hoff = (static_cast<size_t>(loc.b) * Hkv + g) * cap_pad * RB + 16 * j;
+    const char* Kb = K + hoff;
+    const char* Vb = V + hoff;
+
+    float m[GROUP], lp[GROUP], o[GROUP][16];
+#pragma unroll
+    for (int h = 0; h < GROUP; ++h) {
+        m[h] = kNegBig;
+        lp[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[h][e] = 0.f;
+    }
+
+    constexpr int kWaveRows = 16 * U;
+    for (int r0 = row0 + wave * kWaveRows; r0 < row_end; r0 += WAVES * kWaveRows) {
+        uint4 kr[U][2], vr[U][2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = min(r0 + 16 * u + slot, row_end - 1);
+            const char* kp = Kb + static_cast<size_t>(r) * RB;
+            const char* vp = Vb + static_cast<size_t>(r) * RB;
+            kr[u][0] = load16_stream(kp);
+            kr[u][1] = load16_stream(kp + 64);
+            vr[u][0] = load16_stream(vp);
+            vr[u][1] = load16_stream(vp + 64);
+        }
+        float sc[U][GROUP];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool valid = r0 + 16 * u + slot < row_end;
+            const bf16x8 b0 = __builtin_bit_cast(bf16x8, kr[u][0]);
+            const bf16x8 b1 = __builtin_bit_cast(bf16x8, kr[u][1]);
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_hi[p][0], b0, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_lo[p][0], b0, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_hi[p][1], b1, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_lo[p][1], b1, c, 0, 0, 0);
+                // output row 4j + r of the instruction is head 4p + r, column = this lane's row
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sc[u][4 * p + r] = valid ? c[r] : -INFINITY;
+            }
+        }
+        float vf[U][16];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            unpack<2>(vr[u][0], *reinterpret_cast<float(*)[8]>(&vf[u][0]));
+            unpack<2>(vr[u][1], *reinterpret_cast<float(*)[8]>(&vf[u][8]));
+        }
+#pragma unroll
+        for (int h = 0; h < GROUP; ++h) {
+            float mx = sc[0][h];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u][h]);
+            mx = row_max16(mx);
+            const float mn = fmaxf(m[h], mx);
+            const float alpha = fast_exp2(m[h] - mn);
+            m[h] = mn;
+            float pu[U];
+            float ps = 0.f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                pu[u] = fast_exp2(sc[u][h] - mn);
+                ps += pu[u];
+            }
+            lp[h] = fmaf(lp[h], alpha, ps);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float acc = o[h][e] * alpha;
+#pragma unroll
+                for (int u = 0; u < U; ++u) acc = fmaf(pu[u], vf[u][e], acc);
+                o[h][e] = acc;
+            }
+        }
+    }
+
+    // Sum l and o over the 16 row slots (m is already uniform).
+#pragma unroll
+    for (int h = 0; h < GROUP; ++h) {
+        lp[h] = row_sum<16>(lp[h]);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[h][e] = row_sum<16>(o[h][e]);
+    }
+
+    __shared__ float sm_o[WAVES][GROUP][kHeadDim];
+    __shared__ float sm_m[WAVES][GROUP];
+    __shared__ float sm_l[WAVES][GROUP];
+    // lane (j, slot) stores element `slot` of its 16: dim 8j + slot, or
+    // 32 + 8j + slot - 8 for the second half
+    const int my_dim = slot < 8 ? 8 * j + slot : 32 + 8 * j + (slot - 8);
+#pragma unroll
+    for (int h = 0; h < GROUP; ++h) {
+        float mine = o[h][0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mine = (slot == e) ? o[h][e] : mine;
+        sm_o[wave][h][my_dim] = mine;
+        if (lane == 0) {
+            sm_m[wave][h] = m[h];
+            sm_l[wave][h] = lp[h];
+        }
+    }
+    finish_block<WAVES, GROUP>(sm_o, sm_m, sm_l, wave, lane, loc, g, Hq, out, part_o, part_ml);
+}
+
+// ---------------------------------------------------------------------------
+// merge: one wave per (sequence, query head).  Lane c first takes chunk c's
+// (m, l) -- all loads issued at once -- to form the global max M and the
+// weights w_c = 2^(m_c - M); then lane d sums w_c * o_c[d] over the chunks
+// in chunk order (a fixed order: the result does not depend on scheduling).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ lens, int B, int Hq,
                                                     int T, int cap_pad,
@@ -380,7 +586,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
     const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (w >= B * Hq) return;
     const int b = w / Hq, h = w - b * Hq;
-    // exclusive prefix of chunk counts over sequences < b
+    // exclusive prefix of chunk counts over sequences < b, and this sequence's count
     int acc = 0;
     for (int b0 = 0; b0 < b; b0 += 64) {
         const int bi = b0 + lane;
@@ -391,15 +597,51 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
     const int nch = max(1, (min(max(lens[b], 0), cap_pad) + T - 1) / T);
     if (nch == 1) return;     // finished by the attend kernel
     const size_t first = static_cast<size_t>(acc);
+
+    // global max over the chunks' m (lane-parallel)
     float M = kNegBig;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, part_ml[(first + c) * Hq + h].x);
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+        const int c = c0 + lane;
+        if (c < nch) M = fmaxf(M, part_ml[(first + c) * Hq + h].x);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
+
     float Lsum = 0.f, o = 0.f;
-    for (int c = 0; c < nch; ++c) {
-        const size_t slot = (first + c) * Hq + h;
-        const float2 ml = part_ml[slot];
-        const float sc = fast_exp2(ml.x - M);
-        Lsum = fmaf(ml.y, sc, Lsum);
-        o = fmaf(part_o[slot * kHeadDim + lane], sc, o);
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+        const int c = c0 + lane;
+        float wc = 0.f, lc = 0.f;
+        if (c < nch) {
+            const float2 ml = part_ml[(first + c) * Hq + h];
+            wc = fast_exp2(ml.x - M);
+            lc = ml.y;
+        }
+        const int n = min(64, nch - c0);
+        // sum of w_c * l_c in chunk order: every lane walks the same sequence
+        int k = 0;
+        for (; k + 4 <= n; k += 4) {
+            const size_t s0 = (first + c0 + k) * Hq + h;
+            const float o0 = part_o[s0 * kHeadDim + lane];
+            const float o1 = part_o[(s0 + Hq) * kHeadDim + lane];
+            const float o2 = part_o[(s0 + 2 * Hq) * kHeadDim + lane];
+            const float o3 = part_o[(s0 + 3 * Hq) * kHeadDim + lane];
+            const float w0 = __shfl(wc, k), w1 = __shfl(wc, k + 1);
+            const float w2 = __shfl(wc, k + 2), w3 = __shfl(wc, k + 3);
+            Lsum = fmaf(__shfl(lc, k), w0, Lsum);
+            Lsum = fmaf(__shfl(lc, k + 1), w1, Lsum);
+            Lsum = fmaf(__shfl(lc, k + 2), w2, Lsum);
+            Lsum = fmaf(__shfl(lc, k + 3), w3, Lsum);
+            o = fmaf(o0, w0, o);
+            o = fmaf(o1, w1, o);
+            o = fmaf(o2, w2, o);
+            o = fmaf(o3, w3, o);
+        }
+        for (; k < n; ++k) {
+            const size_t s0 = (first + c0 + k) * Hq + h;
+            const float wk = __shfl(wc, k);
+            Lsum = fmaf(__shfl(lc, k), wk, Lsum);
+            o = fmaf(part_o[s0 * kHeadDim + lane], wk, o);
+        }
     }
     out[static_cast<size_t>(w) * kHeadDim + lane] = (Lsum > 0.f) ? o / Lsum : 0.f;
 }
@@ -492,9 +734,32 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int GROUP, int WAVES, int U>
+hipError_t attend_gqa_t(const AttendArgs& a, hipStream_t s)
+{
+    char* ws = static_cast<char*>(a.ws);
+    float* po = reinterpret_cast<float*>(ws + a.part.o_offset);
+    float2* pml = reinterpret_cast<float2*>(ws + a.part.ml_offset);
+    const dim3 grid(static_cast<unsigned>(a.n_chunks), a.n_kv_heads), block(WAVES * 64);
+    hipLaunchKernelGGL((attend_gqa_mfma_kernel<GROUP, WAVES, U>), grid, block, 0, s, a.q,
+                       static_cast<const char*>(a.k), static_cast<const char*>(a.v), a.lens,
+                       a.batch, a.n_kv_heads, a.cap_pad, a.chunk_rows, a.qscale, a.out, po, pml);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.need_merge) return e;
+    const int Hq = a.n_kv_heads * GROUP;
+    const int waves = a.batch * Hq;
+    hipLaunchKernelGGL(merge_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, a.lens, a.batch, Hq,
+                       a.chunk_rows, a.cap_pad, po, pml, a.out);
+    return hipGetLastError();
+}
+
 template <int ESZ>
 hipError_t attend_dispatch_group(const AttendArgs& a, hipStream_t s)
 {
+    if constexpr (ESZ == 2) {
+        // bf16 K/V with 4 query heads per KV head: scores on MFMA
+        if (a.group == 4) return attend_gqa_t<4, 4, 2>(a, s);
+    }
     switch (a.group) {
         case 1: return attend_t<ESZ, 1>(a, s);
         case 2: return attend_t<ESZ, 2>(a, s);
