@@ -192,6 +192,25 @@ class Bench:
             self.cross.close()
 
 
+def measured_traffic(workload):
+    """HBM bytes per attend launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy of known size), or
+    None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    src = os.path.join(ROOT, "kv_cached_decode_kvdec_amd", "csrc", "kvdec_kernels.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            cur = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None, None
+    if rec.get("kernel_source_sha256") != cur:
+        return None, rec.get("kernel")
+    return int(rec["traffic_bytes_per_launch"]), rec.get("kernel")
+
+
 def copy_bandwidth(torch, nbytes=2 << 30, reps=10):
     """Plain device-to-device copy (read + write), the achievable-bandwidth probe."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -322,6 +341,7 @@ def main():
 
     h = results[head]
     wl = gen.WORKLOADS[head]
+    traffic, kname = measured_traffic(head)
     line = {
         "metric": METRIC,
         "value": round(h["steps_per_s"], 2),
@@ -344,9 +364,10 @@ def main():
         "cold_ms_per_step": round(h.get("cold_ms_per_step", 0.0), 5),
         "cold_pct_of_hbm_peak": round(h.get("cold_pct_of_hbm_peak", 0.0), 2),
         "copy_kernel_gbps": round(copy_gbps, 1),
-        "roofline": {"bound": "hbm", "kernel": "attend_kernel (one launch per attend call)",
+        "roofline": {"bound": "hbm",
+                     "kernel": kname or "attend kernel (one launch per attend call)",
                      "achieved": round(h["attend_gbps"], 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(h["attend_frac"], 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(h["attend_frac"], 4), "traffic": traffic,
                      "avg_launch_us": round(h["attend_avg_us"], 2),
                      "bytes_per_launch": int(h["attend_bytes_per_launch"])},
         "per_workload": {n: {k: (round(v, 4) if isinstance(v, float) else v)
