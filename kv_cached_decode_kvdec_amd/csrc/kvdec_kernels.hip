@@ -407,47 +407,56 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// attend, grouped-query heads on MFMA (bf16 K/V, 4 query heads per KV
-// head).  Scores of a 16-row K tile for all heads of the group come from
-// v_mfma_f32_16x16x32_bf16: B = K^T (16 rows x 32 dims per instruction, two
-// instructions per 64-dim row), A = the group's q rows repeated to the 16
-// rows of the instruction, in bf16 as hi + lo parts (q = hi + lo to ~2^-16
-// relative), so the scores carry f32-level accuracy.  Lane l owns KV row
-// (l & 15) of the tile and, with j = l >> 4, dims 8j .. 8j+7 and
-// 32+8j .. 32+8j+7 of that row: each of the two 16-byte loads of a wave then
-// covers one contiguous 64-byte half of all 16 rows.  The MFMA output puts
-// every head's score of the lane's row in the lane, and the V sum is done on
-// the VALU from the same lane's 32 bytes of V.  Softmax is online per 16-row
-// tile (tile max over the 16 row slots with DPP).
+// attend, grouped-query heads on MFMA (bf16 K/V, 4 query heads per KV head).
+//
+// Per wave iteration: 32 KV rows = two 16-row tiles.  Lane l = 16G + i.
+//  scores  S^T = K q^T on v_mfma_f32_16x16x32_bf16: A = K tile (row i, dims
+//          8G..8G+7 and 32+8G..; two 16-byte loads per lane, each wave load
+//          covering one contiguous 64-byte half of all 16 rows), B = the
+//          group's q (column i is head i % 4) as bf16 hi + lo parts, so the
+//          scores keep ~f32 accuracy.  Lane l receives head l % 4 for rows
+//          4G .. 4G+3 of each tile.
+//  softmax online per 32 rows; tile max per head across the four G groups.
+//  P.V     O = P V on the same MFMA: A = P (row m of A is head m % 4, k-slot
+//          8G+t <-> tile t/4, row 4G + t%4 -- exactly the lane's own eight
+//          weights, in bf16 hi + lo), B = V from LDS with the gfx950 transpose
+//          read ds_read_b64_tr_b16 (V rows staged row-major, 160-byte row
+//          stride), four 16-dim column blocks.  The accumulator is 16 floats
+//          per lane: head r, dim 16c + i.
 // ---------------------------------------------------------------------------
-template <int GROUP, int WAVES, int U>
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+constexpr int kGqaLdsStride = 160;     // bytes per staged V row (conflict-free tr16 reads)
+
+template <int GROUP, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
     const int32_t* __restrict__ lens, int B, int Hkv, int cap_pad, int T, float qscale,
     float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml)
 {
-    static_assert(GROUP % 4 == 0, "MFMA path takes groups of 4 query heads");
-    constexpr int P = GROUP / 4;           // MFMA passes, 4 heads each
+    static_assert(GROUP == 4, "MFMA path takes groups of 4 query heads");
     constexpr int RB = 128;                // bf16 row bytes
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int slot = lane & 15;            // KV row inside the 16-row tile
-    const int j = lane >> 4;               // dims 8j .. 8j+7 and 32+8j .. 32+8j+7
+    const int i = lane & 15;
+    const int G = lane >> 4;
+    const int hl = lane & 3;               // head whose scores this lane holds
     const int g = blockIdx.y;
     const int Hq = Hkv * GROUP;
+
+    __shared__ __attribute__((aligned(16))) char sm_v[WAVES][32 * kGqaLdsStride];
 
     Located loc;
     if (!locate(lens, B, T, cap_pad, blockIdx.x, lane, loc)) return;
     const int row0 = loc.c * T;
     const int row_end = min(loc.len, row0 + T);
 
-    // A operands.  Instruction t of a row covers k-slots 8j .. 8j+7 <-> dims
-    // 32t + 8j .. +8 (the lane's own 16 bytes of K); A row i is head 4p + (i & 3).
-    bf16x8 qa_hi[P][2], qa_lo[P][2];
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-        const int head = g * GROUP + 4 * p + (slot & 3);
-        const float* qp = q + (static_cast<size_t>(loc.b) * Hq + head) * kHeadDim + 8 * j;
+    // B operand of the score MFMA: column i is head i % 4; k-slot 8G+e of
+    // instruction t is dim 32t + 8G + e.
+    bf16x8 qb_hi[2], qb_lo[2];
+    {
+        const float* qp = q + (static_cast<size_t>(loc.b) * Hq + g * GROUP + (i & 3)) * kHeadDim + 8 * G;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const float4 x0 = *reinterpret_cast<const float4*>(qp + 32 * t);
@@ -457,115 +466,128 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
             for (int e = 0; e < 8; ++e) {
                 const float xv = xs[e] * qscale;
                 const uint32_t hb = bf16_rne(xv);
-                const float hf = __uint_as_float(hb << 16);
-                const uint32_t lb = bf16_rne(xv - hf);
-                qa_hi[p][t][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hb));
-                qa_lo[p][t][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lb));
+                const uint32_t lb = bf16_rne(xv - __uint_as_float(hb << 16));
+                qb_hi[t][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hb));
+                qb_lo[t][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lb));
             }
         }
     }
 
-    const size_t hoff = (static_cast<size_t>(loc.b) * Hkv + g) * cap_pad * RB + 16 * j;
-    const char* Kb = K + hoff;
-    const char* Vb = V + hoff;
+    const size_t head_base = (static_cast<size_t>(loc.b) * Hkv + g) * cap_pad * RB;
+    const char* Kb = K + head_base + 16 * G;          // + row * 128 (+64)
+    const char* Vb = V + head_base + 16 * (lane & 7); // + row * 128, row = lane >> 3 (+8c)
+    char* my_v = sm_v[wave];
+    // transpose-read addresses: lane m = 4e + q of group G reads row 4G + e,
+    // dims d0 + 4q .. +4 (d0 added per column block), for the second half +16 rows
+    const int tr_off = (4 * G + (i >> 2)) * kGqaLdsStride + 8 * (i & 3);
 
-    float m[GROUP], lp[GROUP], o[GROUP][16];
+    float m = kNegBig, lpart = 0.f;
+    f32x4 o[4];
 #pragma unroll
-    for (int h = 0; h < GROUP; ++h) {
-        m[h] = kNegBig;
-        lp[h] = 0.f;
+    for (int c = 0; c < 4; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int r0 = row0 + wave * 32; r0 < row_end; r0 += WAVES * 32) {
+        uint4 kr[2][2], vr[4];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[h][e] = 0.f;
+        for (int tile = 0; tile < 2; ++tile) {
+            const int r = min(r0 + 16 * tile + i, row_end - 1);
+            kr[tile][0] = load16_stream(Kb + static_cast<size_t>(r) * RB);
+            kr[tile][1] = load16_stream(Kb + static_cast<size_t>(r) * RB + 64);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int r = min(r0 + 8 * c + (lane >> 3), row_end - 1);
+            vr[c] = load16_stream(Vb + static_cast<size_t>(r) * RB);
+        }
+        // scores: lane holds head hl for rows r0 + 16*tile + 4G + rr
+        float sc[2][4];
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile) {
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const bf16x8 ka = __builtin_bit_cast(bf16x8, kr[tile][t]);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb_hi[t], c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb_lo[t], c, 0, 0, 0);
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                sc[tile][rr] = (r0 + 16 * tile + 4 * G + rr < row_end) ? c[rr] : -INFINITY;
+        }
+        // stage V rows r0 .. r0+31 (row-major) for the transpose reads
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            *reinterpret_cast<uint4*>(my_v + (8 * c + (lane >> 3)) * kGqaLdsStride + 16 * (lane & 7)) = vr[c];
+
+        // online softmax for head hl over these 32 rows
+        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - mn);
+        m = mn;
+        float pw[2][4];
+        float ps = 0.f;
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                pw[tile][rr] = fast_exp2(sc[tile][rr] - mn);
+                ps += pw[tile][rr];
+            }
+        lpart = fmaf(lpart, alpha, ps);
+        // A operand of P.V: k-slot 8G + t <-> tile t / 4, row 4G + t % 4
+        bf16x8 pa_hi, pa_lo;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float pv = pw[t >> 2][t & 3];
+            const uint32_t hb = bf16_rne(pv);
+            const uint32_t lb = bf16_rne(pv - __uint_as_float(hb << 16));
+            pa_hi[t] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hb));
+            pa_lo[t] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lb));
+        }
+        // rescale the accumulator: output row 4G + rr is head rr
+        const float al[4] = {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0)),
+                             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1)),
+                             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2)),
+                             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3))};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) o[c][rr] *= al[rr];
+        // P.V, one 16-dim column block at a time
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+            typedef __attribute__((address_space(3))) char lds_char;
+            lds_char* base = (lds_char*)(my_v) + tr_off + 32 * c;
+            const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base));
+            const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16*)(base + 16 * kGqaLdsStride));
+            const v8i16 vv = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 vb = __builtin_bit_cast(bf16x8, vv);
+            o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb, o[c], 0, 0, 0);
+            o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb, o[c], 0, 0, 0);
+        }
     }
 
-    constexpr int kWaveRows = 16 * U;
-    for (int r0 = row0 + wave * kWaveRows; r0 < row_end; r0 += WAVES * kWaveRows) {
-        uint4 kr[U][2], vr[U][2];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int r = min(r0 + 16 * u + slot, row_end - 1);
-            const char* kp = Kb + static_cast<size_t>(r) * RB;
-            const char* vp = Vb + static_cast<size_t>(r) * RB;
-            kr[u][0] = load16_stream(kp);
-            kr[u][1] = load16_stream(kp + 64);
-            vr[u][0] = load16_stream(vp);
-            vr[u][1] = load16_stream(vp + 64);
-        }
-        float sc[U][GROUP];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const bool valid = r0 + 16 * u + slot < row_end;
-            const bf16x8 b0 = __builtin_bit_cast(bf16x8, kr[u][0]);
-            const bf16x8 b1 = __builtin_bit_cast(bf16x8, kr[u][1]);
-#pragma unroll
-            for (int p = 0; p < P; ++p) {
-                f32x4 c = {0.f, 0.f, 0.f, 0.f};
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_hi[p][0], b0, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_lo[p][0], b0, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_hi[p][1], b1, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_lo[p][1], b1, c, 0, 0, 0);
-                // output row 4j + r of the instruction is head 4p + r, column = this lane's row
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sc[u][4 * p + r] = valid ? c[r] : -INFINITY;
-            }
-        }
-        float vf[U][16];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            unpack<2>(vr[u][0], *reinterpret_cast<float(*)[8]>(&vf[u][0]));
-            unpack<2>(vr[u][1], *reinterpret_cast<float(*)[8]>(&vf[u][8]));
-        }
-#pragma unroll
-        for (int h = 0; h < GROUP; ++h) {
-            float mx = sc[0][h];
-#pragma unroll
-            for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u][h]);
-            mx = row_max16(mx);
-            const float mn = fmaxf(m[h], mx);
-            const float alpha = fast_exp2(m[h] - mn);
-            m[h] = mn;
-            float pu[U];
-            float ps = 0.f;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                pu[u] = fast_exp2(sc[u][h] - mn);
-                ps += pu[u];
-            }
-            lp[h] = fmaf(lp[h], alpha, ps);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float acc = o[h][e] * alpha;
-#pragma unroll
-                for (int u = 0; u < U; ++u) acc = fmaf(pu[u], vf[u][e], acc);
-                o[h][e] = acc;
-            }
-        }
-    }
-
-    // Sum l and o over the 16 row slots (m is already uniform).
-#pragma unroll
-    for (int h = 0; h < GROUP; ++h) {
-        lp[h] = row_sum<16>(lp[h]);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[h][e] = row_sum<16>(o[h][e]);
-    }
+    // l: sum over the four G groups (the i & ~3 lanes of a group repeat it)
+    lpart += __shfl_xor(lpart, 16);
+    lpart += __shfl_xor(lpart, 32);
 
     __shared__ float sm_o[WAVES][GROUP][kHeadDim];
     __shared__ float sm_m[WAVES][GROUP];
     __shared__ float sm_l[WAVES][GROUP];
-    // lane (j, slot) stores element `slot` of its 16: dim 8j + slot, or
-    // 32 + 8j + slot - 8 for the second half
-    const int my_dim = slot < 8 ? 8 * j + slot : 32 + 8 * j + (slot - 8);
+    if (G == 0) {
 #pragma unroll
-    for (int h = 0; h < GROUP; ++h) {
-        float mine = o[h][0];
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int e = 1; e < 16; ++e) mine = (slot == e) ? o[h][e] : mine;
-        sm_o[wave][h][my_dim] = mine;
-        if (lane == 0) {
-            sm_m[wave][h] = m[h];
-            sm_l[wave][h] = lp[h];
-        }
+            for (int rr = 0; rr < 4; ++rr) sm_o[wave][rr][16 * c + i] = o[c][rr];
+    }
+    if (lane < GROUP) {
+        sm_m[wave][lane] = m;
+        sm_l[wave][lane] = lpart;
     }
     finish_block<WAVES, GROUP>(sm_o, sm_m, sm_l, wave, lane, loc, g, Hq, out, part_o, part_ml);
 }
@@ -734,14 +756,14 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int GROUP, int WAVES, int U>
+template <int GROUP, int WAVES>
 hipError_t attend_gqa_t(const AttendArgs& a, hipStream_t s)
 {
     char* ws = static_cast<char*>(a.ws);
     float* po = reinterpret_cast<float*>(ws + a.part.o_offset);
     float2* pml = reinterpret_cast<float2*>(ws + a.part.ml_offset);
     const dim3 grid(static_cast<unsigned>(a.n_chunks), a.n_kv_heads), block(WAVES * 64);
-    hipLaunchKernelGGL((attend_gqa_mfma_kernel<GROUP, WAVES, U>), grid, block, 0, s, a.q,
+    hipLaunchKernelGGL((attend_gqa_mfma_kernel<GROUP, WAVES>), grid, block, 0, s, a.q,
                        static_cast<const char*>(a.k), static_cast<const char*>(a.v), a.lens,
                        a.batch, a.n_kv_heads, a.cap_pad, a.chunk_rows, a.qscale, a.out, po, pml);
     hipError_t e = hipGetLastError();
@@ -758,7 +780,7 @@ hipError_t attend_dispatch_group(const AttendArgs& a, hipStream_t s)
 {
     if constexpr (ESZ == 2) {
         // bf16 K/V with 4 query heads per KV head: scores on MFMA
-        if (a.group == 4) return attend_gqa_t<4, 4, 2>(a, s);
+        if (a.group == 4) return attend_gqa_t<4, 4>(a, s);
     }
     switch (a.group) {
         case 1: return attend_t<ESZ, 1>(a, s);
