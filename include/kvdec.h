@@ -64,6 +64,11 @@ typedef struct kvdec_cache kvdec_cache;
  *          elements of `dtype`.  One row is 256 B (f32) or 128 B (bf16), so a
  *          (sequence, KV head) pair is one contiguous run of rows.
  *   lens : (device) int32[batch], rows currently held per sequence.
+ * Sliding-window ring (window == capacity, dynamic caches only): lens[b]
+ * counts every token the sequence has seen; token t lives in row t % window,
+ * and attention reads the last min(lens[b], window) tokens -- the circular
+ * buffer of [WA-DEC] `CircularKVBuffer` (slot = position mod window) and the
+ * window of [WA-DEC] `StreamingKVCache`.  Appends never overflow a ring.
  * This is the head-first GPU cache of [WA-CUDA]
  * `init_gpu_decoder_kv_cache_head_first` ([n_heads, max_seq_len, head_dim] per
  * layer) extended by a batch axis and row padding; one handle is one layer's
@@ -78,6 +83,8 @@ typedef struct {
     int32_t capacity;    /* rows each sequence may hold, >= 1 */
     int32_t dtype;       /* kvdec_dtype */
     int32_t is_static;   /* 0: self cache (appendable); 1: static encoder cache */
+    int32_t window;      /* 0: linear cache; == capacity: sliding-window ring (see below) */
+    int32_t reserved0;   /* must be 0 */
     void* k;             /* (device) */
     void* v;             /* (device) */
     int32_t* lens;       /* (device) */
@@ -90,8 +97,9 @@ int32_t kvdec_padded_capacity(int32_t capacity);
 /* Create a handle over caller-owned memory and write the initial lengths
  * lens_host[batch] (host) to desc->lens on `stream`.  Cache contents are not
  * touched.  Errors: KVDEC_E_INVALID (NULL/misaligned pointers, batch < 1,
- * unknown dtype), KVDEC_E_SHAPE (head_dim != 64, a length outside
- * [0, capacity]).  *out receives the handle (host). */
+ * unknown dtype, a static ring, reserved0 != 0), KVDEC_E_SHAPE (head_dim !=
+ * 64, window not 0 or capacity, a length outside [0, capacity] for a linear
+ * cache or negative for a ring).  *out receives the handle (host). */
 int32_t kvdec_cache_create(const kvdec_cache_desc* desc, const int32_t* lens_host,
                            void* stream, kvdec_cache** out);
 

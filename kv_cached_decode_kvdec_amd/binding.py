@@ -42,6 +42,7 @@ class CacheDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("capacity", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("is_static", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("reserved0", ctypes.c_int32),
                 ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("lens", ctypes.c_void_p)]
 
 

@@ -42,7 +42,7 @@ def _ptr(t):
 
 class KVCache:
     def __init__(self, batch, n_kv_heads, capacity, dtype="f32", static=False, lens=None,
-                 device="cuda", k=None, v=None):
+                 device="cuda", k=None, v=None, window=0):
         self.batch, self.n_kv_heads, self.capacity = int(batch), int(n_kv_heads), int(capacity)
         self.dtype, self.static = dtype, bool(static)
         self.cap_pad = B.kvdec_padded_capacity(capacity)
@@ -54,8 +54,9 @@ class KVCache:
             if tuple(t.shape) != shape or t.dtype != tdt or not t.is_contiguous():
                 raise ValueError(f"cache tensor must be contiguous {shape} {tdt}")
         self.lens_dev = torch.zeros(self.batch, dtype=torch.int32, device=device)
+        self.window = int(window)
         self.desc = B.CacheDesc(self.batch, self.n_kv_heads, B.HEAD_DIM, self.capacity,
-                                _CODE[dtype], int(self.static), self.k.data_ptr(),
+                                _CODE[dtype], int(self.static), self.window, 0, self.k.data_ptr(),
                                 self.v.data_ptr(), self.lens_dev.data_ptr())
         lens = [0] * self.batch if lens is None else [int(x) for x in lens]
         self.handle = B.kvdec_cache_create(self.desc, lens, current_stream())

@@ -45,14 +45,26 @@ int32_t hip_fail(hipError_t e, const char* what)
     return fail(KVDEC_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-int32_t check_lens(const int32_t* lens_host, int32_t batch, int32_t capacity)
+// Lengths count the tokens a sequence holds.  A linear cache holds at most
+// `capacity`; a sliding-window ring counts every token it has seen (it keeps
+// the last `window` of them), so any non-negative length is valid.
+int32_t check_lens(const int32_t* lens_host, int32_t batch, int32_t capacity, int32_t window)
 {
     if (!lens_host) return fail(KVDEC_E_INVALID, "lens_host is NULL");
     for (int32_t b = 0; b < batch; ++b)
-        if (lens_host[b] < 0 || lens_host[b] > capacity)
+        if (lens_host[b] < 0 || (window == 0 && lens_host[b] > capacity))
             return fail(KVDEC_E_SHAPE, "length %d of sequence %d outside [0, %d]", lens_host[b], b,
                         capacity);
     return KVDEC_OK;
+}
+
+// Rows an attend call reads per sequence: min(len, window) for a ring.
+std::vector<int32_t> attended_rows(const kvdec_cache* c)
+{
+    std::vector<int32_t> r(c->lens);
+    if (c->d.window > 0)
+        for (auto& x : r) x = x < c->d.window ? x : c->d.window;
+    return r;
 }
 
 int64_t chunks_for(const std::vector<int32_t>& lens, int32_t T)
@@ -65,18 +77,18 @@ int64_t chunks_for(const std::vector<int32_t>& lens, int32_t T)
     return n;
 }
 
-// Automatic chunk size (rows per workgroup), measured on MI355X:
-//  - with at least kPairsOneChunk (sequence, KV head) pairs and lengths within
-//    2x of their mean, one chunk per sequence: enough workgroups to fill the
-//    256 CUs, even work per workgroup, and no merge launch;
-//  - otherwise the largest power of two in [64, 4096] that still gives at
-//    least kTargetBlocks workgroups (a few per CU, so ragged lengths balance)
-//    -- at this size the merge traffic is well under 1% of the K/V bytes.
-constexpr int64_t kPairsOneChunk = 1024;
-constexpr int64_t kTargetBlocks = 1536;
-
-int32_t auto_chunk(const std::vector<int32_t>& lens, int32_t n_kv_heads)
+// Automatic chunk size (rows per workgroup), from sweeps on MI355X, in
+// terms of R = attend workgroups resident at once on the device:
+//  - one chunk per sequence when the (sequence, KV head) pairs alone give at
+//    least R/2 workgroups and lengths are within 2x of their mean: even work
+//    per workgroup and no merge launch;
+//  - otherwise the largest power of two in [64, 4096] that still gives about
+//    one full residency round (>= 0.85 R workgroups), so ragged lengths
+//    balance over the CUs while the merge traffic stays well under 1% of the
+//    K/V bytes.
+int32_t auto_chunk(const std::vector<int32_t>& lens, int32_t n_kv_heads, int64_t resident)
 {
+    if (resident <= 0) resident = 2048;
     int64_t total = 0;
     int32_t longest = 0;
     for (int32_t l : lens) {
@@ -84,14 +96,15 @@ int32_t auto_chunk(const std::vector<int32_t>& lens, int32_t n_kv_heads)
         longest = l > longest ? l : longest;
     }
     const int64_t pairs = static_cast<int64_t>(lens.size()) * n_kv_heads;
-    if (pairs >= kPairsOneChunk && longest <= KVDEC_MAX_CHUNK &&
+    if (2 * pairs >= resident && longest <= KVDEC_MAX_CHUNK &&
         static_cast<int64_t>(longest) * static_cast<int64_t>(lens.size()) <= 2 * total) {
         int32_t T = KVDEC_MIN_CHUNK;
         while (T < longest) T <<= 1;
         return T;
     }
+    const int64_t target = resident * 85 / 100;
     for (int32_t T = KVDEC_MAX_CHUNK; T > KVDEC_MIN_CHUNK; T >>= 1)
-        if (chunks_for(lens, T) * n_kv_heads >= kTargetBlocks) return T;
+        if (chunks_for(lens, T) * n_kv_heads >= target) return T;
     return KVDEC_MIN_CHUNK;
 }
 
@@ -131,8 +144,12 @@ int32_t attend_common(const kvdec_cache* c, const float* q, int32_t n_q_heads, f
     a.n_kv_heads = c->d.n_kv_heads;
     a.group = group;
     a.cap_pad = c->cap_pad;
-    a.chunk_rows = chunk_rows ? chunk_rows : auto_chunk(c->lens, c->d.n_kv_heads);
-    a.n_chunks = chunks_for(c->lens, a.chunk_rows);
+    const std::vector<int32_t> rows = attended_rows(c);
+    a.row_limit = c->d.window > 0 ? c->d.window : c->d.capacity;
+    a.chunk_rows = chunk_rows ? chunk_rows
+                              : auto_chunk(rows, c->d.n_kv_heads,
+                                           kvdec::resident_attend_blocks(c->d.dtype, group));
+    a.n_chunks = chunks_for(rows, a.chunk_rows);
     a.need_merge = a.n_chunks > c->d.batch;   // some sequence has more than one chunk
     a.qscale = scale * 1.4426950408889634f;
     a.out = out;
@@ -169,11 +186,17 @@ int32_t kvdec_cache_create(const kvdec_cache_desc* desc, const int32_t* lens_hos
     if (d.dtype != KVDEC_F32 && d.dtype != KVDEC_BF16)
         return fail(KVDEC_E_INVALID, "unknown dtype %d", d.dtype);
     if (d.is_static != 0 && d.is_static != 1) return fail(KVDEC_E_INVALID, "is_static must be 0 or 1");
+    if (d.window != 0 && d.window != d.capacity)
+        return fail(KVDEC_E_SHAPE, "window must be 0 or equal to capacity (%d), got %d", d.capacity,
+                    d.window);
+    if (d.window != 0 && d.is_static)
+        return fail(KVDEC_E_INVALID, "a static (encoder) cache cannot be a sliding-window ring");
+    if (d.reserved0 != 0) return fail(KVDEC_E_INVALID, "reserved0 must be 0");
     if (!aligned16(d.k) || !aligned16(d.v) || !aligned16(d.lens))
         return fail(KVDEC_E_INVALID, "k, v and lens must be non-NULL, 16-byte aligned device pointers");
     const int32_t cap_pad = kvdec_padded_capacity(d.capacity);
     if (cap_pad == 0) return fail(KVDEC_E_SHAPE, "capacity %d too large", d.capacity);
-    int32_t rc = check_lens(lens_host, d.batch, d.capacity);
+    int32_t rc = check_lens(lens_host, d.batch, d.capacity, d.window);
     if (rc) return rc;
     kvdec_cache* c = new kvdec_cache;
     c->d = d;
@@ -195,7 +218,7 @@ int32_t kvdec_reset_lens(kvdec_cache* c, const int32_t* lens_host, void* stream)
 {
     g_err.clear();
     if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
-    int32_t rc = check_lens(lens_host, c->d.batch, c->d.capacity);
+    int32_t rc = check_lens(lens_host, c->d.batch, c->d.capacity, c->d.window);
     if (rc) return rc;
     const hipError_t e = kvdec::launch_set_lens(c->d.lens, lens_host, c->d.batch,
                                                 static_cast<hipStream_t>(stream));
@@ -238,13 +261,17 @@ int32_t kvdec_append(kvdec_cache* c, const void* k_new, const void* v_new, void*
     if (c->d.is_static) return fail(KVDEC_E_STATIC, "append on a static (encoder) cache");
     if (!aligned16(k_new) || !aligned16(v_new))
         return fail(KVDEC_E_INVALID, "k_new and v_new must be non-NULL, 16-byte aligned device pointers");
-    for (int32_t b = 0; b < c->d.batch; ++b)
-        if (c->lens[b] + 1 > c->d.capacity)
+    for (int32_t b = 0; b < c->d.batch; ++b) {
+        if (c->d.window == 0 && c->lens[b] + 1 > c->d.capacity)
             return fail(KVDEC_E_OVERFLOW, "cache overflow: sequence %d holds %d + 1 > %d", b,
                         c->lens[b], c->d.capacity);
+        if (c->lens[b] == INT32_MAX)
+            return fail(KVDEC_E_OVERFLOW, "token count of sequence %d would overflow int32", b);
+    }
     const hipError_t e = kvdec::launch_append(c->d.dtype, c->d.k, c->d.v, k_new, v_new, c->d.lens,
                                               c->d.batch, c->d.n_kv_heads, c->d.capacity,
-                                              c->cap_pad, static_cast<hipStream_t>(stream));
+                                              c->cap_pad, c->d.window,
+                                              static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "append launch");
     for (auto& l : c->lens) ++l;
     return KVDEC_OK;

@@ -33,7 +33,8 @@ struct AttendArgs {
     int32_t batch;
     int32_t n_kv_heads;
     int32_t group;          // query heads per KV head
-    int32_t cap_pad;        // padded rows per (sequence, KV head)
+    int32_t cap_pad;        // padded rows per (sequence, KV head): the row stride
+    int32_t row_limit;      // rows attended are min(len, row_limit)
     int32_t chunk_rows;     // rows per split-sequence chunk
     int64_t n_chunks;       // sum over sequences of max(1, ceil(len / chunk_rows))
     bool need_merge;        // some sequence spans more than one chunk
@@ -46,10 +47,14 @@ struct AttendArgs {
 hipError_t launch_set_lens(int32_t* lens, const int32_t* host, int32_t n, hipStream_t s);
 hipError_t launch_append(int dtype, void* k, void* v, const void* k_new, const void* v_new,
                          int32_t* lens, int32_t batch, int32_t n_kv_heads, int32_t capacity,
-                         int32_t cap_pad, hipStream_t s);
+                         int32_t cap_pad, int32_t window, hipStream_t s);
 hipError_t launch_seed(int dtype, void* k, void* v, const void* k_tok, const void* v_tok,
                        int32_t batch, int32_t rows, int32_t n_kv_heads, int32_t cap_pad,
                        hipStream_t s);
 hipError_t launch_attend(int dtype, const AttendArgs& a, hipStream_t s);
+
+// Workgroups of the attend kernel for (dtype, group) that are resident on the
+// current device at once (occupancy x compute units); 0 if unknown.  Cached.
+int resident_attend_blocks(int dtype, int group);
 
 }  // namespace kvdec

@@ -29,6 +29,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
+#include "../../include/kvdec.h"
 #include "kvdec_internal.h"
 
 namespace kvdec {
@@ -210,12 +213,15 @@ __global__ __launch_bounds__(256) void append_kernel(char* __restrict__ K, char*
                                                      const char* __restrict__ kn,
                                                      const char* __restrict__ vn,
                                                      int32_t* __restrict__ lens, int Hkv,
-                                                     int capacity, int cap_pad)
+                                                     int capacity, int cap_pad, int window)
 {
     constexpr int VPR = ROW_BYTES / 16;
     const int b = blockIdx.x;
     const int len = lens[b];
-    if (len < 0 || len >= capacity) return;     // host already rejected this
+    // linear cache: row `len`, refused at capacity (the host already rejected
+    // it); sliding-window ring: slot len % window, the oldest row is replaced
+    if (len < 0 || len == INT32_MAX || (window == 0 && len >= capacity)) return;
+    const int slot = window > 0 ? len % window : len;
     const int n = Hkv * VPR;
     for (int t = threadIdx.x; t < 2 * n; t += blockDim.x) {
         const bool isv = t >= n;
@@ -224,7 +230,7 @@ __global__ __launch_bounds__(256) void append_kernel(char* __restrict__ K, char*
         const size_t hg = static_cast<size_t>(b) * Hkv + g;
         const uint4* src = reinterpret_cast<const uint4*>((isv ? vn : kn) + hg * ROW_BYTES) + w;
         uint4* dst = reinterpret_cast<uint4*>((isv ? V : K) +
-                                              (hg * cap_pad + len) * ROW_BYTES) + w;
+                                              (hg * cap_pad + slot) * ROW_BYTES) + w;
         *dst = *src;
     }
     __syncthreads();
@@ -270,8 +276,8 @@ __global__ __launch_bounds__(256) void seed_kernel(char* __restrict__ K, char* _
 template <int ESZ, int GROUP, int WAVES, int U>
 __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
-    const int32_t* __restrict__ lens, int B, int Hkv, int cap_pad, int T, float qscale,
-    float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml)
+    const int32_t* __restrict__ lens, int B, int Hkv, int cap_pad, int row_limit, int T,
+    float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml)
 {
     using L = Lay<ESZ>;
     constexpr int EPL = L::kEPL, LPR = L::kLPR, RPI = L::kRPI, RB = L::kRowBytes;
@@ -283,7 +289,7 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
     const int Hq = Hkv * GROUP;
 
     Located loc;
-    if (!locate(lens, B, T, cap_pad, blockIdx.x, lane, loc)) return;
+    if (!locate(lens, B, T, row_limit, blockIdx.x, lane, loc)) return;
     const int row0 = loc.c * T;
     const int row_end = min(loc.len, row0 + T);
 
@@ -432,8 +438,8 @@ constexpr int kGqaLdsStride = 160;     // bytes per staged V row (conflict-free 
 template <int GROUP, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
-    const int32_t* __restrict__ lens, int B, int Hkv, int cap_pad, int T, float qscale,
-    float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml)
+    const int32_t* __restrict__ lens, int B, int Hkv, int cap_pad, int row_limit, int T,
+    float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml)
 {
     static_assert(GROUP == 4, "MFMA path takes groups of 4 query heads");
     constexpr int RB = 128;                // bf16 row bytes
@@ -448,7 +454,7 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
     __shared__ __attribute__((aligned(16))) char sm_v[WAVES][32 * kGqaLdsStride];
 
     Located loc;
-    if (!locate(lens, B, T, cap_pad, blockIdx.x, lane, loc)) return;
+    if (!locate(lens, B, T, row_limit, blockIdx.x, lane, loc)) return;
     const int row0 = loc.c * T;
     const int row_end = min(loc.len, row0 + T);
 
@@ -599,7 +605,7 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
 // in chunk order (a fixed order: the result does not depend on scheduling).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ lens, int B, int Hq,
-                                                    int T, int cap_pad,
+                                                    int T, int row_limit,
                                                     const float* __restrict__ part_o,
                                                     const float2* __restrict__ part_ml,
                                                     float* __restrict__ out)
@@ -612,11 +618,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
     int acc = 0;
     for (int b0 = 0; b0 < b; b0 += 64) {
         const int bi = b0 + lane;
-        if (bi < b) acc += max(1, (min(max(lens[bi], 0), cap_pad) + T - 1) / T);
+        if (bi < b) acc += max(1, (min(max(lens[bi], 0), row_limit) + T - 1) / T);
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
-    const int nch = max(1, (min(max(lens[b], 0), cap_pad) + T - 1) / T);
+    const int nch = max(1, (min(max(lens[b], 0), row_limit) + T - 1) / T);
     if (nch == 1) return;     // finished by the attend kernel
     const size_t first = static_cast<size_t>(acc);
 
@@ -698,17 +704,17 @@ hipError_t launch_set_lens(int32_t* lens, const int32_t* host, int32_t n, hipStr
 
 hipError_t launch_append(int dtype, void* k, void* v, const void* k_new, const void* v_new,
                          int32_t* lens, int32_t batch, int32_t n_kv_heads, int32_t capacity,
-                         int32_t cap_pad, hipStream_t s)
+                         int32_t cap_pad, int32_t window, hipStream_t s)
 {
     const dim3 grid(batch), block(256);
     if (dtype == 0)
         hipLaunchKernelGGL(append_kernel<256>, grid, block, 0, s, static_cast<char*>(k),
                            static_cast<char*>(v), static_cast<const char*>(k_new),
-                           static_cast<const char*>(v_new), lens, n_kv_heads, capacity, cap_pad);
+                           static_cast<const char*>(v_new), lens, n_kv_heads, capacity, cap_pad, window);
     else
         hipLaunchKernelGGL(append_kernel<128>, grid, block, 0, s, static_cast<char*>(k),
                            static_cast<char*>(v), static_cast<const char*>(k_new),
-                           static_cast<const char*>(v_new), lens, n_kv_heads, capacity, cap_pad);
+                           static_cast<const char*>(v_new), lens, n_kv_heads, capacity, cap_pad, window);
     return hipGetLastError();
 }
 
@@ -746,13 +752,14 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
     const dim3 grid(static_cast<unsigned>(a.n_chunks), a.n_kv_heads), block(kWaves * 64);
     hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWaves, kUnroll>), grid, block, 0, s, a.q,
                        static_cast<const char*>(a.k), static_cast<const char*>(a.v), a.lens,
-                       a.batch, a.n_kv_heads, a.cap_pad, a.chunk_rows, a.qscale, a.out, po, pml);
+                       a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows, a.qscale,
+                       a.out, po, pml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.need_merge) return e;
     const int Hq = a.n_kv_heads * GROUP;
     const int waves = a.batch * Hq;
     hipLaunchKernelGGL(merge_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, a.lens, a.batch, Hq,
-                       a.chunk_rows, a.cap_pad, po, pml, a.out);
+                       a.chunk_rows, a.row_limit, po, pml, a.out);
     return hipGetLastError();
 }
 
@@ -765,13 +772,14 @@ hipError_t attend_gqa_t(const AttendArgs& a, hipStream_t s)
     const dim3 grid(static_cast<unsigned>(a.n_chunks), a.n_kv_heads), block(WAVES * 64);
     hipLaunchKernelGGL((attend_gqa_mfma_kernel<GROUP, WAVES>), grid, block, 0, s, a.q,
                        static_cast<const char*>(a.k), static_cast<const char*>(a.v), a.lens,
-                       a.batch, a.n_kv_heads, a.cap_pad, a.chunk_rows, a.qscale, a.out, po, pml);
+                       a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows, a.qscale,
+                       a.out, po, pml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.need_merge) return e;
     const int Hq = a.n_kv_heads * GROUP;
     const int waves = a.batch * Hq;
     hipLaunchKernelGGL(merge_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, a.lens, a.batch, Hq,
-                       a.chunk_rows, a.cap_pad, po, pml, a.out);
+                       a.chunk_rows, a.row_limit, po, pml, a.out);
     return hipGetLastError();
 }
 
@@ -796,6 +804,51 @@ hipError_t attend_dispatch_group(const AttendArgs& a, hipStream_t s)
 }
 
 }  // namespace
+
+namespace {
+
+template <int ESZ>
+const void* attend_kernel_ptr(int group, int* block)
+{
+    *block = kWaves * 64;
+    if constexpr (ESZ == 2)
+        if (group == 4) return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<4, kWaves>);
+    switch (group) {
+        case 1: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 1, kWaves, kUnroll>);
+        case 2: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 2, kWaves, kUnroll>);
+        case 3: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 3, kWaves, kUnroll>);
+        case 4: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 4, kWaves, kUnroll>);
+        case 5: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 5, kWaves, kUnroll>);
+        case 6: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 6, kWaves, kUnroll>);
+        case 7: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 7, kWaves, kUnroll>);
+        case 8: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 8, kWaves, kUnroll>);
+        default: return nullptr;
+    }
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_resident[kMaxDevices][2][KVDEC_MAX_GROUP + 1];
+
+}  // namespace
+
+int resident_attend_blocks(int dtype, int group)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    if (group < 1 || group > KVDEC_MAX_GROUP) return 0;
+    std::atomic<int>& slot = g_resident[dev][dtype == 0 ? 0 : 1][group];
+    int cached = slot.load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+    int block = 0;
+    const void* fn = dtype == 0 ? attend_kernel_ptr<4>(group, &block) : attend_kernel_ptr<2>(group, &block);
+    int per_cu = 0, cus = 0;
+    if (!fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    const int n = per_cu * cus;
+    if (n > 0) slot.store(n, std::memory_order_relaxed);
+    return n;
+}
 
 hipError_t launch_attend(int dtype, const AttendArgs& a, hipStream_t s)
 {

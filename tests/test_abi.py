@@ -47,7 +47,7 @@ def test_padded_capacity():
 
 def _desc(**kw):
     d = dict(batch=2, n_kv_heads=2, head_dim=64, capacity=10, dtype=0, is_static=0,
-             k=4096, v=8192, lens=12288)
+             window=0, reserved0=0, k=4096, v=8192, lens=12288)
     d.update(kw)
     return B.CacheDesc(**d)
 
@@ -63,6 +63,9 @@ def _desc(**kw):
     (dict(k=0), B.KVDEC_E_INVALID),
     (dict(v=8200), B.KVDEC_E_INVALID),       # not 16-byte aligned
     (dict(lens=0), B.KVDEC_E_INVALID),
+    (dict(window=5), B.KVDEC_E_SHAPE),          # a ring's window equals its capacity
+    (dict(window=10, is_static=1), B.KVDEC_E_INVALID),
+    (dict(reserved0=1), B.KVDEC_E_INVALID),
 ])
 def test_create_rejects_bad_descriptions(kw, code):
     with pytest.raises(B.KvdecError) as e:
@@ -76,6 +79,18 @@ def test_create_rejects_lengths_outside_capacity(lens):
     with pytest.raises(B.KvdecError) as e:
         B.kvdec_cache_create(_desc(), lens)
     assert e.value.code == B.KVDEC_E_SHAPE
+
+
+def test_ring_accepts_lengths_beyond_capacity_but_not_negative():
+    with pytest.raises(B.KvdecError) as e:
+        B.kvdec_cache_create(_desc(window=10), [-3, 0])
+    assert e.value.code == B.KVDEC_E_SHAPE
+    # a length beyond the window passes validation; with no GPU the call then
+    # fails at the device step (set lengths), not at the check
+    try:
+        B.kvdec_cache_create(_desc(window=10), [25, 3])
+    except B.KvdecError as e2:
+        assert e2.code == B.KVDEC_E_HIP
 
 
 def test_null_handle_calls_fail_cleanly():
