@@ -186,6 +186,24 @@ int32_t kvdec_attend_cross(const kvdec_cache* cache, const float* q, int32_t n_q
                            float scale, int32_t chunk_rows, float* out, void* ws,
                            size_t ws_bytes, void* stream);
 
+/*
+ * Replay mode, for decode steps captured once in a HIP graph and replayed
+ * for consecutive tokens (the graph-replayed decoder step of [WA-CUDA]
+ * `forward_decoder_token_gpu_stream`: one stream, no host synchronisation).
+ * chunk_rows > 0 (a multiple of 64 in [KVDEC_MIN_CHUNK, KVDEC_MAX_CHUNK])
+ * enters replay mode with that fixed chunk size; 0 leaves it.  In replay
+ * mode every attend call is launched for the most rows a sequence can hold
+ * (capacity, or the window of a ring) and the merge launch is always made
+ * when a sequence can span several chunks, so the launches read the current
+ * lengths from the device and stay valid as appends inside replays grow
+ * them.  The host mirror of the lengths is not advanced by replays, so
+ * kvdec_append does not check capacity on the host in replay mode; on the
+ * device an append to a full linear cache writes nothing and leaves the
+ * length unchanged (a ring never fills).  kvdec_reset_lens keeps working and
+ * is capturable.  Errors: KVDEC_E_INVALID.
+ */
+int32_t kvdec_set_replay_mode(kvdec_cache* cache, int32_t chunk_rows);
+
 /* Static description of a status code. */
 const char* kvdec_status_str(int32_t status);
 

@@ -28,7 +28,8 @@ MAX_GROUP = 8
 EXPORTED = [
     "kvdec_padded_capacity", "kvdec_cache_create", "kvdec_cache_destroy", "kvdec_reset_lens",
     "kvdec_get_lens", "kvdec_seed", "kvdec_append", "kvdec_workspace_bytes",
-    "kvdec_attend_self", "kvdec_attend_cross", "kvdec_status_str", "kvdec_last_error",
+    "kvdec_attend_self", "kvdec_attend_cross", "kvdec_set_replay_mode", "kvdec_status_str",
+    "kvdec_last_error",
 ]
 
 
@@ -70,6 +71,7 @@ def load():
         "kvdec_workspace_bytes": (_sz, [_vp, _i32]),
         "kvdec_attend_self": (_i32, [_vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz, _vp]),
         "kvdec_attend_cross": (_i32, [_vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz, _vp]),
+        "kvdec_set_replay_mode": (_i32, [_vp, _i32]),
         "kvdec_status_str": (ctypes.c_char_p, [_i32]),
         "kvdec_last_error": (ctypes.c_char_p, []),
     }
@@ -144,3 +146,7 @@ def kvdec_attend_cross(handle, q_ptr, n_q_heads, scale, chunk_rows, out_ptr, ws_
                        stream=None):
     _check(load().kvdec_attend_cross(handle, q_ptr, int(n_q_heads), float(scale), int(chunk_rows),
                                      out_ptr, ws_ptr, int(ws_bytes), stream), "kvdec_attend_cross")
+
+
+def kvdec_set_replay_mode(handle, chunk_rows):
+    _check(load().kvdec_set_replay_mode(handle, int(chunk_rows)), "kvdec_set_replay_mode")

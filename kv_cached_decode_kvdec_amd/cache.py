@@ -69,6 +69,9 @@ class KVCache:
     def reset_lens(self, lens):
         B.kvdec_reset_lens(self.handle, [int(x) for x in lens], current_stream())
 
+    def set_replay_mode(self, chunk_rows):
+        B.kvdec_set_replay_mode(self.handle, chunk_rows)
+
     def close(self):
         if getattr(self, "handle", None):
             B.kvdec_cache_destroy(self.handle)

@@ -19,6 +19,7 @@ struct kvdec_cache {
     kvdec_cache_desc d;
     int32_t cap_pad;
     std::vector<int32_t> lens;   // host mirror of d.lens
+    int32_t replay_chunk = 0;    // > 0: replay mode with this fixed chunk size
 };
 
 namespace {
@@ -144,13 +145,24 @@ int32_t attend_common(const kvdec_cache* c, const float* q, int32_t n_q_heads, f
     a.n_kv_heads = c->d.n_kv_heads;
     a.group = group;
     a.cap_pad = c->cap_pad;
-    const std::vector<int32_t> rows = attended_rows(c);
     a.row_limit = c->d.window > 0 ? c->d.window : c->d.capacity;
-    a.chunk_rows = chunk_rows ? chunk_rows
-                              : auto_chunk(rows, c->d.n_kv_heads,
-                                           kvdec::resident_attend_blocks(c->d.dtype, group));
-    a.n_chunks = chunks_for(rows, a.chunk_rows);
-    a.need_merge = a.n_chunks > c->d.batch;   // some sequence has more than one chunk
+    if (c->replay_chunk > 0) {
+        // Replay mode: sized for the most rows any sequence can hold, so the
+        // launch stays valid while the device lengths grow between graph
+        // replays (surplus workgroups exit at once; the merge checks every
+        // sequence's chunk count on the device).
+        a.chunk_rows = chunk_rows ? chunk_rows : c->replay_chunk;
+        const int64_t per_seq = (static_cast<int64_t>(a.row_limit) + a.chunk_rows - 1) / a.chunk_rows;
+        a.n_chunks = static_cast<int64_t>(c->d.batch) * (per_seq > 0 ? per_seq : 1);
+        a.need_merge = per_seq > 1;
+    } else {
+        const std::vector<int32_t> rows = attended_rows(c);
+        a.chunk_rows = chunk_rows ? chunk_rows
+                                  : auto_chunk(rows, c->d.n_kv_heads,
+                                               kvdec::resident_attend_blocks(c->d.dtype, group));
+        a.n_chunks = chunks_for(rows, a.chunk_rows);
+        a.need_merge = a.n_chunks > c->d.batch;   // some sequence has more than one chunk
+    }
     a.qscale = scale * 1.4426950408889634f;
     a.out = out;
     a.ws = ws;
@@ -261,7 +273,7 @@ int32_t kvdec_append(kvdec_cache* c, const void* k_new, const void* v_new, void*
     if (c->d.is_static) return fail(KVDEC_E_STATIC, "append on a static (encoder) cache");
     if (!aligned16(k_new) || !aligned16(v_new))
         return fail(KVDEC_E_INVALID, "k_new and v_new must be non-NULL, 16-byte aligned device pointers");
-    for (int32_t b = 0; b < c->d.batch; ++b) {
+    for (int32_t b = 0; b < c->d.batch && c->replay_chunk == 0; ++b) {
         if (c->d.window == 0 && c->lens[b] + 1 > c->d.capacity)
             return fail(KVDEC_E_OVERFLOW, "cache overflow: sequence %d holds %d + 1 > %d", b,
                         c->lens[b], c->d.capacity);
@@ -299,6 +311,18 @@ int32_t kvdec_attend_cross(const kvdec_cache* c, const float* q, int32_t n_q_hea
     if (c && !c->d.is_static)
         return fail(KVDEC_E_STATIC, "cross-attention needs a static (encoder) cache");
     return attend_common(c, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
+}
+
+int32_t kvdec_set_replay_mode(kvdec_cache* c, int32_t chunk_rows)
+{
+    g_err.clear();
+    if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
+    if (chunk_rows != 0 && (chunk_rows < KVDEC_MIN_CHUNK || chunk_rows > KVDEC_MAX_CHUNK ||
+                            chunk_rows % 64 != 0))
+        return fail(KVDEC_E_INVALID, "chunk_rows %d must be 0 or a multiple of 64 in [%d, %d]",
+                    chunk_rows, KVDEC_MIN_CHUNK, KVDEC_MAX_CHUNK);
+    c->replay_chunk = chunk_rows;
+    return KVDEC_OK;
 }
 
 const char* kvdec_status_str(int32_t s)

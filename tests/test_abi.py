@@ -108,3 +108,8 @@ def test_status_strings():
     for code in range(7):
         assert lib.kvdec_status_str(code).decode()
     assert lib.kvdec_status_str(99).decode() == "unknown status"
+
+
+def test_replay_mode_argument_checks():
+    lib = B.load()
+    assert lib.kvdec_set_replay_mode(None, 64) == B.KVDEC_E_INVALID
