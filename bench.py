@@ -111,8 +111,9 @@ class Bench:
             self.p_wsc = vp(self.ws_cross.data_ptr())
             self.n_wsc = self.ws_cross.numel()
 
-    def step(self, i, events=None):
-        lib, st, s, Hq = self.lib, self.stream, i % self.S, self.wl.n_q_heads
+    def step(self, i, events=None, stream=None):
+        lib, s, Hq = self.lib, i % self.S, self.wl.n_q_heads
+        st = self.stream if stream is None else stream
         if s == 0:
             rc = lib.kvdec_reset_lens(self.h_self, self.lens0_c, st)
             assert rc == 0, lib.kvdec_last_error()
@@ -185,6 +186,39 @@ class Bench:
             res["cold_pct_of_hbm_peak"] = 100.0 * res["cold_gbps"] / HBM_PEAK_GBPS
             del flush
         return res
+
+    def run_graph(self, steps):
+        """The same steps with one workload cycle captured in a HIP graph (the
+        caches in replay mode) and replayed: launch overhead removed."""
+        import ctypes
+        torch = self.torch
+        caches = [self.self_cache] + ([self.cross] if self.cross is not None else [])
+        for c in caches:
+            c.set_replay_mode(-1)
+        # one graph holds whole cycles, at least 32 steps, so the graph launch
+        # itself is amortised
+        per_graph = self.S * max(1, -(-32 // self.S))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for s in range(per_graph):
+                self.step(s, stream=st)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // per_graph)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        for c in caches:
+            c.set_replay_mode(0)
+        n = reps * per_graph
+        step_bytes = reps * (per_graph // self.S) * sum(self.step_bytes)
+        return {"graph_ms_per_step": wall * 1e3 / n, "graph_steps_per_s": n / wall,
+                "graph_gbps": step_bytes / wall / 1e9,
+                "graph_pct_of_hbm_peak": 100.0 * step_bytes / wall / 1e9 / HBM_PEAK_GBPS}
 
     def close(self):
         self.self_cache.close()
@@ -288,6 +322,8 @@ def main():
                     help="comma list of extra workloads to report on stderr/JSON, or 'none'")
     ap.add_argument("--cold-steps", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay measurement")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the plain copy kernel (for counter calibration)")
     args = ap.parse_args()
@@ -326,6 +362,8 @@ def main():
         else:
             res = bench.run(max(K // 2, wl.steps), max(args.warmup // 2, 4),
                             cold_steps=args.cold_steps)
+        if not args.no_graph:
+            res.update(bench.run_graph(max(K // 2, wl.steps)))
         bench.close()
         del bench
         torch.cuda.empty_cache()
@@ -334,7 +372,9 @@ def main():
             f"{res['effective_gbps']:.0f} GB/s ({res['pct_of_hbm_peak']:.1f}% of 8 TB/s); "
             f"cold {res.get('cold_ms_per_step', 0) * 1e3:.1f} us/step "
             f"({res.get('cold_pct_of_hbm_peak', 0):.1f}%); attend kernel "
-            f"{res['attend_avg_us']:.1f} us avg, {res['attend_gbps']:.0f} GB/s")
+            f"{res['attend_avg_us']:.1f} us avg, {res['attend_gbps']:.0f} GB/s; graph replay "
+            f"{res.get('graph_ms_per_step', 0) * 1e3:.1f} us/step "
+            f"({res.get('graph_pct_of_hbm_peak', 0):.1f}%)")
 
     copy_gbps = copy_bandwidth(torch)
     log(f"plain copy kernel: {copy_gbps:.0f} GB/s (read + write)")
@@ -362,6 +402,8 @@ def main():
         "effective_kv_gbps": round(h["effective_gbps"], 1),
         "pct_of_hbm_peak": round(h["pct_of_hbm_peak"], 2),
         "cold_ms_per_step": round(h.get("cold_ms_per_step", 0.0), 5),
+        "graph_ms_per_step": round(h.get("graph_ms_per_step", 0.0), 5),
+        "graph_steps_per_s": round(h.get("graph_steps_per_s", 0.0), 2),
         "cold_pct_of_hbm_peak": round(h.get("cold_pct_of_hbm_peak", 0.0), 2),
         "copy_kernel_gbps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm",

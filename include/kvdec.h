@@ -52,6 +52,7 @@ typedef enum { KVDEC_F32 = 0, KVDEC_BF16 = 1 } kvdec_dtype;
 #define KVDEC_MIN_CHUNK 64     /* smallest split-sequence chunk, rows */
 #define KVDEC_MAX_CHUNK 4096   /* largest split-sequence chunk, rows */
 #define KVDEC_MAX_GROUP 8      /* query heads per KV head supported */
+#define KVDEC_REPLAY_AUTO (-1) /* kvdec_set_replay_mode: pick the chunk from current lengths */
 
 /* Opaque host-side handle: the cache description plus a host mirror of the
  * per-sequence lengths (used for validation and launch sizing, so no call
@@ -191,7 +192,8 @@ int32_t kvdec_attend_cross(const kvdec_cache* cache, const float* q, int32_t n_q
  * for consecutive tokens (the graph-replayed decoder step of [WA-CUDA]
  * `forward_decoder_token_gpu_stream`: one stream, no host synchronisation).
  * chunk_rows > 0 (a multiple of 64 in [KVDEC_MIN_CHUNK, KVDEC_MAX_CHUNK])
- * enters replay mode with that fixed chunk size; 0 leaves it.  In replay
+ * enters replay mode with that fixed chunk size, KVDEC_REPLAY_AUTO with the
+ * automatic choice for the current lengths; 0 leaves it.  In replay
  * mode every attend call is launched for the most rows a sequence can hold
  * (capacity, or the window of a ring) and the merge launch is always made
  * when a sequence can span several chunks, so the launches read the current

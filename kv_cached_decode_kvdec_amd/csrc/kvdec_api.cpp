@@ -317,10 +317,17 @@ int32_t kvdec_set_replay_mode(kvdec_cache* c, int32_t chunk_rows)
 {
     g_err.clear();
     if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
+    if (chunk_rows == KVDEC_REPLAY_AUTO) {
+        // the automatic choice for the current lengths, with the query-head
+        // group of a plain MHA call (the grid shape does not depend on it)
+        c->replay_chunk = auto_chunk(attended_rows(c), c->d.n_kv_heads,
+                                     kvdec::resident_attend_blocks(c->d.dtype, 1));
+        return KVDEC_OK;
+    }
     if (chunk_rows != 0 && (chunk_rows < KVDEC_MIN_CHUNK || chunk_rows > KVDEC_MAX_CHUNK ||
                             chunk_rows % 64 != 0))
-        return fail(KVDEC_E_INVALID, "chunk_rows %d must be 0 or a multiple of 64 in [%d, %d]",
-                    chunk_rows, KVDEC_MIN_CHUNK, KVDEC_MAX_CHUNK);
+        return fail(KVDEC_E_INVALID, "chunk_rows %d must be 0, KVDEC_REPLAY_AUTO or a multiple of "
+                    "64 in [%d, %d]", chunk_rows, KVDEC_MIN_CHUNK, KVDEC_MAX_CHUNK);
     c->replay_chunk = chunk_rows;
     return KVDEC_OK;
 }
