@@ -141,6 +141,25 @@ int32_t kvdec_seed(kvdec_cache* cache, const void* k_tok, const void* v_tok, int
  */
 int32_t kvdec_append(kvdec_cache* cache, const void* k_new, const void* v_new, void* stream);
 
+/*
+ * Append with rotary position embedding: like kvdec_append, but k_new holds
+ * the un-rotated keys; each is rotated at its token's position (the
+ * sequence's length before this append) before it is stored, and, when q is
+ * given, the queries are rotated at the same position into q_rot -- the
+ * order of [FO-Q2] `qwen2_decode_step` (RoPE on q and k, then append, then
+ * attend).  NEOX rotate-half: dims (i, i+32) rotate by pos * theta^(-2i/64)
+ * ([LAT-Q8] `full_attention_step_q8` stride-half pairing; theta = 1e6 for
+ * Qwen2 per [FO-Q2]).  Angles and rotation in double, rounded to float (and
+ * to bf16, nearest even, for bf16 caches).  V rows are copied unchanged.
+ *   q, q_rot : (device) float [batch][n_q_heads][64], both NULL or both
+ *              given; they may be the same buffer.
+ * Errors: those of kvdec_append, plus KVDEC_E_INVALID (theta not a positive
+ * finite number, only one of q / q_rot given) and KVDEC_E_SHAPE (n_q_heads
+ * not a positive multiple of n_kv_heads).
+ */
+int32_t kvdec_append_rope(kvdec_cache* cache, const void* k_new, const void* v_new, float theta,
+                          const float* q, float* q_rot, int32_t n_q_heads, void* stream);
+
 /* Workspace bytes any attend call on `cache` with n_q_heads query heads may
  * need (split-sequence partial results).  Its contents need no
  * initialisation and carry nothing between calls; calls sharing one

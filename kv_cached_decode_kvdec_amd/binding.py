@@ -27,7 +27,7 @@ MAX_GROUP = 8
 
 EXPORTED = [
     "kvdec_padded_capacity", "kvdec_cache_create", "kvdec_cache_destroy", "kvdec_reset_lens",
-    "kvdec_get_lens", "kvdec_seed", "kvdec_append", "kvdec_workspace_bytes",
+    "kvdec_get_lens", "kvdec_seed", "kvdec_append", "kvdec_append_rope", "kvdec_workspace_bytes",
     "kvdec_attend_self", "kvdec_attend_cross", "kvdec_set_replay_mode", "kvdec_status_str",
     "kvdec_last_error",
 ]
@@ -68,6 +68,7 @@ def load():
         "kvdec_get_lens": (_i32, [_vp, _vp]),
         "kvdec_seed": (_i32, [_vp, _vp, _vp, _i32, _vp]),
         "kvdec_append": (_i32, [_vp, _vp, _vp, _vp]),
+        "kvdec_append_rope": (_i32, [_vp, _vp, _vp, ctypes.c_float, _vp, _vp, _i32, _vp]),
         "kvdec_workspace_bytes": (_sz, [_vp, _i32]),
         "kvdec_attend_self": (_i32, [_vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz, _vp]),
         "kvdec_attend_cross": (_i32, [_vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz, _vp]),
@@ -130,6 +131,12 @@ def kvdec_seed(handle, k_tok_ptr, v_tok_ptr, rows, stream=None):
 
 def kvdec_append(handle, k_new_ptr, v_new_ptr, stream=None):
     _check(load().kvdec_append(handle, k_new_ptr, v_new_ptr, stream), "kvdec_append")
+
+
+def kvdec_append_rope(handle, k_new_ptr, v_new_ptr, theta, q_ptr=None, q_rot_ptr=None,
+                      n_q_heads=0, stream=None):
+    _check(load().kvdec_append_rope(handle, k_new_ptr, v_new_ptr, float(theta), q_ptr, q_rot_ptr,
+                                    int(n_q_heads), stream), "kvdec_append_rope")
 
 
 def kvdec_workspace_bytes(handle, n_q_heads):

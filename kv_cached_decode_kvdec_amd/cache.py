@@ -103,6 +103,24 @@ class KVCache:
         self._check_rows(v_new, shape, "v_new")
         B.kvdec_append(self.handle, _ptr(k_new), _ptr(v_new), current_stream())
 
+    def append_rope(self, k_new, v_new, theta, q=None, q_rot=None):
+        """Append un-rotated keys, rotating them (and q into q_rot) at each
+        sequence's current position.  Returns q_rot (or None)."""
+        shape = (self.batch, self.n_kv_heads, B.HEAD_DIM)
+        self._check_rows(k_new, shape, "k_new")
+        self._check_rows(v_new, shape, "v_new")
+        qp = qr = None
+        Hq = 0
+        if q is not None:
+            if q.dtype != torch.float32 or q.dim() != 3 or not q.is_contiguous():
+                raise ValueError("q must be a contiguous float32 [batch, n_q_heads, 64] tensor")
+            if q_rot is None:
+                q_rot = torch.empty_like(q)
+            Hq, qp, qr = q.shape[1], _ptr(q), _ptr(q_rot)
+        B.kvdec_append_rope(self.handle, _ptr(k_new), _ptr(v_new), theta, qp, qr, Hq,
+                            current_stream())
+        return q_rot
+
     def workspace(self, n_q_heads):
         ws = self._ws.get(n_q_heads)
         if ws is None:

@@ -172,6 +172,22 @@ int32_t attend_common(const kvdec_cache* c, const float* q, int32_t n_q_heads, f
     return KVDEC_OK;
 }
 
+int32_t check_append(const kvdec_cache* c, const void* k_new, const void* v_new)
+{
+    if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
+    if (c->d.is_static) return fail(KVDEC_E_STATIC, "append on a static (encoder) cache");
+    if (!aligned16(k_new) || !aligned16(v_new))
+        return fail(KVDEC_E_INVALID, "k_new and v_new must be non-NULL, 16-byte aligned device pointers");
+    for (int32_t b = 0; b < c->d.batch && c->replay_chunk == 0; ++b) {
+        if (c->d.window == 0 && c->lens[b] + 1 > c->d.capacity)
+            return fail(KVDEC_E_OVERFLOW, "cache overflow: sequence %d holds %d + 1 > %d", b,
+                        c->lens[b], c->d.capacity);
+        if (c->lens[b] == INT32_MAX)
+            return fail(KVDEC_E_OVERFLOW, "token count of sequence %d would overflow int32", b);
+    }
+    return KVDEC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -269,21 +285,38 @@ int32_t kvdec_seed(kvdec_cache* c, const void* k_tok, const void* v_tok, int32_t
 int32_t kvdec_append(kvdec_cache* c, const void* k_new, const void* v_new, void* stream)
 {
     g_err.clear();
-    if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
-    if (c->d.is_static) return fail(KVDEC_E_STATIC, "append on a static (encoder) cache");
-    if (!aligned16(k_new) || !aligned16(v_new))
-        return fail(KVDEC_E_INVALID, "k_new and v_new must be non-NULL, 16-byte aligned device pointers");
-    for (int32_t b = 0; b < c->d.batch && c->replay_chunk == 0; ++b) {
-        if (c->d.window == 0 && c->lens[b] + 1 > c->d.capacity)
-            return fail(KVDEC_E_OVERFLOW, "cache overflow: sequence %d holds %d + 1 > %d", b,
-                        c->lens[b], c->d.capacity);
-        if (c->lens[b] == INT32_MAX)
-            return fail(KVDEC_E_OVERFLOW, "token count of sequence %d would overflow int32", b);
-    }
+    const int32_t rc = check_append(c, k_new, v_new);
+    if (rc) return rc;
     const hipError_t e = kvdec::launch_append(c->d.dtype, c->d.k, c->d.v, k_new, v_new, c->d.lens,
                                               c->d.batch, c->d.n_kv_heads, c->d.capacity,
                                               c->cap_pad, c->d.window,
                                               static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+    for (auto& l : c->lens) ++l;
+    return KVDEC_OK;
+}
+
+int32_t kvdec_append_rope(kvdec_cache* c, const void* k_new, const void* v_new, float theta,
+                          const float* q, float* q_rot, int32_t n_q_heads, void* stream)
+{
+    g_err.clear();
+    const int32_t rc = check_append(c, k_new, v_new);
+    if (rc) return rc;
+    if (!(theta > 0.f) || !std::isfinite(theta))
+        return fail(KVDEC_E_INVALID, "theta must be a positive finite number");
+    if ((q == nullptr) != (q_rot == nullptr))
+        return fail(KVDEC_E_INVALID, "q and q_rot must both be given or both be NULL");
+    if (q) {
+        if (!aligned16(q) || !aligned16(q_rot))
+            return fail(KVDEC_E_INVALID, "q and q_rot must be 16-byte aligned device pointers");
+        if (n_q_heads <= 0 || n_q_heads % c->d.n_kv_heads != 0)
+            return fail(KVDEC_E_SHAPE, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                        n_q_heads, c->d.n_kv_heads);
+    }
+    const hipError_t e = kvdec::launch_append_rope(
+        c->d.dtype, c->d.k, c->d.v, k_new, v_new, c->d.lens, c->d.batch, c->d.n_kv_heads,
+        c->d.capacity, c->cap_pad, c->d.window, q, q_rot, q ? n_q_heads : 0,
+        static_cast<double>(theta), static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "append launch");
     for (auto& l : c->lens) ++l;
     return KVDEC_OK;

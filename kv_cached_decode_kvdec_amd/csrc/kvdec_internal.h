@@ -48,6 +48,10 @@ hipError_t launch_set_lens(int32_t* lens, const int32_t* host, int32_t n, hipStr
 hipError_t launch_append(int dtype, void* k, void* v, const void* k_new, const void* v_new,
                          int32_t* lens, int32_t batch, int32_t n_kv_heads, int32_t capacity,
                          int32_t cap_pad, int32_t window, hipStream_t s);
+hipError_t launch_append_rope(int dtype, void* k, void* v, const void* k_new, const void* v_new,
+                              int32_t* lens, int32_t batch, int32_t n_kv_heads, int32_t capacity,
+                              int32_t cap_pad, int32_t window, const float* q, float* q_rot,
+                              int32_t n_q_heads, double theta, hipStream_t s);
 hipError_t launch_seed(int dtype, void* k, void* v, const void* k_tok, const void* v_tok,
                        int32_t batch, int32_t rows, int32_t n_kv_heads, int32_t cap_pad,
                        hipStream_t s);

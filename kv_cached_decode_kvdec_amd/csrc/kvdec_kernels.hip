@@ -238,6 +238,76 @@ __global__ __launch_bounds__(256) void append_kernel(char* __restrict__ K, char*
 }
 
 // ---------------------------------------------------------------------------
+// append with rotary position embedding: the new key (and optionally the
+// query) of every sequence is rotated at the token's position (= its length
+// before the append) before the key is stored -- the RoPE-then-append order
+// of franken_ocr 0.8.0 decoder_qwen2.rs (`qwen2_decode_step`), NEOX
+// rotate-half pairs (i, i + 32) as in lattice-inference 0.4.0 cpu_q8.rs
+// (`full_attention_step_q8`), angle pos * theta^(-2i/64).  Angles, sin/cos
+// and the rotation are computed in double (positions reach 8k and beyond,
+// where a float angle would be off by ~1e-3 rad); the result is rounded to
+// float, then to bf16 (nearest even) for bf16 caches.
+// ---------------------------------------------------------------------------
+template <int ESZ>
+__global__ __launch_bounds__(256) void append_rope_kernel(
+    char* __restrict__ K, char* __restrict__ V, const char* __restrict__ kn,
+    const char* __restrict__ vn, int32_t* __restrict__ lens, int Hkv, int capacity, int cap_pad,
+    int window, const float* q_in, float* q_out, int Hq, double theta)
+{
+    constexpr int RB = kHeadDim * ESZ;
+    constexpr int VPR = RB / 16;
+    const int b = blockIdx.x;
+    const int len = lens[b];
+    if (len < 0 || len == INT32_MAX || (window == 0 && len >= capacity)) return;
+    const int slot = window > 0 ? len % window : len;
+    const double pos = static_cast<double>(len);
+    const int rot_rows = Hkv + (q_in ? Hq : 0);
+    for (int t = threadIdx.x; t < rot_rows * 32; t += blockDim.x) {
+        const int row = t >> 5, i = t & 31;
+        double sn, cs;
+        sincos(pos * pow(theta, -2.0 * i / 64.0), &sn, &cs);
+        if (row < Hkv) {
+            const size_t hg = static_cast<size_t>(b) * Hkv + row;
+            double x0, x1;
+            if constexpr (ESZ == 4) {
+                const float* src = reinterpret_cast<const float*>(kn) + hg * kHeadDim;
+                x0 = src[i];
+                x1 = src[i + 32];
+            } else {
+                const uint16_t* src = reinterpret_cast<const uint16_t*>(kn) + hg * kHeadDim;
+                x0 = __uint_as_float(static_cast<uint32_t>(src[i]) << 16);
+                x1 = __uint_as_float(static_cast<uint32_t>(src[i + 32]) << 16);
+            }
+            const float y0 = static_cast<float>(x0 * cs - x1 * sn);
+            const float y1 = static_cast<float>(x0 * sn + x1 * cs);
+            const size_t dst = (hg * cap_pad + slot) * kHeadDim;
+            if constexpr (ESZ == 4) {
+                reinterpret_cast<float*>(K)[dst + i] = y0;
+                reinterpret_cast<float*>(K)[dst + i + 32] = y1;
+            } else {
+                reinterpret_cast<uint16_t*>(K)[dst + i] = static_cast<uint16_t>(bf16_rne(y0));
+                reinterpret_cast<uint16_t*>(K)[dst + i + 32] = static_cast<uint16_t>(bf16_rne(y1));
+            }
+        } else {
+            // q_in and q_out may alias: each thread reads and writes its own pair
+            const size_t qi = (static_cast<size_t>(b) * Hq + (row - Hkv)) * kHeadDim;
+            const double x0 = q_in[qi + i], x1 = q_in[qi + i + 32];
+            q_out[qi + i] = static_cast<float>(x0 * cs - x1 * sn);
+            q_out[qi + i + 32] = static_cast<float>(x0 * sn + x1 * cs);
+        }
+    }
+    // V rows: plain 16-byte copies
+    for (int t = threadIdx.x; t < Hkv * VPR; t += blockDim.x) {
+        const int g = t / VPR, w = t - g * VPR;
+        const size_t hg = static_cast<size_t>(b) * Hkv + g;
+        reinterpret_cast<uint4*>(V + (hg * cap_pad + slot) * RB)[w] =
+            reinterpret_cast<const uint4*>(vn + hg * RB)[w];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) lens[b] = len + 1;
+}
+
+// ---------------------------------------------------------------------------
 // seed: token-major -> head-major, grid-stride over 16-byte words.
 // ---------------------------------------------------------------------------
 template <int ROW_BYTES>
@@ -715,6 +785,25 @@ hipError_t launch_append(int dtype, void* k, void* v, const void* k_new, const v
         hipLaunchKernelGGL(append_kernel<128>, grid, block, 0, s, static_cast<char*>(k),
                            static_cast<char*>(v), static_cast<const char*>(k_new),
                            static_cast<const char*>(v_new), lens, n_kv_heads, capacity, cap_pad, window);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_rope(int dtype, void* k, void* v, const void* k_new, const void* v_new,
+                              int32_t* lens, int32_t batch, int32_t n_kv_heads, int32_t capacity,
+                              int32_t cap_pad, int32_t window, const float* q, float* q_rot,
+                              int32_t n_q_heads, double theta, hipStream_t s)
+{
+    const dim3 grid(batch), block(256);
+    if (dtype == 0)
+        hipLaunchKernelGGL(append_rope_kernel<4>, grid, block, 0, s, static_cast<char*>(k),
+                           static_cast<char*>(v), static_cast<const char*>(k_new),
+                           static_cast<const char*>(v_new), lens, n_kv_heads, capacity, cap_pad,
+                           window, q, q_rot, n_q_heads, theta);
+    else
+        hipLaunchKernelGGL(append_rope_kernel<2>, grid, block, 0, s, static_cast<char*>(k),
+                           static_cast<char*>(v), static_cast<const char*>(k_new),
+                           static_cast<const char*>(v_new), lens, n_kv_heads, capacity, cap_pad,
+                           window, q, q_rot, n_q_heads, theta);
     return hipGetLastError();
 }
 

@@ -4,5 +4,5 @@ Only the tests, the smoke check and the benchmark's CPU-baseline leg import
 this package.  It wraps the plain-C f64 reference in kvdec_oracle.c through
 ctypes; it shares no code with the HIP library.
 """
-from .oracle import (attend, prefill_causal, append, seed, bf16_to_f32, load,  # noqa: F401
+from .oracle import (attend, prefill_causal, append, seed, rope, bf16_to_f32, load,  # noqa: F401
                      SCALE_HEAD_DIM_64)

@@ -272,3 +272,35 @@ int kvdec_oracle_seed(void* dst, const void* src, int64_t esz, int64_t B, int64_
             }
     return ORACLE_OK;
 }
+
+/*
+ * Rotary position embedding, NEOX rotate-half form, on rows of D values:
+ * dims (i, i + D/2) form a pair rotated by the angle pos * theta^(-2i/D):
+ *   x_i'       = x_i cos(a) - x_{i+D/2} sin(a)
+ *   x_{i+D/2}' = x_i sin(a) + x_{i+D/2} cos(a)
+ * Stride-half pairing as in [LAT-Q8] `full_attention_step_q8` (pairs
+ * (i, half + i)), frequencies theta^(-2i/D) with theta = 1e6 for Qwen2 as
+ * named in [FO-Q2] (NEOX rotate-half, applied to q and k before the key is
+ * cached).  Everything in double.
+ *
+ *   x   : double [n][D]   (D even)
+ *   pos : int32  [n]      position of each row
+ *   out : double [n][D]   (may alias x)
+ */
+int kvdec_oracle_rope(const double* x, int64_t n, int64_t D, const int32_t* pos, double theta,
+                      double* out)
+{
+    if (n < 0 || D <= 0 || D % 2 != 0 || !(theta > 0.0)) return ORACLE_E_SHAPE;
+    const int64_t half = D / 2;
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t i = 0; i < half; ++i) {
+            const double inv_freq = pow(theta, -2.0 * (double)i / (double)D);
+            const double a = (double)pos[r] * inv_freq;
+            const double c = cos(a), s = sin(a);
+            const double x0 = x[r * D + i], x1 = x[r * D + half + i];
+            out[r * D + i] = x0 * c - x1 * s;
+            out[r * D + half + i] = x0 * s + x1 * c;
+        }
+    }
+    return ORACLE_OK;
+}

@@ -34,8 +34,9 @@ def load():
                                                     ctypes.c_double, _vp]
         lib.kvdec_oracle_append.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp]
         lib.kvdec_oracle_seed.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64]
+        lib.kvdec_oracle_rope.argtypes = [_vp, _i64, _i64, _vp, ctypes.c_double, _vp]
         for f in (lib.kvdec_oracle_attend, lib.kvdec_oracle_prefill_causal,
-                  lib.kvdec_oracle_append, lib.kvdec_oracle_seed):
+                  lib.kvdec_oracle_append, lib.kvdec_oracle_seed, lib.kvdec_oracle_rope):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -122,3 +123,18 @@ def seed(dst, src):
     if rc != 0:
         raise ValueError(f"oracle seed rejected the arguments (code {rc})")
     return dst
+
+
+def rope(x, positions, theta):
+    """NEOX rotate-half RoPE in f64 on the last axis.  x [..., D]; positions
+    broadcast against x.shape[:-1].  Returns float64."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    flat = np.ascontiguousarray(x.reshape(-1, D))
+    pos = np.ascontiguousarray(np.broadcast_to(np.asarray(positions, dtype=np.int32),
+                                               x.shape[:-1]).reshape(-1))
+    out = np.empty_like(flat)
+    rc = load().kvdec_oracle_rope(_ptr(flat), flat.shape[0], D, _ptr(pos), float(theta), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle rope rejected the arguments (code {rc})")
+    return out.reshape(x.shape)

@@ -404,3 +404,39 @@ def test_workload_lengths_follow_their_laws():
     assert abs(x.mean() - (8192 - 16) / math.log(512)) < 40
     u = gen.draw_lens(rng, "uniform:1:4096", 20000)
     assert u.min() >= 1 and u.max() <= 4096 and abs(u.mean() - 2048.5) < 30
+
+
+# ---- pins of the oracle's RoPE (rotate-half, stride-half pairs) ----------------
+
+def test_oracle_rope_closed_forms():
+    rng = _rng(27)
+    x = rng.standard_normal((6, D))
+    # position 0 is the identity, exactly
+    assert np.array_equal(oracle.rope(x, np.zeros(6, np.int32), 1e6), x)
+    # pair (i, i+32) keeps its norm
+    y = oracle.rope(x, np.arange(6) * 777 + 3, 1e6)
+    np.testing.assert_allclose(y[:, :32] ** 2 + y[:, 32:] ** 2, x[:, :32] ** 2 + x[:, 32:] ** 2,
+                               rtol=1e-13)
+    # e_0 rotates into e_32 at the position itself (inv_freq_0 = 1)
+    e0 = np.zeros((1, D))
+    e0[0, 0] = 1.0
+    r = oracle.rope(e0, [5], 1e6)[0]
+    assert abs(r[0] - math.cos(5.0)) < 1e-15 and abs(r[32] - math.sin(5.0)) < 1e-15
+    assert np.count_nonzero(r) == 2
+    # e_16 uses theta^(-1/2) = 1e-3 at theta = 1e6, pairing with e_48
+    e16 = np.zeros((1, D))
+    e16[0, 16] = 1.0
+    r = oracle.rope(e16, [1000], 1e6)[0]
+    assert abs(r[16] - math.cos(1.0)) < 1e-12 and abs(r[48] - math.sin(1.0)) < 1e-12
+    # rotations compose: R(b) R(a) = R(a + b)
+    np.testing.assert_allclose(oracle.rope(oracle.rope(x, 300, 1e6), 700, 1e6),
+                               oracle.rope(x, 1000, 1e6), rtol=0, atol=1e-12)
+    # scores depend on relative position only
+    q, k = x[0], x[1]
+    s1 = oracle.rope(q[None], [50], 1e6)[0] @ oracle.rope(k[None], [20], 1e6)[0]
+    s2 = oracle.rope(q[None], [4050], 1e6)[0] @ oracle.rope(k[None], [4020], 1e6)[0]
+    assert abs(s1 - s2) < 1e-10
+    # and it agrees with the generator's rotation (f64 there too, cast to f32)
+    g = gen.rope_rotate(x.astype(np.float32), np.arange(6) * 777 + 3, 1e6)
+    np.testing.assert_allclose(g, oracle.rope(x.astype(np.float32), np.arange(6) * 777 + 3, 1e6),
+                               rtol=0, atol=2e-6)
