@@ -206,6 +206,70 @@ int32_t kvdec_attend_cross(const kvdec_cache* cache, const float* q, int32_t n_q
                            float scale, int32_t chunk_rows, float* out, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Paged KV cache: K and V live in a pool of fixed-size pages shared by all
+ * sequences, and each sequence owns a block table of page ids -- the paged
+ * cache of [WA-DEC] `PagedDecoderKVCache` over realizar's `PagedKvCache`
+ * (page = position / page size, offset = position % page size; on an
+ * allocation failure nothing changes).  The library keeps the page
+ * allocator (a host-side free list) and host mirrors of the lengths and
+ * block tables; the caller owns every device buffer.
+ *   k_pages, v_pages : (device) [num_pages][n_kv_heads][page_rows][64] elements
+ *                      of dtype: one (page, KV head) is a contiguous run of rows
+ *   block_table      : (device) int32 [batch][max_pages_per_seq]; written by
+ *                      the library's appends, never read past a sequence's pages
+ *   lens             : (device) int32 [batch], all zero after create
+ * ------------------------------------------------------------------------- */
+typedef struct kvdec_paged kvdec_paged;
+
+typedef struct {
+    int32_t batch;              /* sequences, >= 1 */
+    int32_t n_kv_heads;         /* >= 1 */
+    int32_t head_dim;           /* must be 64 */
+    int32_t dtype;              /* kvdec_dtype */
+    int32_t page_rows;          /* rows per page: a power of two in [16, 4096] */
+    int32_t num_pages;          /* pages in the pool, >= 1 */
+    int32_t max_pages_per_seq;  /* block table width, >= 1 */
+    int32_t reserved0;          /* must be 0 */
+    void* k_pages;
+    void* v_pages;
+    int32_t* block_table;
+    int32_t* lens;
+} kvdec_paged_desc;
+
+/* Create a paged cache: every sequence empty, every page free; writes zero
+ * lengths on `stream`.  Errors: KVDEC_E_INVALID, KVDEC_E_SHAPE (head_dim,
+ * page_rows not a power of two in range). */
+int32_t kvdec_paged_create(const kvdec_paged_desc* desc, void* stream, kvdec_paged** out);
+void kvdec_paged_destroy(kvdec_paged* paged);
+
+/* Append one token to every sequence (same k_new / v_new layout as
+ * kvdec_append).  A sequence whose new row starts a page takes a free page
+ * (lowest-numbered first, in sequence order).  Errors: KVDEC_E_OVERFLOW
+ * when a sequence would exceed max_pages_per_seq * page_rows or the pool
+ * has too few free pages -- checked before anything changes; a failed
+ * launch (KVDEC_E_HIP) returns the pages taken. */
+int32_t kvdec_paged_append(kvdec_paged* paged, const void* k_new, const void* v_new, void* stream);
+
+/* End sequence `seq`: its pages return to the pool and its length becomes 0
+ * (written on `stream`). */
+int32_t kvdec_paged_release(kvdec_paged* paged, int32_t seq, void* stream);
+
+/* Host mirrors: lengths [batch], block table [batch][max_pages_per_seq]
+ * (-1 where no page is held), and the number of free pages (-1 for NULL). */
+int32_t kvdec_paged_get_lens(const kvdec_paged* paged, int32_t* lens_out);
+int32_t kvdec_paged_get_table(const kvdec_paged* paged, int32_t* table_out);
+int32_t kvdec_paged_free_pages(const kvdec_paged* paged);
+
+/* Workspace for kvdec_paged_attend (same rules as kvdec_workspace_bytes). */
+size_t kvdec_paged_workspace_bytes(const kvdec_paged* paged, int32_t n_q_heads);
+
+/* Decode attention over the paged cache: the computation of
+ * kvdec_attend_self, with each row found through the block table. */
+int32_t kvdec_paged_attend(const kvdec_paged* paged, const float* q, int32_t n_q_heads,
+                           float scale, int32_t chunk_rows, float* out, void* ws, size_t ws_bytes,
+                           void* stream);
+
 /*
  * Replay mode, for decode steps captured once in a HIP graph and replayed
  * for consecutive tokens (the graph-replayed decoder step of [WA-CUDA]

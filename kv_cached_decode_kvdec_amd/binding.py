@@ -29,7 +29,9 @@ EXPORTED = [
     "kvdec_padded_capacity", "kvdec_cache_create", "kvdec_cache_destroy", "kvdec_reset_lens",
     "kvdec_get_lens", "kvdec_seed", "kvdec_append", "kvdec_append_rope", "kvdec_workspace_bytes",
     "kvdec_attend_self", "kvdec_attend_cross", "kvdec_set_replay_mode", "kvdec_status_str",
-    "kvdec_last_error",
+    "kvdec_last_error", "kvdec_paged_create", "kvdec_paged_destroy", "kvdec_paged_append",
+    "kvdec_paged_release", "kvdec_paged_get_lens", "kvdec_paged_get_table",
+    "kvdec_paged_free_pages", "kvdec_paged_workspace_bytes", "kvdec_paged_attend",
 ]
 
 
@@ -45,6 +47,15 @@ class CacheDesc(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("is_static", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("reserved0", ctypes.c_int32),
                 ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("lens", ctypes.c_void_p)]
+
+
+class PagedDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("page_rows", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("lens", ctypes.c_void_p)]
 
 
 _lib = None
@@ -73,6 +84,15 @@ def load():
         "kvdec_attend_self": (_i32, [_vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz, _vp]),
         "kvdec_attend_cross": (_i32, [_vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz, _vp]),
         "kvdec_set_replay_mode": (_i32, [_vp, _i32]),
+        "kvdec_paged_create": (_i32, [ctypes.POINTER(PagedDesc), _vp, ctypes.POINTER(_vp)]),
+        "kvdec_paged_destroy": (None, [_vp]),
+        "kvdec_paged_append": (_i32, [_vp, _vp, _vp, _vp]),
+        "kvdec_paged_release": (_i32, [_vp, _i32, _vp]),
+        "kvdec_paged_get_lens": (_i32, [_vp, _vp]),
+        "kvdec_paged_get_table": (_i32, [_vp, _vp]),
+        "kvdec_paged_free_pages": (_i32, [_vp]),
+        "kvdec_paged_workspace_bytes": (_sz, [_vp, _i32]),
+        "kvdec_paged_attend": (_i32, [_vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz, _vp]),
         "kvdec_status_str": (ctypes.c_char_p, [_i32]),
         "kvdec_last_error": (ctypes.c_char_p, []),
     }
@@ -157,3 +177,49 @@ def kvdec_attend_cross(handle, q_ptr, n_q_heads, scale, chunk_rows, out_ptr, ws_
 
 def kvdec_set_replay_mode(handle, chunk_rows):
     _check(load().kvdec_set_replay_mode(handle, int(chunk_rows)), "kvdec_set_replay_mode")
+
+
+def kvdec_paged_create(desc, stream=None):
+    h = _vp()
+    _check(load().kvdec_paged_create(ctypes.byref(desc), stream, ctypes.byref(h)),
+           "kvdec_paged_create")
+    return h
+
+
+def kvdec_paged_destroy(handle):
+    if handle:
+        load().kvdec_paged_destroy(handle)
+
+
+def kvdec_paged_append(handle, k_new_ptr, v_new_ptr, stream=None):
+    _check(load().kvdec_paged_append(handle, k_new_ptr, v_new_ptr, stream), "kvdec_paged_append")
+
+
+def kvdec_paged_release(handle, seq, stream=None):
+    _check(load().kvdec_paged_release(handle, int(seq), stream), "kvdec_paged_release")
+
+
+def kvdec_paged_get_lens(handle, batch):
+    arr = (ctypes.c_int32 * batch)()
+    _check(load().kvdec_paged_get_lens(handle, arr), "kvdec_paged_get_lens")
+    return list(arr)
+
+
+def kvdec_paged_get_table(handle, batch, max_pages):
+    arr = (ctypes.c_int32 * (batch * max_pages))()
+    _check(load().kvdec_paged_get_table(handle, arr), "kvdec_paged_get_table")
+    return [list(arr[b * max_pages:(b + 1) * max_pages]) for b in range(batch)]
+
+
+def kvdec_paged_free_pages(handle):
+    return load().kvdec_paged_free_pages(handle)
+
+
+def kvdec_paged_workspace_bytes(handle, n_q_heads):
+    return load().kvdec_paged_workspace_bytes(handle, int(n_q_heads))
+
+
+def kvdec_paged_attend(handle, q_ptr, n_q_heads, scale, chunk_rows, out_ptr, ws_ptr, ws_bytes,
+                       stream=None):
+    _check(load().kvdec_paged_attend(handle, q_ptr, int(n_q_heads), float(scale), int(chunk_rows),
+                                     out_ptr, ws_ptr, int(ws_bytes), stream), "kvdec_paged_attend")

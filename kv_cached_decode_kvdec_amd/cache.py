@@ -141,3 +141,70 @@ class KVCache:
         fn(self.handle, _ptr(q), Hq, scale, chunk_rows, _ptr(out), _ptr(ws), ws.numel(),
            current_stream())
         return out
+
+
+class PagedKVCache:
+    """Paged K/V pool + block table over the kvdec_paged_* entry points."""
+
+    def __init__(self, batch, n_kv_heads, page_rows, num_pages, max_pages_per_seq, dtype="f32",
+                 device="cuda"):
+        self.batch, self.n_kv_heads = int(batch), int(n_kv_heads)
+        self.page_rows, self.num_pages = int(page_rows), int(num_pages)
+        self.max_pages = int(max_pages_per_seq)
+        self.dtype = dtype
+        tdt = _TORCH_DTYPE[dtype]
+        shape = (self.num_pages, self.n_kv_heads, self.page_rows, B.HEAD_DIM)
+        self.k = torch.zeros(shape, dtype=tdt, device=device)
+        self.v = torch.zeros(shape, dtype=tdt, device=device)
+        self.table_dev = torch.full((self.batch, self.max_pages), -1, dtype=torch.int32,
+                                    device=device)
+        self.lens_dev = torch.zeros(self.batch, dtype=torch.int32, device=device)
+        self.desc = B.PagedDesc(self.batch, self.n_kv_heads, B.HEAD_DIM, _CODE[dtype],
+                                self.page_rows, self.num_pages, self.max_pages, 0,
+                                self.k.data_ptr(), self.v.data_ptr(), self.table_dev.data_ptr(),
+                                self.lens_dev.data_ptr())
+        self.handle = B.kvdec_paged_create(self.desc, current_stream())
+        self._ws = {}
+
+    def lens(self):
+        return B.kvdec_paged_get_lens(self.handle, self.batch)
+
+    def table(self):
+        return B.kvdec_paged_get_table(self.handle, self.batch, self.max_pages)
+
+    def free_pages(self):
+        return B.kvdec_paged_free_pages(self.handle)
+
+    def append(self, k_new, v_new):
+        shape = (self.batch, self.n_kv_heads, B.HEAD_DIM)
+        for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+            if t.dtype != self.k.dtype or tuple(t.shape) != shape or not t.is_contiguous():
+                raise ValueError(f"{n} must be a contiguous {shape} {self.k.dtype} tensor")
+        B.kvdec_paged_append(self.handle, _ptr(k_new), _ptr(v_new), current_stream())
+
+    def release(self, seq):
+        B.kvdec_paged_release(self.handle, seq, current_stream())
+
+    def attend(self, q, scale=0.125, chunk_rows=0, out=None):
+        Hq = q.shape[1]
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self._ws.get(Hq)
+        if ws is None:
+            ws = torch.empty(B.kvdec_paged_workspace_bytes(self.handle, Hq), dtype=torch.uint8,
+                             device=self.k.device)
+            self._ws[Hq] = ws
+        B.kvdec_paged_attend(self.handle, _ptr(q), Hq, scale, chunk_rows, _ptr(out), _ptr(ws),
+                             ws.numel(), current_stream())
+        return out
+
+    def close(self):
+        if getattr(self, "handle", None):
+            B.kvdec_paged_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

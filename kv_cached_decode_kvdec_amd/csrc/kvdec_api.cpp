@@ -15,6 +15,14 @@
 
 #include "kvdec_internal.h"
 
+struct kvdec_paged {
+    kvdec_paged_desc d;
+    int32_t pshift;
+    std::vector<int32_t> lens;        // host mirror of d.lens
+    std::vector<int32_t> table;       // host mirror of d.block_table, -1: no page
+    std::vector<int32_t> free_pages;  // pool pages not held by any sequence (a stack)
+};
+
 struct kvdec_cache {
     kvdec_cache_desc d;
     int32_t cap_pad;
@@ -114,16 +122,28 @@ int64_t max_chunks(const kvdec_cache* c)
     return static_cast<int64_t>(c->d.batch) * ((c->cap_pad + KVDEC_MIN_CHUNK - 1) / KVDEC_MIN_CHUNK);
 }
 
-int32_t attend_common(const kvdec_cache* c, const float* q, int32_t n_q_heads, float scale,
-                      int32_t chunk_rows, float* out, void* ws, size_t ws_bytes, void* stream)
+// What an attend call needs to know about the cache it reads, for both the
+// contiguous and the paged layouts.
+struct AttendView {
+    int32_t batch, n_kv_heads, dtype, cap_pad, row_limit, replay_chunk;
+    const void* k;
+    const void* v;
+    const int32_t* lens_dev;
+    std::vector<int32_t> rows;     // rows attended per sequence (host mirror)
+    int64_t max_chunks;            // workspace sizing bound
+    const int32_t* table = nullptr;
+    int32_t table_stride = 0, pshift = 0;
+};
+
+int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, float scale,
+                    int32_t chunk_rows, float* out, void* ws, size_t ws_bytes, void* stream)
 {
-    if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
     if (!aligned16(q) || !aligned16(out))
         return fail(KVDEC_E_INVALID, "q and out must be non-NULL, 16-byte aligned device pointers");
-    if (n_q_heads <= 0 || n_q_heads % c->d.n_kv_heads != 0)
+    if (n_q_heads <= 0 || n_q_heads % v.n_kv_heads != 0)
         return fail(KVDEC_E_SHAPE, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
-                    n_q_heads, c->d.n_kv_heads);
-    const int32_t group = n_q_heads / c->d.n_kv_heads;
+                    n_q_heads, v.n_kv_heads);
+    const int32_t group = n_q_heads / v.n_kv_heads;
     if (group > KVDEC_MAX_GROUP)
         return fail(KVDEC_E_SHAPE, "group size %d exceeds %d", group, KVDEC_MAX_GROUP);
     if (!std::isfinite(scale)) return fail(KVDEC_E_INVALID, "scale must be finite");
@@ -131,45 +151,66 @@ int32_t attend_common(const kvdec_cache* c, const float* q, int32_t n_q_heads, f
                             chunk_rows % 64 != 0))
         return fail(KVDEC_E_INVALID, "chunk_rows %d must be 0 or a multiple of 64 in [%d, %d]",
                     chunk_rows, KVDEC_MIN_CHUNK, KVDEC_MAX_CHUNK);
-    const kvdec::PartialLayout part = kvdec::partial_layout(max_chunks(c), n_q_heads);
+    const kvdec::PartialLayout part = kvdec::partial_layout(v.max_chunks, n_q_heads);
     if (!aligned16(ws) || ws_bytes < part.bytes)
         return fail(KVDEC_E_WORKSPACE, "workspace needs %zu bytes at a 16-byte aligned address, got %zu",
                     part.bytes, ws_bytes);
 
     kvdec::AttendArgs a;
     a.q = q;
-    a.k = c->d.k;
-    a.v = c->d.v;
-    a.lens = c->d.lens;
-    a.batch = c->d.batch;
-    a.n_kv_heads = c->d.n_kv_heads;
+    a.k = v.k;
+    a.v = v.v;
+    a.lens = v.lens_dev;
+    a.batch = v.batch;
+    a.n_kv_heads = v.n_kv_heads;
     a.group = group;
-    a.cap_pad = c->cap_pad;
-    a.row_limit = c->d.window > 0 ? c->d.window : c->d.capacity;
-    if (c->replay_chunk > 0) {
+    a.cap_pad = v.cap_pad;
+    a.row_limit = v.row_limit;
+    if (v.replay_chunk > 0) {
         // Replay mode: sized for the most rows any sequence can hold, so the
         // launch stays valid while the device lengths grow between graph
         // replays (surplus workgroups exit at once; the merge checks every
         // sequence's chunk count on the device).
-        a.chunk_rows = chunk_rows ? chunk_rows : c->replay_chunk;
+        a.chunk_rows = chunk_rows ? chunk_rows : v.replay_chunk;
         const int64_t per_seq = (static_cast<int64_t>(a.row_limit) + a.chunk_rows - 1) / a.chunk_rows;
-        a.n_chunks = static_cast<int64_t>(c->d.batch) * (per_seq > 0 ? per_seq : 1);
+        a.n_chunks = static_cast<int64_t>(v.batch) * (per_seq > 0 ? per_seq : 1);
         a.need_merge = per_seq > 1;
     } else {
-        const std::vector<int32_t> rows = attended_rows(c);
         a.chunk_rows = chunk_rows ? chunk_rows
-                                  : auto_chunk(rows, c->d.n_kv_heads,
-                                               kvdec::resident_attend_blocks(c->d.dtype, group));
-        a.n_chunks = chunks_for(rows, a.chunk_rows);
-        a.need_merge = a.n_chunks > c->d.batch;   // some sequence has more than one chunk
+                                  : auto_chunk(v.rows, v.n_kv_heads,
+                                               kvdec::resident_attend_blocks(v.dtype, group));
+        a.n_chunks = chunks_for(v.rows, a.chunk_rows);
+        a.need_merge = a.n_chunks > v.batch;   // some sequence has more than one chunk
     }
     a.qscale = scale * 1.4426950408889634f;
     a.out = out;
     a.ws = ws;
     a.part = part;
-    const hipError_t e = kvdec::launch_attend(c->d.dtype, a, static_cast<hipStream_t>(stream));
+    a.table = v.table;
+    a.table_stride = v.table_stride;
+    a.pshift = v.pshift;
+    const hipError_t e = kvdec::launch_attend(v.dtype, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "attend launch");
     return KVDEC_OK;
+}
+
+int32_t attend_common(const kvdec_cache* c, const float* q, int32_t n_q_heads, float scale,
+                      int32_t chunk_rows, float* out, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
+    AttendView v;
+    v.batch = c->d.batch;
+    v.n_kv_heads = c->d.n_kv_heads;
+    v.dtype = c->d.dtype;
+    v.cap_pad = c->cap_pad;
+    v.row_limit = c->d.window > 0 ? c->d.window : c->d.capacity;
+    v.replay_chunk = c->replay_chunk;
+    v.k = c->d.k;
+    v.v = c->d.v;
+    v.lens_dev = c->d.lens;
+    v.rows = attended_rows(c);
+    v.max_chunks = max_chunks(c);
+    return attend_view(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
 }
 
 int32_t check_append(const kvdec_cache* c, const void* k_new, const void* v_new)
@@ -363,6 +404,166 @@ int32_t kvdec_set_replay_mode(kvdec_cache* c, int32_t chunk_rows)
                     "64 in [%d, %d]", chunk_rows, KVDEC_MIN_CHUNK, KVDEC_MAX_CHUNK);
     c->replay_chunk = chunk_rows;
     return KVDEC_OK;
+}
+
+
+int32_t kvdec_paged_create(const kvdec_paged_desc* desc, void* stream, kvdec_paged** out)
+{
+    g_err.clear();
+    if (!desc || !out) return fail(KVDEC_E_INVALID, "desc and out must not be NULL");
+    *out = nullptr;
+    const kvdec_paged_desc& d = *desc;
+    if (d.batch < 1 || d.n_kv_heads < 1 || d.num_pages < 1 || d.max_pages_per_seq < 1)
+        return fail(KVDEC_E_INVALID, "batch, n_kv_heads, num_pages and max_pages_per_seq must be >= 1");
+    if (d.head_dim != KVDEC_HEAD_DIM)
+        return fail(KVDEC_E_SHAPE, "head_dim must be %d, got %d", KVDEC_HEAD_DIM, d.head_dim);
+    if (d.dtype != KVDEC_F32 && d.dtype != KVDEC_BF16)
+        return fail(KVDEC_E_INVALID, "unknown dtype %d", d.dtype);
+    int32_t pshift = 0;
+    while ((1 << pshift) < d.page_rows && pshift < 13) ++pshift;
+    if (d.page_rows < 16 || d.page_rows > KVDEC_MAX_CHUNK || (1 << pshift) != d.page_rows)
+        return fail(KVDEC_E_SHAPE, "page_rows must be a power of two in [16, %d], got %d",
+                    KVDEC_MAX_CHUNK, d.page_rows);
+    if (static_cast<int64_t>(d.max_pages_per_seq) * d.page_rows > INT32_MAX / 2)
+        return fail(KVDEC_E_SHAPE, "max_pages_per_seq * page_rows too large");
+    if (d.reserved0 != 0) return fail(KVDEC_E_INVALID, "reserved0 must be 0");
+    if (!aligned16(d.k_pages) || !aligned16(d.v_pages) || !aligned16(d.block_table) ||
+        !aligned16(d.lens))
+        return fail(KVDEC_E_INVALID,
+                    "k_pages, v_pages, block_table and lens must be non-NULL, 16-byte aligned device pointers");
+    kvdec_paged* p = new kvdec_paged;
+    p->d = d;
+    p->pshift = pshift;
+    p->lens.assign(d.batch, 0);
+    p->table.assign(static_cast<size_t>(d.batch) * d.max_pages_per_seq, -1);
+    p->free_pages.reserve(d.num_pages);
+    for (int32_t i = d.num_pages - 1; i >= 0; --i) p->free_pages.push_back(i);   // pops 0, 1, 2, ...
+    const hipError_t e = kvdec::launch_set_lens(d.lens, p->lens.data(), d.batch,
+                                                static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        delete p;
+        return hip_fail(e, "set lengths");
+    }
+    *out = p;
+    return KVDEC_OK;
+}
+
+void kvdec_paged_destroy(kvdec_paged* p) { delete p; }
+
+int32_t kvdec_paged_append(kvdec_paged* p, const void* k_new, const void* v_new, void* stream)
+{
+    g_err.clear();
+    if (!p) return fail(KVDEC_E_INVALID, "paged cache handle is NULL");
+    if (!aligned16(k_new) || !aligned16(v_new))
+        return fail(KVDEC_E_INVALID, "k_new and v_new must be non-NULL, 16-byte aligned device pointers");
+    const int32_t P = p->d.page_rows;
+    const int64_t cap = static_cast<int64_t>(p->d.max_pages_per_seq) * P;
+    int32_t needed = 0;
+    for (int32_t b = 0; b < p->d.batch; ++b) {
+        if (p->lens[b] + 1 > cap)
+            return fail(KVDEC_E_OVERFLOW, "cache overflow: sequence %d holds %d + 1 > %lld", b,
+                        p->lens[b], static_cast<long long>(cap));
+        if (p->lens[b] % P == 0) ++needed;
+    }
+    if (needed > static_cast<int32_t>(p->free_pages.size()))
+        return fail(KVDEC_E_OVERFLOW, "page pool exhausted: %d new pages needed, %zu free", needed,
+                    p->free_pages.size());
+    // take pages (sequence order), install them in the host mirror, launch;
+    // on a launch failure give everything back
+    std::vector<int32_t> fresh(p->d.batch, -1);
+    for (int32_t b = 0; b < p->d.batch; ++b)
+        if (p->lens[b] % P == 0) {
+            fresh[b] = p->free_pages.back();
+            p->free_pages.pop_back();
+            p->table[static_cast<size_t>(b) * p->d.max_pages_per_seq + p->lens[b] / P] = fresh[b];
+        }
+    const hipError_t e = kvdec::launch_paged_append(
+        p->d.dtype, p->d.k_pages, p->d.v_pages, k_new, v_new, p->d.lens, p->d.block_table,
+        p->d.max_pages_per_seq, p->d.batch, p->d.n_kv_heads, p->pshift, fresh.data(),
+        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        for (int32_t b = p->d.batch - 1; b >= 0; --b)
+            if (fresh[b] >= 0) {
+                p->table[static_cast<size_t>(b) * p->d.max_pages_per_seq + p->lens[b] / P] = -1;
+                p->free_pages.push_back(fresh[b]);
+            }
+        return hip_fail(e, "paged append launch");
+    }
+    for (auto& l : p->lens) ++l;
+    return KVDEC_OK;
+}
+
+int32_t kvdec_paged_release(kvdec_paged* p, int32_t seq, void* stream)
+{
+    g_err.clear();
+    if (!p) return fail(KVDEC_E_INVALID, "paged cache handle is NULL");
+    if (seq < 0 || seq >= p->d.batch)
+        return fail(KVDEC_E_INVALID, "sequence %d outside [0, %d)", seq, p->d.batch);
+    const int32_t zero = 0;
+    const hipError_t e = kvdec::launch_set_lens(p->d.lens + seq, &zero, 1,
+                                                static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "set lengths");
+    const size_t base = static_cast<size_t>(seq) * p->d.max_pages_per_seq;
+    const int32_t held = (p->lens[seq] + p->d.page_rows - 1) / p->d.page_rows;
+    for (int32_t i = held - 1; i >= 0; --i) {
+        p->free_pages.push_back(p->table[base + i]);
+        p->table[base + i] = -1;
+    }
+    p->lens[seq] = 0;
+    return KVDEC_OK;
+}
+
+int32_t kvdec_paged_get_lens(const kvdec_paged* p, int32_t* lens_out)
+{
+    g_err.clear();
+    if (!p || !lens_out) return fail(KVDEC_E_INVALID, "handle and lens_out must not be NULL");
+    std::memcpy(lens_out, p->lens.data(), sizeof(int32_t) * p->lens.size());
+    return KVDEC_OK;
+}
+
+int32_t kvdec_paged_get_table(const kvdec_paged* p, int32_t* table_out)
+{
+    g_err.clear();
+    if (!p || !table_out) return fail(KVDEC_E_INVALID, "handle and table_out must not be NULL");
+    std::memcpy(table_out, p->table.data(), sizeof(int32_t) * p->table.size());
+    return KVDEC_OK;
+}
+
+int32_t kvdec_paged_free_pages(const kvdec_paged* p)
+{
+    return p ? static_cast<int32_t>(p->free_pages.size()) : -1;
+}
+
+size_t kvdec_paged_workspace_bytes(const kvdec_paged* p, int32_t n_q_heads)
+{
+    if (!p || n_q_heads <= 0) return 0;
+    const int64_t cap = static_cast<int64_t>(p->d.max_pages_per_seq) * p->d.page_rows;
+    return kvdec::partial_layout(p->d.batch * ((cap + KVDEC_MIN_CHUNK - 1) / KVDEC_MIN_CHUNK),
+                                 n_q_heads).bytes;
+}
+
+int32_t kvdec_paged_attend(const kvdec_paged* p, const float* q, int32_t n_q_heads, float scale,
+                           int32_t chunk_rows, float* out, void* ws, size_t ws_bytes, void* stream)
+{
+    g_err.clear();
+    if (!p) return fail(KVDEC_E_INVALID, "paged cache handle is NULL");
+    const int64_t cap = static_cast<int64_t>(p->d.max_pages_per_seq) * p->d.page_rows;
+    AttendView v;
+    v.batch = p->d.batch;
+    v.n_kv_heads = p->d.n_kv_heads;
+    v.dtype = p->d.dtype;
+    v.cap_pad = 0;
+    v.row_limit = static_cast<int32_t>(cap);
+    v.replay_chunk = 0;
+    v.k = p->d.k_pages;
+    v.v = p->d.v_pages;
+    v.lens_dev = p->d.lens;
+    v.rows = p->lens;
+    v.max_chunks = p->d.batch * ((cap + KVDEC_MIN_CHUNK - 1) / KVDEC_MIN_CHUNK);
+    v.table = p->d.block_table;
+    v.table_stride = p->d.max_pages_per_seq;
+    v.pshift = p->pshift;
+    return attend_view(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
 }
 
 const char* kvdec_status_str(int32_t s)

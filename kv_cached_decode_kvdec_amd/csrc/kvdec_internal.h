@@ -42,6 +42,16 @@ struct AttendArgs {
     float* out;
     void* ws;
     PartialLayout part;
+    // paged layout (table == nullptr: contiguous [B][Hkv][cap_pad][64])
+    const int32_t* table = nullptr;
+    int32_t table_stride = 0;
+    int32_t pshift = 0;
+};
+
+constexpr int kPagesPerLaunch = 256;   // new-page ids carried by value in one paged append
+
+struct PageBlock {
+    int32_t v[kPagesPerLaunch];        // new page for each sequence of the slice, or -1
 };
 
 hipError_t launch_set_lens(int32_t* lens, const int32_t* host, int32_t n, hipStream_t s);
@@ -52,6 +62,10 @@ hipError_t launch_append_rope(int dtype, void* k, void* v, const void* k_new, co
                               int32_t* lens, int32_t batch, int32_t n_kv_heads, int32_t capacity,
                               int32_t cap_pad, int32_t window, const float* q, float* q_rot,
                               int32_t n_q_heads, double theta, hipStream_t s);
+hipError_t launch_paged_append(int dtype, void* k_pages, void* v_pages, const void* k_new,
+                               const void* v_new, int32_t* lens, int32_t* table,
+                               int32_t table_stride, int32_t batch, int32_t n_kv_heads,
+                               int32_t pshift, const int32_t* new_pages, hipStream_t s);
 hipError_t launch_seed(int dtype, void* k, void* v, const void* k_tok, const void* v_tok,
                        int32_t batch, int32_t rows, int32_t n_kv_heads, int32_t cap_pad,
                        hipStream_t s);

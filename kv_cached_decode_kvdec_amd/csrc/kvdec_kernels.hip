@@ -193,6 +193,47 @@ __device__ __forceinline__ void finish_block(const float (&sm_o)[WAVES][GROUP][k
     }
 }
 
+
+// Paged layout: row r of (sequence b, KV head g) lives in page
+// table[b * table_stride + (r >> pshift)], slot r & (2^pshift - 1); a page is
+// [n_kv_heads][2^pshift rows][64].  A workgroup stages the page ids of its
+// chunk in LDS once, then addresses rows from them.
+struct PageMap {
+    const int32_t* table;   // device block table (nullptr: contiguous layout)
+    int stride;             // entries per sequence
+    int pshift;             // log2(rows per page)
+};
+
+constexpr int kMaxChunkPages = KVDEC_MAX_CHUNK / 16 + 1;
+
+template <bool PAGED>
+__device__ __forceinline__ void stage_pages(const PageMap& pm, int b, int row0, int row_end,
+                                            int* sm_pages)
+{
+    if constexpr (PAGED) {
+        const int p0 = row0 >> pm.pshift;
+        const int np = row_end > row0 ? ((row_end - 1) >> pm.pshift) - p0 + 1 : 0;
+        for (int t = threadIdx.x; t < np; t += blockDim.x)
+            sm_pages[t] = pm.table[static_cast<size_t>(b) * pm.stride + p0 + t];
+        __syncthreads();
+    }
+}
+
+// Byte offset of row r of (sequence b, KV head g) from the pool / cache base.
+template <bool PAGED, int RB>
+__device__ __forceinline__ size_t row_offset(const PageMap& pm, const int* sm_pages, int b, int g,
+                                             int Hkv, int cap_pad, int row0, int r)
+{
+    if constexpr (PAGED) {
+        const int page = sm_pages[(r >> pm.pshift) - (row0 >> pm.pshift)];
+        const size_t rows = ((static_cast<size_t>(page) * Hkv + g) << pm.pshift) +
+                            (r & ((1 << pm.pshift) - 1));
+        return rows * RB;
+    } else {
+        return ((static_cast<size_t>(b) * Hkv + g) * cap_pad + r) * RB;
+    }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -308,6 +349,51 @@ __global__ __launch_bounds__(256) void append_rope_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// paged append: a page pool [num_pages][n_kv_heads][2^pshift rows][64] and a
+// block table per sequence (the paged cache of whisper-apr 0.3.3
+// decoder_generated.rs, `PagedDecoderKVCache`: page = position / page size,
+// slot = position % page size).  When a sequence's row lands at the start of
+// a page, the host has chosen a free page for it (passed by value); the
+// kernel installs it in the table before writing the row.
+// ---------------------------------------------------------------------------
+template <int ROW_BYTES>
+__global__ __launch_bounds__(256) void paged_append_kernel(
+    char* __restrict__ Kp, char* __restrict__ Vp, const char* __restrict__ kn,
+    const char* __restrict__ vn, int32_t* __restrict__ lens, int32_t* __restrict__ table,
+    int table_stride, int Hkv, int pshift, int b0, PageBlock new_pages)
+{
+    constexpr int VPR = ROW_BYTES / 16;
+    const int b = b0 + blockIdx.x;
+    const int len = lens[b];
+    if (len < 0) return;
+    const int pidx = len >> pshift;
+    if (pidx >= table_stride) return;                 // host already rejected this
+    const int slot = len & ((1 << pshift) - 1);
+    int32_t* entry = table + static_cast<size_t>(b) * table_stride + pidx;
+    int page;
+    if (slot == 0) {
+        page = new_pages.v[blockIdx.x];
+        if (page < 0) return;                         // host already rejected this
+        if (threadIdx.x == 0) *entry = page;
+    } else {
+        page = *entry;
+    }
+    const int n = Hkv * VPR;
+    for (int t = threadIdx.x; t < 2 * n; t += blockDim.x) {
+        const bool isv = t >= n;
+        const int tt = isv ? t - n : t;
+        const int g = tt / VPR, w = tt - g * VPR;
+        const size_t hg = static_cast<size_t>(b) * Hkv + g;
+        const size_t row = ((static_cast<size_t>(page) * Hkv + g) << pshift) + slot;
+        const uint4* src = reinterpret_cast<const uint4*>((isv ? vn : kn) + hg * ROW_BYTES) + w;
+        uint4* dst = reinterpret_cast<uint4*>((isv ? Vp : Kp) + row * ROW_BYTES) + w;
+        *dst = *src;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) lens[b] = len + 1;
+}
+
+// ---------------------------------------------------------------------------
 // seed: token-major -> head-major, grid-stride over 16-byte words.
 // ---------------------------------------------------------------------------
 template <int ROW_BYTES>
@@ -343,11 +429,12 @@ __global__ __launch_bounds__(256) void seed_kernel(char* __restrict__ K, char* _
 // bytes (EPL dims) of a row, `sub` the row slot (RPI slots per load).  One
 // wave iteration loads U rows per slot: rows r0 + u * RPI + sub.
 // WAVES waves interleave over the chunk in steps of U * RPI rows.
-template <int ESZ, int GROUP, int WAVES, int U>
+template <int ESZ, int GROUP, int WAVES, int U, bool PAGED>
 __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
     const int32_t* __restrict__ lens, int B, int Hkv, int cap_pad, int row_limit, int T,
-    float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml)
+    float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
+    PageMap pm)
 {
     using L = Lay<ESZ>;
     constexpr int EPL = L::kEPL, LPR = L::kLPR, RPI = L::kRPI, RB = L::kRowBytes;
@@ -378,9 +465,10 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
         }
     }
 
-    const size_t hoff = (static_cast<size_t>(loc.b) * Hkv + g) * cap_pad * RB + part * 16;
-    const char* Kb = K + hoff;
-    const char* Vb = V + hoff;
+    __shared__ int sm_pages[PAGED ? kMaxChunkPages : 1];
+    stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages);
+    const char* Kb = K + part * 16;
+    const char* Vb = V + part * 16;
 
     float m[GROUP], l[GROUP], o[GROUP][EPL];
 #pragma unroll
@@ -397,8 +485,9 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = min(r0 + u * RPI + sub, row_end - 1);
-            kr[u] = load16_stream(Kb + static_cast<size_t>(r) * RB);
-            vr[u] = load16_stream(Vb + static_cast<size_t>(r) * RB);
+            const size_t off = row_offset<PAGED, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0, r);
+            kr[u] = load16_stream(Kb + off);
+            vr[u] = load16_stream(Vb + off);
         }
         float s[U][GROUP];
 #pragma unroll
@@ -505,11 +594,12 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 
 constexpr int kGqaLdsStride = 160;     // bytes per staged V row (conflict-free tr16 reads)
 
-template <int GROUP, int WAVES>
+template <int GROUP, int WAVES, bool PAGED>
 __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
     const int32_t* __restrict__ lens, int B, int Hkv, int cap_pad, int row_limit, int T,
-    float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml)
+    float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
+    PageMap pm)
 {
     static_assert(GROUP == 4, "MFMA path takes groups of 4 query heads");
     constexpr int RB = 128;                // bf16 row bytes
@@ -549,9 +639,10 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
         }
     }
 
-    const size_t head_base = (static_cast<size_t>(loc.b) * Hkv + g) * cap_pad * RB;
-    const char* Kb = K + head_base + 16 * G;          // + row * 128 (+64)
-    const char* Vb = V + head_base + 16 * (lane & 7); // + row * 128, row = lane >> 3 (+8c)
+    __shared__ int sm_pages[PAGED ? kMaxChunkPages : 1];
+    stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages);
+    const char* Kb = K + 16 * G;          // + row offset (+64)
+    const char* Vb = V + 16 * (lane & 7); // + row offset, row = r0 + 8c + (lane >> 3)
     char* my_v = sm_v[wave];
     // transpose-read addresses: lane m = 4e + q of group G reads row 4G + e,
     // dims d0 + 4q .. +4 (d0 added per column block), for the second half +16 rows
@@ -567,13 +658,15 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
 #pragma unroll
         for (int tile = 0; tile < 2; ++tile) {
             const int r = min(r0 + 16 * tile + i, row_end - 1);
-            kr[tile][0] = load16_stream(Kb + static_cast<size_t>(r) * RB);
-            kr[tile][1] = load16_stream(Kb + static_cast<size_t>(r) * RB + 64);
+            const size_t off = row_offset<PAGED, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0, r);
+            kr[tile][0] = load16_stream(Kb + off);
+            kr[tile][1] = load16_stream(Kb + off + 64);
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int r = min(r0 + 8 * c + (lane >> 3), row_end - 1);
-            vr[c] = load16_stream(Vb + static_cast<size_t>(r) * RB);
+            vr[c] = load16_stream(
+                Vb + row_offset<PAGED, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0, r));
         }
         // scores: lane holds head hl for rows r0 + 16*tile + 4G + rr
         float sc[2][4];
@@ -807,6 +900,32 @@ hipError_t launch_append_rope(int dtype, void* k, void* v, const void* k_new, co
     return hipGetLastError();
 }
 
+hipError_t launch_paged_append(int dtype, void* k_pages, void* v_pages, const void* k_new,
+                               const void* v_new, int32_t* lens, int32_t* table,
+                               int32_t table_stride, int32_t batch, int32_t n_kv_heads,
+                               int32_t pshift, const int32_t* new_pages, hipStream_t s)
+{
+    for (int32_t b0 = 0; b0 < batch; b0 += kPagesPerLaunch) {
+        const int32_t cnt = (batch - b0) < kPagesPerLaunch ? (batch - b0) : kPagesPerLaunch;
+        PageBlock blk;
+        for (int32_t i = 0; i < kPagesPerLaunch; ++i) blk.v[i] = i < cnt ? new_pages[b0 + i] : -1;
+        const dim3 grid(cnt), block(256);
+        if (dtype == 0)
+            hipLaunchKernelGGL(paged_append_kernel<256>, grid, block, 0, s,
+                               static_cast<char*>(k_pages), static_cast<char*>(v_pages),
+                               static_cast<const char*>(k_new), static_cast<const char*>(v_new),
+                               lens, table, table_stride, n_kv_heads, pshift, b0, blk);
+        else
+            hipLaunchKernelGGL(paged_append_kernel<128>, grid, block, 0, s,
+                               static_cast<char*>(k_pages), static_cast<char*>(v_pages),
+                               static_cast<const char*>(k_new), static_cast<const char*>(v_new),
+                               lens, table, table_stride, n_kv_heads, pshift, b0, blk);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_seed(int dtype, void* k, void* v, const void* k_tok, const void* v_tok,
                        int32_t batch, int32_t rows, int32_t n_kv_heads, int32_t cap_pad,
                        hipStream_t s)
@@ -832,17 +951,24 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kUnroll = 4;
 
-template <int ESZ, int GROUP>
+template <int ESZ, int GROUP, bool PAGED>
 hipError_t attend_t(const AttendArgs& a, hipStream_t s)
 {
     char* ws = static_cast<char*>(a.ws);
     float* po = reinterpret_cast<float*>(ws + a.part.o_offset);
     float2* pml = reinterpret_cast<float2*>(ws + a.part.ml_offset);
+    const PageMap pm{a.table, a.table_stride, a.pshift};
     const dim3 grid(static_cast<unsigned>(a.n_chunks), a.n_kv_heads), block(kWaves * 64);
-    hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWaves, kUnroll>), grid, block, 0, s, a.q,
-                       static_cast<const char*>(a.k), static_cast<const char*>(a.v), a.lens,
-                       a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows, a.qscale,
-                       a.out, po, pml);
+    if constexpr (ESZ == 2 && GROUP == 4)
+        hipLaunchKernelGGL((attend_gqa_mfma_kernel<4, kWaves, PAGED>), grid, block, 0, s, a.q,
+                           static_cast<const char*>(a.k), static_cast<const char*>(a.v), a.lens,
+                           a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows, a.qscale,
+                           a.out, po, pml, pm);
+    else
+        hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWaves, kUnroll, PAGED>), grid, block, 0, s,
+                           a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v),
+                           a.lens, a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows,
+                           a.qscale, a.out, po, pml, pm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.need_merge) return e;
     const int Hq = a.n_kv_heads * GROUP;
@@ -852,42 +978,18 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int GROUP, int WAVES>
-hipError_t attend_gqa_t(const AttendArgs& a, hipStream_t s)
-{
-    char* ws = static_cast<char*>(a.ws);
-    float* po = reinterpret_cast<float*>(ws + a.part.o_offset);
-    float2* pml = reinterpret_cast<float2*>(ws + a.part.ml_offset);
-    const dim3 grid(static_cast<unsigned>(a.n_chunks), a.n_kv_heads), block(WAVES * 64);
-    hipLaunchKernelGGL((attend_gqa_mfma_kernel<GROUP, WAVES>), grid, block, 0, s, a.q,
-                       static_cast<const char*>(a.k), static_cast<const char*>(a.v), a.lens,
-                       a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows, a.qscale,
-                       a.out, po, pml);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !a.need_merge) return e;
-    const int Hq = a.n_kv_heads * GROUP;
-    const int waves = a.batch * Hq;
-    hipLaunchKernelGGL(merge_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, a.lens, a.batch, Hq,
-                       a.chunk_rows, a.row_limit, po, pml, a.out);
-    return hipGetLastError();
-}
-
-template <int ESZ>
+template <int ESZ, bool PAGED>
 hipError_t attend_dispatch_group(const AttendArgs& a, hipStream_t s)
 {
-    if constexpr (ESZ == 2) {
-        // bf16 K/V with 4 query heads per KV head: scores on MFMA
-        if (a.group == 4) return attend_gqa_t<4, 4>(a, s);
-    }
     switch (a.group) {
-        case 1: return attend_t<ESZ, 1>(a, s);
-        case 2: return attend_t<ESZ, 2>(a, s);
-        case 3: return attend_t<ESZ, 3>(a, s);
-        case 4: return attend_t<ESZ, 4>(a, s);
-        case 5: return attend_t<ESZ, 5>(a, s);
-        case 6: return attend_t<ESZ, 6>(a, s);
-        case 7: return attend_t<ESZ, 7>(a, s);
-        case 8: return attend_t<ESZ, 8>(a, s);
+        case 1: return attend_t<ESZ, 1, PAGED>(a, s);
+        case 2: return attend_t<ESZ, 2, PAGED>(a, s);
+        case 3: return attend_t<ESZ, 3, PAGED>(a, s);
+        case 4: return attend_t<ESZ, 4, PAGED>(a, s);
+        case 5: return attend_t<ESZ, 5, PAGED>(a, s);
+        case 6: return attend_t<ESZ, 6, PAGED>(a, s);
+        case 7: return attend_t<ESZ, 7, PAGED>(a, s);
+        case 8: return attend_t<ESZ, 8, PAGED>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -901,16 +1003,16 @@ const void* attend_kernel_ptr(int group, int* block)
 {
     *block = kWaves * 64;
     if constexpr (ESZ == 2)
-        if (group == 4) return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<4, kWaves>);
+        if (group == 4) return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<4, kWaves, false>);
     switch (group) {
-        case 1: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 1, kWaves, kUnroll>);
-        case 2: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 2, kWaves, kUnroll>);
-        case 3: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 3, kWaves, kUnroll>);
-        case 4: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 4, kWaves, kUnroll>);
-        case 5: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 5, kWaves, kUnroll>);
-        case 6: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 6, kWaves, kUnroll>);
-        case 7: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 7, kWaves, kUnroll>);
-        case 8: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 8, kWaves, kUnroll>);
+        case 1: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 1, kWaves, kUnroll, false>);
+        case 2: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 2, kWaves, kUnroll, false>);
+        case 3: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 3, kWaves, kUnroll, false>);
+        case 4: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 4, kWaves, kUnroll, false>);
+        case 5: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 5, kWaves, kUnroll, false>);
+        case 6: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 6, kWaves, kUnroll, false>);
+        case 7: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 7, kWaves, kUnroll, false>);
+        case 8: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 8, kWaves, kUnroll, false>);
         default: return nullptr;
     }
 }
@@ -941,7 +1043,9 @@ int resident_attend_blocks(int dtype, int group)
 
 hipError_t launch_attend(int dtype, const AttendArgs& a, hipStream_t s)
 {
-    return dtype == 0 ? attend_dispatch_group<4>(a, s) : attend_dispatch_group<2>(a, s);
+    if (a.table)
+        return dtype == 0 ? attend_dispatch_group<4, true>(a, s) : attend_dispatch_group<2, true>(a, s);
+    return dtype == 0 ? attend_dispatch_group<4, false>(a, s) : attend_dispatch_group<2, false>(a, s);
 }
 
 }  // namespace kvdec
