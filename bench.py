@@ -245,6 +245,135 @@ def measured_traffic(workload):
     return int(rec["traffic_bytes_per_launch"]), rec.get("kernel")
 
 
+class VariantBench(Bench):
+    """The same workload through one of the other cache forms:
+      paged<P>    : paged pool with P-row pages (block table read per chunk),
+                    lengths rolled back each cycle with kvdec_paged_truncate;
+      rope        : kvdec_append_rope (key and query rotated at the position)
+                    instead of a plain append, on the un-rotated inputs;
+      window<W>   : sliding-window ring of W rows (attends the last W tokens).
+    Self-attention only (cross-attention is the same static cache as the
+    plain form)."""
+
+    def __init__(self, name, variant, torch, gen, B, KVCache, to_device):
+        from kv_cached_decode_kvdec_amd.cache import PagedKVCache
+        import ctypes
+        wl = gen.WORKLOADS[name]
+        self.wl, self.torch, self.variant = wl, torch, variant
+        t0 = time.time()
+        inp = gen.make_inputs(wl, canary=False)
+        nb = wl.batch
+        self.lens0 = inp.lens.copy()
+        self.S = wl.steps
+        self.cross = None
+        self.kn = [to_device(x) for x in inp.k_new]
+        self.vn = [to_device(x) for x in inp.v_new]
+        self.q = [to_device(x) for x in inp.q_self]
+        self.out = torch.empty_like(self.q[0])
+        self.qrot = torch.empty_like(self.q[0])
+        self.paged = None
+        self.window = 0
+        rows_attended = lambda post: post
+        if variant.startswith("paged"):
+            P = int(variant[5:])
+            cap = inp.cap
+            maxp = -(-cap // P)
+            need = int(sum(-(-(int(l) + self.S) // P) for l in self.lens0))
+            self.paged = PagedKVCache(nb, wl.n_kv_heads, P, num_pages=need + nb,
+                                      max_pages_per_seq=maxp, dtype=wl.dtype)
+            self.paged.load_contiguous(to_device(inp.k_cache), to_device(inp.v_cache), self.lens0)
+            self.ws = self.paged._ws.setdefault(
+                wl.n_q_heads, torch.empty(B.kvdec_paged_workspace_bytes(self.paged.handle,
+                                                                          wl.n_q_heads),
+                                          dtype=torch.uint8, device="cuda"))
+        elif variant.startswith("window"):
+            W = int(variant[6:])
+            self.window = W
+            Wp = gen.padded_rows(W)
+            kc = np.zeros((nb, wl.n_kv_heads, Wp, 64), inp.k_cache.dtype)
+            vc = np.zeros_like(kc)
+            for b in range(nb):
+                n = int(self.lens0[b])
+                for t in range(max(0, n - W), n):
+                    kc[b, :, t % W] = inp.k_cache[b, :, t]
+                    vc[b, :, t % W] = inp.v_cache[b, :, t]
+            self.self_cache = KVCache(nb, wl.n_kv_heads, W, wl.dtype, lens=self.lens0,
+                                      k=to_device(kc), v=to_device(vc), window=W)
+            rows_attended = lambda post: np.minimum(post, W)
+        else:
+            self.self_cache = KVCache(nb, wl.n_kv_heads, inp.cap, wl.dtype, lens=self.lens0,
+                                      k=to_device(inp.k_cache), v=to_device(inp.v_cache))
+        inp.k_cache = inp.v_cache = None
+        torch.cuda.synchronize()
+        self.self_bytes, self.step_bytes = [], []
+        for s in range(self.S):
+            post = rows_attended(self.lens0 + s + 1)
+            self.self_bytes.append(attend_bytes(wl, post))
+            self.step_bytes.append(attend_bytes(wl, post) + nb * wl.n_kv_heads * 64 * 2 *
+                                   (4 if wl.dtype == "f32" else 2) * 2)
+        self.cross_bytes = 0
+        lib = B.load()
+        self.lib = lib
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        vp = ctypes.c_void_p
+        self.p_kn = [vp(t.data_ptr()) for t in self.kn]
+        self.p_vn = [vp(t.data_ptr()) for t in self.vn]
+        self.p_q = [vp(t.data_ptr()) for t in self.q]
+        self.p_out = vp(self.out.data_ptr())
+        self.p_qrot = vp(self.qrot.data_ptr())
+        self.lens0_c = (ctypes.c_int32 * len(self.lens0))(*self.lens0.tolist())
+        if self.paged is None:
+            self.h_self = self.self_cache.handle
+            self.ws_self = self.self_cache.workspace(wl.n_q_heads)
+            self.p_ws, self.n_ws = vp(self.ws_self.data_ptr()), self.ws_self.numel()
+        else:
+            self.p_ws, self.n_ws = vp(self.ws.data_ptr()), self.ws.numel()
+        log(f"[{name}+{variant}] inputs ready in {time.time() - t0:.1f}s")
+
+    def step(self, i, events=None, stream=None):
+        lib, s, Hq = self.lib, i % self.S, self.wl.n_q_heads
+        st = self.stream if stream is None else stream
+        if self.paged is not None:
+            h = self.paged.handle
+            if s == 0:
+                rc = lib.kvdec_paged_truncate(h, self.lens0_c, st)
+                assert rc == 0, lib.kvdec_last_error()
+            rc = lib.kvdec_paged_append(h, self.p_kn[s], self.p_vn[s], st)
+            assert rc == 0, lib.kvdec_last_error()
+            if events is not None:
+                events[0].record()
+            rc = lib.kvdec_paged_attend(h, self.p_q[s], Hq, 0.125, 0, self.p_out, self.p_ws,
+                                        self.n_ws, st)
+            assert rc == 0, lib.kvdec_last_error()
+            if events is not None:
+                events[1].record()
+            return
+        if s == 0:
+            rc = lib.kvdec_reset_lens(self.h_self, self.lens0_c, st)
+            assert rc == 0, lib.kvdec_last_error()
+        if self.variant == "rope":
+            rc = lib.kvdec_append_rope(self.h_self, self.p_kn[s], self.p_vn[s], 1.0e6, self.p_q[s],
+                                       self.p_qrot, Hq, st)
+            qp = self.p_qrot
+        else:
+            rc = lib.kvdec_append(self.h_self, self.p_kn[s], self.p_vn[s], st)
+            qp = self.p_q[s]
+        assert rc == 0, lib.kvdec_last_error()
+        if events is not None:
+            events[0].record()
+        rc = lib.kvdec_attend_self(self.h_self, qp, Hq, 0.125, 0, self.p_out, self.p_ws,
+                                   self.n_ws, st)
+        assert rc == 0, lib.kvdec_last_error()
+        if events is not None:
+            events[1].record()
+
+    def close(self):
+        if self.paged is not None:
+            self.paged.close()
+        else:
+            self.self_cache.close()
+
+
 def copy_bandwidth(torch, nbytes=2 << 30, reps=10):
     """Plain device-to-device copy (read + write), the achievable-bandwidth probe."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -324,6 +453,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay measurement")
+    ap.add_argument("--variants", default="qwen2-0.5b+paged16,gqa+paged16,qwen2-0.5b+rope,"
+                                           "qwen2-0.5b+window1024",
+                    help="workload+form pairs (paged<P>, rope, window<W>) to report, or 'none'")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the plain copy kernel (for counter calibration)")
     args = ap.parse_args()
@@ -375,6 +507,19 @@ def main():
             f"{res['attend_avg_us']:.1f} us avg, {res['attend_gbps']:.0f} GB/s; graph replay "
             f"{res.get('graph_ms_per_step', 0) * 1e3:.1f} us/step "
             f"({res.get('graph_pct_of_hbm_peak', 0):.1f}%)")
+
+    for spec in ([] if args.variants == "none" else args.variants.split(",")):
+        name, variant = spec.split("+")
+        vb = VariantBench(name, variant, torch, gen, Bd, KVCache, to_device)
+        wl = gen.WORKLOADS[name]
+        res = vb.run(max(args.steps // 2, wl.steps), max(args.warmup // 2, 4), cold_steps=0)
+        vb.close()
+        del vb
+        torch.cuda.empty_cache()
+        results[spec] = res
+        log(f"[{spec}] {res['steps_per_s']:.0f} steps/s, {res['ms_per_step'] * 1e3:.1f} us/step, "
+            f"{res['effective_gbps']:.0f} GB/s ({res['pct_of_hbm_peak']:.1f}% of 8 TB/s); attend "
+            f"{res['attend_avg_us']:.1f} us avg, {res['attend_gbps']:.0f} GB/s")
 
     copy_gbps = copy_bandwidth(torch)
     log(f"plain copy kernel: {copy_gbps:.0f} GB/s (read + write)")

@@ -255,6 +255,20 @@ int32_t kvdec_paged_append(kvdec_paged* paged, const void* k_new, const void* v_
  * (written on `stream`). */
 int32_t kvdec_paged_release(kvdec_paged* paged, int32_t seq, void* stream);
 
+/* Give the empty sequence `seq` ceil(len / page_rows) free pages and the
+ * length `len` (table entries and length written on `stream`): the hand-off
+ * from a prefill that writes the rows into those pages itself (read their
+ * ids with kvdec_paged_get_table).  Errors: KVDEC_E_INVALID (bad seq, or
+ * the sequence is not empty), KVDEC_E_OVERFLOW (len beyond the block table,
+ * or too few free pages; nothing changes). */
+int32_t kvdec_paged_reserve(kvdec_paged* paged, int32_t seq, int32_t len, void* stream);
+
+/* Shorten sequences to lens_host[batch] (each <= its current length): pages
+ * past the new ends return to the pool, rows before them are kept -- rolling
+ * back speculative tokens, or replaying a benchmark cycle.  Errors:
+ * KVDEC_E_INVALID, KVDEC_E_SHAPE (a length outside [0, current]). */
+int32_t kvdec_paged_truncate(kvdec_paged* paged, const int32_t* lens_host, void* stream);
+
 /* Host mirrors: lengths [batch], block table [batch][max_pages_per_seq]
  * (-1 where no page is held), and the number of free pages (-1 for NULL). */
 int32_t kvdec_paged_get_lens(const kvdec_paged* paged, int32_t* lens_out);

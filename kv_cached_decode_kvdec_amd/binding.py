@@ -30,7 +30,8 @@ EXPORTED = [
     "kvdec_get_lens", "kvdec_seed", "kvdec_append", "kvdec_append_rope", "kvdec_workspace_bytes",
     "kvdec_attend_self", "kvdec_attend_cross", "kvdec_set_replay_mode", "kvdec_status_str",
     "kvdec_last_error", "kvdec_paged_create", "kvdec_paged_destroy", "kvdec_paged_append",
-    "kvdec_paged_release", "kvdec_paged_get_lens", "kvdec_paged_get_table",
+    "kvdec_paged_release", "kvdec_paged_reserve", "kvdec_paged_truncate",
+    "kvdec_paged_get_lens", "kvdec_paged_get_table",
     "kvdec_paged_free_pages", "kvdec_paged_workspace_bytes", "kvdec_paged_attend",
 ]
 
@@ -88,6 +89,8 @@ def load():
         "kvdec_paged_destroy": (None, [_vp]),
         "kvdec_paged_append": (_i32, [_vp, _vp, _vp, _vp]),
         "kvdec_paged_release": (_i32, [_vp, _i32, _vp]),
+        "kvdec_paged_reserve": (_i32, [_vp, _i32, _i32, _vp]),
+        "kvdec_paged_truncate": (_i32, [_vp, _vp, _vp]),
         "kvdec_paged_get_lens": (_i32, [_vp, _vp]),
         "kvdec_paged_get_table": (_i32, [_vp, _vp]),
         "kvdec_paged_free_pages": (_i32, [_vp]),
@@ -197,6 +200,14 @@ def kvdec_paged_append(handle, k_new_ptr, v_new_ptr, stream=None):
 
 def kvdec_paged_release(handle, seq, stream=None):
     _check(load().kvdec_paged_release(handle, int(seq), stream), "kvdec_paged_release")
+
+
+def kvdec_paged_reserve(handle, seq, length, stream=None):
+    _check(load().kvdec_paged_reserve(handle, int(seq), int(length), stream), "kvdec_paged_reserve")
+
+
+def kvdec_paged_truncate(handle, lens_host, stream=None):
+    _check(load().kvdec_paged_truncate(handle, _int_array(lens_host), stream), "kvdec_paged_truncate")
 
 
 def kvdec_paged_get_lens(handle, batch):

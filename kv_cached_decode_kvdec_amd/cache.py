@@ -185,6 +185,26 @@ class PagedKVCache:
     def release(self, seq):
         B.kvdec_paged_release(self.handle, seq, current_stream())
 
+    def reserve(self, seq, length):
+        B.kvdec_paged_reserve(self.handle, seq, length, current_stream())
+
+    def truncate(self, lens):
+        B.kvdec_paged_truncate(self.handle, [int(x) for x in lens], current_stream())
+
+    def load_contiguous(self, k, v, lens):
+        """Reserve pages for empty sequences and copy rows [0, lens[b]) of a
+        contiguous [B][Hkv][cap][64] cache into them (a prefill hand-off)."""
+        for b, n in enumerate(lens):
+            self.reserve(b, int(n))
+        table = self.table()
+        P = self.page_rows
+        for b, n in enumerate(lens):
+            n = int(n)
+            for i in range((n + P - 1) // P):
+                rows = min(P, n - i * P)
+                self.k[table[b][i], :, :rows] = k[b, :, i * P:i * P + rows]
+                self.v[table[b][i], :, :rows] = v[b, :, i * P:i * P + rows]
+
     def attend(self, q, scale=0.125, chunk_rows=0, out=None):
         Hq = q.shape[1]
         if out is None:

@@ -513,6 +513,64 @@ int32_t kvdec_paged_release(kvdec_paged* p, int32_t seq, void* stream)
     return KVDEC_OK;
 }
 
+int32_t kvdec_paged_reserve(kvdec_paged* p, int32_t seq, int32_t len, void* stream)
+{
+    g_err.clear();
+    if (!p) return fail(KVDEC_E_INVALID, "paged cache handle is NULL");
+    if (seq < 0 || seq >= p->d.batch)
+        return fail(KVDEC_E_INVALID, "sequence %d outside [0, %d)", seq, p->d.batch);
+    if (p->lens[seq] != 0)
+        return fail(KVDEC_E_INVALID, "sequence %d is not empty (%d rows)", seq, p->lens[seq]);
+    const int64_t cap = static_cast<int64_t>(p->d.max_pages_per_seq) * p->d.page_rows;
+    if (len < 0 || len > cap)
+        return fail(KVDEC_E_OVERFLOW, "length %d outside [0, %lld]", len, static_cast<long long>(cap));
+    const int32_t n = (len + p->d.page_rows - 1) / p->d.page_rows;
+    if (n > static_cast<int32_t>(p->free_pages.size()))
+        return fail(KVDEC_E_OVERFLOW, "page pool exhausted: %d pages needed, %zu free", n,
+                    p->free_pages.size());
+    std::vector<int32_t> pages(n);
+    for (int32_t i = 0; i < n; ++i) {
+        pages[i] = p->free_pages.back();
+        p->free_pages.pop_back();
+    }
+    const hipError_t e = kvdec::launch_paged_reserve(p->d.block_table, p->d.max_pages_per_seq,
+                                                     p->d.lens, seq, pages.data(), n, len,
+                                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        for (int32_t i = n - 1; i >= 0; --i) p->free_pages.push_back(pages[i]);
+        return hip_fail(e, "paged reserve launch");
+    }
+    const size_t base = static_cast<size_t>(seq) * p->d.max_pages_per_seq;
+    for (int32_t i = 0; i < n; ++i) p->table[base + i] = pages[i];
+    p->lens[seq] = len;
+    return KVDEC_OK;
+}
+
+int32_t kvdec_paged_truncate(kvdec_paged* p, const int32_t* lens_host, void* stream)
+{
+    g_err.clear();
+    if (!p || !lens_host) return fail(KVDEC_E_INVALID, "handle and lens_host must not be NULL");
+    for (int32_t b = 0; b < p->d.batch; ++b)
+        if (lens_host[b] < 0 || lens_host[b] > p->lens[b])
+            return fail(KVDEC_E_SHAPE, "new length %d of sequence %d outside [0, %d]", lens_host[b], b,
+                        p->lens[b]);
+    const hipError_t e = kvdec::launch_set_lens(p->d.lens, lens_host, p->d.batch,
+                                                static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "set lengths");
+    const int32_t P = p->d.page_rows;
+    for (int32_t b = 0; b < p->d.batch; ++b) {
+        const size_t base = static_cast<size_t>(b) * p->d.max_pages_per_seq;
+        const int32_t keep = (lens_host[b] + P - 1) / P;
+        const int32_t held = (p->lens[b] + P - 1) / P;
+        for (int32_t i = held - 1; i >= keep; --i) {
+            p->free_pages.push_back(p->table[base + i]);
+            p->table[base + i] = -1;
+        }
+        p->lens[b] = lens_host[b];
+    }
+    return KVDEC_OK;
+}
+
 int32_t kvdec_paged_get_lens(const kvdec_paged* p, int32_t* lens_out)
 {
     g_err.clear();

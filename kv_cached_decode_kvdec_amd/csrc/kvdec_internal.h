@@ -66,6 +66,8 @@ hipError_t launch_paged_append(int dtype, void* k_pages, void* v_pages, const vo
                                const void* v_new, int32_t* lens, int32_t* table,
                                int32_t table_stride, int32_t batch, int32_t n_kv_heads,
                                int32_t pshift, const int32_t* new_pages, hipStream_t s);
+hipError_t launch_paged_reserve(int32_t* table, int32_t table_stride, int32_t* lens, int32_t seq,
+                                const int32_t* pages, int32_t n_pages, int32_t len, hipStream_t s);
 hipError_t launch_seed(int dtype, void* k, void* v, const void* k_tok, const void* v_tok,
                        int32_t batch, int32_t rows, int32_t n_kv_heads, int32_t cap_pad,
                        hipStream_t s);

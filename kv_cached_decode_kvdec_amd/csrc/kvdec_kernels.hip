@@ -393,6 +393,17 @@ __global__ __launch_bounds__(256) void paged_append_kernel(
     if (threadIdx.x == 0) lens[b] = len + 1;
 }
 
+// Install host-chosen pages in a block table (one sequence, a slice of its
+// entries) and set the sequence's length: the prefill hand-off of a paged
+// cache, whose rows the caller writes itself.
+__global__ void paged_reserve_kernel(int32_t* __restrict__ table, int32_t* __restrict__ lens,
+                                     int seq, int first, int n, int len, PageBlock pages)
+{
+    const int t = threadIdx.x;
+    if (t < n) table[first + t] = pages.v[t];
+    if (t == 0 && len >= 0) lens[seq] = len;
+}
+
 // ---------------------------------------------------------------------------
 // seed: token-major -> head-major, grid-stride over 16-byte words.
 // ---------------------------------------------------------------------------
@@ -922,6 +933,25 @@ hipError_t launch_paged_append(int dtype, void* k_pages, void* v_pages, const vo
                                lens, table, table_stride, n_kv_heads, pshift, b0, blk);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_paged_reserve(int32_t* table, int32_t table_stride, int32_t* lens, int32_t seq,
+                                const int32_t* pages, int32_t n_pages, int32_t len, hipStream_t s)
+{
+    const size_t base = static_cast<size_t>(seq) * table_stride;
+    for (int32_t off = 0; off < n_pages || (off == 0 && n_pages == 0); off += kPagesPerLaunch) {
+        const int32_t cnt = (n_pages - off) < kPagesPerLaunch ? (n_pages - off) : kPagesPerLaunch;
+        PageBlock blk;
+        for (int32_t i = 0; i < kPagesPerLaunch; ++i) blk.v[i] = i < cnt ? pages[off + i] : -1;
+        // the length is written by the last launch, after every table entry
+        const bool last = off + kPagesPerLaunch >= n_pages;
+        hipLaunchKernelGGL(paged_reserve_kernel, dim3(1), dim3(kPagesPerLaunch), 0, s, table + base,
+                           lens, seq, off, cnt, last ? len : -1, blk);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (n_pages == 0) break;
     }
     return hipSuccess;
 }

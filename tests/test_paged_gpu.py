@@ -102,3 +102,34 @@ def test_paged_allocator_limits_change_nothing():
     assert e.value.code == B.KVDEC_E_OVERFLOW
     torch.cuda.synchronize()
     assert pc.lens_dev.cpu().tolist() == [P, 2 * P]
+
+
+def test_paged_reserve_truncate_roundtrip():
+    rng = np.random.default_rng(77)
+    Bsz, Hkv, Hq, P = 3, 4, 16, 16
+    lens0 = np.array([0, 37, 300], np.int32)
+    cap = 400
+    K = _rows(rng, (Bsz, Hkv, gen.padded_rows(cap), 64), "bf16")
+    V = _rows(rng, (Bsz, Hkv, gen.padded_rows(cap), 64), "bf16")
+    pc = PagedKVCache(Bsz, Hkv, P, num_pages=60, max_pages_per_seq=(cap + P - 1) // P, dtype="bf16")
+    pc.load_contiguous(to_device(K), to_device(V), lens0)
+    assert pc.lens() == lens0.tolist()
+    q = rng.standard_normal((Bsz, Hq, 64), dtype=np.float32)
+    out = pc.attend(to_device(q))
+    torch.cuda.synchronize()
+    assert_attention_close(out.cpu().numpy(), oracle.attend(q, K, V, lens0), "bf16", "reserved")
+    free0 = pc.free_pages()
+    # grow by 20 tokens, then roll back to the reserved lengths
+    for _ in range(20):
+        kn = _rows(rng, (Bsz, Hkv, 64), "bf16")
+        pc.append(to_device(kn), to_device(kn))
+    assert pc.lens() == (lens0 + 20).tolist() and pc.free_pages() < free0
+    pc.truncate(lens0)
+    assert pc.lens() == lens0.tolist() and pc.free_pages() == free0
+    out2 = pc.attend(to_device(q))
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    with pytest.raises(B.KvdecError):
+        pc.reserve(1, 5)                   # not empty
+    with pytest.raises(B.KvdecError):
+        pc.truncate([0, 38, 300])          # cannot grow by truncation
