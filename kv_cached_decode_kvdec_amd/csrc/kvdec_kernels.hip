@@ -586,12 +586,15 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
 // attend, grouped-query heads on MFMA (bf16 K/V, 4 query heads per KV head).
 //
 // Per wave iteration: 32 KV rows = two 16-row tiles.  Lane l = 16G + i.
+//  loads   K and V rows as whole 128-byte rows (a wave load covers 8 full
+//          rows), staged in LDS per wave: K at a 144-byte row stride, V at 160
+//          (stride choices keep the 16-byte K reads and the V transpose reads
+//          free of bank conflicts).
 //  scores  S^T = K q^T on v_mfma_f32_16x16x32_bf16: A = K tile (row i, dims
-//          8G..8G+7 and 32+8G..; two 16-byte loads per lane, each wave load
-//          covering one contiguous 64-byte half of all 16 rows), B = the
-//          group's q (column i is head i % 4) as bf16 hi + lo parts, so the
-//          scores keep ~f32 accuracy.  Lane l receives head l % 4 for rows
-//          4G .. 4G+3 of each tile.
+//          8G..8G+7 and 32+8G.., read back from LDS), B = the group's q
+//          (column i is head i % 4) as bf16 hi + lo parts, so the scores keep
+//          ~f32 accuracy.  Lane l receives head l % 4 for rows 4G .. 4G+3 of
+//          each tile.
 //  softmax online per 32 rows; tile max per head across the four G groups.
 //  P.V     O = P V on the same MFMA: A = P (row m of A is head m % 4, k-slot
 //          8G+t <-> tile t/4, row 4G + t%4 -- exactly the lane's own eight
@@ -604,6 +607,7 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 
 constexpr int kGqaLdsStride = 160;     // bytes per staged V row (conflict-free tr16 reads)
+constexpr int kGqaKStride = 144;       // bytes per staged K row (conflict-free 16-byte reads)
 
 template <int GROUP, int WAVES, bool PAGED>
 __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
@@ -622,7 +626,12 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
     const int g = blockIdx.y;
     const int Hq = Hkv * GROUP;
 
-    __shared__ __attribute__((aligned(16))) char sm_v[WAVES][32 * kGqaLdsStride];
+    // per-wave staging of V (then K) rows; after the loop the same LDS holds
+    // the per-wave partial outputs for the workgroup merge
+    constexpr int kStage = 32 * (kGqaLdsStride + kGqaKStride);
+    static_assert(kStage * WAVES >= static_cast<int>(sizeof(float)) * WAVES * GROUP * kHeadDim,
+                  "merge area must fit in the staging LDS");
+    __shared__ __attribute__((aligned(16))) char sm_stage[WAVES * kStage];
 
     Located loc;
     if (!locate(lens, B, T, row_limit, blockIdx.x, lane, loc)) return;
@@ -652,9 +661,10 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
 
     __shared__ int sm_pages[PAGED ? kMaxChunkPages : 1];
     stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages);
-    const char* Kb = K + 16 * G;          // + row offset (+64)
-    const char* Vb = V + 16 * (lane & 7); // + row offset, row = r0 + 8c + (lane >> 3)
-    char* my_v = sm_v[wave];
+    const char* Kb = K + 16 * (lane & 7); // + row offset, row = r0 + 8c + (lane >> 3)
+    const char* Vb = V + 16 * (lane & 7);
+    char* my_v = sm_stage + wave * kStage;
+    char* my_k = my_v + 32 * kGqaLdsStride;
     // transpose-read addresses: lane m = 4e + q of group G reads row 4G + e,
     // dims d0 + 4q .. +4 (d0 added per column block), for the second half +16 rows
     const int tr_off = (4 * G + (i >> 2)) * kGqaLdsStride + 8 * (i & 3);
@@ -665,19 +675,25 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
     for (int c = 0; c < 4; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     for (int r0 = row0 + wave * 32; r0 < row_end; r0 += WAVES * 32) {
-        uint4 kr[2][2], vr[4];
-#pragma unroll
-        for (int tile = 0; tile < 2; ++tile) {
-            const int r = min(r0 + 16 * tile + i, row_end - 1);
-            const size_t off = row_offset<PAGED, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0, r);
-            kr[tile][0] = load16_stream(Kb + off);
-            kr[tile][1] = load16_stream(Kb + off + 64);
-        }
+        uint4 kw[4], vr[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int r = min(r0 + 8 * c + (lane >> 3), row_end - 1);
-            vr[c] = load16_stream(
-                Vb + row_offset<PAGED, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0, r));
+            const size_t off = row_offset<PAGED, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0, r);
+            kw[c] = load16_stream(Kb + off);
+            vr[c] = load16_stream(Vb + off);
+        }
+        // stage K rows r0 .. r0+31, then read the A operand: row 16*tile + i,
+        // bytes 16G .. and 64 + 16G ..
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            *reinterpret_cast<uint4*>(my_k + (8 * c + (lane >> 3)) * kGqaKStride + 16 * (lane & 7)) = kw[c];
+        uint4 kr[2][2];
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile) {
+            const char* kp = my_k + (16 * tile + i) * kGqaKStride + 16 * G;
+            kr[tile][0] = *reinterpret_cast<const uint4*>(kp);
+            kr[tile][1] = *reinterpret_cast<const uint4*>(kp + 64);
         }
         // scores: lane holds head hl for rows r0 + 16*tile + 4G + rr
         float sc[2][4];
@@ -756,7 +772,9 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
     lpart += __shfl_xor(lpart, 16);
     lpart += __shfl_xor(lpart, 32);
 
-    __shared__ float sm_o[WAVES][GROUP][kHeadDim];
+    // every wave must be done with its staging LDS before it becomes sm_o
+    __syncthreads();
+    auto& sm_o = *reinterpret_cast<float (*)[WAVES][GROUP][kHeadDim]>(sm_stage);
     __shared__ float sm_m[WAVES][GROUP];
     __shared__ float sm_l[WAVES][GROUP];
     if (G == 0) {
