@@ -31,6 +31,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Every entry point is exported with default visibility; the library hides
+ * everything else. */
+#if defined(__GNUC__)
+#define KVDEC_API __attribute__((visibility("default")))
+#else
+#define KVDEC_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -93,7 +101,7 @@ typedef struct {
 
 /* Rows per (sequence, KV head) actually laid out for `capacity`: capacity
  * rounded up to a multiple of KVDEC_ROW_ALIGN.  Returns 0 for capacity < 1. */
-int32_t kvdec_padded_capacity(int32_t capacity);
+KVDEC_API int32_t kvdec_padded_capacity(int32_t capacity);
 
 /* Create a handle over caller-owned memory and write the initial lengths
  * lens_host[batch] (host) to desc->lens on `stream`.  Cache contents are not
@@ -101,20 +109,20 @@ int32_t kvdec_padded_capacity(int32_t capacity);
  * unknown dtype, a static ring, reserved0 != 0), KVDEC_E_SHAPE (head_dim !=
  * 64, window not 0 or capacity, a length outside [0, capacity] for a linear
  * cache or negative for a ring).  *out receives the handle (host). */
-int32_t kvdec_cache_create(const kvdec_cache_desc* desc, const int32_t* lens_host,
+KVDEC_API int32_t kvdec_cache_create(const kvdec_cache_desc* desc, const int32_t* lens_host,
                            void* stream, kvdec_cache** out);
 
 /* Release the handle (host memory only; the caller's device memory is not freed). */
-void kvdec_cache_destroy(kvdec_cache* cache);
+KVDEC_API void kvdec_cache_destroy(kvdec_cache* cache);
 
 /* Set every sequence's length from lens_host[batch] (host), device and mirror,
  * leaving cache rows untouched ([WA-DEC] `LayerKVCache::reset` keeps the
  * storage).  Errors: KVDEC_E_INVALID, KVDEC_E_SHAPE (length outside
  * [0, capacity]). */
-int32_t kvdec_reset_lens(kvdec_cache* cache, const int32_t* lens_host, void* stream);
+KVDEC_API int32_t kvdec_reset_lens(kvdec_cache* cache, const int32_t* lens_host, void* stream);
 
 /* Copy the host mirror of the lengths into lens_out[batch] (host).  No device access. */
-int32_t kvdec_get_lens(const kvdec_cache* cache, int32_t* lens_out);
+KVDEC_API int32_t kvdec_get_lens(const kvdec_cache* cache, int32_t* lens_out);
 
 /*
  * Seed rows [0, rows) of every sequence from token-major data and set every
@@ -125,7 +133,7 @@ int32_t kvdec_get_lens(const kvdec_cache* cache, int32_t* lens_out);
  * Allowed on static and dynamic caches.  Errors: KVDEC_E_INVALID,
  * KVDEC_E_SHAPE (rows < 0 or rows > capacity).
  */
-int32_t kvdec_seed(kvdec_cache* cache, const void* k_tok, const void* v_tok, int32_t rows,
+KVDEC_API int32_t kvdec_seed(kvdec_cache* cache, const void* k_tok, const void* v_tok, int32_t rows,
                    void* stream);
 
 /*
@@ -139,7 +147,7 @@ int32_t kvdec_seed(kvdec_cache* cache, const void* k_tok, const void* v_tok, int
  * anything is enqueued, like the "cache overflow" check of
  * `LayerKVCache::append`; KVDEC_E_STATIC on a static cache; KVDEC_E_INVALID.
  */
-int32_t kvdec_append(kvdec_cache* cache, const void* k_new, const void* v_new, void* stream);
+KVDEC_API int32_t kvdec_append(kvdec_cache* cache, const void* k_new, const void* v_new, void* stream);
 
 /*
  * Append with rotary position embedding: like kvdec_append, but k_new holds
@@ -157,7 +165,7 @@ int32_t kvdec_append(kvdec_cache* cache, const void* k_new, const void* v_new, v
  * finite number, only one of q / q_rot given) and KVDEC_E_SHAPE (n_q_heads
  * not a positive multiple of n_kv_heads).
  */
-int32_t kvdec_append_rope(kvdec_cache* cache, const void* k_new, const void* v_new, float theta,
+KVDEC_API int32_t kvdec_append_rope(kvdec_cache* cache, const void* k_new, const void* v_new, float theta,
                           const float* q, float* q_rot, int32_t n_q_heads, void* stream);
 
 /* Workspace bytes any attend call on `cache` with n_q_heads query heads may
@@ -165,7 +173,7 @@ int32_t kvdec_append_rope(kvdec_cache* cache, const void* k_new, const void* v_n
  * initialisation and carry nothing between calls; calls sharing one
  * workspace must not run concurrently (use one stream, or one workspace per
  * stream).  0 on invalid arguments. */
-size_t kvdec_workspace_bytes(const kvdec_cache* cache, int32_t n_q_heads);
+KVDEC_API size_t kvdec_workspace_bytes(const kvdec_cache* cache, int32_t n_q_heads);
 
 /*
  * Decode attention of one query per head over the cached rows of each
@@ -191,7 +199,7 @@ size_t kvdec_workspace_bytes(const kvdec_cache* cache, int32_t n_q_heads);
  * group > KVDEC_MAX_GROUP), KVDEC_E_STATIC, KVDEC_E_WORKSPACE, KVDEC_E_INVALID,
  * KVDEC_E_HIP.
  */
-int32_t kvdec_attend_self(const kvdec_cache* cache, const float* q, int32_t n_q_heads,
+KVDEC_API int32_t kvdec_attend_self(const kvdec_cache* cache, const float* q, int32_t n_q_heads,
                           float scale, int32_t chunk_rows, float* out, void* ws,
                           size_t ws_bytes, void* stream);
 
@@ -202,7 +210,7 @@ int32_t kvdec_attend_self(const kvdec_cache* cache, const float* q, int32_t n_q_
  * [WA-CUDA] `forward_decoder_block_gpu_stream` (incremental attention with
  * seq_len = encoder length).  The cache must be static (KVDEC_E_STATIC otherwise).
  */
-int32_t kvdec_attend_cross(const kvdec_cache* cache, const float* q, int32_t n_q_heads,
+KVDEC_API int32_t kvdec_attend_cross(const kvdec_cache* cache, const float* q, int32_t n_q_heads,
                            float scale, int32_t chunk_rows, float* out, void* ws,
                            size_t ws_bytes, void* stream);
 
@@ -240,8 +248,8 @@ typedef struct {
 /* Create a paged cache: every sequence empty, every page free; writes zero
  * lengths on `stream`.  Errors: KVDEC_E_INVALID, KVDEC_E_SHAPE (head_dim,
  * page_rows not a power of two in range). */
-int32_t kvdec_paged_create(const kvdec_paged_desc* desc, void* stream, kvdec_paged** out);
-void kvdec_paged_destroy(kvdec_paged* paged);
+KVDEC_API int32_t kvdec_paged_create(const kvdec_paged_desc* desc, void* stream, kvdec_paged** out);
+KVDEC_API void kvdec_paged_destroy(kvdec_paged* paged);
 
 /* Append one token to every sequence (same k_new / v_new layout as
  * kvdec_append).  A sequence whose new row starts a page takes a free page
@@ -249,11 +257,11 @@ void kvdec_paged_destroy(kvdec_paged* paged);
  * when a sequence would exceed max_pages_per_seq * page_rows or the pool
  * has too few free pages -- checked before anything changes; a failed
  * launch (KVDEC_E_HIP) returns the pages taken. */
-int32_t kvdec_paged_append(kvdec_paged* paged, const void* k_new, const void* v_new, void* stream);
+KVDEC_API int32_t kvdec_paged_append(kvdec_paged* paged, const void* k_new, const void* v_new, void* stream);
 
 /* End sequence `seq`: its pages return to the pool and its length becomes 0
  * (written on `stream`). */
-int32_t kvdec_paged_release(kvdec_paged* paged, int32_t seq, void* stream);
+KVDEC_API int32_t kvdec_paged_release(kvdec_paged* paged, int32_t seq, void* stream);
 
 /* Give the empty sequence `seq` ceil(len / page_rows) free pages and the
  * length `len` (table entries and length written on `stream`): the hand-off
@@ -261,26 +269,26 @@ int32_t kvdec_paged_release(kvdec_paged* paged, int32_t seq, void* stream);
  * ids with kvdec_paged_get_table).  Errors: KVDEC_E_INVALID (bad seq, or
  * the sequence is not empty), KVDEC_E_OVERFLOW (len beyond the block table,
  * or too few free pages; nothing changes). */
-int32_t kvdec_paged_reserve(kvdec_paged* paged, int32_t seq, int32_t len, void* stream);
+KVDEC_API int32_t kvdec_paged_reserve(kvdec_paged* paged, int32_t seq, int32_t len, void* stream);
 
 /* Shorten sequences to lens_host[batch] (each <= its current length): pages
  * past the new ends return to the pool, rows before them are kept -- rolling
  * back speculative tokens, or replaying a benchmark cycle.  Errors:
  * KVDEC_E_INVALID, KVDEC_E_SHAPE (a length outside [0, current]). */
-int32_t kvdec_paged_truncate(kvdec_paged* paged, const int32_t* lens_host, void* stream);
+KVDEC_API int32_t kvdec_paged_truncate(kvdec_paged* paged, const int32_t* lens_host, void* stream);
 
 /* Host mirrors: lengths [batch], block table [batch][max_pages_per_seq]
  * (-1 where no page is held), and the number of free pages (-1 for NULL). */
-int32_t kvdec_paged_get_lens(const kvdec_paged* paged, int32_t* lens_out);
-int32_t kvdec_paged_get_table(const kvdec_paged* paged, int32_t* table_out);
-int32_t kvdec_paged_free_pages(const kvdec_paged* paged);
+KVDEC_API int32_t kvdec_paged_get_lens(const kvdec_paged* paged, int32_t* lens_out);
+KVDEC_API int32_t kvdec_paged_get_table(const kvdec_paged* paged, int32_t* table_out);
+KVDEC_API int32_t kvdec_paged_free_pages(const kvdec_paged* paged);
 
 /* Workspace for kvdec_paged_attend (same rules as kvdec_workspace_bytes). */
-size_t kvdec_paged_workspace_bytes(const kvdec_paged* paged, int32_t n_q_heads);
+KVDEC_API size_t kvdec_paged_workspace_bytes(const kvdec_paged* paged, int32_t n_q_heads);
 
 /* Decode attention over the paged cache: the computation of
  * kvdec_attend_self, with each row found through the block table. */
-int32_t kvdec_paged_attend(const kvdec_paged* paged, const float* q, int32_t n_q_heads,
+KVDEC_API int32_t kvdec_paged_attend(const kvdec_paged* paged, const float* q, int32_t n_q_heads,
                            float scale, int32_t chunk_rows, float* out, void* ws, size_t ws_bytes,
                            void* stream);
 
@@ -301,13 +309,13 @@ int32_t kvdec_paged_attend(const kvdec_paged* paged, const float* q, int32_t n_q
  * length unchanged (a ring never fills).  kvdec_reset_lens keeps working and
  * is capturable.  Errors: KVDEC_E_INVALID.
  */
-int32_t kvdec_set_replay_mode(kvdec_cache* cache, int32_t chunk_rows);
+KVDEC_API int32_t kvdec_set_replay_mode(kvdec_cache* cache, int32_t chunk_rows);
 
 /* Static description of a status code. */
-const char* kvdec_status_str(int32_t status);
+KVDEC_API const char* kvdec_status_str(int32_t status);
 
 /* Detail of the last error raised on the calling thread ("" if none). */
-const char* kvdec_last_error(void);
+KVDEC_API const char* kvdec_last_error(void);
 
 #ifdef __cplusplus
 }

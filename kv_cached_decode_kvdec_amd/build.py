@@ -32,6 +32,7 @@ def build(force: bool = True, verbose: bool = False) -> str:
         return LIB
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-fvisibility=hidden",
            "-Wall", "-Wno-unused-command-line-argument", *DEVICE_FLAGS,
            "-I", os.path.join(ROOT, "include"), "-o", tmp, *SOURCES]
     if verbose:
