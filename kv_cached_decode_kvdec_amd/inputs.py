@@ -2,12 +2,14 @@
 
 This module is shared by the HIP path's tests/benchmark and by the oracle's
 tests.  It only draws random numbers and lays them out; it holds none of the
-decode arithmetic (no score, softmax or weighted sum).  The one transform it
-applies, the rotary position embedding of the Qwen2-shaped workload, is part
-of how those inputs are made: the pages apply RoPE to q and k before the key
-is cached (franken_ocr 0.8.0 decoder_qwen2.rs, `qwen2_decode_step`:
-RopeTable::build, apply_rope(q), apply_rope(k), then append), so the cache
-holds post-RoPE keys.
+decode arithmetic (no score, softmax, weighted sum or rotary embedding).
+
+The Qwen2-shaped workload caches post-RoPE keys on the pages (franken_ocr
+0.8.0 decoder_qwen2.rs, `qwen2_decode_step`: RoPE on q and k, then append).
+Drawing the rotated vectors directly is the same thing in distribution: a
+rotation of each dim pair (i, i+32) maps an i.i.d. normal pair to an i.i.d.
+normal pair, so rotated standard-normal keys and queries are standard normal.
+The RoPE arithmetic itself is exercised by the rotate-at-append entry point.
 
 Recipe (fixed draw order, numpy PCG64, seed = 1000 + workload index):
   1. pre-append lengths per sequence;
@@ -39,7 +41,7 @@ class Workload:
     steps: int              # consecutive decode steps with append
     cross: bool             # cross-attention over ENC_LEN static rows
     input_scale: float = 1.0
-    rope_theta: float = 0.0  # > 0: NEOX rotate-half RoPE applied to q and k
+    rope_theta: float = 0.0  # > 0: RoPE base of the model (rotate-at-append variant)
     seed: int = 0
     describe: str = field(default="", compare=False)
 
@@ -92,25 +94,6 @@ def draw_lens(rng: np.random.Generator, law: str, batch: int) -> np.ndarray:
     raise ValueError(f"unknown length law {law!r}")
 
 
-def rope_rotate(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
-    """NEOX rotate-half RoPE on the last axis (64), pairing dims (i, i + 32).
-
-    x[..., i]    <- x_i cos(a) - x_{i+32} sin(a)
-    x[..., i+32] <- x_i sin(a) + x_{i+32} cos(a),   a = pos * theta^(-2i/64)
-    (lattice-inference 0.4.0 cpu_q8.rs, `full_attention_step_q8`, stride-half
-    pairing; franken_ocr 0.8.0 decoder_qwen2.rs, NEOX rotate-half at theta 1e6.)
-    `positions` broadcasts against x.shape[:-1].  Computed in float64.
-    """
-    half = HEAD_DIM // 2
-    inv = theta ** (-2.0 * np.arange(half, dtype=np.float64) / HEAD_DIM)
-    ang = np.asarray(positions, dtype=np.float64)[..., None] * inv
-    c, s = np.cos(ang), np.sin(ang)
-    xd = x.astype(np.float64)
-    a, b = xd[..., :half], xd[..., half:]
-    out = np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
-    return out.astype(np.float32)
-
-
 @dataclass
 class Inputs:
     wl: Workload
@@ -160,10 +143,6 @@ def make_inputs(wl: Workload, *, seed=None, batch=None, lens=None, steps=None,
 
     kc = normal((B, Hkv, cap, D))
     vc = normal((B, Hkv, cap, D))
-    if wl.rope_theta > 0:
-        pos = np.broadcast_to(np.arange(cap)[None, :], (Hkv, cap))
-        for b in range(B):                    # row j of the cache sits at position j
-            kc[b] = rope_rotate(kc[b], pos, wl.rope_theta)
     k_new, v_new, q_self, q_cross = [], [], [], []
     for s in range(S):
         kn = normal((B, Hkv, D))
@@ -171,10 +150,6 @@ def make_inputs(wl: Workload, *, seed=None, batch=None, lens=None, steps=None,
         qs = normal((B, Hq, D))
         if wl.cross:
             q_cross.append(normal((B, Hq, D)))
-        if wl.rope_theta > 0:
-            p = (lens + s)[:, None]                  # position of the new token
-            kn = rope_rotate(kn, np.broadcast_to(p, (B, Hkv)), wl.rope_theta)
-            qs = rope_rotate(qs, np.broadcast_to(p, (B, Hq)), wl.rope_theta)
         k_new.append(_to_cache_dtype(kn, wl.dtype))
         v_new.append(_to_cache_dtype(vn, wl.dtype))
         q_self.append(qs.astype(np.float32))

@@ -361,31 +361,6 @@ def test_bf16_rounding_is_nearest_even():
     assert np.isnan(oracle.bf16_to_f32(bits[5:])[0])
 
 
-def test_rope_is_stride_half_and_relative():
-    rng = _rng(25)
-    x = rng.standard_normal((5, D)).astype(np.float32)
-    # position 0 is the identity
-    assert np.allclose(gen.rope_rotate(x, np.zeros(5), 1e6), x, atol=0)
-    # each pair (i, i+32) keeps its norm
-    y = gen.rope_rotate(x, np.arange(5) * 100 + 7, 1e6).astype(np.float64)
-    xd = x.astype(np.float64)
-    np.testing.assert_allclose(y[:, :32] ** 2 + y[:, 32:] ** 2, xd[:, :32] ** 2 + xd[:, 32:] ** 2,
-                               rtol=1e-5)
-    # pair (0, 32) rotates by the position itself (inv_freq_0 = 1): e_0 -> cos p e_0 + sin p e_32
-    e0 = np.zeros((1, D), np.float32)
-    e0[0, 0] = 1.0
-    r = gen.rope_rotate(e0, np.array([1.0]), 1e6)[0]
-    assert abs(r[0] - math.cos(1.0)) < 1e-7 and abs(r[32] - math.sin(1.0)) < 1e-7
-    assert np.all(r[1:32] == 0) and np.all(r[33:] == 0)
-    # scores depend on relative position only
-    q, k = x[0], x[1]
-    def s(m, n):
-        return float(gen.rope_rotate(q[None], np.array([m]), 1e6)[0].astype(np.float64)
-                     @ gen.rope_rotate(k[None], np.array([n]), 1e6)[0].astype(np.float64))
-    assert abs(s(10, 3) - s(110, 103)) < 1e-4
-    assert abs(s(10, 3) - s(10, 4)) > 1e-3
-
-
 def test_generator_is_deterministic_and_canaried():
     wl = gen.WORKLOADS["qwen2-0.5b"]
     a = gen.make_inputs(wl, batch=3, lens=np.array([1, 70, 5], np.int32))
@@ -436,7 +411,3 @@ def test_oracle_rope_closed_forms():
     s1 = oracle.rope(q[None], [50], 1e6)[0] @ oracle.rope(k[None], [20], 1e6)[0]
     s2 = oracle.rope(q[None], [4050], 1e6)[0] @ oracle.rope(k[None], [4020], 1e6)[0]
     assert abs(s1 - s2) < 1e-10
-    # and it agrees with the generator's rotation (f64 there too, cast to f32)
-    g = gen.rope_rotate(x.astype(np.float32), np.arange(6) * 777 + 3, 1e6)
-    np.testing.assert_allclose(g, oracle.rope(x.astype(np.float32), np.arange(6) * 777 + 3, 1e6),
-                               rtol=0, atol=2e-6)
