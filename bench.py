@@ -1,9 +1,10 @@
 """Benchmark of the single-token KV-cached decode step on one MI355X.
 
 One step = one decode token for every sequence of one layer: append the new
-K/V row (kvdec_append), self-attention over the cached rows
-(kvdec_attend_self) and, for the Whisper-shaped workloads, cross-attention
-over the 1500 static encoder rows (kvdec_attend_cross).  Workloads with
+K/V row and self-attention over the cached rows (kvdec_append_attend, one
+launch; --unfused times kvdec_append then kvdec_attend_self instead) and, for
+the Whisper-shaped workloads, cross-attention over the 1500 static encoder
+rows (kvdec_attend_cross).  Workloads with
 several consecutive steps (Whisper-large: 32, GQA: 8) cycle through them; the
 lengths are rolled back to the workload's starting lengths at the start of
 each cycle (one tiny kernel, counted inside the step time).
@@ -16,7 +17,9 @@ Inputs are seeded synthetic tensors resident in HBM before the timed region
 starts.  The timed region is K back-to-back steps bracketed by device
 synchronisation.  HIP events around every attend call inside the timed
 region give the attend kernel's average launch duration (one kernel per
-attend call) and its achieved algorithmic bandwidth.
+attend call, plus the merge launch when a sequence spans several chunks) and
+its achieved algorithmic bandwidth; the fused call's bytes include the store
+of the new K/V row.
 """
 import argparse
 import json
@@ -48,10 +51,15 @@ def attend_bytes(wl, lens_post):
     return rows * wl.n_kv_heads * 64 * 2 * s + B * wl.n_q_heads * 64 * 4 * 2
 
 
+def new_row_bytes(wl):
+    """Bytes of the appended K and V rows of one step (one row per KV head)."""
+    return wl.batch * wl.n_kv_heads * 64 * 2 * (4 if wl.dtype == "f32" else 2)
+
+
 class Bench:
-    def __init__(self, name, torch, gen, B, KVCache, to_device):
+    def __init__(self, name, torch, gen, B, KVCache, to_device, fused=True):
         wl = gen.WORKLOADS[name]
-        self.wl, self.torch, self.B = wl, torch, B
+        self.wl, self.torch, self.B, self.fused = wl, torch, B, fused
         t0 = time.time()
         inp = gen.make_inputs(wl, canary=False)
         self.inp = inp
@@ -78,7 +86,7 @@ class Bench:
         self.self_bytes, self.step_bytes = [], []
         for s in range(self.S):
             post = self.lens0 + s + 1
-            self.self_bytes.append(attend_bytes(wl, post))
+            self.self_bytes.append(attend_bytes(wl, post) + (new_row_bytes(wl) if fused else 0))
             self.step_bytes.append(gen.kv_bytes_per_step(wl, post))
         self.cross_bytes = attend_bytes(wl, np.full(nb, gen.ENC_LEN)) if wl.cross else 0
         self._prep_raw()
@@ -117,12 +125,18 @@ class Bench:
         if s == 0:
             rc = lib.kvdec_reset_lens(self.h_self, self.lens0_c, st)
             assert rc == 0, lib.kvdec_last_error()
-        rc = lib.kvdec_append(self.h_self, self.p_kn[s], self.p_vn[s], st)
-        assert rc == 0, lib.kvdec_last_error()
-        if events is not None:
-            events[0].record()
-        rc = lib.kvdec_attend_self(self.h_self, self.p_q[s], Hq, 0.125, 0, self.p_out, self.p_ws,
-                                   self.n_ws, st)
+        if self.fused:
+            if events is not None:
+                events[0].record()
+            rc = lib.kvdec_append_attend(self.h_self, self.p_kn[s], self.p_vn[s], self.p_q[s], Hq,
+                                         0.125, 0, self.p_out, self.p_ws, self.n_ws, st)
+        else:
+            rc = lib.kvdec_append(self.h_self, self.p_kn[s], self.p_vn[s], st)
+            assert rc == 0, lib.kvdec_last_error()
+            if events is not None:
+                events[0].record()
+            rc = lib.kvdec_attend_self(self.h_self, self.p_q[s], Hq, 0.125, 0, self.p_out,
+                                       self.p_ws, self.n_ws, st)
         assert rc == 0, lib.kvdec_last_error()
         if events is not None:
             events[1].record()
@@ -250,8 +264,9 @@ class VariantBench(Bench):
       paged<P>    : paged pool with P-row pages (block table read per chunk),
                     lengths rolled back each cycle with kvdec_paged_truncate;
       rope        : kvdec_append_rope (key and query rotated at the position)
-                    instead of a plain append, on the un-rotated inputs;
-      window<W>   : sliding-window ring of W rows (attends the last W tokens).
+                    instead of a plain append, then kvdec_attend_self;
+      window<W>   : sliding-window ring of W rows (attends the last W tokens),
+                    through kvdec_append_attend.
     Self-attention only (cross-attention is the same static cache as the
     plain form)."""
 
@@ -308,9 +323,9 @@ class VariantBench(Bench):
         self.self_bytes, self.step_bytes = [], []
         for s in range(self.S):
             post = rows_attended(self.lens0 + s + 1)
-            self.self_bytes.append(attend_bytes(wl, post))
-            self.step_bytes.append(attend_bytes(wl, post) + nb * wl.n_kv_heads * 64 * 2 *
-                                   (4 if wl.dtype == "f32" else 2) * 2)
+            fused_store = new_row_bytes(wl) if variant.startswith("window") else 0
+            self.self_bytes.append(attend_bytes(wl, post) + fused_store)
+            self.step_bytes.append(attend_bytes(wl, post) + 2 * new_row_bytes(wl))
         self.cross_bytes = 0
         lib = B.load()
         self.lib = lib
@@ -352,17 +367,18 @@ class VariantBench(Bench):
             rc = lib.kvdec_reset_lens(self.h_self, self.lens0_c, st)
             assert rc == 0, lib.kvdec_last_error()
         if self.variant == "rope":
-            rc = lib.kvdec_append_rope(self.h_self, self.p_kn[s], self.p_vn[s], 1.0e6, self.p_q[s],
-                                       self.p_qrot, Hq, st)
-            qp = self.p_qrot
-        else:
-            rc = lib.kvdec_append(self.h_self, self.p_kn[s], self.p_vn[s], st)
-            qp = self.p_q[s]
-        assert rc == 0, lib.kvdec_last_error()
-        if events is not None:
-            events[0].record()
-        rc = lib.kvdec_attend_self(self.h_self, qp, Hq, 0.125, 0, self.p_out, self.p_ws,
-                                   self.n_ws, st)
+            rc = lib.kvdec_append_rope(self.h_self, self.p_kn[s], self.p_vn[s],
+                                       self.wl.rope_theta, self.p_q[s], self.p_qrot, Hq, st)
+            assert rc == 0, lib.kvdec_last_error()
+            if events is not None:
+                events[0].record()
+            rc = lib.kvdec_attend_self(self.h_self, self.p_qrot, Hq, 0.125, 0, self.p_out,
+                                       self.p_ws, self.n_ws, st)
+        else:                 # ring: append fused into the attend launch
+            if events is not None:
+                events[0].record()
+            rc = lib.kvdec_append_attend(self.h_self, self.p_kn[s], self.p_vn[s], self.p_q[s], Hq,
+                                         0.125, 0, self.p_out, self.p_ws, self.n_ws, st)
         assert rc == 0, lib.kvdec_last_error()
         if events is not None:
             events[1].record()
@@ -456,6 +472,8 @@ def main():
     ap.add_argument("--variants", default="qwen2-0.5b+paged16,gqa+paged16,qwen2-0.5b+rope,"
                                            "qwen2-0.5b+window1024",
                     help="workload+form pairs (paged<P>, rope, window<W>) to report, or 'none'")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time kvdec_append + kvdec_attend_self instead of kvdec_append_attend")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the plain copy kernel (for counter calibration)")
     args = ap.parse_args()
@@ -487,7 +505,7 @@ def main():
     results = {}
     for name in names:
         wl = gen.WORKLOADS[name]
-        bench = Bench(name, torch, gen, Bd, KVCache, to_device)
+        bench = Bench(name, torch, gen, Bd, KVCache, to_device, fused=not args.unfused)
         K = args.steps
         if name == head:
             res = bench.run(K, args.warmup, cold_steps=args.cold_steps)

@@ -61,6 +61,7 @@ typedef enum { KVDEC_F32 = 0, KVDEC_BF16 = 1 } kvdec_dtype;
 #define KVDEC_MAX_CHUNK 4096   /* largest split-sequence chunk, rows */
 #define KVDEC_MAX_GROUP 8      /* query heads per KV head supported */
 #define KVDEC_REPLAY_AUTO (-1) /* kvdec_set_replay_mode: pick the chunk from current lengths */
+#define KVDEC_MAX_FUSED_BATCH 512 /* kvdec_append_attend fuses the append up to this batch */
 
 /* Opaque host-side handle: the cache description plus a host mirror of the
  * per-sequence lengths (used for validation and launch sizing, so no call
@@ -202,6 +203,22 @@ KVDEC_API size_t kvdec_workspace_bytes(const kvdec_cache* cache, int32_t n_q_hea
 KVDEC_API int32_t kvdec_attend_self(const kvdec_cache* cache, const float* q, int32_t n_q_heads,
                           float scale, int32_t chunk_rows, float* out, void* ws,
                           size_t ws_bytes, void* stream);
+
+/*
+ * kvdec_append followed by kvdec_attend_self, as one call: the decode step
+ * of one layer's self-attention.  Same arguments and errors as the two
+ * calls (everything is checked before anything is enqueued).  For batches
+ * up to KVDEC_MAX_FUSED_BATCH outside replay mode it is a single attend
+ * launch (plus the merge launch when needed): each workgroup reads the new
+ * row straight from k_new / v_new, the one whose chunk holds it also stores
+ * it in the cache, and the pre-append lengths come from the host mirror --
+ * the append-plus-attend call of [WA-CUDA] `flash_attention_cached`.
+ * Otherwise it enqueues the two calls.
+ */
+KVDEC_API int32_t kvdec_append_attend(kvdec_cache* cache, const void* k_new, const void* v_new,
+                                      const float* q, int32_t n_q_heads, float scale,
+                                      int32_t chunk_rows, float* out, void* ws, size_t ws_bytes,
+                                      void* stream);
 
 /*
  * Cross-attention over a static encoder cache: the same computation as

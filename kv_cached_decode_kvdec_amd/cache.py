@@ -129,6 +129,18 @@ class KVCache:
             self._ws[n_q_heads] = ws
         return ws
 
+    def append_attend(self, k_new, v_new, q, scale=0.125, chunk_rows=0, out=None):
+        """Append one token and attend, as one call (one launch when possible)."""
+        shape = (self.batch, self.n_kv_heads, B.HEAD_DIM)
+        self._check_rows(k_new, shape, "k_new")
+        self._check_rows(v_new, shape, "v_new")
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self.workspace(q.shape[1])
+        B.kvdec_append_attend(self.handle, _ptr(k_new), _ptr(v_new), _ptr(q), q.shape[1], scale,
+                              chunk_rows, _ptr(out), _ptr(ws), ws.numel(), current_stream())
+        return out
+
     def attend(self, q, scale=0.125, chunk_rows=0, out=None):
         Hq = q.shape[1]
         if q.dtype != torch.float32 or q.dim() != 3 or q.shape[0] != self.batch \

@@ -133,10 +133,17 @@ struct AttendView {
     int64_t max_chunks;            // workspace sizing bound
     const int32_t* table = nullptr;
     int32_t table_stride = 0, pshift = 0;
+    // append fused into the attend launch
+    const int32_t* fused_lens = nullptr;   // pre-append lengths (host mirror)
+    const void* k_new = nullptr;
+    const void* v_new = nullptr;
+    int32_t* lens_out = nullptr;
+    int32_t window = 0;
 };
 
-int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, float scale,
-                    int32_t chunk_rows, float* out, void* ws, size_t ws_bytes, void* stream)
+// Argument checks of an attend call; nothing is enqueued.
+int32_t check_attend(const AttendView& v, const float* q, int32_t n_q_heads, float scale,
+                     int32_t chunk_rows, const float* out, const void* ws, size_t ws_bytes)
 {
     if (!aligned16(q) || !aligned16(out))
         return fail(KVDEC_E_INVALID, "q and out must be non-NULL, 16-byte aligned device pointers");
@@ -155,6 +162,16 @@ int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, floa
     if (!aligned16(ws) || ws_bytes < part.bytes)
         return fail(KVDEC_E_WORKSPACE, "workspace needs %zu bytes at a 16-byte aligned address, got %zu",
                     part.bytes, ws_bytes);
+    return KVDEC_OK;
+}
+
+int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, float scale,
+                    int32_t chunk_rows, float* out, void* ws, size_t ws_bytes, void* stream)
+{
+    const int32_t rc = check_attend(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes);
+    if (rc) return rc;
+    const int32_t group = n_q_heads / v.n_kv_heads;
+    const kvdec::PartialLayout part = kvdec::partial_layout(v.max_chunks, n_q_heads);
 
     kvdec::AttendArgs a;
     a.q = q;
@@ -189,15 +206,18 @@ int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, floa
     a.table = v.table;
     a.table_stride = v.table_stride;
     a.pshift = v.pshift;
+    a.fused_lens = v.fused_lens;
+    a.k_new = v.k_new;
+    a.v_new = v.v_new;
+    a.lens_out = v.lens_out;
+    a.window = v.window;
     const hipError_t e = kvdec::launch_attend(v.dtype, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "attend launch");
     return KVDEC_OK;
 }
 
-int32_t attend_common(const kvdec_cache* c, const float* q, int32_t n_q_heads, float scale,
-                      int32_t chunk_rows, float* out, void* ws, size_t ws_bytes, void* stream)
+AttendView view_of(const kvdec_cache* c)
 {
-    if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
     AttendView v;
     v.batch = c->d.batch;
     v.n_kv_heads = c->d.n_kv_heads;
@@ -210,7 +230,14 @@ int32_t attend_common(const kvdec_cache* c, const float* q, int32_t n_q_heads, f
     v.lens_dev = c->d.lens;
     v.rows = attended_rows(c);
     v.max_chunks = max_chunks(c);
-    return attend_view(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
+    return v;
+}
+
+int32_t attend_common(const kvdec_cache* c, const float* q, int32_t n_q_heads, float scale,
+                      int32_t chunk_rows, float* out, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
+    return attend_view(view_of(c), q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
 }
 
 int32_t check_append(const kvdec_cache* c, const void* k_new, const void* v_new)
@@ -622,6 +649,39 @@ int32_t kvdec_paged_attend(const kvdec_paged* p, const float* q, int32_t n_q_hea
     v.table_stride = p->d.max_pages_per_seq;
     v.pshift = p->pshift;
     return attend_view(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
+}
+
+int32_t kvdec_append_attend(kvdec_cache* c, const void* k_new, const void* v_new, const float* q,
+                            int32_t n_q_heads, float scale, int32_t chunk_rows, float* out, void* ws,
+                            size_t ws_bytes, void* stream)
+{
+    g_err.clear();
+    int32_t rc = check_append(c, k_new, v_new);
+    if (rc) return rc;
+    AttendView v = view_of(c);
+    rc = check_attend(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes);
+    if (rc) return rc;
+    if (c->d.batch > KVDEC_MAX_FUSED_BATCH || c->replay_chunk > 0) {
+        // separate launches: the arguments are already checked, so the
+        // append cannot leave a half-done call behind
+        rc = kvdec_append(c, k_new, v_new, stream);
+        if (rc) return rc;
+        return kvdec_attend_self(c, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
+    }
+    // one launch: lengths from the host mirror, rows attended after the append
+    for (auto& r : v.rows) {
+        const int64_t n = static_cast<int64_t>(r) + 1;
+        r = static_cast<int32_t>(c->d.window > 0 && n > c->d.window ? c->d.window : n);
+    }
+    v.fused_lens = c->lens.data();
+    v.k_new = k_new;
+    v.v_new = v_new;
+    v.lens_out = c->d.lens;
+    v.window = c->d.window;
+    rc = attend_view(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
+    if (rc) return rc;
+    for (auto& l : c->lens) ++l;
+    return KVDEC_OK;
 }
 
 const char* kvdec_status_str(int32_t s)

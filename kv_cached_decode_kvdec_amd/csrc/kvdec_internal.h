@@ -46,6 +46,13 @@ struct AttendArgs {
     const int32_t* table = nullptr;
     int32_t table_stride = 0;
     int32_t pshift = 0;
+    // append fused into the launch (fused_lens != nullptr): pre-append
+    // lengths (host), new rows, the device lengths to bump, ring window
+    const int32_t* fused_lens = nullptr;
+    const void* k_new = nullptr;
+    const void* v_new = nullptr;
+    int32_t* lens_out = nullptr;
+    int32_t window = 0;
 };
 
 constexpr int kPagesPerLaunch = 256;   // new-page ids carried by value in one paged append

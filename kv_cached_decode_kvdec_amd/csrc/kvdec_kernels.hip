@@ -38,6 +38,7 @@ namespace kvdec {
 
 namespace {
 
+constexpr int kMaxFusedBatch = KVDEC_MAX_FUSED_BATCH;
 constexpr float kNegBig = -1.0e30f;   // finite "no row seen yet" running max
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -129,13 +130,41 @@ struct Located {
     int b, c, len, nch;
 };
 
-__device__ __forceinline__ bool locate(const int32_t* __restrict__ lens, int B, int T, int cap,
-                                       int blk, int lane, Located& r)
+// Where an attend launch gets the per-sequence lengths from.  Plain launch:
+// the device array, rows = lens[b].  Fused append: the pre-append lengths by
+// value (host mirror), rows = len + 1, plus the new rows and the cache to
+// store them in (the launch itself reads no device length).
+template <bool FUSED>
+struct LensSrc;
+
+template <>
+struct LensSrc<false> {
+    const int32_t* lens;
+    static constexpr int kPlus = 0;
+    __device__ __forceinline__ int get(int b) const { return lens[b]; }
+};
+
+template <>
+struct LensSrc<true> {
+    int32_t v[kMaxFusedBatch];
+    const char* k_new;      // [B][Hkv][64] elements
+    const char* v_new;
+    char* K;                // contiguous cache, written at the new row's slot
+    char* V;
+    int32_t* lens_out;      // device lengths, bumped by one per sequence
+    int window;             // ring window, 0 for a linear cache
+    static constexpr int kPlus = 1;
+    __device__ __forceinline__ int get(int b) const { return v[b]; }
+};
+
+template <bool FUSED>
+__device__ __forceinline__ bool locate(const LensSrc<FUSED>& ls, int B, int T, int cap, int blk,
+                                       int lane, Located& r)
 {
     int base = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
         const int bi = b0 + lane;
-        const int ln = bi < B ? min(max(lens[bi], 0), cap) : 0;
+        const int ln = bi < B ? min(max(ls.get(bi) + LensSrc<FUSED>::kPlus, 0), cap) : 0;
         const int cnt = bi < B ? max(1, (ln + T - 1) / T) : 0;
         int incl = cnt;
 #pragma unroll
@@ -156,6 +185,32 @@ __device__ __forceinline__ bool locate(const int32_t* __restrict__ lens, int B, 
         base += total;
     }
     return false;
+}
+
+// Fused append, inside an attend workgroup of (sequence b, KV head g) whose
+// rows are [row0, row_end): the workgroup whose rows hold the new token's
+// slot stores the new K/V row of head g there (the one of head 0 also bumps
+// the length), then waits at a workgroup barrier, which makes those stores
+// visible to all its waves before any of them reads the slot.  No other
+// workgroup reads that slot, so the launch needs no wider synchronisation.
+template <int RB>
+__device__ __forceinline__ void fused_append(const LensSrc<true>& ls, int b, int g, int Hkv,
+                                            int cap_pad, int row0, int row_end)
+{
+    const int len0 = ls.v[b];
+    const int slot = ls.window > 0 ? len0 % ls.window : len0;
+    if (row0 <= slot && slot < row_end) {
+        const size_t hg = static_cast<size_t>(b) * Hkv + g;
+        constexpr int VPR = RB / 16;
+        for (int t = threadIdx.x; t < 2 * VPR; t += blockDim.x) {
+            const bool isv = t >= VPR;
+            const int w = isv ? t - VPR : t;
+            const uint4 x = reinterpret_cast<const uint4*>((isv ? ls.v_new : ls.k_new) + hg * RB)[w];
+            reinterpret_cast<uint4*>((isv ? ls.V : ls.K) + (hg * cap_pad + slot) * RB)[w] = x;
+        }
+        if (g == 0 && threadIdx.x == 0) ls.lens_out[b] = len0 + 1;
+        __syncthreads();
+    }
 }
 
 // Combine the WAVES per-wave states of a workgroup (staged in LDS) and
@@ -440,10 +495,10 @@ __global__ __launch_bounds__(256) void seed_kernel(char* __restrict__ K, char* _
 // bytes (EPL dims) of a row, `sub` the row slot (RPI slots per load).  One
 // wave iteration loads U rows per slot: rows r0 + u * RPI + sub.
 // WAVES waves interleave over the chunk in steps of U * RPI rows.
-template <int ESZ, int GROUP, int WAVES, int U, bool PAGED>
+template <int ESZ, int GROUP, int WAVES, int U, bool PAGED, bool FUSED>
 __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
-    const int32_t* __restrict__ lens, int B, int Hkv, int cap_pad, int row_limit, int T,
+    LensSrc<FUSED> ls, int B, int Hkv, int cap_pad, int row_limit, int T,
     float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
     PageMap pm)
 {
@@ -457,7 +512,7 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
     const int Hq = Hkv * GROUP;
 
     Located loc;
-    if (!locate(lens, B, T, row_limit, blockIdx.x, lane, loc)) return;
+    if (!locate<FUSED>(ls, B, T, row_limit, blockIdx.x, lane, loc)) return;
     const int row0 = loc.c * T;
     const int row_end = min(loc.len, row0 + T);
 
@@ -480,6 +535,7 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
     stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages);
     const char* Kb = K + part * 16;
     const char* Vb = V + part * 16;
+    if constexpr (FUSED) fused_append<RB>(ls, loc.b, g, Hkv, cap_pad, row0, row_end);
 
     float m[GROUP], l[GROUP], o[GROUP][EPL];
 #pragma unroll
@@ -609,10 +665,10 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 constexpr int kGqaLdsStride = 160;     // bytes per staged V row (conflict-free tr16 reads)
 constexpr int kGqaKStride = 144;       // bytes per staged K row (conflict-free 16-byte reads)
 
-template <int GROUP, int WAVES, bool PAGED>
+template <int GROUP, int WAVES, bool PAGED, bool FUSED>
 __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
-    const int32_t* __restrict__ lens, int B, int Hkv, int cap_pad, int row_limit, int T,
+    LensSrc<FUSED> ls, int B, int Hkv, int cap_pad, int row_limit, int T,
     float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
     PageMap pm)
 {
@@ -634,7 +690,7 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
     __shared__ __attribute__((aligned(16))) char sm_stage[WAVES * kStage];
 
     Located loc;
-    if (!locate(lens, B, T, row_limit, blockIdx.x, lane, loc)) return;
+    if (!locate<FUSED>(ls, B, T, row_limit, blockIdx.x, lane, loc)) return;
     const int row0 = loc.c * T;
     const int row_end = min(loc.len, row0 + T);
 
@@ -663,6 +719,7 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
     stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages);
     const char* Kb = K + 16 * (lane & 7); // + row offset, row = r0 + 8c + (lane >> 3)
     const char* Vb = V + 16 * (lane & 7);
+    if constexpr (FUSED) fused_append<RB>(ls, loc.b, g, Hkv, cap_pad, row0, row_end);
     char* my_v = sm_stage + wave * kStage;
     char* my_k = my_v + 32 * kGqaLdsStride;
     // transpose-read addresses: lane m = 4e + q of group G reads row 4G + e,
@@ -796,12 +853,14 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
 // weights w_c = 2^(m_c - M); then lane d sums w_c * o_c[d] over the chunks
 // in chunk order (a fixed order: the result does not depend on scheduling).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ lens, int B, int Hq,
+template <bool FUSED>
+__global__ __launch_bounds__(256) void merge_kernel(LensSrc<FUSED> ls, int B, int Hq,
                                                     int T, int row_limit,
                                                     const float* __restrict__ part_o,
                                                     const float2* __restrict__ part_ml,
                                                     float* __restrict__ out)
 {
+    constexpr int plus = LensSrc<FUSED>::kPlus;
     const int lane = threadIdx.x & 63;
     const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (w >= B * Hq) return;
@@ -810,11 +869,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
     int acc = 0;
     for (int b0 = 0; b0 < b; b0 += 64) {
         const int bi = b0 + lane;
-        if (bi < b) acc += max(1, (min(max(lens[bi], 0), row_limit) + T - 1) / T);
+        if (bi < b) acc += max(1, (min(max(ls.get(bi) + plus, 0), row_limit) + T - 1) / T);
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
-    const int nch = max(1, (min(max(lens[b], 0), row_limit) + T - 1) / T);
+    const int nch = max(1, (min(max(ls.get(b) + plus, 0), row_limit) + T - 1) / T);
     if (nch == 1) return;     // finished by the attend kernel
     const size_t first = static_cast<size_t>(acc);
 
@@ -999,45 +1058,57 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kUnroll = 4;
 
-template <int ESZ, int GROUP, bool PAGED>
+template <int ESZ, int GROUP, bool PAGED, bool FUSED>
 hipError_t attend_t(const AttendArgs& a, hipStream_t s)
 {
     char* ws = static_cast<char*>(a.ws);
     float* po = reinterpret_cast<float*>(ws + a.part.o_offset);
     float2* pml = reinterpret_cast<float2*>(ws + a.part.ml_offset);
     const PageMap pm{a.table, a.table_stride, a.pshift};
+    LensSrc<FUSED> ls;
+    if constexpr (FUSED) {
+        for (int b = 0; b < kMaxFusedBatch; ++b) ls.v[b] = b < a.batch ? a.fused_lens[b] : 0;
+        ls.k_new = static_cast<const char*>(a.k_new);
+        ls.v_new = static_cast<const char*>(a.v_new);
+        ls.K = static_cast<char*>(const_cast<void*>(a.k));
+        ls.V = static_cast<char*>(const_cast<void*>(a.v));
+        ls.lens_out = a.lens_out;
+        ls.window = a.window;
+    } else {
+        ls.lens = a.lens;
+    }
     const dim3 grid(static_cast<unsigned>(a.n_chunks), a.n_kv_heads), block(kWaves * 64);
     if constexpr (ESZ == 2 && GROUP == 4)
-        hipLaunchKernelGGL((attend_gqa_mfma_kernel<4, kWaves, PAGED>), grid, block, 0, s, a.q,
-                           static_cast<const char*>(a.k), static_cast<const char*>(a.v), a.lens,
+        hipLaunchKernelGGL((attend_gqa_mfma_kernel<4, kWaves, PAGED, FUSED>), grid, block, 0, s,
+                           a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v), ls,
                            a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows, a.qscale,
                            a.out, po, pml, pm);
     else
-        hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWaves, kUnroll, PAGED>), grid, block, 0, s,
-                           a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v),
-                           a.lens, a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows,
+        hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWaves, kUnroll, PAGED, FUSED>), grid, block,
+                           0, s, a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v),
+                           ls, a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows,
                            a.qscale, a.out, po, pml, pm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.need_merge) return e;
     const int Hq = a.n_kv_heads * GROUP;
     const int waves = a.batch * Hq;
-    hipLaunchKernelGGL(merge_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, a.lens, a.batch, Hq,
-                       a.chunk_rows, a.row_limit, po, pml, a.out);
+    hipLaunchKernelGGL((merge_kernel<FUSED>), dim3((waves + 3) / 4), dim3(256), 0, s, ls, a.batch,
+                       Hq, a.chunk_rows, a.row_limit, po, pml, a.out);
     return hipGetLastError();
 }
 
-template <int ESZ, bool PAGED>
+template <int ESZ, bool PAGED, bool FUSED>
 hipError_t attend_dispatch_group(const AttendArgs& a, hipStream_t s)
 {
     switch (a.group) {
-        case 1: return attend_t<ESZ, 1, PAGED>(a, s);
-        case 2: return attend_t<ESZ, 2, PAGED>(a, s);
-        case 3: return attend_t<ESZ, 3, PAGED>(a, s);
-        case 4: return attend_t<ESZ, 4, PAGED>(a, s);
-        case 5: return attend_t<ESZ, 5, PAGED>(a, s);
-        case 6: return attend_t<ESZ, 6, PAGED>(a, s);
-        case 7: return attend_t<ESZ, 7, PAGED>(a, s);
-        case 8: return attend_t<ESZ, 8, PAGED>(a, s);
+        case 1: return attend_t<ESZ, 1, PAGED, FUSED>(a, s);
+        case 2: return attend_t<ESZ, 2, PAGED, FUSED>(a, s);
+        case 3: return attend_t<ESZ, 3, PAGED, FUSED>(a, s);
+        case 4: return attend_t<ESZ, 4, PAGED, FUSED>(a, s);
+        case 5: return attend_t<ESZ, 5, PAGED, FUSED>(a, s);
+        case 6: return attend_t<ESZ, 6, PAGED, FUSED>(a, s);
+        case 7: return attend_t<ESZ, 7, PAGED, FUSED>(a, s);
+        case 8: return attend_t<ESZ, 8, PAGED, FUSED>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1051,16 +1122,17 @@ const void* attend_kernel_ptr(int group, int* block)
 {
     *block = kWaves * 64;
     if constexpr (ESZ == 2)
-        if (group == 4) return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<4, kWaves, false>);
+        if (group == 4)
+            return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<4, kWaves, false, false>);
     switch (group) {
-        case 1: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 1, kWaves, kUnroll, false>);
-        case 2: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 2, kWaves, kUnroll, false>);
-        case 3: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 3, kWaves, kUnroll, false>);
-        case 4: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 4, kWaves, kUnroll, false>);
-        case 5: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 5, kWaves, kUnroll, false>);
-        case 6: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 6, kWaves, kUnroll, false>);
-        case 7: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 7, kWaves, kUnroll, false>);
-        case 8: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 8, kWaves, kUnroll, false>);
+        case 1: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 1, kWaves, kUnroll, false, false>);
+        case 2: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 2, kWaves, kUnroll, false, false>);
+        case 3: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 3, kWaves, kUnroll, false, false>);
+        case 4: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 4, kWaves, kUnroll, false, false>);
+        case 5: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 5, kWaves, kUnroll, false, false>);
+        case 6: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 6, kWaves, kUnroll, false, false>);
+        case 7: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 7, kWaves, kUnroll, false, false>);
+        case 8: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 8, kWaves, kUnroll, false, false>);
         default: return nullptr;
     }
 }
@@ -1092,8 +1164,15 @@ int resident_attend_blocks(int dtype, int group)
 hipError_t launch_attend(int dtype, const AttendArgs& a, hipStream_t s)
 {
     if (a.table)
-        return dtype == 0 ? attend_dispatch_group<4, true>(a, s) : attend_dispatch_group<2, true>(a, s);
-    return dtype == 0 ? attend_dispatch_group<4, false>(a, s) : attend_dispatch_group<2, false>(a, s);
+        return dtype == 0 ? attend_dispatch_group<4, true, false>(a, s)
+                          : attend_dispatch_group<2, true, false>(a, s);
+    if (a.fused_lens) {
+        if (a.batch > kMaxFusedBatch) return hipErrorInvalidValue;
+        return dtype == 0 ? attend_dispatch_group<4, false, true>(a, s)
+                          : attend_dispatch_group<2, false, true>(a, s);
+    }
+    return dtype == 0 ? attend_dispatch_group<4, false, false>(a, s)
+                      : attend_dispatch_group<2, false, false>(a, s);
 }
 
 }  // namespace kvdec

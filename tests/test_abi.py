@@ -28,6 +28,21 @@ def test_library_exports_every_declared_symbol():
     assert sorted(B.EXPORTED) == names
 
 
+def test_binding_constants_match_header():
+    with open(os.path.join(ROOT, "include", "kvdec.h")) as f:
+        text = f.read()
+    defs = dict(re.findall(r"#define\s+(KVDEC_[A-Z0-9_]+)\s+(-?\d+)", text))
+    defs.update(re.findall(r"\b(KVDEC_[A-Z0-9_]+)\s*=\s*(\d+)", text))     # enumerators
+    assert int(defs["KVDEC_HEAD_DIM"]) == B.HEAD_DIM
+    assert int(defs["KVDEC_MIN_CHUNK"]) == B.MIN_CHUNK
+    assert int(defs["KVDEC_MAX_CHUNK"]) == B.MAX_CHUNK
+    assert int(defs["KVDEC_MAX_GROUP"]) == B.MAX_GROUP
+    assert int(defs["KVDEC_MAX_FUSED_BATCH"]) == B.KVDEC_MAX_FUSED_BATCH
+    for name in ("KVDEC_OK", "KVDEC_E_INVALID", "KVDEC_E_SHAPE", "KVDEC_E_OVERFLOW",
+                 "KVDEC_E_STATIC", "KVDEC_E_WORKSPACE", "KVDEC_E_HIP", "KVDEC_F32", "KVDEC_BF16"):
+        assert int(defs[name]) == getattr(B, name), name
+
+
 def test_library_is_gfx950_native():
     # the shared object carries a gfx950 code object bundle
     with open(B.LIB_PATH, "rb") as f:
