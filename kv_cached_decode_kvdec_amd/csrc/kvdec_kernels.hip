@@ -848,10 +848,12 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// merge: one wave per (sequence, query head).  Lane c first takes chunk c's
-// (m, l) -- all loads issued at once -- to form the global max M and the
-// weights w_c = 2^(m_c - M); then lane d sums w_c * o_c[d] over the chunks
-// in chunk order (a fixed order: the result does not depend on scheduling).
+// merge: one wave per (sequence, query head).  Lane c takes chunk c's (m, l)
+// to form the global max M and the weights w_c = 2^(m_c - M); lane d sums
+// w_c * o_c[d] over the chunks in chunk order (a fixed order: the result does
+// not depend on scheduling).  The kernel is latency-bound (a few KB per
+// wave), so the loads are grouped to keep the chain of dependent round trips
+// short: lengths -> {(m, l), first 16 o rows} -> further batches of 16.
 // ---------------------------------------------------------------------------
 template <bool FUSED>
 __global__ __launch_bounds__(256) void merge_kernel(LensSrc<FUSED> ls, int B, int Hq,
@@ -877,49 +879,51 @@ __global__ __launch_bounds__(256) void merge_kernel(LensSrc<FUSED> ls, int B, in
     if (nch == 1) return;     // finished by the attend kernel
     const size_t first = static_cast<size_t>(acc);
 
+    // Chunk c's (m, l) is read by lane c % 64; the o rows are read kBatch
+    // chunks at a time, all loads of a batch in flight together, and the
+    // first batch is issued with the (m, l) loads (it does not need M).
+    // Indices past the last chunk are clamped (their values are not used).
+    constexpr int kBatch = 16;
+    float ov[kBatch];
+    auto load_batch = [&](int cb) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const size_t c = first + min(cb + j, nch - 1);
+            ov[j] = part_o[(c * Hq + h) * kHeadDim + lane];
+        }
+    };
+    float2 ml0 = make_float2(kNegBig, 0.f);
+    if (lane < nch) ml0 = part_ml[(first + lane) * Hq + h];
+    load_batch(0);
+
     // global max over the chunks' m (lane-parallel)
-    float M = kNegBig;
-    for (int c0 = 0; c0 < nch; c0 += 64) {
+    float M = ml0.x;
+    for (int c0 = 64; c0 < nch; c0 += 64) {
         const int c = c0 + lane;
         if (c < nch) M = fmaxf(M, part_ml[(first + c) * Hq + h].x);
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
 
+    // weights w_c = 2^(m_c - M); sums of w_c l_c and w_c o_c in chunk order
     float Lsum = 0.f, o = 0.f;
     for (int c0 = 0; c0 < nch; c0 += 64) {
         const int c = c0 + lane;
-        float wc = 0.f, lc = 0.f;
-        if (c < nch) {
-            const float2 ml = part_ml[(first + c) * Hq + h];
-            wc = fast_exp2(ml.x - M);
-            lc = ml.y;
-        }
+        float2 ml = ml0;
+        if (c0 > 0) ml = c < nch ? part_ml[(first + c) * Hq + h] : make_float2(kNegBig, 0.f);
+        const float wc = c < nch ? fast_exp2(ml.x - M) : 0.f;
+        const float lc = c < nch ? ml.y : 0.f;
         const int n = min(64, nch - c0);
-        // sum of w_c * l_c in chunk order: every lane walks the same sequence
-        int k = 0;
-        for (; k + 4 <= n; k += 4) {
-            const size_t s0 = (first + c0 + k) * Hq + h;
-            const float o0 = part_o[s0 * kHeadDim + lane];
-            const float o1 = part_o[(s0 + Hq) * kHeadDim + lane];
-            const float o2 = part_o[(s0 + 2 * Hq) * kHeadDim + lane];
-            const float o3 = part_o[(s0 + 3 * Hq) * kHeadDim + lane];
-            const float w0 = __shfl(wc, k), w1 = __shfl(wc, k + 1);
-            const float w2 = __shfl(wc, k + 2), w3 = __shfl(wc, k + 3);
-            Lsum = fmaf(__shfl(lc, k), w0, Lsum);
-            Lsum = fmaf(__shfl(lc, k + 1), w1, Lsum);
-            Lsum = fmaf(__shfl(lc, k + 2), w2, Lsum);
-            Lsum = fmaf(__shfl(lc, k + 3), w3, Lsum);
-            o = fmaf(o0, w0, o);
-            o = fmaf(o1, w1, o);
-            o = fmaf(o2, w2, o);
-            o = fmaf(o3, w3, o);
-        }
-        for (; k < n; ++k) {
-            const size_t s0 = (first + c0 + k) * Hq + h;
-            const float wk = __shfl(wc, k);
-            Lsum = fmaf(__shfl(lc, k), wk, Lsum);
-            o = fmaf(part_o[s0 * kHeadDim + lane], wk, o);
+        for (int k0 = 0; k0 < n; k0 += kBatch) {
+            if (c0 + k0 > 0) load_batch(c0 + k0);
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (k0 + j < n) {
+                    const float wk = __shfl(wc, k0 + j);
+                    Lsum = fmaf(__shfl(lc, k0 + j), wk, Lsum);
+                    o = fmaf(ov[j], wk, o);
+                }
+            }
         }
     }
     out[static_cast<size_t>(w) * kHeadDim + lane] = (Lsum > 0.f) ? o / Lsum : 0.f;
