@@ -516,26 +516,23 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
     const int row0 = loc.c * T;
     const int row_end = min(loc.len, row0 + T);
 
-    // q for the GROUP heads sharing KV head g, this lane's dims, pre-scaled.
-    float qv[GROUP][EPL];
-#pragma unroll
-    for (int i = 0; i < GROUP; ++i) {
-        const float* qp = q + (static_cast<size_t>(loc.b) * Hq + g * GROUP + i) * kHeadDim + part * EPL;
-#pragma unroll
-        for (int e = 0; e < EPL; e += 4) {
-            const float4 t = *reinterpret_cast<const float4*>(qp + e);
-            qv[i][e + 0] = t.x * qscale;
-            qv[i][e + 1] = t.y * qscale;
-            qv[i][e + 2] = t.z * qscale;
-            qv[i][e + 3] = t.w * qscale;
-        }
-    }
-
     __shared__ int sm_pages[PAGED ? kMaxChunkPages : 1];
     stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages);
     const char* Kb = K + part * 16;
     const char* Vb = V + part * 16;
     if constexpr (FUSED) fused_append<RB>(ls, loc.b, g, Hkv, cap_pad, row0, row_end);
+
+    // q for the GROUP heads sharing KV head g, this lane's dims.  It is not
+    // waited for before the loop: the first rows' loads are issued first and
+    // the scale (times log2 e) is applied to each score, so the workgroup
+    // pays one memory round trip before its first scores, not two.
+    float4 qv[GROUP][EPL / 4];
+#pragma unroll
+    for (int i = 0; i < GROUP; ++i) {
+        const float* qp = q + (static_cast<size_t>(loc.b) * Hq + g * GROUP + i) * kHeadDim + part * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) qv[i][e / 4] = *reinterpret_cast<const float4*>(qp + e);
+    }
 
     float m[GROUP], l[GROUP], o[GROUP][EPL];
 #pragma unroll
@@ -566,8 +563,13 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
             for (int i = 0; i < GROUP; ++i) {
                 float d = 0.f;
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) d = fmaf(qv[i][e], kf[e], d);
-                d = row_sum<LPR>(d);
+                for (int e = 0; e < EPL; e += 4) {
+                    d = fmaf(qv[i][e / 4].x, kf[e + 0], d);
+                    d = fmaf(qv[i][e / 4].y, kf[e + 1], d);
+                    d = fmaf(qv[i][e / 4].z, kf[e + 2], d);
+                    d = fmaf(qv[i][e / 4].w, kf[e + 3], d);
+                }
+                d = row_sum<LPR>(d) * qscale;
                 s[u][i] = valid ? d : -INFINITY;
             }
         }
