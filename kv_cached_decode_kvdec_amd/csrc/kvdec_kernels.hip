@@ -647,7 +647,11 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
 //  loads   K and V rows as whole 128-byte rows (a wave load covers 8 full
 //          rows), staged in LDS per wave: K at a 144-byte row stride, V at 160
 //          (stride choices keep the 16-byte K reads and the V transpose reads
-//          free of bank conflicts).
+//          free of bank conflicts).  Software-pipelined: the next 32 rows are
+//          requested as soon as the current ones are in LDS.  That keeps 32
+//          more VGPRs live through the math, so the kernel asks the compiler
+//          for 4 waves per SIMD (amdgpu_waves_per_eu), the occupancy its
+//          39 KB of LDS allows anyway; it then fits in 128 registers.
 //  scores  S^T = K q^T on v_mfma_f32_16x16x32_bf16: A = K tile (row i, dims
 //          8G..8G+7 and 32+8G.., read back from LDS), B = the group's q
 //          (column i is head i % 4) as bf16 hi + lo parts, so the scores keep
@@ -668,7 +672,8 @@ constexpr int kGqaLdsStride = 160;     // bytes per staged V row (conflict-free 
 constexpr int kGqaKStride = 144;       // bytes per staged K row (conflict-free 16-byte reads)
 
 template <int GROUP, int WAVES, bool PAGED, bool FUSED>
-__global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void attend_gqa_mfma_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
     LensSrc<FUSED> ls, int B, int Hkv, int cap_pad, int row_limit, int T,
     float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
@@ -696,32 +701,55 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
     const int row0 = loc.c * T;
     const int row_end = min(loc.len, row0 + T);
 
-    // B operand of the score MFMA: column i is head i % 4; k-slot 8G+e of
-    // instruction t is dim 32t + 8G + e.
-    bf16x8 qb_hi[2], qb_lo[2];
-    {
-        const float* qp = q + (static_cast<size_t>(loc.b) * Hq + g * GROUP + (i & 3)) * kHeadDim + 8 * G;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const float4 x0 = *reinterpret_cast<const float4*>(qp + 32 * t);
-            const float4 x1 = *reinterpret_cast<const float4*>(qp + 32 * t + 4);
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float xv = xs[e] * qscale;
-                const uint32_t hb = bf16_rne(xv);
-                const uint32_t lb = bf16_rne(xv - __uint_as_float(hb << 16));
-                qb_hi[t][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hb));
-                qb_lo[t][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lb));
-            }
-        }
-    }
-
     __shared__ int sm_pages[PAGED ? kMaxChunkPages : 1];
     stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages);
     const char* Kb = K + 16 * (lane & 7); // + row offset, row = r0 + 8c + (lane >> 3)
     const char* Vb = V + 16 * (lane & 7);
     if constexpr (FUSED) fused_append<RB>(ls, loc.b, g, Hkv, cap_pad, row0, row_end);
+
+    // q loads, then the wave's first 32 rows, both in flight before either is
+    // waited for.  The loop is software-pipelined: once a tile sits in LDS
+    // its registers take the next tile's loads, which overlap the MFMA and
+    // softmax work on the current one.
+    float4 qraw[2][2];
+    {
+        const float* qp = q + (static_cast<size_t>(loc.b) * Hq + g * GROUP + (i & 3)) * kHeadDim + 8 * G;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            qraw[t][0] = *reinterpret_cast<const float4*>(qp + 32 * t);
+            qraw[t][1] = *reinterpret_cast<const float4*>(qp + 32 * t + 4);
+        }
+    }
+    uint4 kw[4], vr[4];
+    auto load_tile = [&](int r0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int r = min(r0 + 8 * c + (lane >> 3), row_end - 1);
+            const size_t off = row_offset<PAGED, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0, r);
+            kw[c] = load16_stream(Kb + off);
+            vr[c] = load16_stream(Vb + off);
+        }
+    };
+    int r0 = row0 + wave * 32;
+    if (r0 < row_end) load_tile(r0);
+
+    // B operand of the score MFMA: column i is head i % 4; k-slot 8G+e of
+    // instruction t is dim 32t + 8G + e.
+    bf16x8 qb_hi[2], qb_lo[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const float4 x0 = qraw[t][0], x1 = qraw[t][1];
+        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float xv = xs[e] * qscale;
+            const uint32_t hb = bf16_rne(xv);
+            const uint32_t lb = bf16_rne(xv - __uint_as_float(hb << 16));
+            qb_hi[t][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hb));
+            qb_lo[t][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lb));
+        }
+    }
+
     char* my_v = sm_stage + wave * kStage;
     char* my_k = my_v + 32 * kGqaLdsStride;
     // transpose-read addresses: lane m = 4e + q of group G reads row 4G + e,
@@ -733,20 +761,16 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int r0 = row0 + wave * 32; r0 < row_end; r0 += WAVES * 32) {
-        uint4 kw[4], vr[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int r = min(r0 + 8 * c + (lane >> 3), row_end - 1);
-            const size_t off = row_offset<PAGED, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0, r);
-            kw[c] = load16_stream(Kb + off);
-            vr[c] = load16_stream(Vb + off);
-        }
+    while (r0 < row_end) {
         // stage K rows r0 .. r0+31, then read the A operand: row 16*tile + i,
         // bytes 16G .. and 64 + 16G ..
 #pragma unroll
         for (int c = 0; c < 4; ++c)
             *reinterpret_cast<uint4*>(my_k + (8 * c + (lane >> 3)) * kGqaKStride + 16 * (lane & 7)) = kw[c];
+        // stage V rows r0 .. r0+31 (row-major) for the transpose reads
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            *reinterpret_cast<uint4*>(my_v + (8 * c + (lane >> 3)) * kGqaLdsStride + 16 * (lane & 7)) = vr[c];
         uint4 kr[2][2];
 #pragma unroll
         for (int tile = 0; tile < 2; ++tile) {
@@ -754,6 +778,8 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
             kr[tile][0] = *reinterpret_cast<const uint4*>(kp);
             kr[tile][1] = *reinterpret_cast<const uint4*>(kp + 64);
         }
+        const int rn = r0 + WAVES * 32;
+        if (rn < row_end) load_tile(rn);
         // scores: lane holds head hl for rows r0 + 16*tile + 4G + rr
         float sc[2][4];
 #pragma unroll
@@ -769,10 +795,6 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
             for (int rr = 0; rr < 4; ++rr)
                 sc[tile][rr] = (r0 + 16 * tile + 4 * G + rr < row_end) ? c[rr] : -INFINITY;
         }
-        // stage V rows r0 .. r0+31 (row-major) for the transpose reads
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            *reinterpret_cast<uint4*>(my_v + (8 * c + (lane >> 3)) * kGqaLdsStride + 16 * (lane & 7)) = vr[c];
 
         // online softmax for head hl over these 32 rows
         float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
@@ -825,6 +847,7 @@ __global__ __launch_bounds__(WAVES * 64) void attend_gqa_mfma_kernel(
             o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb, o[c], 0, 0, 0);
             o[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb, o[c], 0, 0, 0);
         }
+        r0 = rn;
     }
 
     // l: sum over the four G groups (the i & ~3 lanes of a group repeat it)
