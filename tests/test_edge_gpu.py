@@ -1,0 +1,95 @@
+"""Edge sizes of the decode step against the f64 oracle, through the C ABI.
+
+- one very long sequence split into more than a thousand chunks (the merge
+  walks its chunk list in several 64-chunk groups and 16-chunk batches);
+- a batch of 2048 short ragged sequences (the chunk lookup scans the lengths
+  in 32 groups of 64; most sequences fit one chunk, some span two);
+- the fused append at exactly its largest batch (512), where it still runs as
+  one launch;
+- group 8 over a single KV head with a ragged batch, through the fused call.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cached_decode_kvdec_amd import binding as B
+from kv_cached_decode_kvdec_amd import inputs as gen
+from kv_cached_decode_kvdec_amd.cache import KVCache, to_device, to_host_bits
+
+from helpers import assert_attention_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _rows(rng, shape, dtype):
+    x = rng.standard_normal(shape, dtype=np.float32)
+    return x if dtype == "f32" else gen.f32_to_bf16_bits(x)
+
+
+def test_one_sequence_over_a_thousand_chunks():
+    rng = np.random.default_rng(81)
+    L, Hkv, Hq = 100_000, 1, 8
+    cap = gen.padded_rows(L)
+    K = _rows(rng, (1, Hkv, cap, 64), "bf16")
+    V = _rows(rng, (1, Hkv, cap, 64), "bf16")
+    q = rng.standard_normal((1, Hq, 64), dtype=np.float32)
+    _log(f"long sequence: {L} rows, chunk 64 -> {-(-L // 64)} chunks")
+    c = KVCache(1, Hkv, L, "bf16", lens=[L], k=to_device(K), v=to_device(V))
+    ref = oracle.attend(q, K, V, np.array([L], np.int32))
+    for T in (64, 4096, 0):
+        out = c.attend(to_device(q), chunk_rows=T)
+        torch.cuda.synchronize()
+        assert_attention_close(out.cpu().numpy(), ref, "bf16", f"L={L} T={T}")
+
+
+def test_batch_of_2048_ragged_sequences():
+    rng = np.random.default_rng(82)
+    Bsz, Hkv, Hq = 2048, 2, 4
+    lens = rng.integers(0, 130, size=Bsz).astype(np.int32)
+    lens[::97] = 0
+    cap = gen.padded_rows(int(lens.max()) + 1)
+    K = _rows(rng, (Bsz, Hkv, cap, 64), "f32")
+    V = _rows(rng, (Bsz, Hkv, cap, 64), "f32")
+    q = rng.standard_normal((Bsz, Hq, 64), dtype=np.float32)
+    _log(f"batch {Bsz}: lengths 0..{lens.max()}")
+    c = KVCache(Bsz, Hkv, cap, "f32", lens=lens, k=to_device(K), v=to_device(V))
+    ref = oracle.attend(q, K, V, lens)
+    for T in (64, 128, 0):
+        out = c.attend(to_device(q), chunk_rows=T)
+        torch.cuda.synchronize()
+        assert_attention_close(out.cpu().numpy(), ref, "f32", f"B={Bsz} T={T}")
+
+
+@pytest.mark.parametrize("Bsz", [B.KVDEC_MAX_FUSED_BATCH, 1])
+def test_fused_append_at_its_batch_limits(Bsz):
+    rng = np.random.default_rng(83 + Bsz)
+    Hkv, Hq = 1, 8                                   # group 8 on the VALU kernel
+    lens = rng.integers(0, 200, size=Bsz).astype(np.int32)
+    cap = gen.padded_rows(int(lens.max()) + 2)
+    K = _rows(rng, (Bsz, Hkv, cap, 64), "bf16")
+    V = _rows(rng, (Bsz, Hkv, cap, 64), "bf16")
+    for b in range(Bsz):                             # canaries past each length
+        K[b, :, lens[b]:] = 0x7FC1
+        V[b, :, lens[b]:] = 0x7FC1
+    _log(f"fused append at batch {Bsz}")
+    c = KVCache(Bsz, Hkv, cap, "bf16", lens=lens, k=to_device(K), v=to_device(V))
+    Kh, Vh, ln = K.copy(), V.copy(), lens.copy()
+    for s in range(2):
+        kn = _rows(rng, (Bsz, Hkv, 64), "bf16")
+        vn = _rows(rng, (Bsz, Hkv, 64), "bf16")
+        q = rng.standard_normal((Bsz, Hq, 64), dtype=np.float32)
+        out = c.append_attend(to_device(kn), to_device(vn), to_device(q), chunk_rows=64 * (s + 1))
+        torch.cuda.synchronize()
+        ln = oracle.append(Kh, Vh, kn, vn, ln)
+        ref = oracle.attend(q, Kh, Vh, ln)
+        assert_attention_close(out.cpu().numpy(), ref, "bf16", f"fused B={Bsz} step {s}")
+    assert to_host_bits(c.k).tobytes() == Kh.tobytes()
+    assert to_host_bits(c.v).tobytes() == Vh.tobytes()
+    assert c.lens() == ln.tolist() and c.lens_dev.cpu().tolist() == ln.tolist()
