@@ -21,7 +21,10 @@ kernel's average launch duration (one kernel per attend call, plus the merge
 launch when a sequence spans several chunks) and its achieved algorithmic
 bandwidth; the fused call's bytes include the store of the new K/V row.
 (Event markers cost the stream a few microseconds each, so the step rate is
-not taken from the pass that carries them.)
+not taken from the pass that carries them.)  "cold" figures read a 1 GiB
+buffer before every step, which evicts the 256 MB Infinity Cache, and take
+the step time as the difference between a pass of flush + step and a pass of
+the flush alone.
 """
 import argparse
 import json
@@ -38,7 +41,7 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attention steps/sec + effective KV HBM GB/s (% of peak), batch 64"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
-FLUSH_BYTES = 1 << 30           # > 256 MB Infinity Cache
+FLUSH_BYTES = 1 << 30           # read before each cold step; > 256 MB Infinity Cache
 
 
 def log(*a):
@@ -196,21 +199,34 @@ class Bench:
         res["pct_of_hbm_peak"] = 100.0 * res["effective_gbps"] / HBM_PEAK_GBPS
         res["attend_frac"] = res["attend_gbps"] / HBM_PEAK_GBPS
         if cold_steps:
+            # cold: before every step, a read of a 1 GiB buffer evicts the
+            # 256 MB Infinity Cache (a read, so no dirty lines are left to be
+            # written back during the step).  The step time is the difference
+            # of two marker-free passes: flush + step, and flush alone.
             flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(cold_steps)]
-            for i in range(cold_steps):
-                flush.zero_()
-                ev[i][0].record()
-                self.step(i)
-                ev[i][1].record()
+            flush.fill_(1.0)
+            sink = torch.empty((), dtype=torch.float32, device="cuda")
+            torch.sum(flush, dim=0, out=sink)
             torch.cuda.synchronize()
-            ms = [a.elapsed_time(b) for a, b in ev]
-            cb = sum(self.step_bytes[i % self.S] for i in range(cold_steps))
-            res["cold_ms_per_step"] = float(np.mean(ms))
-            res["cold_gbps"] = cb / (float(np.sum(ms)) * 1e-3) / 1e9
+
+            def timed(with_step):
+                t = time.perf_counter()
+                for i in range(cold_steps):
+                    torch.sum(flush, dim=0, out=sink)
+                    if with_step:
+                        self.step(i)
+                torch.cuda.synchronize()
+                return time.perf_counter() - t
+
+            timed(True)
+            t_flush = min(timed(False), timed(False))
+            t_both = min(timed(True), timed(True))
+            cold_s = max(t_both - t_flush, 1e-9) / cold_steps
+            cb = sum(self.step_bytes[i % self.S] for i in range(cold_steps)) / cold_steps
+            res["cold_ms_per_step"] = cold_s * 1e3
+            res["cold_gbps"] = cb / cold_s / 1e9
             res["cold_pct_of_hbm_peak"] = 100.0 * res["cold_gbps"] / HBM_PEAK_GBPS
-            del flush
+            del flush, sink
         return res
 
     def run_graph(self, steps):
