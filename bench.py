@@ -21,7 +21,7 @@ kernel's average launch duration (one kernel per attend call, plus the merge
 launch when a sequence spans several chunks) and its achieved algorithmic
 bandwidth; the fused call's bytes include the store of the new K/V row.
 (Event markers cost the stream a few microseconds each, so the step rate is
-not taken from the pass that carries them.)  "cold" figures read a 1 GiB
+not taken from the pass that carries them.)  "cold" figures write a 1 GiB
 buffer before every step, which evicts the 256 MB Infinity Cache, and take
 the step time as the difference between a pass of flush + step and a pass of
 the flush alone.
@@ -41,7 +41,7 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attention steps/sec + effective KV HBM GB/s (% of peak), batch 64"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
-FLUSH_BYTES = 1 << 30           # read before each cold step; > 256 MB Infinity Cache
+FLUSH_BYTES = 1 << 30           # written before each cold step; > 256 MB Infinity Cache
 
 
 def log(*a):
@@ -199,20 +199,19 @@ class Bench:
         res["pct_of_hbm_peak"] = 100.0 * res["effective_gbps"] / HBM_PEAK_GBPS
         res["attend_frac"] = res["attend_gbps"] / HBM_PEAK_GBPS
         if cold_steps:
-            # cold: before every step, a read of a 1 GiB buffer evicts the
-            # 256 MB Infinity Cache (a read, so no dirty lines are left to be
-            # written back during the step).  The step time is the difference
-            # of two marker-free passes: flush + step, and flush alone.
+            # cold: before every step, writing a 1 GiB buffer evicts the
+            # 256 MB Infinity Cache.  The step time is the difference of two
+            # marker-free passes, flush + step and flush alone; both passes
+            # write back the same dirty lines in total, so the difference is
+            # the steps' own time.
             flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
-            flush.fill_(1.0)
-            sink = torch.empty((), dtype=torch.float32, device="cuda")
-            torch.sum(flush, dim=0, out=sink)
+            flush.zero_()
             torch.cuda.synchronize()
 
             def timed(with_step):
                 t = time.perf_counter()
                 for i in range(cold_steps):
-                    torch.sum(flush, dim=0, out=sink)
+                    flush.zero_()
                     if with_step:
                         self.step(i)
                 torch.cuda.synchronize()
@@ -226,7 +225,7 @@ class Bench:
             res["cold_ms_per_step"] = cold_s * 1e3
             res["cold_gbps"] = cb / cold_s / 1e9
             res["cold_pct_of_hbm_peak"] = 100.0 * res["cold_gbps"] / HBM_PEAK_GBPS
-            del flush, sink
+            del flush
         return res
 
     def run_graph(self, steps):
