@@ -495,8 +495,14 @@ __global__ __launch_bounds__(256) void seed_kernel(char* __restrict__ K, char* _
 // bytes (EPL dims) of a row, `sub` the row slot (RPI slots per load).  One
 // wave iteration loads U rows per slot: rows r0 + u * RPI + sub.
 // WAVES waves interleave over the chunk in steps of U * RPI rows.
+// Waves per SIMD the VALU kernel asks the compiler to fit (1: no request):
+// f32 groups 2 and 6 land one or two VGPRs past an occupancy step without it.
+template <int ESZ, int GROUP>
+constexpr int valu_min_waves() { return ESZ == 4 && GROUP == 2 ? 7 : ESZ == 4 && GROUP == 6 ? 4 : 1; }
+
 template <int ESZ, int GROUP, int WAVES, int U, bool PAGED, bool FUSED>
-__global__ __launch_bounds__(WAVES * 64) void attend_kernel(
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(valu_min_waves<ESZ, GROUP>())))
+void attend_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
     LensSrc<FUSED> ls, int B, int Hkv, int cap_pad, int row_limit, int T,
     float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
@@ -641,7 +647,8 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// attend, grouped-query heads on MFMA (bf16 K/V, 4 query heads per KV head).
+// attend, grouped-query heads on MFMA (bf16 K/V, GROUP = 2..8 query heads per
+// KV head; the 16 MFMA columns / rows hold head (index mod GROUP)).
 //
 // Per wave iteration: 32 KV rows = two 16-row tiles.  Lane l = 16G + i.
 //  loads   K and V rows as whole 128-byte rows (a wave load covers 8 full
@@ -654,16 +661,16 @@ __global__ __launch_bounds__(WAVES * 64) void attend_kernel(
 //          39 KB of LDS allows anyway; it then fits in 128 registers.
 //  scores  S^T = K q^T on v_mfma_f32_16x16x32_bf16: A = K tile (row i, dims
 //          8G..8G+7 and 32+8G.., read back from LDS), B = the group's q
-//          (column i is head i % 4) as bf16 hi + lo parts, so the scores keep
-//          ~f32 accuracy.  Lane l receives head l % 4 for rows 4G .. 4G+3 of
-//          each tile.
+//          (column i is head i % GROUP) as bf16 hi + lo parts, so the scores
+//          keep ~f32 accuracy.  Lane l receives head (l % 16) % GROUP for rows
+//          4G .. 4G+3 of each tile.
 //  softmax online per 32 rows; tile max per head across the four G groups.
-//  P.V     O = P V on the same MFMA: A = P (row m of A is head m % 4, k-slot
+//  P.V     O = P V on the same MFMA: A = P (row m of A is head m % GROUP, k-slot
 //          8G+t <-> tile t/4, row 4G + t%4 -- exactly the lane's own eight
 //          weights, in bf16 hi + lo), B = V from LDS with the gfx950 transpose
 //          read ds_read_b64_tr_b16 (V rows staged row-major, 160-byte row
 //          stride), four 16-dim column blocks.  The accumulator is 16 floats
-//          per lane: head r, dim 16c + i.
+//          per lane: output row 4G + r (head (4G + r) % GROUP), dim 16c + i.
 // ---------------------------------------------------------------------------
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -679,13 +686,13 @@ void attend_gqa_mfma_kernel(
     float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
     PageMap pm)
 {
-    static_assert(GROUP == 4, "MFMA path takes groups of 4 query heads");
+    static_assert(GROUP >= 2 && GROUP <= 8, "MFMA path takes 2..8 query heads per KV head");
     constexpr int RB = 128;                // bf16 row bytes
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int i = lane & 15;
     const int G = lane >> 4;
-    const int hl = lane & 3;               // head whose scores this lane holds
+    const int hl = i % GROUP;              // head whose scores this lane holds
     const int g = blockIdx.y;
     const int Hq = Hkv * GROUP;
 
@@ -713,7 +720,7 @@ void attend_gqa_mfma_kernel(
     // softmax work on the current one.
     float4 qraw[2][2];
     {
-        const float* qp = q + (static_cast<size_t>(loc.b) * Hq + g * GROUP + (i & 3)) * kHeadDim + 8 * G;
+        const float* qp = q + (static_cast<size_t>(loc.b) * Hq + g * GROUP + hl) * kHeadDim + 8 * G;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             qraw[t][0] = *reinterpret_cast<const float4*>(qp + 32 * t);
@@ -824,11 +831,18 @@ void attend_gqa_mfma_kernel(
             pa_hi[t] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hb));
             pa_lo[t] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lb));
         }
-        // rescale the accumulator: output row 4G + rr is head rr
-        const float al[4] = {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0)),
-                             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1)),
-                             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2)),
-                             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3))};
+        // rescale the accumulator: output row 4G + rr is head (4G + rr) % GROUP,
+        // whose alpha lane (4G + rr) % GROUP holds (its column is that head)
+        float ah[GROUP];                   // alpha of every head, wave-uniform
+#pragma unroll
+        for (int h = 0; h < GROUP; ++h)
+            ah[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
+        float al[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            al[rr] = G == 0 ? ah[rr % GROUP]
+                   : G == 1 ? ah[(4 + rr) % GROUP]
+                   : G == 2 ? ah[(8 + rr) % GROUP] : ah[(12 + rr) % GROUP];
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -850,7 +864,7 @@ void attend_gqa_mfma_kernel(
         r0 = rn;
     }
 
-    // l: sum over the four G groups (the i & ~3 lanes of a group repeat it)
+    // l: sum over the four G groups (lanes whose columns repeat a head repeat it)
     lpart += __shfl_xor(lpart, 16);
     lpart += __shfl_xor(lpart, 32);
 
@@ -859,11 +873,13 @@ void attend_gqa_mfma_kernel(
     auto& sm_o = *reinterpret_cast<float (*)[WAVES][GROUP][kHeadDim]>(sm_stage);
     __shared__ float sm_m[WAVES][GROUP];
     __shared__ float sm_l[WAVES][GROUP];
-    if (G == 0) {
+    // output rows 0 .. GROUP-1 are the heads; later rows repeat them
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+    for (int rr = 0; rr < 4; ++rr) {
+        if (4 * G + rr < GROUP) {
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) sm_o[wave][rr][16 * c + i] = o[c][rr];
+            for (int c = 0; c < 4; ++c) sm_o[wave][4 * G + rr][16 * c + i] = o[c][rr];
+        }
     }
     if (lane < GROUP) {
         sm_m[wave][lane] = m;
@@ -1107,8 +1123,8 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
         ls.lens = a.lens;
     }
     const dim3 grid(static_cast<unsigned>(a.n_chunks), a.n_kv_heads), block(kWaves * 64);
-    if constexpr (ESZ == 2 && GROUP == 4)
-        hipLaunchKernelGGL((attend_gqa_mfma_kernel<4, kWaves, PAGED, FUSED>), grid, block, 0, s,
+    if constexpr (ESZ == 2 && GROUP >= 2)
+        hipLaunchKernelGGL((attend_gqa_mfma_kernel<GROUP, kWaves, PAGED, FUSED>), grid, block, 0, s,
                            a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v), ls,
                            a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows, a.qscale,
                            a.out, po, pml, pm);
@@ -1150,19 +1166,30 @@ template <int ESZ>
 const void* attend_kernel_ptr(int group, int* block)
 {
     *block = kWaves * 64;
-    if constexpr (ESZ == 2)
-        if (group == 4)
-            return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<4, kWaves, false, false>);
-    switch (group) {
-        case 1: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 1, kWaves, kUnroll, false, false>);
-        case 2: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 2, kWaves, kUnroll, false, false>);
-        case 3: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 3, kWaves, kUnroll, false, false>);
-        case 4: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 4, kWaves, kUnroll, false, false>);
-        case 5: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 5, kWaves, kUnroll, false, false>);
-        case 6: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 6, kWaves, kUnroll, false, false>);
-        case 7: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 7, kWaves, kUnroll, false, false>);
-        case 8: return reinterpret_cast<const void*>(&attend_kernel<ESZ, 8, kWaves, kUnroll, false, false>);
-        default: return nullptr;
+    if constexpr (ESZ == 2) {
+        switch (group) {
+            case 1: return reinterpret_cast<const void*>(&attend_kernel<2, 1, kWaves, kUnroll, false, false>);
+            case 2: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<2, kWaves, false, false>);
+            case 3: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<3, kWaves, false, false>);
+            case 4: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<4, kWaves, false, false>);
+            case 5: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<5, kWaves, false, false>);
+            case 6: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<6, kWaves, false, false>);
+            case 7: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<7, kWaves, false, false>);
+            case 8: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<8, kWaves, false, false>);
+            default: return nullptr;
+        }
+    } else {
+        switch (group) {
+            case 1: return reinterpret_cast<const void*>(&attend_kernel<4, 1, kWaves, kUnroll, false, false>);
+            case 2: return reinterpret_cast<const void*>(&attend_kernel<4, 2, kWaves, kUnroll, false, false>);
+            case 3: return reinterpret_cast<const void*>(&attend_kernel<4, 3, kWaves, kUnroll, false, false>);
+            case 4: return reinterpret_cast<const void*>(&attend_kernel<4, 4, kWaves, kUnroll, false, false>);
+            case 5: return reinterpret_cast<const void*>(&attend_kernel<4, 5, kWaves, kUnroll, false, false>);
+            case 6: return reinterpret_cast<const void*>(&attend_kernel<4, 6, kWaves, kUnroll, false, false>);
+            case 7: return reinterpret_cast<const void*>(&attend_kernel<4, 7, kWaves, kUnroll, false, false>);
+            case 8: return reinterpret_cast<const void*>(&attend_kernel<4, 8, kWaves, kUnroll, false, false>);
+            default: return nullptr;
+        }
     }
 }
 

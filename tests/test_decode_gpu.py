@@ -95,7 +95,8 @@ def test_small_parity_every_workload(name, chunk_rows):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("Hq,Hkv", [(2, 1), (6, 2), (12, 4), (16, 4), (8, 1), (14, 2), (7, 7)])
+@pytest.mark.parametrize("Hq,Hkv", [(2, 1), (6, 2), (12, 4), (16, 4), (10, 2), (12, 2), (8, 1),
+                                    (14, 2), (7, 7)])
 def test_gqa_groups(dtype, Hq, Hkv):
     wl = gen.Workload("g", 5, Hq, Hkv, dtype, "const:1", 1, False, seed=31)
     lens = np.array([0, 1, 130, 700, 2000], np.int32)
