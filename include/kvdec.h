@@ -207,13 +207,19 @@ KVDEC_API int32_t kvdec_attend_self(const kvdec_cache* cache, const float* q, in
 /*
  * kvdec_append followed by kvdec_attend_self, as one call: the decode step
  * of one layer's self-attention.  Same arguments and errors as the two
- * calls (everything is checked before anything is enqueued).  For batches
- * up to KVDEC_MAX_FUSED_BATCH outside replay mode it is a single attend
- * launch (plus the merge launch when needed): each workgroup reads the new
- * row straight from k_new / v_new, the one whose chunk holds it also stores
- * it in the cache, and the pre-append lengths come from the host mirror --
- * the append-plus-attend call of [WA-CUDA] `flash_attention_cached`.
- * Otherwise it enqueues the two calls.
+ * calls (everything is checked before anything is enqueued); results, cache
+ * bytes and lengths are bitwise those of the two calls.  The append is fused
+ * into the attend launch -- the append-plus-attend cached call of [WA-CUDA]
+ * `flash_attention_cached`: each workgroup reads the rows it attends, and the
+ * one whose chunk holds the new slot first stores the new K/V row there.
+ *   - batch <= KVDEC_MAX_FUSED_BATCH outside replay mode: one launch (plus
+ *     the merge launch when a sequence spans several chunks); the pre-append
+ *     lengths go by value from the host mirror and the launch bumps them.
+ *   - otherwise (replay mode, larger batches): the attend launch reads the
+ *     lengths from the device and the merge launch, which then always runs,
+ *     bumps them; two launches, capturable in a graph like every call in
+ *     replay mode.  As with kvdec_append in replay mode, a full linear
+ *     cache keeps its length and gets no row.
  */
 KVDEC_API int32_t kvdec_append_attend(kvdec_cache* cache, const void* k_new, const void* v_new,
                                       const float* q, int32_t n_q_heads, float scale,

@@ -135,6 +135,7 @@ struct AttendView {
     int32_t table_stride = 0, pshift = 0;
     // append fused into the attend launch
     const int32_t* fused_lens = nullptr;   // pre-append lengths (host mirror)
+    bool fused_device = false;             // append fused, lengths from the device
     const void* k_new = nullptr;
     const void* v_new = nullptr;
     int32_t* lens_out = nullptr;
@@ -158,7 +159,7 @@ int32_t check_attend(const AttendView& v, const float* q, int32_t n_q_heads, flo
                             chunk_rows % 64 != 0))
         return fail(KVDEC_E_INVALID, "chunk_rows %d must be 0 or a multiple of 64 in [%d, %d]",
                     chunk_rows, KVDEC_MIN_CHUNK, KVDEC_MAX_CHUNK);
-    const kvdec::PartialLayout part = kvdec::partial_layout(v.max_chunks, n_q_heads);
+    const kvdec::PartialLayout part = kvdec::partial_layout(v.max_chunks, n_q_heads, v.batch);
     if (!aligned16(ws) || ws_bytes < part.bytes)
         return fail(KVDEC_E_WORKSPACE, "workspace needs %zu bytes at a 16-byte aligned address, got %zu",
                     part.bytes, ws_bytes);
@@ -171,7 +172,7 @@ int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, floa
     const int32_t rc = check_attend(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes);
     if (rc) return rc;
     const int32_t group = n_q_heads / v.n_kv_heads;
-    const kvdec::PartialLayout part = kvdec::partial_layout(v.max_chunks, n_q_heads);
+    const kvdec::PartialLayout part = kvdec::partial_layout(v.max_chunks, n_q_heads, v.batch);
 
     kvdec::AttendArgs a;
     a.q = q;
@@ -207,6 +208,8 @@ int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, floa
     a.table_stride = v.table_stride;
     a.pshift = v.pshift;
     a.fused_lens = v.fused_lens;
+    a.fused_device = v.fused_device;
+    if (v.fused_device) a.need_merge = true;   // the merge launch bumps the lengths
     a.k_new = v.k_new;
     a.v_new = v.v_new;
     a.lens_out = v.lens_out;
@@ -393,7 +396,7 @@ int32_t kvdec_append_rope(kvdec_cache* c, const void* k_new, const void* v_new, 
 size_t kvdec_workspace_bytes(const kvdec_cache* c, int32_t n_q_heads)
 {
     if (!c || n_q_heads <= 0) return 0;
-    return kvdec::partial_layout(max_chunks(c), n_q_heads).bytes;
+    return kvdec::partial_layout(max_chunks(c), n_q_heads, c->d.batch).bytes;
 }
 
 int32_t kvdec_attend_self(const kvdec_cache* c, const float* q, int32_t n_q_heads, float scale,
@@ -624,7 +627,7 @@ size_t kvdec_paged_workspace_bytes(const kvdec_paged* p, int32_t n_q_heads)
     if (!p || n_q_heads <= 0) return 0;
     const int64_t cap = static_cast<int64_t>(p->d.max_pages_per_seq) * p->d.page_rows;
     return kvdec::partial_layout(p->d.batch * ((cap + KVDEC_MIN_CHUNK - 1) / KVDEC_MIN_CHUNK),
-                                 n_q_heads).bytes;
+                                 n_q_heads, p->d.batch).bytes;
 }
 
 int32_t kvdec_paged_attend(const kvdec_paged* p, const float* q, int32_t n_q_heads, float scale,
@@ -661,19 +664,15 @@ int32_t kvdec_append_attend(kvdec_cache* c, const void* k_new, const void* v_new
     AttendView v = view_of(c);
     rc = check_attend(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes);
     if (rc) return rc;
-    if (c->d.batch > KVDEC_MAX_FUSED_BATCH || c->replay_chunk > 0) {
-        // separate launches: the arguments are already checked, so the
-        // append cannot leave a half-done call behind
-        rc = kvdec_append(c, k_new, v_new, stream);
-        if (rc) return rc;
-        return kvdec_attend_self(c, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
-    }
-    // one launch: lengths from the host mirror, rows attended after the append
+    // rows attended after the append
     for (auto& r : v.rows) {
         const int64_t n = static_cast<int64_t>(r) + 1;
         r = static_cast<int32_t>(c->d.window > 0 && n > c->d.window ? c->d.window : n);
     }
-    v.fused_lens = c->lens.data();
+    if (c->d.batch > KVDEC_MAX_FUSED_BATCH || c->replay_chunk > 0)
+        v.fused_device = true;         // attend + merge launch; the lengths stay on the device
+    else
+        v.fused_lens = c->lens.data(); // one launch; pre-append lengths by value
     v.k_new = k_new;
     v.v_new = v_new;
     v.lens_out = c->d.lens;

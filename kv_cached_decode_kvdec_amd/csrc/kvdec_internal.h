@@ -20,10 +20,11 @@ struct LensBlock {
 struct PartialLayout {
     size_t o_offset;        // float [slots][64]
     size_t ml_offset;       // float2 [slots]
+    size_t snap_offset;     // int32 [batch]: pre-append lengths (device-fused append)
     size_t bytes;
 };
 
-PartialLayout partial_layout(int64_t max_chunks, int32_t n_q_heads);
+PartialLayout partial_layout(int64_t max_chunks, int32_t n_q_heads, int32_t batch);
 
 struct AttendArgs {
     const float* q;
@@ -49,6 +50,7 @@ struct AttendArgs {
     // append fused into the launch (fused_lens != nullptr): pre-append
     // lengths (host), new rows, the device lengths to bump, ring window
     const int32_t* fused_lens = nullptr;
+    bool fused_device = false;    // append fused, lengths from the device (merge bumps)
     const void* k_new = nullptr;
     const void* v_new = nullptr;
     int32_t* lens_out = nullptr;

@@ -130,41 +130,70 @@ struct Located {
     int b, c, len, nch;
 };
 
-// Where an attend launch gets the per-sequence lengths from.  Plain launch:
-// the device array, rows = lens[b].  Fused append: the pre-append lengths by
-// value (host mirror), rows = len + 1, plus the new rows and the cache to
-// store them in (the launch itself reads no device length).
-template <bool FUSED>
+// Where an attend launch gets the per-sequence lengths from (LM, the length
+// mode):
+//  kLensDevice       the device array, rows = lens[b];
+//  kLensHostFused    append fused into the launch, the pre-append lengths by
+//                    value from the host mirror (the launch reads no device
+//                    length), rows = len + 1; the launch bumps the lengths;
+//  kLensDeviceFused  append fused into the launch, the pre-append lengths
+//                    from the device array (replay mode, any batch), rows =
+//                    len + 1; the attend launch snapshots them into the
+//                    workspace and the merge launch, which always follows,
+//                    reads the snapshot and bumps the lengths (no launch both
+//                    reads and writes them).
+constexpr int kLensDevice = 0;
+constexpr int kLensHostFused = 1;
+constexpr int kLensDeviceFused = 2;
+
+template <int LM>
 struct LensSrc;
 
 template <>
-struct LensSrc<false> {
+struct LensSrc<kLensDevice> {
     const int32_t* lens;
     static constexpr int kPlus = 0;
     __device__ __forceinline__ int get(int b) const { return lens[b]; }
+    __device__ __forceinline__ int merge_get(int b) const { return lens[b]; }
 };
 
-template <>
-struct LensSrc<true> {
-    int32_t v[kMaxFusedBatch];
+// the new rows and the cache they are stored into (fused modes)
+struct FusedRows {
     const char* k_new;      // [B][Hkv][64] elements
     const char* v_new;
     char* K;                // contiguous cache, written at the new row's slot
     char* V;
     int32_t* lens_out;      // device lengths, bumped by one per sequence
     int window;             // ring window, 0 for a linear cache
-    static constexpr int kPlus = 1;
-    __device__ __forceinline__ int get(int b) const { return v[b]; }
 };
 
-template <bool FUSED>
-__device__ __forceinline__ bool locate(const LensSrc<FUSED>& ls, int B, int T, int cap, int blk,
+template <>
+struct LensSrc<kLensHostFused> {
+    int32_t v[kMaxFusedBatch];
+    FusedRows f;
+    static constexpr int kPlus = 1;
+    __device__ __forceinline__ int get(int b) const { return v[b]; }
+    __device__ __forceinline__ int merge_get(int b) const { return v[b]; }
+};
+
+template <>
+struct LensSrc<kLensDeviceFused> {
+    const int32_t* lens;    // pre-append lengths (read by the attend launch only)
+    int32_t* snap;          // workspace copy of them (read by the merge launch)
+    FusedRows f;
+    static constexpr int kPlus = 1;
+    __device__ __forceinline__ int get(int b) const { return lens[b]; }
+    __device__ __forceinline__ int merge_get(int b) const { return snap[b]; }
+};
+
+template <int LM>
+__device__ __forceinline__ bool locate(const LensSrc<LM>& ls, int B, int T, int cap, int blk,
                                        int lane, Located& r)
 {
     int base = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
         const int bi = b0 + lane;
-        const int ln = bi < B ? min(max(ls.get(bi) + LensSrc<FUSED>::kPlus, 0), cap) : 0;
+        const int ln = bi < B ? min(max(ls.get(bi) + LensSrc<LM>::kPlus, 0), cap) : 0;
         const int cnt = bi < B ? max(1, (ln + T - 1) / T) : 0;
         int incl = cnt;
 #pragma unroll
@@ -187,30 +216,38 @@ __device__ __forceinline__ bool locate(const LensSrc<FUSED>& ls, int B, int T, i
     return false;
 }
 
-// Fused append, inside an attend workgroup of (sequence b, KV head g) whose
-// rows are [row0, row_end): the workgroup whose rows hold the new token's
-// slot stores the new K/V row of head g there (the one of head 0 also bumps
-// the length), then waits at a workgroup barrier, which makes those stores
-// visible to all its waves before any of them reads the slot.  No other
-// workgroup reads that slot, so the launch needs no wider synchronisation.
-template <int RB>
-__device__ __forceinline__ void fused_append(const LensSrc<true>& ls, int b, int g, int Hkv,
-                                            int cap_pad, int row0, int row_end)
+// Fused append, inside an attend workgroup of (sequence b, KV head g, chunk c)
+// whose rows are [row0, row_end): the workgroup whose rows hold the new
+// token's slot stores the new K/V row of head g there, then waits at a
+// workgroup barrier, which makes those stores visible to all its waves
+// before any of them reads the slot.  No other workgroup reads that slot, so
+// the launch needs no wider synchronisation.  Host-fused: the slot's head-0
+// workgroup also bumps the length.  Device-fused: workgroup (c 0, head 0)
+// snapshots the pre-append length for the merge launch, which bumps it.  (A
+// full linear cache puts the slot at row `capacity`, past every chunk: no
+// store, and the merge leaves the length as it is.)
+template <int RB, int LM>
+__device__ __forceinline__ void fused_append(const LensSrc<LM>& ls, const Located& loc, int g,
+                                            int Hkv, int cap_pad, int row0, int row_end)
 {
-    const int len0 = ls.v[b];
-    const int slot = ls.window > 0 ? len0 % ls.window : len0;
+    const int b = loc.b;
+    const int len0 = ls.get(b);
+    const int slot = ls.f.window > 0 ? len0 % ls.f.window : len0;
     if (row0 <= slot && slot < row_end) {
         const size_t hg = static_cast<size_t>(b) * Hkv + g;
         constexpr int VPR = RB / 16;
         for (int t = threadIdx.x; t < 2 * VPR; t += blockDim.x) {
             const bool isv = t >= VPR;
             const int w = isv ? t - VPR : t;
-            const uint4 x = reinterpret_cast<const uint4*>((isv ? ls.v_new : ls.k_new) + hg * RB)[w];
-            reinterpret_cast<uint4*>((isv ? ls.V : ls.K) + (hg * cap_pad + slot) * RB)[w] = x;
+            const uint4 x = reinterpret_cast<const uint4*>((isv ? ls.f.v_new : ls.f.k_new) + hg * RB)[w];
+            reinterpret_cast<uint4*>((isv ? ls.f.V : ls.f.K) + (hg * cap_pad + slot) * RB)[w] = x;
         }
-        if (g == 0 && threadIdx.x == 0) ls.lens_out[b] = len0 + 1;
+        if constexpr (LM == kLensHostFused)
+            if (g == 0 && threadIdx.x == 0) ls.f.lens_out[b] = len0 + 1;
         __syncthreads();
     }
+    if constexpr (LM == kLensDeviceFused)
+        if (loc.c == 0 && g == 0 && threadIdx.x == 0) ls.snap[b] = len0;
 }
 
 // Combine the WAVES per-wave states of a workgroup (staged in LDS) and
@@ -500,11 +537,11 @@ __global__ __launch_bounds__(256) void seed_kernel(char* __restrict__ K, char* _
 template <int ESZ, int GROUP>
 constexpr int valu_min_waves() { return ESZ == 4 && GROUP == 2 ? 7 : ESZ == 4 && GROUP == 6 ? 4 : 1; }
 
-template <int ESZ, int GROUP, int WAVES, int U, bool PAGED, bool FUSED>
+template <int ESZ, int GROUP, int WAVES, int U, bool PAGED, int LM>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(valu_min_waves<ESZ, GROUP>())))
 void attend_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
-    LensSrc<FUSED> ls, int B, int Hkv, int cap_pad, int row_limit, int T,
+    LensSrc<LM> ls, int B, int Hkv, int cap_pad, int row_limit, int T,
     float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
     PageMap pm)
 {
@@ -518,7 +555,7 @@ void attend_kernel(
     const int Hq = Hkv * GROUP;
 
     Located loc;
-    if (!locate<FUSED>(ls, B, T, row_limit, blockIdx.x, lane, loc)) return;
+    if (!locate<LM>(ls, B, T, row_limit, blockIdx.x, lane, loc)) return;
     const int row0 = loc.c * T;
     const int row_end = min(loc.len, row0 + T);
 
@@ -526,7 +563,7 @@ void attend_kernel(
     stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages);
     const char* Kb = K + part * 16;
     const char* Vb = V + part * 16;
-    if constexpr (FUSED) fused_append<RB>(ls, loc.b, g, Hkv, cap_pad, row0, row_end);
+    if constexpr (LM != kLensDevice) fused_append<RB>(ls, loc, g, Hkv, cap_pad, row0, row_end);
 
     // q for the GROUP heads sharing KV head g, this lane's dims.  It is not
     // waited for before the loop: the first rows' loads are issued first and
@@ -678,11 +715,11 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 constexpr int kGqaLdsStride = 160;     // bytes per staged V row (conflict-free tr16 reads)
 constexpr int kGqaKStride = 144;       // bytes per staged K row (conflict-free 16-byte reads)
 
-template <int GROUP, int WAVES, bool PAGED, bool FUSED>
+template <int GROUP, int WAVES, bool PAGED, int LM>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void attend_gqa_mfma_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
-    LensSrc<FUSED> ls, int B, int Hkv, int cap_pad, int row_limit, int T,
+    LensSrc<LM> ls, int B, int Hkv, int cap_pad, int row_limit, int T,
     float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
     PageMap pm)
 {
@@ -704,7 +741,7 @@ void attend_gqa_mfma_kernel(
     __shared__ __attribute__((aligned(16))) char sm_stage[WAVES * kStage];
 
     Located loc;
-    if (!locate<FUSED>(ls, B, T, row_limit, blockIdx.x, lane, loc)) return;
+    if (!locate<LM>(ls, B, T, row_limit, blockIdx.x, lane, loc)) return;
     const int row0 = loc.c * T;
     const int row_end = min(loc.len, row0 + T);
 
@@ -712,7 +749,7 @@ void attend_gqa_mfma_kernel(
     stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages);
     const char* Kb = K + 16 * (lane & 7); // + row offset, row = r0 + 8c + (lane >> 3)
     const char* Vb = V + 16 * (lane & 7);
-    if constexpr (FUSED) fused_append<RB>(ls, loc.b, g, Hkv, cap_pad, row0, row_end);
+    if constexpr (LM != kLensDevice) fused_append<RB>(ls, loc, g, Hkv, cap_pad, row0, row_end);
 
     // q loads, then the wave's first 32 rows, both in flight before either is
     // waited for.  The loop is software-pipelined: once a tile sits in LDS
@@ -896,14 +933,14 @@ void attend_gqa_mfma_kernel(
 // wave), so the loads are grouped to keep the chain of dependent round trips
 // short: lengths -> {(m, l), first 16 o rows} -> further batches of 16.
 // ---------------------------------------------------------------------------
-template <bool FUSED>
-__global__ __launch_bounds__(256) void merge_kernel(LensSrc<FUSED> ls, int B, int Hq,
+template <int LM>
+__global__ __launch_bounds__(256) void merge_kernel(LensSrc<LM> ls, int B, int Hq,
                                                     int T, int row_limit,
                                                     const float* __restrict__ part_o,
                                                     const float2* __restrict__ part_ml,
                                                     float* __restrict__ out)
 {
-    constexpr int plus = LensSrc<FUSED>::kPlus;
+    constexpr int plus = LensSrc<LM>::kPlus;
     const int lane = threadIdx.x & 63;
     const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (w >= B * Hq) return;
@@ -912,11 +949,17 @@ __global__ __launch_bounds__(256) void merge_kernel(LensSrc<FUSED> ls, int B, in
     int acc = 0;
     for (int b0 = 0; b0 < b; b0 += 64) {
         const int bi = b0 + lane;
-        if (bi < b) acc += max(1, (min(max(ls.get(bi) + plus, 0), row_limit) + T - 1) / T);
+        if (bi < b) acc += max(1, (min(max(ls.merge_get(bi) + plus, 0), row_limit) + T - 1) / T);
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
-    const int nch = max(1, (min(max(ls.get(b) + plus, 0), row_limit) + T - 1) / T);
+    const int len0 = ls.merge_get(b);
+    if constexpr (LM == kLensDeviceFused) {
+        // the device-fused append's length bump (refused, like kvdec_append,
+        // when a linear cache is full: row_limit is its capacity)
+        if (h == 0 && lane == 0 && (ls.f.window > 0 || len0 < row_limit)) ls.f.lens_out[b] = len0 + 1;
+    }
+    const int nch = max(1, (min(max(len0 + plus, 0), row_limit) + T - 1) / T);
     if (nch == 1) return;     // finished by the attend kernel
     const size_t first = static_cast<size_t>(acc);
 
@@ -973,14 +1016,15 @@ __global__ __launch_bounds__(256) void merge_kernel(LensSrc<FUSED> ls, int B, in
 // ---------------------------------------------------------------------------
 // host-side launchers
 // ---------------------------------------------------------------------------
-PartialLayout partial_layout(int64_t max_chunks, int32_t n_q_heads)
+PartialLayout partial_layout(int64_t max_chunks, int32_t n_q_heads, int32_t batch)
 {
     auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
     PartialLayout p;
     const size_t slots = static_cast<size_t>(max_chunks) * static_cast<size_t>(n_q_heads);
     p.o_offset = 0;
     p.ml_offset = up(slots * kHeadDim * sizeof(float));
-    p.bytes = p.ml_offset + up(slots * sizeof(float2));
+    p.snap_offset = p.ml_offset + up(slots * sizeof(float2));
+    p.bytes = p.snap_offset + up(static_cast<size_t>(batch) * sizeof(int32_t));
     return p;
 }
 
@@ -1103,33 +1147,38 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kUnroll = 4;
 
-template <int ESZ, int GROUP, bool PAGED, bool FUSED>
+template <int ESZ, int GROUP, bool PAGED, int LM>
 hipError_t attend_t(const AttendArgs& a, hipStream_t s)
 {
     char* ws = static_cast<char*>(a.ws);
     float* po = reinterpret_cast<float*>(ws + a.part.o_offset);
     float2* pml = reinterpret_cast<float2*>(ws + a.part.ml_offset);
     const PageMap pm{a.table, a.table_stride, a.pshift};
-    LensSrc<FUSED> ls;
-    if constexpr (FUSED) {
-        for (int b = 0; b < kMaxFusedBatch; ++b) ls.v[b] = b < a.batch ? a.fused_lens[b] : 0;
-        ls.k_new = static_cast<const char*>(a.k_new);
-        ls.v_new = static_cast<const char*>(a.v_new);
-        ls.K = static_cast<char*>(const_cast<void*>(a.k));
-        ls.V = static_cast<char*>(const_cast<void*>(a.v));
-        ls.lens_out = a.lens_out;
-        ls.window = a.window;
-    } else {
+    LensSrc<LM> ls;
+    if constexpr (LM == kLensDevice) {
         ls.lens = a.lens;
+    } else {
+        if constexpr (LM == kLensHostFused) {
+            for (int b = 0; b < kMaxFusedBatch; ++b) ls.v[b] = b < a.batch ? a.fused_lens[b] : 0;
+        } else {
+            ls.lens = a.lens;
+            ls.snap = reinterpret_cast<int32_t*>(ws + a.part.snap_offset);
+        }
+        ls.f.k_new = static_cast<const char*>(a.k_new);
+        ls.f.v_new = static_cast<const char*>(a.v_new);
+        ls.f.K = static_cast<char*>(const_cast<void*>(a.k));
+        ls.f.V = static_cast<char*>(const_cast<void*>(a.v));
+        ls.f.lens_out = a.lens_out;
+        ls.f.window = a.window;
     }
     const dim3 grid(static_cast<unsigned>(a.n_chunks), a.n_kv_heads), block(kWaves * 64);
     if constexpr (ESZ == 2 && GROUP >= 2)
-        hipLaunchKernelGGL((attend_gqa_mfma_kernel<GROUP, kWaves, PAGED, FUSED>), grid, block, 0, s,
+        hipLaunchKernelGGL((attend_gqa_mfma_kernel<GROUP, kWaves, PAGED, LM>), grid, block, 0, s,
                            a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v), ls,
                            a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows, a.qscale,
                            a.out, po, pml, pm);
     else
-        hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWaves, kUnroll, PAGED, FUSED>), grid, block,
+        hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWaves, kUnroll, PAGED, LM>), grid, block,
                            0, s, a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v),
                            ls, a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows,
                            a.qscale, a.out, po, pml, pm);
@@ -1137,23 +1186,23 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
     if (e != hipSuccess || !a.need_merge) return e;
     const int Hq = a.n_kv_heads * GROUP;
     const int waves = a.batch * Hq;
-    hipLaunchKernelGGL((merge_kernel<FUSED>), dim3((waves + 3) / 4), dim3(256), 0, s, ls, a.batch,
+    hipLaunchKernelGGL((merge_kernel<LM>), dim3((waves + 3) / 4), dim3(256), 0, s, ls, a.batch,
                        Hq, a.chunk_rows, a.row_limit, po, pml, a.out);
     return hipGetLastError();
 }
 
-template <int ESZ, bool PAGED, bool FUSED>
+template <int ESZ, bool PAGED, int LM>
 hipError_t attend_dispatch_group(const AttendArgs& a, hipStream_t s)
 {
     switch (a.group) {
-        case 1: return attend_t<ESZ, 1, PAGED, FUSED>(a, s);
-        case 2: return attend_t<ESZ, 2, PAGED, FUSED>(a, s);
-        case 3: return attend_t<ESZ, 3, PAGED, FUSED>(a, s);
-        case 4: return attend_t<ESZ, 4, PAGED, FUSED>(a, s);
-        case 5: return attend_t<ESZ, 5, PAGED, FUSED>(a, s);
-        case 6: return attend_t<ESZ, 6, PAGED, FUSED>(a, s);
-        case 7: return attend_t<ESZ, 7, PAGED, FUSED>(a, s);
-        case 8: return attend_t<ESZ, 8, PAGED, FUSED>(a, s);
+        case 1: return attend_t<ESZ, 1, PAGED, LM>(a, s);
+        case 2: return attend_t<ESZ, 2, PAGED, LM>(a, s);
+        case 3: return attend_t<ESZ, 3, PAGED, LM>(a, s);
+        case 4: return attend_t<ESZ, 4, PAGED, LM>(a, s);
+        case 5: return attend_t<ESZ, 5, PAGED, LM>(a, s);
+        case 6: return attend_t<ESZ, 6, PAGED, LM>(a, s);
+        case 7: return attend_t<ESZ, 7, PAGED, LM>(a, s);
+        case 8: return attend_t<ESZ, 8, PAGED, LM>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1168,26 +1217,26 @@ const void* attend_kernel_ptr(int group, int* block)
     *block = kWaves * 64;
     if constexpr (ESZ == 2) {
         switch (group) {
-            case 1: return reinterpret_cast<const void*>(&attend_kernel<2, 1, kWaves, kUnroll, false, false>);
-            case 2: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<2, kWaves, false, false>);
-            case 3: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<3, kWaves, false, false>);
-            case 4: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<4, kWaves, false, false>);
-            case 5: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<5, kWaves, false, false>);
-            case 6: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<6, kWaves, false, false>);
-            case 7: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<7, kWaves, false, false>);
-            case 8: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<8, kWaves, false, false>);
+            case 1: return reinterpret_cast<const void*>(&attend_kernel<2, 1, kWaves, kUnroll, false, kLensDevice>);
+            case 2: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<2, kWaves, false, kLensDevice>);
+            case 3: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<3, kWaves, false, kLensDevice>);
+            case 4: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<4, kWaves, false, kLensDevice>);
+            case 5: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<5, kWaves, false, kLensDevice>);
+            case 6: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<6, kWaves, false, kLensDevice>);
+            case 7: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<7, kWaves, false, kLensDevice>);
+            case 8: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<8, kWaves, false, kLensDevice>);
             default: return nullptr;
         }
     } else {
         switch (group) {
-            case 1: return reinterpret_cast<const void*>(&attend_kernel<4, 1, kWaves, kUnroll, false, false>);
-            case 2: return reinterpret_cast<const void*>(&attend_kernel<4, 2, kWaves, kUnroll, false, false>);
-            case 3: return reinterpret_cast<const void*>(&attend_kernel<4, 3, kWaves, kUnroll, false, false>);
-            case 4: return reinterpret_cast<const void*>(&attend_kernel<4, 4, kWaves, kUnroll, false, false>);
-            case 5: return reinterpret_cast<const void*>(&attend_kernel<4, 5, kWaves, kUnroll, false, false>);
-            case 6: return reinterpret_cast<const void*>(&attend_kernel<4, 6, kWaves, kUnroll, false, false>);
-            case 7: return reinterpret_cast<const void*>(&attend_kernel<4, 7, kWaves, kUnroll, false, false>);
-            case 8: return reinterpret_cast<const void*>(&attend_kernel<4, 8, kWaves, kUnroll, false, false>);
+            case 1: return reinterpret_cast<const void*>(&attend_kernel<4, 1, kWaves, kUnroll, false, kLensDevice>);
+            case 2: return reinterpret_cast<const void*>(&attend_kernel<4, 2, kWaves, kUnroll, false, kLensDevice>);
+            case 3: return reinterpret_cast<const void*>(&attend_kernel<4, 3, kWaves, kUnroll, false, kLensDevice>);
+            case 4: return reinterpret_cast<const void*>(&attend_kernel<4, 4, kWaves, kUnroll, false, kLensDevice>);
+            case 5: return reinterpret_cast<const void*>(&attend_kernel<4, 5, kWaves, kUnroll, false, kLensDevice>);
+            case 6: return reinterpret_cast<const void*>(&attend_kernel<4, 6, kWaves, kUnroll, false, kLensDevice>);
+            case 7: return reinterpret_cast<const void*>(&attend_kernel<4, 7, kWaves, kUnroll, false, kLensDevice>);
+            case 8: return reinterpret_cast<const void*>(&attend_kernel<4, 8, kWaves, kUnroll, false, kLensDevice>);
             default: return nullptr;
         }
     }
@@ -1220,15 +1269,20 @@ int resident_attend_blocks(int dtype, int group)
 hipError_t launch_attend(int dtype, const AttendArgs& a, hipStream_t s)
 {
     if (a.table)
-        return dtype == 0 ? attend_dispatch_group<4, true, false>(a, s)
-                          : attend_dispatch_group<2, true, false>(a, s);
+        return dtype == 0 ? attend_dispatch_group<4, true, kLensDevice>(a, s)
+                          : attend_dispatch_group<2, true, kLensDevice>(a, s);
     if (a.fused_lens) {
         if (a.batch > kMaxFusedBatch) return hipErrorInvalidValue;
-        return dtype == 0 ? attend_dispatch_group<4, false, true>(a, s)
-                          : attend_dispatch_group<2, false, true>(a, s);
+        return dtype == 0 ? attend_dispatch_group<4, false, kLensHostFused>(a, s)
+                          : attend_dispatch_group<2, false, kLensHostFused>(a, s);
     }
-    return dtype == 0 ? attend_dispatch_group<4, false, false>(a, s)
-                      : attend_dispatch_group<2, false, false>(a, s);
+    if (a.fused_device) {
+        if (!a.need_merge) return hipErrorInvalidValue;   // the merge launch bumps the lengths
+        return dtype == 0 ? attend_dispatch_group<4, false, kLensDeviceFused>(a, s)
+                          : attend_dispatch_group<2, false, kLensDeviceFused>(a, s);
+    }
+    return dtype == 0 ? attend_dispatch_group<4, false, kLensDevice>(a, s)
+                      : attend_dispatch_group<2, false, kLensDevice>(a, s);
 }
 
 }  // namespace kvdec

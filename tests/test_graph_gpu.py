@@ -1,6 +1,7 @@
 """A multi-layer decode step captured once in a HIP graph and replayed for
 consecutive tokens (replay mode), checked against the oracle after every
-replay, with eager library calls between replays."""
+replay, with eager library calls between replays; the step either appends
+and attends in two calls or through kvdec_append_attend."""
 import numpy as np
 import pytest
 import torch
@@ -19,10 +20,11 @@ def _rows(rng, shape, dtype):
     return x if dtype == "f32" else gen.f32_to_bf16_bits(x)
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("dtype,Hq,Hkv,cross,window", [("f32", 6, 6, True, 0),
                                                         ("bf16", 16, 4, False, 0),
                                                         ("bf16", 8, 8, False, 128)])
-def test_graph_replayed_multilayer_step(dtype, Hq, Hkv, cross, window):
+def test_graph_replayed_multilayer_step(dtype, Hq, Hkv, cross, window, fused):
     rng = np.random.default_rng(7 + Hq)
     L, B, T, enc = 3, 2, 9, 300
     cap = 200 if window == 0 else window
@@ -65,8 +67,11 @@ def test_graph_replayed_multilayer_step(dtype, Hq, Hkv, cross, window):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for lay in layers:
-            lay["sc"].append(lay["kn"], lay["vn"])
-            lay["sc"].attend(lay["q"], out=lay["out"])
+            if fused:   # replay mode: attend launch + merge launch (which bumps the lengths)
+                lay["sc"].append_attend(lay["kn"], lay["vn"], lay["q"], out=lay["out"])
+            else:
+                lay["sc"].append(lay["kn"], lay["vn"])
+                lay["sc"].attend(lay["q"], out=lay["out"])
             if cross:
                 lay["cc"].attend(lay["qc"], out=lay["cout"])
 
@@ -108,3 +113,32 @@ def test_graph_replayed_multilayer_step(dtype, Hq, Hkv, cross, window):
             torch.cuda.synchronize()
             assert torch.equal(eager, lay["out"])
         assert layers[0]["sc"].lens_dev.cpu().tolist() == lens.tolist()
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv", [("f32", 4, 4), ("bf16", 8, 2)])
+def test_replay_fused_append_refused_at_capacity(dtype, Hq, Hkv):
+    """Replay mode cannot check capacity on the host; like kvdec_append, the
+    fused call then stores nothing and keeps the length once a linear cache
+    is full, and attends the full cache."""
+    rng = np.random.default_rng(91)
+    B, cap = 2, 130
+    start = np.array([cap - 1, 40], np.int32)
+    cp = gen.padded_rows(cap)
+    K = _rows(rng, (B, Hkv, cp, 64), dtype)
+    V = _rows(rng, (B, Hkv, cp, 64), dtype)
+    mk = lambda: KVCache(B, Hkv, cap, dtype, lens=start, k=to_device(K), v=to_device(V))
+    two, one = mk(), mk()
+    for c in (two, one):
+        c.set_replay_mode(64)
+    for s in range(3):
+        kn = to_device(_rows(rng, (B, Hkv, 64), dtype))
+        vn = to_device(_rows(rng, (B, Hkv, 64), dtype))
+        q = torch.from_numpy(rng.standard_normal((B, Hq, 64), dtype=np.float32)).cuda()
+        two.append(kn, vn)
+        ref = two.attend(q)
+        got = one.append_attend(kn, vn, q)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"step {s}"
+    want = [cap, 43]
+    assert one.lens_dev.cpu().tolist() == want and two.lens_dev.cpu().tolist() == want
+    assert torch.equal(one.k, two.k) and torch.equal(one.v, two.v)
