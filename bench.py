@@ -4,10 +4,11 @@ One step = one decode token for every sequence of one layer: append the new
 K/V row and self-attention over the cached rows (kvdec_append_attend, one
 launch; --unfused times kvdec_append then kvdec_attend_self instead) and, for
 the Whisper-shaped workloads, cross-attention over the 1500 static encoder
-rows (kvdec_attend_cross).  Workloads with
-several consecutive steps (Whisper-large: 32, GQA: 8) cycle through them; the
-lengths are rolled back to the workload's starting lengths at the start of
-each cycle (one tiny kernel, counted inside the step time).
+rows (kvdec_attend_cross).  Workloads with several consecutive steps
+(Whisper-large: 32, GQA: 8) cycle through them; the first step of each cycle
+runs at the workload's starting positions (kvdec_append_attend_at, which
+rewinds the lengths inside the same launch; --unfused rolls them back with
+kvdec_reset_lens, one tiny kernel counted in the step).
 
 Prints ONE JSON line on stdout (the headline workload, default
 whisper-large: batch 64, 20 heads, bf16 K/V, self 448 -> 480 over 32 steps
@@ -127,15 +128,20 @@ class Bench:
     def step(self, i, events=None, stream=None):
         lib, s, Hq = self.lib, i % self.S, self.wl.n_q_heads
         st = self.stream if stream is None else stream
-        if s == 0:
-            rc = lib.kvdec_reset_lens(self.h_self, self.lens0_c, st)
-            assert rc == 0, lib.kvdec_last_error()
         if self.fused:
             if events is not None:
                 events[0].record()
-            rc = lib.kvdec_append_attend(self.h_self, self.p_kn[s], self.p_vn[s], self.p_q[s], Hq,
-                                         0.125, 0, self.p_out, self.p_ws, self.n_ws, st)
+            if s == 0:      # cycle start: the step at the workload's starting positions
+                rc = lib.kvdec_append_attend_at(self.h_self, self.lens0_c, self.p_kn[s],
+                                                self.p_vn[s], self.p_q[s], Hq, 0.125, 0,
+                                                self.p_out, self.p_ws, self.n_ws, st)
+            else:
+                rc = lib.kvdec_append_attend(self.h_self, self.p_kn[s], self.p_vn[s], self.p_q[s],
+                                             Hq, 0.125, 0, self.p_out, self.p_ws, self.n_ws, st)
         else:
+            if s == 0:
+                rc = lib.kvdec_reset_lens(self.h_self, self.lens0_c, st)
+                assert rc == 0, lib.kvdec_last_error()
             rc = lib.kvdec_append(self.h_self, self.p_kn[s], self.p_vn[s], st)
             assert rc == 0, lib.kvdec_last_error()
             if events is not None:
@@ -390,7 +396,7 @@ class VariantBench(Bench):
             if events is not None:
                 events[1].record()
             return
-        if s == 0:
+        if s == 0 and self.variant == "rope":
             rc = lib.kvdec_reset_lens(self.h_self, self.lens0_c, st)
             assert rc == 0, lib.kvdec_last_error()
         if self.variant == "rope":
@@ -404,8 +410,13 @@ class VariantBench(Bench):
         else:                 # ring: append fused into the attend launch
             if events is not None:
                 events[0].record()
-            rc = lib.kvdec_append_attend(self.h_self, self.p_kn[s], self.p_vn[s], self.p_q[s], Hq,
-                                         0.125, 0, self.p_out, self.p_ws, self.n_ws, st)
+            if s == 0:        # cycle start at the starting positions
+                rc = lib.kvdec_append_attend_at(self.h_self, self.lens0_c, self.p_kn[s],
+                                                self.p_vn[s], self.p_q[s], Hq, 0.125, 0,
+                                                self.p_out, self.p_ws, self.n_ws, st)
+            else:
+                rc = lib.kvdec_append_attend(self.h_self, self.p_kn[s], self.p_vn[s], self.p_q[s],
+                                             Hq, 0.125, 0, self.p_out, self.p_ws, self.n_ws, st)
         assert rc == 0, lib.kvdec_last_error()
         if events is not None:
             events[1].record()

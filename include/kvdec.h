@@ -227,6 +227,23 @@ KVDEC_API int32_t kvdec_append_attend(kvdec_cache* cache, const void* k_new, con
                                       void* stream);
 
 /*
+ * kvdec_reset_lens(lens_host) then kvdec_append_attend, as one call: the
+ * decode step at explicit positions ([CERA] `decode_step_into` takes the
+ * token's position and leaves the cache length at position + 1), which also
+ * rewinds a sequence, for example after draft tokens were rejected.
+ * lens_host[b] (host) is the number of tokens sequence b keeps before this
+ * one; afterwards it holds lens_host[b] + 1.  Where
+ * kvdec_append_attend is one launch, the positions go to it by value and it
+ * writes the device lengths, so the rewind costs no launch of its own;
+ * otherwise the lengths are set on the device first.  Errors: those of the
+ * two calls (a linear cache needs lens_host[b] < capacity).
+ */
+KVDEC_API int32_t kvdec_append_attend_at(kvdec_cache* cache, const int32_t* lens_host,
+                                         const void* k_new, const void* v_new, const float* q,
+                                         int32_t n_q_heads, float scale, int32_t chunk_rows,
+                                         float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Cross-attention over a static encoder cache: the same computation as
  * kvdec_attend_self over every seeded row (1500 for Whisper's 30 s window),
  * with the decoder's cross query: [CERA] `decode_step_into` cross block and

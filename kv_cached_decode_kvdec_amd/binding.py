@@ -29,7 +29,8 @@ KVDEC_MAX_FUSED_BATCH = 512
 EXPORTED = [
     "kvdec_padded_capacity", "kvdec_cache_create", "kvdec_cache_destroy", "kvdec_reset_lens",
     "kvdec_get_lens", "kvdec_seed", "kvdec_append", "kvdec_append_rope", "kvdec_workspace_bytes",
-    "kvdec_attend_self", "kvdec_attend_cross", "kvdec_append_attend", "kvdec_set_replay_mode",
+    "kvdec_attend_self", "kvdec_attend_cross", "kvdec_append_attend", "kvdec_append_attend_at",
+    "kvdec_set_replay_mode",
     "kvdec_status_str",
     "kvdec_last_error", "kvdec_paged_create", "kvdec_paged_destroy", "kvdec_paged_append",
     "kvdec_paged_release", "kvdec_paged_reserve", "kvdec_paged_truncate",
@@ -89,6 +90,8 @@ def load():
         "kvdec_set_replay_mode": (_i32, [_vp, _i32]),
         "kvdec_append_attend": (_i32, [_vp, _vp, _vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz,
                                        _vp]),
+        "kvdec_append_attend_at": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float, _i32, _vp,
+                                          _vp, _sz, _vp]),
         "kvdec_paged_create": (_i32, [ctypes.POINTER(PagedDesc), _vp, ctypes.POINTER(_vp)]),
         "kvdec_paged_destroy": (None, [_vp]),
         "kvdec_paged_append": (_i32, [_vp, _vp, _vp, _vp]),
@@ -245,3 +248,13 @@ def kvdec_append_attend(handle, k_new_ptr, v_new_ptr, q_ptr, n_q_heads, scale, c
     _check(load().kvdec_append_attend(handle, k_new_ptr, v_new_ptr, q_ptr, int(n_q_heads),
                                       float(scale), int(chunk_rows), out_ptr, ws_ptr, int(ws_bytes),
                                       stream), "kvdec_append_attend")
+
+
+def kvdec_append_attend_at(handle, lens_host, k_new_ptr, v_new_ptr, q_ptr, n_q_heads, scale,
+                           chunk_rows, out_ptr, ws_ptr, ws_bytes, stream=None):
+    """lens_host: a sequence of ints or a ctypes int32 array (host)."""
+    if not isinstance(lens_host, ctypes.Array):
+        lens_host = (ctypes.c_int32 * len(lens_host))(*[int(x) for x in lens_host])
+    _check(load().kvdec_append_attend_at(handle, lens_host, k_new_ptr, v_new_ptr, q_ptr,
+                                         int(n_q_heads), float(scale), int(chunk_rows), out_ptr,
+                                         ws_ptr, int(ws_bytes), stream), "kvdec_append_attend_at")

@@ -129,25 +129,49 @@ class KVCache:
             self._ws[n_q_heads] = ws
         return ws
 
+    def _q_out(self, q, out):
+        """Check q ([batch, n_q_heads, 64] f32 on the cache's device) and out
+        (same, allocated when None); returns out."""
+        if q.dtype != torch.float32 or q.dim() != 3 or q.shape[0] != self.batch \
+                or q.shape[2] != B.HEAD_DIM or not q.is_contiguous() or q.device != self.k.device:
+            raise ValueError("q must be a contiguous float32 [batch, n_q_heads, 64] device tensor")
+        if out is None:
+            return torch.empty_like(q)
+        if out.dtype != torch.float32 or out.shape != q.shape or not out.is_contiguous() \
+                or out.device != q.device:
+            raise ValueError("out must be a contiguous float32 tensor shaped like q")
+        return out
+
     def append_attend(self, k_new, v_new, q, scale=0.125, chunk_rows=0, out=None):
         """Append one token and attend, as one call (one launch when possible)."""
         shape = (self.batch, self.n_kv_heads, B.HEAD_DIM)
         self._check_rows(k_new, shape, "k_new")
         self._check_rows(v_new, shape, "v_new")
-        if out is None:
-            out = torch.empty_like(q)
+        out = self._q_out(q, out)
         ws = self.workspace(q.shape[1])
         B.kvdec_append_attend(self.handle, _ptr(k_new), _ptr(v_new), _ptr(q), q.shape[1], scale,
                               chunk_rows, _ptr(out), _ptr(ws), ws.numel(), current_stream())
         return out
 
+    def append_attend_at(self, lens, k_new, v_new, q, scale=0.125, chunk_rows=0, out=None):
+        """Set the lengths to `lens` (the new token's positions), then append
+        and attend, as one call."""
+        shape = (self.batch, self.n_kv_heads, B.HEAD_DIM)
+        self._check_rows(k_new, shape, "k_new")
+        self._check_rows(v_new, shape, "v_new")
+        lens = [int(x) for x in lens]
+        if len(lens) != self.batch:
+            raise ValueError(f"lens must hold {self.batch} positions")
+        out = self._q_out(q, out)
+        ws = self.workspace(q.shape[1])
+        B.kvdec_append_attend_at(self.handle, lens, _ptr(k_new), _ptr(v_new), _ptr(q), q.shape[1],
+                                 scale, chunk_rows, _ptr(out), _ptr(ws), ws.numel(),
+                                 current_stream())
+        return out
+
     def attend(self, q, scale=0.125, chunk_rows=0, out=None):
         Hq = q.shape[1]
-        if q.dtype != torch.float32 or q.dim() != 3 or q.shape[0] != self.batch \
-                or q.shape[2] != B.HEAD_DIM or not q.is_contiguous() or q.device != self.k.device:
-            raise ValueError("q must be a contiguous float32 [batch, n_q_heads, 64] device tensor")
-        if out is None:
-            out = torch.empty_like(q)
+        out = self._q_out(q, out)
         ws = self.workspace(Hq)
         fn = B.kvdec_attend_cross if self.static else B.kvdec_attend_self
         fn(self.handle, _ptr(q), Hq, scale, chunk_rows, _ptr(out), _ptr(ws), ws.numel(),
@@ -219,8 +243,7 @@ class PagedKVCache:
 
     def attend(self, q, scale=0.125, chunk_rows=0, out=None):
         Hq = q.shape[1]
-        if out is None:
-            out = torch.empty_like(q)
+        out = KVCache._q_out(self, q, out)
         ws = self._ws.get(Hq)
         if ws is None:
             ws = torch.empty(B.kvdec_paged_workspace_bytes(self.handle, Hq), dtype=torch.uint8,

@@ -261,6 +261,49 @@ int32_t check_append(const kvdec_cache* c, const void* k_new, const void* v_new)
 
 }  // namespace
 
+namespace {
+
+// The fused decode step from pre-append lengths `pre` (the host mirror, or
+// the positions kvdec_append_attend_at was given).  Arguments are checked by
+// the callers; `set_device` first writes `pre` to the device lengths where
+// the launch reads them from there.
+int32_t append_attend_from(kvdec_cache* c, const std::vector<int32_t>& pre, bool set_device,
+                           const void* k_new, const void* v_new, const float* q,
+                           int32_t n_q_heads, float scale, int32_t chunk_rows, float* out,
+                           void* ws, size_t ws_bytes, void* stream)
+{
+    AttendView v = view_of(c);
+    // rows attended after the append
+    for (size_t b = 0; b < pre.size(); ++b) {
+        const int64_t n = static_cast<int64_t>(pre[b]) + 1;
+        v.rows[b] = static_cast<int32_t>(c->d.window > 0 && n > c->d.window ? c->d.window : n);
+    }
+    int32_t rc = check_attend(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes);
+    if (rc) return rc;
+    if (c->d.batch > KVDEC_MAX_FUSED_BATCH || c->replay_chunk > 0) {
+        // attend + merge launch; the lengths are read from (and bumped on) the device
+        if (set_device) {
+            const hipError_t e = kvdec::launch_set_lens(c->d.lens, pre.data(), c->d.batch,
+                                                        static_cast<hipStream_t>(stream));
+            if (e != hipSuccess) return hip_fail(e, "set lengths");
+        }
+        v.fused_device = true;
+    } else {
+        v.fused_lens = pre.data();     // one launch; pre-append lengths by value
+    }
+    v.k_new = k_new;
+    v.v_new = v_new;
+    v.lens_out = c->d.lens;
+    v.window = c->d.window;
+    rc = attend_view(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
+    if (rc) return rc;
+    c->lens = pre;
+    for (auto& l : c->lens) ++l;
+    return KVDEC_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t kvdec_padded_capacity(int32_t capacity)
@@ -659,28 +702,35 @@ int32_t kvdec_append_attend(kvdec_cache* c, const void* k_new, const void* v_new
                             size_t ws_bytes, void* stream)
 {
     g_err.clear();
-    int32_t rc = check_append(c, k_new, v_new);
+    const int32_t rc = check_append(c, k_new, v_new);
     if (rc) return rc;
-    AttendView v = view_of(c);
-    rc = check_attend(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes);
+    const std::vector<int32_t> pre = c->lens;
+    return append_attend_from(c, pre, false, k_new, v_new, q, n_q_heads, scale, chunk_rows, out,
+                              ws, ws_bytes, stream);
+}
+
+int32_t kvdec_append_attend_at(kvdec_cache* c, const int32_t* lens_host, const void* k_new,
+                               const void* v_new, const float* q, int32_t n_q_heads, float scale,
+                               int32_t chunk_rows, float* out, void* ws, size_t ws_bytes,
+                               void* stream)
+{
+    g_err.clear();
+    if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
+    int32_t rc = check_lens(lens_host, c->d.batch, c->d.capacity, c->d.window);
     if (rc) return rc;
-    // rows attended after the append
-    for (auto& r : v.rows) {
-        const int64_t n = static_cast<int64_t>(r) + 1;
-        r = static_cast<int32_t>(c->d.window > 0 && n > c->d.window ? c->d.window : n);
+    std::vector<int32_t> pre(lens_host, lens_host + c->d.batch);
+    for (int32_t b = 0; b < c->d.batch; ++b) {
+        if (c->d.window == 0 && pre[b] >= c->d.capacity)
+            return fail(KVDEC_E_OVERFLOW, "cache overflow: sequence %d at position %d, capacity %d",
+                        b, pre[b], c->d.capacity);
+        if (pre[b] == INT32_MAX)
+            return fail(KVDEC_E_OVERFLOW, "token count of sequence %d would overflow int32", b);
     }
-    if (c->d.batch > KVDEC_MAX_FUSED_BATCH || c->replay_chunk > 0)
-        v.fused_device = true;         // attend + merge launch; the lengths stay on the device
-    else
-        v.fused_lens = c->lens.data(); // one launch; pre-append lengths by value
-    v.k_new = k_new;
-    v.v_new = v_new;
-    v.lens_out = c->d.lens;
-    v.window = c->d.window;
-    rc = attend_view(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
-    if (rc) return rc;
-    for (auto& l : c->lens) ++l;
-    return KVDEC_OK;
+    if (c->d.is_static) return fail(KVDEC_E_STATIC, "append on a static (encoder) cache");
+    if (!aligned16(k_new) || !aligned16(v_new))
+        return fail(KVDEC_E_INVALID, "k_new and v_new must be non-NULL, 16-byte aligned device pointers");
+    return append_attend_from(c, pre, true, k_new, v_new, q, n_q_heads, scale, chunk_rows, out, ws,
+                              ws_bytes, stream);
 }
 
 const char* kvdec_status_str(int32_t s)

@@ -5,9 +5,10 @@ does (bit for bit, NaN canaries in unused rows included) and return exactly
 the output of kvdec_append followed by kvdec_attend_self at the same chunk
 size (same chunks, same arithmetic, same order), which is also checked
 against the f64 oracle within the usual tolerance.  Cases: linear and ring
-caches, f32 and bf16, MHA, the MFMA group-4 kernel and VALU groups, one chunk
-and several (merge launch), new rows landing on a chunk boundary, the
-first-ever row, and the two-call fallbacks (large batch, replay mode).
+caches, f32 and bf16, MHA, MFMA and VALU groups, one chunk and several (merge
+launch), new rows landing on a chunk boundary, the first-ever row, the
+device-length mode (replay mode, batches above 512: the merge launch bumps
+the lengths), and kvdec_append_attend_at (explicit positions, rewinds).
 """
 import sys
 
@@ -143,7 +144,7 @@ def test_fused_full_size_workloads():
 
 
 @pytest.mark.parametrize("mode", ["large-batch", "replay"])
-def test_fused_two_call_fallbacks(mode):
+def test_fused_device_length_mode(mode):
     Bsz = B.KVDEC_MAX_FUSED_BATCH + 3 if mode == "large-batch" else 5
     wl = gen.Workload("fb", Bsz, 8, 2, "bf16", "uniform:0:300", 2, False, seed=67)
     inp = gen.make_inputs(wl, batch=Bsz, steps=2)
@@ -189,3 +190,61 @@ def test_fused_errors_enqueue_nothing():
     torch.cuda.synchronize()
     assert torch.equal(c.k, before) and c.lens() == [2, 3] and c2.lens() == [2, 3]
     assert c2.lens_dev.cpu().tolist() == [2, 3] and c.lens_dev.cpu().tolist() == [2, 3]
+
+
+@pytest.mark.parametrize("mode", ["one-launch", "replay", "large-batch"])
+def test_append_attend_at_equals_reset_then_fused(mode):
+    """kvdec_append_attend_at(lens) == kvdec_reset_lens(lens) + kvdec_append_attend, bitwise,
+    including a rewind to earlier positions (their rows are overwritten)."""
+    Bsz = B.KVDEC_MAX_FUSED_BATCH + 5 if mode == "large-batch" else 6
+    wl = gen.Workload("at", Bsz, 8, 2, "bf16", "uniform:10:300", 3, False, seed=97)
+    inp = gen.make_inputs(wl, batch=Bsz, steps=3)
+    two, one = _pair(inp)
+    if mode == "replay":
+        two.set_replay_mode(64)
+        one.set_replay_mode(64)
+    rng = np.random.default_rng(98)
+    Kh, Vh = inp.k_cache.copy(), inp.v_cache.copy()
+    pos = inp.lens.copy()
+    for s in range(3):
+        if s == 2:                                   # rewind every sequence by 0..9 tokens
+            pos = np.maximum(pos - rng.integers(0, 10, size=Bsz).astype(np.int32), 0)
+        kn, vn, q = to_device(inp.k_new[s]), to_device(inp.v_new[s]), to_device(inp.q_self[s])
+        two.reset_lens(pos)
+        ref_dev = two.append_attend(kn, vn, q)
+        got = one.append_attend_at(pos, kn, vn, q)
+        torch.cuda.synchronize()
+        assert got.cpu().numpy().tobytes() == ref_dev.cpu().numpy().tobytes(), f"{mode} step {s}"
+        pos = oracle.append(Kh, Vh, inp.k_new[s], inp.v_new[s], pos)
+        bs = np.arange(0, Bsz, max(1, Bsz // 12))
+        ref = oracle.attend(inp.q_self[s][bs], Kh[bs], Vh[bs], pos[bs])
+        assert_attention_close(got.cpu().numpy()[bs], ref, "bf16", f"{mode} step {s}")
+    assert one.lens() == pos.tolist() and one.lens_dev.cpu().tolist() == pos.tolist()
+    assert to_host_bits(one.k).tobytes() == to_host_bits(two.k).tobytes()
+    assert to_host_bits(one.v).tobytes() == to_host_bits(two.v).tobytes()
+
+
+def test_append_attend_at_errors_enqueue_nothing():
+    c = KVCache(2, 2, 8, "f32", lens=[3, 4])
+    kn = torch.zeros(2, 2, 64, device="cuda")
+    q = torch.zeros(2, 4, 64, device="cuda")
+    for lens, code in (([8, 0], B.KVDEC_E_OVERFLOW), ([-1, 0], B.KVDEC_E_SHAPE),
+                       ([9, 0], B.KVDEC_E_SHAPE)):
+        with pytest.raises(B.KvdecError) as e:
+            c.append_attend_at(lens, kn, kn, q)
+        assert e.value.code == code, lens
+    with pytest.raises(B.KvdecError) as e:
+        c.append_attend_at([0, 0], kn, kn, torch.zeros(2, 3, 64, device="cuda"))
+    assert e.value.code == B.KVDEC_E_SHAPE
+    s = KVCache(2, 2, 10, "f32", static=True, lens=[10, 10])
+    with pytest.raises(B.KvdecError) as e:
+        s.append_attend_at([1, 1], kn, kn, q)
+    assert e.value.code == B.KVDEC_E_STATIC
+    torch.cuda.synchronize()
+    assert c.lens() == [3, 4] and c.lens_dev.cpu().tolist() == [3, 4]
+    assert torch.all(c.k == 0)
+    # a ring accepts any non-negative position
+    r = KVCache(2, 2, 8, "f32", lens=[0, 0], window=8)
+    r.append_attend_at([100, 7], kn, kn, q)
+    torch.cuda.synchronize()
+    assert r.lens() == [101, 8] and r.lens_dev.cpu().tolist() == [101, 8]
