@@ -61,7 +61,7 @@ typedef enum { KVDEC_F32 = 0, KVDEC_BF16 = 1 } kvdec_dtype;
 #define KVDEC_MAX_CHUNK 4096   /* largest split-sequence chunk, rows */
 #define KVDEC_MAX_GROUP 8      /* query heads per KV head supported */
 #define KVDEC_REPLAY_AUTO (-1) /* kvdec_set_replay_mode: pick the chunk from current lengths */
-#define KVDEC_MAX_FUSED_BATCH 512 /* kvdec_append_attend fuses the append up to this batch */
+#define KVDEC_MAX_FUSED_BATCH 512 /* largest batch kvdec_append_attend runs as one launch */
 
 /* Opaque host-side handle: the cache description plus a host mirror of the
  * per-sequence lengths (used for validation and launch sizing, so no call

@@ -777,7 +777,7 @@ void attend_gqa_mfma_kernel(
     int r0 = row0 + wave * 32;
     if (r0 < row_end) load_tile(r0);
 
-    // B operand of the score MFMA: column i is head i % 4; k-slot 8G+e of
+    // B operand of the score MFMA: column i is head i % GROUP; k-slot 8G+e of
     // instruction t is dim 32t + 8G + e.
     bf16x8 qb_hi[2], qb_lo[2];
 #pragma unroll
