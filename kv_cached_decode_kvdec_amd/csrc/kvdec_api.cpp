@@ -286,6 +286,7 @@ int32_t append_attend_from(kvdec_cache* c, const std::vector<int32_t>& pre, bool
             const hipError_t e = kvdec::launch_set_lens(c->d.lens, pre.data(), c->d.batch,
                                                         static_cast<hipStream_t>(stream));
             if (e != hipSuccess) return hip_fail(e, "set lengths");
+            c->lens = pre;             // mirror and device agree even if the attend launch fails
         }
         v.fused_device = true;
     } else {
