@@ -519,7 +519,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: the decode step is data-parallel over sequences "
-              f"with no exchange between GPUs, and this build has no multi-GPU path "
+              f"with no exchange between GPUs, and this library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
 
