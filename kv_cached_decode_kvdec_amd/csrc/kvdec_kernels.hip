@@ -82,6 +82,36 @@ __device__ __forceinline__ float row_max16(float x)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), both rounded to
+// nearest even by the gfx950 conversion v_cvt_pk_bf16_f32 (x - hi is exact
+// in f32).  hi + lo carries 16 significant bits of x.
+__device__ __forceinline__ void split_bf16(const f32x8 x, bf16x8& hi, bf16x8& lo)
+{
+    hi = __builtin_convertvector(x, bf16x8);
+    lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x8), bf16x8);
+}
+
+// Max and sum over the four 16-lane groups of a wave (lanes l, l^16, l^32,
+// l^48) with the gfx950 lane swaps, no LDS round trip: permlane32_swap pairs
+// each lane with lane ^ 32, permlane16_swap with lane ^ 16.  Every lane ends
+// with the same bits (the operations are commutative).
+__device__ __forceinline__ float max_over_groups(float x)
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_over_groups(float x)
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // float -> bfloat16 bits, round to nearest even; NaN stays NaN.
 __device__ __forceinline__ uint32_t bf16_rne(float f)
@@ -201,14 +231,17 @@ __device__ __forceinline__ bool locate(const LensSrc<LM>& ls, int B, int T, int 
             const int t = __shfl_up(incl, d);
             if (lane >= d) incl += t;
         }
-        const int total = __shfl(incl, 63);
+        const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
         if (blk < base + total) {
             const unsigned long long m = __ballot(incl > blk - base);
             const int first = __ffsll(static_cast<long long>(m)) - 1;
+            // equal on every lane; readfirstlane (here and on `total`) lets the
+            // compiler keep them, and the row bounds derived from them, in
+            // scalar registers
             r.b = b0 + first;
-            r.c = blk - base - __shfl(incl - cnt, first);
-            r.len = __shfl(ln, first);
-            r.nch = __shfl(cnt, first);
+            r.c = __builtin_amdgcn_readfirstlane(blk - base - __shfl(incl - cnt, first));
+            r.len = __builtin_amdgcn_readfirstlane(__shfl(ln, first));
+            r.nch = __builtin_amdgcn_readfirstlane(__shfl(cnt, first));
             return true;
         }
         base += total;
@@ -548,7 +581,7 @@ void attend_kernel(
     using L = Lay<ESZ>;
     constexpr int EPL = L::kEPL, LPR = L::kLPR, RPI = L::kRPI, RB = L::kRowBytes;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane / LPR;
     const int part = lane - sub * LPR;
     const int g = blockIdx.y;
@@ -588,7 +621,10 @@ void attend_kernel(
 
     constexpr int kWaveRows = U * RPI;
     for (int r0 = row0 + wave * kWaveRows; r0 < row_end; r0 += WAVES * kWaveRows) {
+        // full: every row of this iteration lies inside the chunk (wave-uniform)
+        const bool full = r0 + kWaveRows <= row_end;
         uint4 kr[U], vr[U];
+        // rows past the end repeat the last row (weight zero, finite V)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = min(r0 + u * RPI + sub, row_end - 1);
@@ -601,7 +637,7 @@ void attend_kernel(
         for (int u = 0; u < U; ++u) {
             float kf[EPL];
             unpack<ESZ>(kr[u], kf);
-            const bool valid = r0 + u * RPI + sub < row_end;
+            const bool valid = full || r0 + u * RPI + sub < row_end;
 #pragma unroll
             for (int i = 0; i < GROUP; ++i) {
                 float d = 0.f;
@@ -726,7 +762,7 @@ void attend_gqa_mfma_kernel(
     static_assert(GROUP >= 2 && GROUP <= 8, "MFMA path takes 2..8 query heads per KV head");
     constexpr int RB = 128;                // bf16 row bytes
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15;
     const int G = lane >> 4;
     const int hl = i % GROUP;              // head whose scores this lane holds
@@ -766,12 +802,26 @@ void attend_gqa_mfma_kernel(
     }
     uint4 kw[4], vr[4];
     auto load_tile = [&](int r0) {
+        if (!PAGED && r0 + 32 <= row_end) {
+            // whole tile inside the chunk (wave-uniform): rows r0 + 8c + lane/8
+            // are 1 KB apart, no clamping
+            const size_t off = row_offset<false, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0,
+                                                     r0 + (lane >> 3));
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int r = min(r0 + 8 * c + (lane >> 3), row_end - 1);
-            const size_t off = row_offset<PAGED, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0, r);
-            kw[c] = load16_stream(Kb + off);
-            vr[c] = load16_stream(Vb + off);
+            for (int c = 0; c < 4; ++c) {
+                kw[c] = load16_stream(Kb + off + 8 * RB * c);
+                vr[c] = load16_stream(Vb + off + 8 * RB * c);
+            }
+        } else {
+            // last tile: rows past the end repeat the last row (its weight is
+            // zero, and the V row is finite)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int r = min(r0 + 8 * c + (lane >> 3), row_end - 1);
+                const size_t off = row_offset<PAGED, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0, r);
+                kw[c] = load16_stream(Kb + off);
+                vr[c] = load16_stream(Vb + off);
+            }
         }
     };
     int r0 = row0 + wave * 32;
@@ -783,15 +833,8 @@ void attend_gqa_mfma_kernel(
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const float4 x0 = qraw[t][0], x1 = qraw[t][1];
-        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float xv = xs[e] * qscale;
-            const uint32_t hb = bf16_rne(xv);
-            const uint32_t lb = bf16_rne(xv - __uint_as_float(hb << 16));
-            qb_hi[t][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hb));
-            qb_lo[t][e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lb));
-        }
+        const f32x8 xs = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        split_bf16(xs * qscale, qb_hi[t], qb_lo[t]);
     }
 
     char* my_v = sm_stage + wave * kStage;
@@ -836,15 +879,20 @@ void attend_gqa_mfma_kernel(
                 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb_lo[t], c, 0, 0, 0);
             }
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                sc[tile][rr] = (r0 + 16 * tile + 4 * G + rr < row_end) ? c[rr] : -INFINITY;
+            for (int rr = 0; rr < 4; ++rr) sc[tile][rr] = c[rr];
+        }
+        if (r0 + 32 > row_end) {           // last tile of the chunk (wave-uniform)
+#pragma unroll
+            for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    if (r0 + 16 * tile + 4 * G + rr >= row_end) sc[tile][rr] = -INFINITY;
         }
 
         // online softmax for head hl over these 32 rows
-        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mx = max_over_groups(
+            fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                  fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3]))));
         const float mn = fmaxf(m, mx);
         const float alpha = fast_exp2(m - mn);
         m = mn;
@@ -860,14 +908,8 @@ void attend_gqa_mfma_kernel(
         lpart = fmaf(lpart, alpha, ps);
         // A operand of P.V: k-slot 8G + t <-> tile t / 4, row 4G + t % 4
         bf16x8 pa_hi, pa_lo;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const float pv = pw[t >> 2][t & 3];
-            const uint32_t hb = bf16_rne(pv);
-            const uint32_t lb = bf16_rne(pv - __uint_as_float(hb << 16));
-            pa_hi[t] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hb));
-            pa_lo[t] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lb));
-        }
+        split_bf16(f32x8{pw[0][0], pw[0][1], pw[0][2], pw[0][3], pw[1][0], pw[1][1], pw[1][2], pw[1][3]},
+                   pa_hi, pa_lo);
         // rescale the accumulator: output row 4G + rr is head (4G + rr) % GROUP,
         // whose alpha lane (4G + rr) % GROUP holds (its column is that head)
         float ah[GROUP];                   // alpha of every head, wave-uniform
@@ -902,8 +944,7 @@ void attend_gqa_mfma_kernel(
     }
 
     // l: sum over the four G groups (lanes whose columns repeat a head repeat it)
-    lpart += __shfl_xor(lpart, 16);
-    lpart += __shfl_xor(lpart, 32);
+    lpart = sum_over_groups(lpart);
 
     // every wave must be done with its staging LDS before it becomes sm_o
     __syncthreads();
