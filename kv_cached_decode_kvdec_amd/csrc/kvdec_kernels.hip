@@ -105,6 +105,18 @@ __device__ __forceinline__ float max_over_groups(float x)
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+__device__ __forceinline__ int wave_sum_int(int x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+    x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+    x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);   // row_half_mirror
+    x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);   // row_mirror
+    const auto a = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(x), static_cast<unsigned>(x), false, false);
+    x = static_cast<int>(a[0] + a[1]);
+    const auto c = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(x), static_cast<unsigned>(x), false, false);
+    return static_cast<int>(c[0] + c[1]);
+}
+
 __device__ __forceinline__ float sum_over_groups(float x)
 {
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -992,8 +1004,7 @@ __global__ __launch_bounds__(256) void merge_kernel(LensSrc<LM> ls, int B, int H
         const int bi = b0 + lane;
         if (bi < b) acc += max(1, (min(max(ls.merge_get(bi) + plus, 0), row_limit) + T - 1) / T);
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
+    acc = wave_sum_int(acc);
     const int len0 = ls.merge_get(b);
     if constexpr (LM == kLensDeviceFused) {
         // the device-fused append's length bump (refused, like kvdec_append,
@@ -1027,8 +1038,7 @@ __global__ __launch_bounds__(256) void merge_kernel(LensSrc<LM> ls, int B, int H
         const int c = c0 + lane;
         if (c < nch) M = fmaxf(M, part_ml[(first + c) * Hq + h].x);
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
+    M = max_over_groups(row_max16(M));
 
     // weights w_c = 2^(m_c - M); sums of w_c l_c and w_c o_c in chunk order
     float Lsum = 0.f, o = 0.f;
@@ -1044,8 +1054,10 @@ __global__ __launch_bounds__(256) void merge_kernel(LensSrc<LM> ls, int B, int H
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
                 if (k0 + j < n) {
-                    const float wk = __shfl(wc, k0 + j);
-                    Lsum = fmaf(__shfl(lc, k0 + j), wk, Lsum);
+                    // chunk c0 + k0 + j's weight and l, from its lane (scalar reads)
+                    const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wc), k0 + j));
+                    const float lk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lc), k0 + j));
+                    Lsum = fmaf(lk, wk, Lsum);
                     o = fmaf(ov[j], wk, o);
                 }
             }
