@@ -1,0 +1,126 @@
+"""Seeded random configurations of the decode step against the f64 oracle.
+
+Each case draws a K/V dtype, a query-head group (1..8), a batch, a length
+law (empty sequences, lengths on and next to 32-row tile and 64-row chunk
+boundaries, short, long and log-uniform mixes), a chunk size, a scale, an
+input magnitude and an entry point (plain attend, the fused append + attend
+for two steps, the fused call at explicit positions, or the paged layout),
+and compares the output with the oracle.  The fused cases also compare the
+cache contents and lengths bit for bit with the oracle's append.  A few
+cases use batches above the one-launch fused limit (512 sequences).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cached_decode_kvdec_amd import binding as B
+from kv_cached_decode_kvdec_amd import inputs as gen
+from kv_cached_decode_kvdec_amd.cache import KVCache, PagedKVCache, to_device, to_host_bits
+
+from helpers import assert_attention_close
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 64
+MODES = ["attend", "fused", "fused_at", "paged"]
+
+
+def _draw_lens(rng, Bsz):
+    law = rng.integers(0, 6)
+    if law == 0:                                  # all empty or nearly
+        return rng.integers(0, 2, size=Bsz)
+    if law == 1:                                  # on and next to tile / chunk boundaries
+        base = rng.choice([32, 64, 96, 128, 256, 512], size=Bsz)
+        return np.maximum(base + rng.integers(-1, 2, size=Bsz), 0)
+    if law == 2:                                  # short
+        return rng.integers(0, 70, size=Bsz)
+    if law == 3:                                  # medium, some empty
+        x = rng.integers(0, 700, size=Bsz)
+        x[rng.random(Bsz) < 0.2] = 0
+        return x
+    if law == 4:                                  # log-uniform up to 2000
+        return np.exp(rng.uniform(0.0, np.log(2000.0), size=Bsz)).astype(np.int64)
+    return np.full(Bsz, int(rng.integers(1, 1500)))   # equal lengths
+
+
+def _rows(rng, shape, dtype, s):
+    x = (rng.standard_normal(shape) * s).astype(np.float32)
+    return x if dtype == "f32" else gen.f32_to_bf16_bits(x)
+
+
+def _case(i):
+    rng = np.random.default_rng(20_000 + i)
+    dtype = ["f32", "bf16"][int(rng.integers(0, 2))]
+    Hkv = int(rng.integers(1, 5))
+    group = int(rng.integers(1, 9))
+    mode = MODES[i % len(MODES)]
+    if i % 16 == 5 and mode != "paged":
+        Bsz = int(rng.integers(513, 600))         # above the one-launch fused batch
+        lens = rng.integers(0, 40, size=Bsz)
+    else:
+        Bsz = int(rng.integers(1, 25))
+        lens = _draw_lens(rng, Bsz)
+    lens = lens.astype(np.int32)
+    T = int(rng.choice([0, 64, 128, 192, 256, 448, 1024]))
+    scale = 0.125 if rng.random() < 0.5 else float(rng.uniform(0.03, 0.3))
+    s = float(rng.choice([0.25, 1.0, 2.0]))
+    return rng, dtype, Hkv, group, mode, Bsz, lens, T, scale, s
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_case(i):
+    rng, dtype, Hkv, group, mode, Bsz, lens, T, scale, s = _case(i)
+    Hq = Hkv * group
+    print(f"case {i}: {mode} {dtype} B={Bsz} Hq={Hq} Hkv={Hkv} T={T} scale={scale:.4f} "
+          f"s={s} lens max {int(lens.max(initial=0))}", file=sys.stderr, flush=True)
+    cap = int(lens.max(initial=0)) + 3
+    cap_pad = gen.padded_rows(cap)
+    K = _rows(rng, (Bsz, Hkv, cap_pad, 64), dtype, s)
+    V = _rows(rng, (Bsz, Hkv, cap_pad, 64), dtype, s)
+    what = f"case {i} ({mode} {dtype} B={Bsz} Hq={Hq} Hkv={Hkv} T={T})"
+
+    if mode == "paged":
+        P = int(rng.choice([16, 32, 64, 128]))
+        max_pages = (cap + P - 1) // P
+        pc = PagedKVCache(Bsz, Hkv, P, num_pages=Bsz * max_pages + 3, max_pages_per_seq=max_pages,
+                          dtype=dtype)
+        pc.load_contiguous(to_device(K), to_device(V), lens)
+        q = (rng.standard_normal((Bsz, Hq, 64)) * s).astype(np.float32)
+        out = pc.attend(to_device(q), scale=scale, chunk_rows=T)
+        torch.cuda.synchronize()
+        assert_attention_close(out.cpu().numpy(), oracle.attend(q, K, V, lens, scale), dtype, what)
+        return
+
+    c = KVCache(Bsz, Hkv, cap, dtype, lens=lens, k=to_device(K), v=to_device(V))
+    if mode == "attend":
+        q = (rng.standard_normal((Bsz, Hq, 64)) * s).astype(np.float32)
+        out = c.attend(to_device(q), scale=scale, chunk_rows=T)
+        torch.cuda.synchronize()
+        assert_attention_close(out.cpu().numpy(), oracle.attend(q, K, V, lens, scale), dtype, what)
+        return
+
+    Kh, Vh, ln = K.copy(), V.copy(), lens.copy()
+    steps = 2 if mode == "fused" else 1
+    for st in range(steps):
+        kn = _rows(rng, (Bsz, Hkv, 64), dtype, s)
+        vn = _rows(rng, (Bsz, Hkv, 64), dtype, s)
+        q = (rng.standard_normal((Bsz, Hq, 64)) * s).astype(np.float32)
+        if mode == "fused":
+            out = c.append_attend(to_device(kn), to_device(vn), to_device(q), scale=scale, chunk_rows=T)
+        else:
+            pos = (rng.random(Bsz) * (ln + 1)).astype(np.int32)   # rewind to any position <= len
+            ln = pos
+            out = c.append_attend_at(pos, to_device(kn), to_device(vn), to_device(q), scale=scale,
+                                     chunk_rows=T)
+        torch.cuda.synchronize()
+        ln = oracle.append(Kh, Vh, kn, vn, ln)
+        assert_attention_close(out.cpu().numpy(), oracle.attend(q, Kh, Vh, ln, scale), dtype,
+                               f"{what} step {st}")
+    assert c.lens() == ln.tolist() and c.lens_dev.cpu().tolist() == ln.tolist()
+    # every row below the lengths is the oracle's; rows the fused call did not
+    # touch keep their bits too (the whole buffer is compared)
+    assert to_host_bits(c.k).tobytes() == Kh.tobytes()
+    assert to_host_bits(c.v).tobytes() == Vh.tobytes()
