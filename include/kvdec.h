@@ -122,7 +122,9 @@ KVDEC_API void kvdec_cache_destroy(kvdec_cache* cache);
  * [0, capacity]). */
 KVDEC_API int32_t kvdec_reset_lens(kvdec_cache* cache, const int32_t* lens_host, void* stream);
 
-/* Copy the host mirror of the lengths into lens_out[batch] (host).  No device access. */
+/* Copy the host mirror of the lengths into lens_out[batch] (host).  No device
+ * access.  Errors: KVDEC_E_INVALID (also while the mirror is unknown after
+ * leaving replay mode; see kvdec_set_replay_mode). */
 KVDEC_API int32_t kvdec_get_lens(const kvdec_cache* cache, int32_t* lens_out);
 
 /*
@@ -347,7 +349,12 @@ KVDEC_API int32_t kvdec_paged_attend(const kvdec_paged* paged, const float* q, i
  * kvdec_append does not check capacity on the host in replay mode; on the
  * device an append to a full linear cache writes nothing and leaves the
  * length unchanged (a ring never fills).  kvdec_reset_lens keeps working and
- * is capturable.  Errors: KVDEC_E_INVALID.
+ * is capturable.  Leaving replay mode (0) on a dynamic cache forgets the host
+ * mirror, since replays may have appended: until kvdec_reset_lens,
+ * kvdec_seed or kvdec_append_attend_at sets the lengths again, calls that
+ * size launches or check capacity from the mirror (kvdec_append,
+ * kvdec_append_rope, kvdec_attend_self, kvdec_append_attend) and
+ * kvdec_get_lens fail with KVDEC_E_INVALID.  Errors: KVDEC_E_INVALID.
  */
 KVDEC_API int32_t kvdec_set_replay_mode(kvdec_cache* cache, int32_t chunk_rows);
 

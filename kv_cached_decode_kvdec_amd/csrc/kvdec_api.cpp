@@ -28,6 +28,11 @@ struct kvdec_cache {
     int32_t cap_pad;
     std::vector<int32_t> lens;   // host mirror of d.lens
     int32_t replay_chunk = 0;    // > 0: replay mode with this fixed chunk size
+    // false after replay mode was left on a dynamic cache: replays may have
+    // advanced the device lengths, so the mirror is not used until the
+    // caller sets the lengths again (kvdec_reset_lens, kvdec_seed,
+    // kvdec_append_attend_at)
+    bool lens_known = true;
 };
 
 namespace {
@@ -236,10 +241,22 @@ AttendView view_of(const kvdec_cache* c)
     return v;
 }
 
+// Calls outside replay mode size their launches (and check capacity) from
+// the host mirror, so they need it to match the device lengths.
+int32_t check_mirror(const kvdec_cache* c)
+{
+    if (c->replay_chunk == 0 && !c->lens_known)
+        return fail(KVDEC_E_INVALID, "lengths unknown after leaving replay mode: set them with "
+                    "kvdec_reset_lens (or kvdec_seed, kvdec_append_attend_at) first");
+    return KVDEC_OK;
+}
+
 int32_t attend_common(const kvdec_cache* c, const float* q, int32_t n_q_heads, float scale,
                       int32_t chunk_rows, float* out, void* ws, size_t ws_bytes, void* stream)
 {
     if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
+    const int32_t rc = check_mirror(c);
+    if (rc) return rc;
     return attend_view(view_of(c), q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
 }
 
@@ -247,6 +264,8 @@ int32_t check_append(const kvdec_cache* c, const void* k_new, const void* v_new)
 {
     if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
     if (c->d.is_static) return fail(KVDEC_E_STATIC, "append on a static (encoder) cache");
+    const int32_t rc = check_mirror(c);
+    if (rc) return rc;
     if (!aligned16(k_new) || !aligned16(v_new))
         return fail(KVDEC_E_INVALID, "k_new and v_new must be non-NULL, 16-byte aligned device pointers");
     for (int32_t b = 0; b < c->d.batch && c->replay_chunk == 0; ++b) {
@@ -287,6 +306,7 @@ int32_t append_attend_from(kvdec_cache* c, const std::vector<int32_t>& pre, bool
                                                         static_cast<hipStream_t>(stream));
             if (e != hipSuccess) return hip_fail(e, "set lengths");
             c->lens = pre;             // mirror and device agree even if the attend launch fails
+            c->lens_known = true;
         }
         v.fused_device = true;
     } else {
@@ -300,6 +320,7 @@ int32_t append_attend_from(kvdec_cache* c, const std::vector<int32_t>& pre, bool
     if (rc) return rc;
     c->lens = pre;
     for (auto& l : c->lens) ++l;
+    if (set_device) c->lens_known = true;     // the positions came from the caller
     return KVDEC_OK;
 }
 
@@ -367,6 +388,7 @@ int32_t kvdec_reset_lens(kvdec_cache* c, const int32_t* lens_host, void* stream)
                                                 static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "set lengths");
     c->lens.assign(lens_host, lens_host + c->d.batch);
+    c->lens_known = true;
     return KVDEC_OK;
 }
 
@@ -374,6 +396,8 @@ int32_t kvdec_get_lens(const kvdec_cache* c, int32_t* lens_out)
 {
     g_err.clear();
     if (!c || !lens_out) return fail(KVDEC_E_INVALID, "cache and lens_out must not be NULL");
+    if (!c->lens_known)
+        return fail(KVDEC_E_INVALID, "lengths unknown after leaving replay mode (kvdec_reset_lens sets them)");
     std::memcpy(lens_out, c->lens.data(), sizeof(int32_t) * c->lens.size());
     return KVDEC_OK;
 }
@@ -394,6 +418,7 @@ int32_t kvdec_seed(kvdec_cache* c, const void* k_tok, const void* v_tok, int32_t
     e = kvdec::launch_set_lens(c->d.lens, l.data(), c->d.batch, s);
     if (e != hipSuccess) return hip_fail(e, "set lengths");
     c->lens = l;
+    c->lens_known = true;
     return KVDEC_OK;
 }
 
@@ -476,6 +501,9 @@ int32_t kvdec_set_replay_mode(kvdec_cache* c, int32_t chunk_rows)
                             chunk_rows % 64 != 0))
         return fail(KVDEC_E_INVALID, "chunk_rows %d must be 0, KVDEC_REPLAY_AUTO or a multiple of "
                     "64 in [%d, %d]", chunk_rows, KVDEC_MIN_CHUNK, KVDEC_MAX_CHUNK);
+    // leaving replay mode: replays may have appended on the device, which
+    // the mirror does not see (a static cache takes no appends)
+    if (chunk_rows == 0 && c->replay_chunk > 0 && !c->d.is_static) c->lens_known = false;
     c->replay_chunk = chunk_rows;
     return KVDEC_OK;
 }

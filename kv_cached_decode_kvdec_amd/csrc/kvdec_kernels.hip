@@ -168,6 +168,11 @@ __device__ __forceinline__ uint4 load16_stream(const char* p)
 // consecutive indices starting at the exclusive prefix sum (an empty
 // sequence keeps one chunk with no rows, which writes its zero row).  Done by one wave with a
 // 64-wide scan per group of 64 sequences; all lanes return the same values.
+// A grid of exactly B workgroups (along x) means every sequence has one
+// chunk (the launch sizes the grid as the sum of the chunk counts, each at
+// least 1, from the same lengths the kernel reads; in replay mode the grid
+// has B workgroups only when the row limit fits one chunk): then chunk blk
+// is sequence blk and no scan is needed.
 struct Located {
     int b, c, len, nch;
 };
@@ -232,6 +237,14 @@ template <int LM>
 __device__ __forceinline__ bool locate(const LensSrc<LM>& ls, int B, int T, int cap, int blk,
                                        int lane, Located& r)
 {
+    if (static_cast<int>(gridDim.x) == B) {
+        const int ln = min(max(ls.get(blk) + LensSrc<LM>::kPlus, 0), cap);
+        r.b = blk;
+        r.c = 0;
+        r.len = __builtin_amdgcn_readfirstlane(ln);
+        r.nch = __builtin_amdgcn_readfirstlane(max(1, (ln + T - 1) / T));
+        return true;
+    }
     int base = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
         const int bi = b0 + lane;

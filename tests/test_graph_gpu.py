@@ -142,3 +142,49 @@ def test_replay_fused_append_refused_at_capacity(dtype, Hq, Hkv):
     want = [cap, 43]
     assert one.lens_dev.cpu().tolist() == want and two.lens_dev.cpu().tolist() == want
     assert torch.equal(one.k, two.k) and torch.equal(one.v, two.v)
+
+
+def test_leaving_replay_mode_needs_lengths_again():
+    """Replays append on the device without the host mirror seeing it, so a
+    dynamic cache that leaves replay mode refuses mirror-sized calls until
+    its lengths are set again; a static cache keeps working."""
+    from kv_cached_decode_kvdec_amd import binding as B
+    rng = np.random.default_rng(93)
+    Bsz, Hkv, Hq, cap = 3, 2, 4, 300
+    lens = np.array([10, 0, 130], np.int32)
+    cp = gen.padded_rows(cap)
+    K = _rows(rng, (Bsz, Hkv, cp, 64), "f32")
+    V = _rows(rng, (Bsz, Hkv, cp, 64), "f32")
+    c = KVCache(Bsz, Hkv, cap, "f32", lens=lens, k=to_device(K), v=to_device(V))
+    st = KVCache(Bsz, Hkv, cap, "f32", static=True, lens=lens, k=to_device(K), v=to_device(V))
+    c.set_replay_mode(64)
+    st.set_replay_mode(64)
+    g = torch.cuda.CUDAGraph()
+    kn = to_device(_rows(rng, (Bsz, Hkv, 64), "f32"))
+    vn = to_device(_rows(rng, (Bsz, Hkv, 64), "f32"))
+    with torch.cuda.graph(g):
+        c.append(kn, vn)
+    for _ in range(4):                      # four appends the mirror does not see
+        g.replay()
+    torch.cuda.synchronize()
+    c.set_replay_mode(0)
+    st.set_replay_mode(0)
+    q = to_device(rng.standard_normal((Bsz, Hq, 64), dtype=np.float32))
+    for call in (lambda: c.attend(q), lambda: c.append(kn, vn), lambda: c.lens(),
+                 lambda: c.append_attend(kn, vn, q)):
+        with pytest.raises(B.KvdecError) as e:
+            call()
+        assert e.value.code == B.KVDEC_E_INVALID
+    st.attend(q)                            # static: no appends, mirror still valid
+    dev = c.lens_dev.cpu().numpy()
+    assert dev.tolist() == (lens + 4).tolist()
+    c.reset_lens(dev)
+    out = c.attend(q)
+    torch.cuda.synchronize()
+    Kh, Vh = K.copy(), V.copy()
+    kh, vh = kn.cpu().numpy(), vn.cpu().numpy()
+    for b in range(Bsz):
+        Kh[b, :, lens[b]:lens[b] + 4] = kh[b][:, None, :]
+        Vh[b, :, lens[b]:lens[b] + 4] = vh[b][:, None, :]
+    assert_attention_close(out.cpu().numpy(), oracle.attend(q.cpu().numpy(), Kh, Vh, dev), "f32",
+                           "after reset_lens")
