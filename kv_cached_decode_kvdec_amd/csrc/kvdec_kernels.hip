@@ -105,6 +105,31 @@ __device__ __forceinline__ float max_over_groups(float x)
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// The values of lane l and lane l ^ 8 / 16 / 32, ordered (lower lane, upper
+// lane), so both lanes of a pair see the same two values in the same order:
+// xor 8 by a DPP row rotation, xor 16 and 32 by the gfx950 lane swaps.
+__device__ __forceinline__ void lane_pair8(float x, int lane, float& x0, float& x1)
+{
+    const float p = dpp<0x128>(x);     // row_ror:8 -> lane ^ 8 within each row of 16
+    const bool up = lane & 8;
+    x0 = up ? p : x;
+    x1 = up ? x : p;
+}
+
+__device__ __forceinline__ void lane_pair16(float x, float& x0, float& x1)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x0 = __uint_as_float(a[0]);
+    x1 = __uint_as_float(a[1]);
+}
+
+__device__ __forceinline__ void lane_pair32(float x, float& x0, float& x1)
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x0 = __uint_as_float(a[0]);
+    x1 = __uint_as_float(a[1]);
+}
+
 __device__ __forceinline__ int wave_sum_int(int x)
 {
     x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
@@ -233,6 +258,21 @@ struct LensSrc<kLensDeviceFused> {
     __device__ __forceinline__ int merge_get(int b) const { return snap[b]; }
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave, without LDS: a
+// Hillis-Steele scan inside each 16-lane row (DPP row shifts; lanes whose
+// source falls off the row add 0), then row 15's total is added to row 1
+// and row 3, and lane 31's to rows 2 and 3 (DPP row broadcasts).
+__device__ __forceinline__ int wave_inclusive_sum(int x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1 and 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2 and 3
+    return x;
+}
+
 template <int LM>
 __device__ __forceinline__ bool locate(const LensSrc<LM>& ls, int B, int T, int cap, int blk,
                                        int lane, Located& r)
@@ -250,23 +290,17 @@ __device__ __forceinline__ bool locate(const LensSrc<LM>& ls, int B, int T, int 
         const int bi = b0 + lane;
         const int ln = bi < B ? min(max(ls.get(bi) + LensSrc<LM>::kPlus, 0), cap) : 0;
         const int cnt = bi < B ? max(1, (ln + T - 1) / T) : 0;
-        int incl = cnt;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int t = __shfl_up(incl, d);
-            if (lane >= d) incl += t;
-        }
-        const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+        const int incl = wave_inclusive_sum(cnt);
+        // lane values read with readlane are wave-uniform (scalar registers),
+        // so the row bounds derived from them stay scalar too
+        const int total = __builtin_amdgcn_readlane(incl, 63);
         if (blk < base + total) {
             const unsigned long long m = __ballot(incl > blk - base);
             const int first = __ffsll(static_cast<long long>(m)) - 1;
-            // equal on every lane; readfirstlane (here and on `total`) lets the
-            // compiler keep them, and the row bounds derived from them, in
-            // scalar registers
             r.b = b0 + first;
-            r.c = __builtin_amdgcn_readfirstlane(blk - base - __shfl(incl - cnt, first));
-            r.len = __builtin_amdgcn_readfirstlane(__shfl(ln, first));
-            r.nch = __builtin_amdgcn_readfirstlane(__shfl(cnt, first));
+            r.c = blk - base - __builtin_amdgcn_readlane(incl - cnt, first);
+            r.len = __builtin_amdgcn_readlane(ln, first);
+            r.nch = __builtin_amdgcn_readlane(cnt, first);
             return true;
         }
         base += total;
@@ -706,24 +740,31 @@ void attend_kernel(
         }
     }
 
-    // Merge the RPI row slots of the wave (lanes with equal `part`).
-#pragma unroll
-    for (int msk = LPR; msk < 64; msk <<= 1) {
+    // Merge the RPI row slots of the wave (lanes with equal `part`): at each
+    // step a lane and its partner lane ^ msk combine the same (lower lane,
+    // upper lane) pair, moved without LDS.
+    auto merge_step = [&](auto pair) {
 #pragma unroll
         for (int i = 0; i < GROUP; ++i) {
-            const float m2 = __shfl_xor(m[i], msk);
-            const float l2 = __shfl_xor(l[i], msk);
-            const float mn = fmaxf(m[i], m2);
-            const float a = fast_exp2(m[i] - mn), c2 = fast_exp2(m2 - mn);
-            l[i] = l[i] * a + l2 * c2;
+            float m0, m1, l0, l1;
+            pair(m[i], m0, m1);
+            pair(l[i], l0, l1);
+            const float mn = fmaxf(m0, m1);
+            const float a0 = fast_exp2(m0 - mn), a1 = fast_exp2(m1 - mn);
+            l[i] = l0 * a0 + l1 * a1;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
-                const float o2 = __shfl_xor(o[i][e], msk);
-                o[i][e] = o[i][e] * a + o2 * c2;
+                float o0, o1;
+                pair(o[i][e], o0, o1);
+                o[i][e] = o0 * a0 + o1 * a1;
             }
             m[i] = mn;
         }
-    }
+    };
+    if constexpr (LPR == 8)
+        merge_step([lane](float x, float& x0, float& x1) { lane_pair8(x, lane, x0, x1); });
+    merge_step([](float x, float& x0, float& x1) { lane_pair16(x, x0, x1); });
+    merge_step([](float x, float& x0, float& x1) { lane_pair32(x, x0, x1); });
 
     // Merge the waves through LDS, then write the output (single-chunk
     // sequence) or the chunk partial.
