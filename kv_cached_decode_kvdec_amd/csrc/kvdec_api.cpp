@@ -96,11 +96,17 @@ int64_t chunks_for(const std::vector<int32_t>& lens, int32_t T)
 //  - one chunk per sequence when the (sequence, KV head) pairs alone give at
 //    least R/2 workgroups and lengths are within 2x of their mean: even work
 //    per workgroup and no merge launch;
-//  - otherwise the largest power of two in [64, 4096] that still gives about
-//    one full residency round (>= 0.85 R workgroups), so ragged lengths
-//    balance over the CUs while the merge traffic stays well under 1% of the
-//    K/V bytes.
-int32_t auto_chunk(const std::vector<int32_t>& lens, int32_t n_kv_heads, int64_t resident)
+//  - otherwise chunks of about 128 KB of K and V rows (256 f32 / 512 bf16
+//    rows), halved while the grid would have fewer than R/4 workgroups.
+//    Sweeps over 64..2048 rows put the fastest chunk at ~128 KB for ragged
+//    and for equal lengths alike (qwen2-0.5b f32: 256 rows; gqa bf16: 512;
+//    whisper-base cross f32: 256); smaller chunks pay per-workgroup set-up
+//    and merge work, larger ones balance ragged lengths worse.  Short
+//    sequences need the R/4 floor (whisper-base self: 64 rows).
+constexpr int32_t kChunkBytes = 128 * 1024;
+
+int32_t auto_chunk(const std::vector<int32_t>& lens, int32_t n_kv_heads, int32_t esz,
+                   int64_t resident)
 {
     if (resident <= 0) resident = 2048;
     int64_t total = 0;
@@ -116,10 +122,10 @@ int32_t auto_chunk(const std::vector<int32_t>& lens, int32_t n_kv_heads, int64_t
         while (T < longest) T <<= 1;
         return T;
     }
-    const int64_t target = resident * 85 / 100;
-    for (int32_t T = KVDEC_MAX_CHUNK; T > KVDEC_MIN_CHUNK; T >>= 1)
-        if (chunks_for(lens, T) * n_kv_heads >= target) return T;
-    return KVDEC_MIN_CHUNK;
+    int32_t T = kChunkBytes / (2 * KVDEC_HEAD_DIM * esz);
+    const int64_t min_blocks = resident / 4;
+    while (T > KVDEC_MIN_CHUNK && chunks_for(lens, T) * n_kv_heads < min_blocks) T >>= 1;
+    return T;
 }
 
 int64_t max_chunks(const kvdec_cache* c)
@@ -200,7 +206,7 @@ int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, floa
         a.need_merge = per_seq > 1;
     } else {
         a.chunk_rows = chunk_rows ? chunk_rows
-                                  : auto_chunk(v.rows, v.n_kv_heads,
+                                  : auto_chunk(v.rows, v.n_kv_heads, esz_of(v.dtype),
                                                kvdec::resident_attend_blocks(v.dtype, group));
         a.n_chunks = chunks_for(v.rows, a.chunk_rows);
         a.need_merge = a.n_chunks > v.batch;   // some sequence has more than one chunk
@@ -493,7 +499,7 @@ int32_t kvdec_set_replay_mode(kvdec_cache* c, int32_t chunk_rows)
     if (chunk_rows == KVDEC_REPLAY_AUTO) {
         // the automatic choice for the current lengths, with the query-head
         // group of a plain MHA call (the grid shape does not depend on it)
-        c->replay_chunk = auto_chunk(attended_rows(c), c->d.n_kv_heads,
+        c->replay_chunk = auto_chunk(attended_rows(c), c->d.n_kv_heads, esz_of(c->d.dtype),
                                      kvdec::resident_attend_blocks(c->d.dtype, 1));
         return KVDEC_OK;
     }
