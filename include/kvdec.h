@@ -24,6 +24,10 @@
  *     kvdec_last_error() describes the failure (thread-local string).
  *   - head_dim is 64.  K/V elements are IEEE binary32 (KVDEC_F32) or
  *     bfloat16 bit patterns (KVDEC_BF16); q and out are always binary32.
+ *   - A handle keeps a host mirror of its lengths: calls on one handle must
+ *     not overlap from several host threads (distinct handles are
+ *     independent), and calls that touch the same cache or workspace must be
+ *     ordered on the device (one stream, or events between streams).
  */
 #ifndef KVDEC_H
 #define KVDEC_H
