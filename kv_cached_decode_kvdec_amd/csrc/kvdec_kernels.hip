@@ -9,9 +9,12 @@
 //             Each 16-byte lane load covers 4 f32 / 8 bf16 dims of a row; a
 //             row's dot product is finished with DPP butterflies inside the
 //             16-lane (f32) or 8-lane (bf16) row group; softmax is online
-//             per row slot with exp2 (scale * log2 e folded into q).  A
-//             sequence that fits one chunk is finished in place; otherwise
-//             each workgroup stores its partial (m, l, o[64]).
+//             per row slot with exp2 (scale * log2 e applied to each
+//             score).  bf16 K/V with 2..8 query heads per KV head runs on
+//             MFMA instead (scores and P.V as 16x16x32 bf16 products, q and
+//             P split into bf16 hi + lo parts).  A sequence that fits one
+//             chunk is finished in place; otherwise each workgroup stores
+//             its partial (m, l, o[64]).
 //   merge   : log-sum-exp merge of the chunk partials of every
 //             (sequence, query head) whose length spans more than one chunk
 //             (a second launch, only when some sequence has several chunks:

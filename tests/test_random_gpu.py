@@ -7,7 +7,12 @@ input magnitude and an entry point (plain attend, the fused append + attend
 for two steps, the fused call at explicit positions, or the paged layout),
 and compares the output with the oracle.  The fused cases also compare the
 cache contents and lengths bit for bit with the oracle's append.  A few
-cases use batches above the one-launch fused limit (512 sequences).
+cases use batches above the one-launch fused limit (512 sequences).  Ring
+cases (window == capacity) run the fused step, or the fused step at
+explicit positions, on a sliding-window cache whose lengths may exceed the
+window: the new row goes to slot len % W and the oracle attends the first
+min(len + 1, W) rows of the ring buffer (attention does not depend on row
+order).
 """
 import sys
 
@@ -24,8 +29,8 @@ from helpers import assert_attention_close
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 64
-MODES = ["attend", "fused", "fused_at", "paged"]
+N_CASES = 96
+MODES = ["attend", "fused", "fused_at", "paged", "ring", "ring_at"]
 
 
 def _draw_lens(rng, Bsz):
@@ -57,7 +62,7 @@ def _case(i):
     Hkv = int(rng.integers(1, 5))
     group = int(rng.integers(1, 9))
     mode = MODES[i % len(MODES)]
-    if i % 16 == 5 and mode != "paged":
+    if i % 16 == 5 and mode in ("attend", "fused", "fused_at"):
         Bsz = int(rng.integers(513, 600))         # above the one-launch fused batch
         lens = rng.integers(0, 40, size=Bsz)
     else:
@@ -76,7 +81,11 @@ def test_random_case(i):
     Hq = Hkv * group
     print(f"case {i}: {mode} {dtype} B={Bsz} Hq={Hq} Hkv={Hkv} T={T} scale={scale:.4f} "
           f"s={s} lens max {int(lens.max(initial=0))}", file=sys.stderr, flush=True)
-    cap = int(lens.max(initial=0)) + 3
+    if mode.startswith("ring"):
+        cap = int(rng.integers(40, 700))          # the window; lengths may exceed it
+        lens = (lens * rng.uniform(0.5, 2.5)).astype(np.int32)
+    else:
+        cap = int(lens.max(initial=0)) + 3
     cap_pad = gen.padded_rows(cap)
     K = _rows(rng, (Bsz, Hkv, cap_pad, 64), dtype, s)
     V = _rows(rng, (Bsz, Hkv, cap_pad, 64), dtype, s)
@@ -92,6 +101,33 @@ def test_random_case(i):
         out = pc.attend(to_device(q), scale=scale, chunk_rows=T)
         torch.cuda.synchronize()
         assert_attention_close(out.cpu().numpy(), oracle.attend(q, K, V, lens, scale), dtype, what)
+        return
+
+    if mode.startswith("ring"):
+        W = cap
+        c = KVCache(Bsz, Hkv, W, dtype, lens=lens, k=to_device(K), v=to_device(V), window=W)
+        Kh, Vh, ln = K.copy(), V.copy(), lens.copy()
+        for st in range(2 if mode == "ring" else 1):
+            kn = _rows(rng, (Bsz, Hkv, 64), dtype, s)
+            vn = _rows(rng, (Bsz, Hkv, 64), dtype, s)
+            q = (rng.standard_normal((Bsz, Hq, 64)) * s).astype(np.float32)
+            if mode == "ring":
+                out = c.append_attend(to_device(kn), to_device(vn), to_device(q), scale=scale,
+                                      chunk_rows=T)
+            else:
+                ln = (rng.random(Bsz) * (ln + 1)).astype(np.int32)
+                out = c.append_attend_at(ln, to_device(kn), to_device(vn), to_device(q),
+                                         scale=scale, chunk_rows=T)
+            torch.cuda.synchronize()
+            for b in range(Bsz):                   # the ring placement of the new row
+                Kh[b, :, ln[b] % W] = kn[b]
+                Vh[b, :, ln[b] % W] = vn[b]
+            ln = ln + 1
+            ref = oracle.attend(q, Kh, Vh, np.minimum(ln, W).astype(np.int32), scale)
+            assert_attention_close(out.cpu().numpy(), ref, dtype, f"{what} W={W} step {st}")
+        assert c.lens() == ln.tolist() and c.lens_dev.cpu().tolist() == ln.tolist()
+        assert to_host_bits(c.k).tobytes() == Kh.tobytes()
+        assert to_host_bits(c.v).tobytes() == Vh.tobytes()
         return
 
     c = KVCache(Bsz, Hkv, cap, dtype, lens=lens, k=to_device(K), v=to_device(V))
