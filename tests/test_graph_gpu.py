@@ -20,11 +20,15 @@ def _rows(rng, shape, dtype):
     return x if dtype == "f32" else gen.f32_to_bf16_bits(x)
 
 
+@pytest.mark.parametrize("rchunk", [64, 256])
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("dtype,Hq,Hkv,cross,window", [("f32", 6, 6, True, 0),
                                                         ("bf16", 16, 4, False, 0),
                                                         ("bf16", 8, 8, False, 128)])
-def test_graph_replayed_multilayer_step(dtype, Hq, Hkv, cross, window, fused):
+def test_graph_replayed_multilayer_step(dtype, Hq, Hkv, cross, window, fused, rchunk):
+    """rchunk 64 splits the 200-row caches over several chunks; 256 holds a
+    whole linear cache in one chunk, so the replayed grid has one workgroup
+    per sequence and KV head (the direct chunk lookup)."""
     rng = np.random.default_rng(7 + Hq)
     L, B, T, enc = 3, 2, 9, 300
     cap = 200 if window == 0 else window
@@ -43,7 +47,7 @@ def test_graph_replayed_multilayer_step(dtype, Hq, Hkv, cross, window, fused):
                 ck[b, :, slot] = hk[b, :, t]
                 cv[b, :, slot] = hv[b, :, t]
         sc = KVCache(B, Hkv, cap, dtype, lens=start, k=to_device(ck), v=to_device(cv), window=window)
-        sc.set_replay_mode(64)
+        sc.set_replay_mode(rchunk)
         lay = dict(hk=hk, hv=hv, sc=sc, kn=to_device(np.zeros((B, Hkv, 64), hk.dtype)),
                    vn=to_device(np.zeros((B, Hkv, 64), hk.dtype)),
                    q=torch.zeros(B, Hq, 64, device="cuda"), out=torch.zeros(B, Hq, 64, device="cuda"))
@@ -67,7 +71,7 @@ def test_graph_replayed_multilayer_step(dtype, Hq, Hkv, cross, window, fused):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for lay in layers:
-            if fused:   # replay mode: attend launch + merge launch (which bumps the lengths)
+            if fused:   # replay mode: lengths read from and bumped on the device
                 lay["sc"].append_attend(lay["kn"], lay["vn"], lay["q"], out=lay["out"])
             else:
                 lay["sc"].append(lay["kn"], lay["vn"])
@@ -115,11 +119,13 @@ def test_graph_replayed_multilayer_step(dtype, Hq, Hkv, cross, window, fused):
         assert layers[0]["sc"].lens_dev.cpu().tolist() == lens.tolist()
 
 
+@pytest.mark.parametrize("rchunk", [64, 192])
 @pytest.mark.parametrize("dtype,Hq,Hkv", [("f32", 4, 4), ("bf16", 8, 2)])
-def test_replay_fused_append_refused_at_capacity(dtype, Hq, Hkv):
+def test_replay_fused_append_refused_at_capacity(dtype, Hq, Hkv, rchunk):
     """Replay mode cannot check capacity on the host; like kvdec_append, the
     fused call then stores nothing and keeps the length once a linear cache
-    is full, and attends the full cache."""
+    is full, and attends the full cache (with 64-row chunks and with one
+    chunk per sequence)."""
     rng = np.random.default_rng(91)
     B, cap = 2, 130
     start = np.array([cap - 1, 40], np.int32)
@@ -129,7 +135,7 @@ def test_replay_fused_append_refused_at_capacity(dtype, Hq, Hkv):
     mk = lambda: KVCache(B, Hkv, cap, dtype, lens=start, k=to_device(K), v=to_device(V))
     two, one = mk(), mk()
     for c in (two, one):
-        c.set_replay_mode(64)
+        c.set_replay_mode(rchunk)
     for s in range(3):
         kn = to_device(_rows(rng, (B, Hkv, 64), dtype))
         vn = to_device(_rows(rng, (B, Hkv, 64), dtype))
