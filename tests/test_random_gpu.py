@@ -12,7 +12,9 @@ cases (window == capacity) run the fused step, or the fused step at
 explicit positions, on a sliding-window cache whose lengths may exceed the
 window: the new row goes to slot len % W and the oracle attends the first
 min(len + 1, W) rows of the ring buffer (attention does not depend on row
-order).
+order).  Cross cases seed a static cache from token-major encoder rows
+(kvdec_seed) and attend it with grouped query heads; the seeded bytes are
+compared with the oracle's head-first permute.
 """
 import sys
 
@@ -29,8 +31,8 @@ from helpers import assert_attention_close
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 96
-MODES = ["attend", "fused", "fused_at", "paged", "ring", "ring_at"]
+N_CASES = 112
+MODES = ["attend", "fused", "fused_at", "paged", "ring", "ring_at", "cross"]
 
 
 def _draw_lens(rng, Bsz):
@@ -81,6 +83,28 @@ def test_random_case(i):
     Hq = Hkv * group
     print(f"case {i}: {mode} {dtype} B={Bsz} Hq={Hq} Hkv={Hkv} T={T} scale={scale:.4f} "
           f"s={s} lens max {int(lens.max(initial=0))}", file=sys.stderr, flush=True)
+    if mode == "cross":
+        rows = int(rng.integers(1, 1600))         # encoder rows
+        cap = rows + int(rng.integers(0, 70))
+        ktok = _rows(rng, (Bsz, rows, Hkv * 64), dtype, s)
+        vtok = _rows(rng, (Bsz, rows, Hkv * 64), dtype, s)
+        c = KVCache(Bsz, Hkv, cap, dtype, static=True, lens=[0] * Bsz)
+        c.seed(to_device(ktok), to_device(vtok))
+        K = np.zeros((Bsz, Hkv, gen.padded_rows(cap), 64), ktok.dtype)
+        V = np.zeros_like(K)
+        oracle.seed(K, ktok)
+        oracle.seed(V, vtok)
+        q = (rng.standard_normal((Bsz, Hq, 64)) * s).astype(np.float32)
+        out = c.attend(to_device(q), scale=scale, chunk_rows=T)
+        torch.cuda.synchronize()
+        n = np.full(Bsz, rows, np.int32)
+        what = f"case {i} (cross {dtype} B={Bsz} Hq={Hq} Hkv={Hkv} T={T} rows={rows})"
+        assert_attention_close(out.cpu().numpy(), oracle.attend(q, K, V, n, scale), dtype, what)
+        assert c.lens() == n.tolist() and c.lens_dev.cpu().tolist() == n.tolist()
+        kd, vd = to_host_bits(c.k), to_host_bits(c.v)
+        assert kd[:, :, :rows].tobytes() == K[:, :, :rows].tobytes()
+        assert vd[:, :, :rows].tobytes() == V[:, :, :rows].tobytes()
+        return
     if mode.startswith("ring"):
         cap = int(rng.integers(40, 700))          # the window; lengths may exceed it
         lens = (lens * rng.uniform(0.5, 2.5)).astype(np.int32)
