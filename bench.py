@@ -495,6 +495,71 @@ def cpu_baseline(name, target_s=12.0):
             "cpu_model": cpu, "machine": platform.machine()}
 
 
+def _oracle_slice_worker(name, b0, b1, n_steps, barrier, results):
+    """One worker of cpu_baseline_all_cores: the oracle on sequences [b0, b1)."""
+    import oracle
+    from kv_cached_decode_kvdec_amd import inputs as gen
+    wl = gen.WORKLOADS[name]
+    full = gen.draw_lens(np.random.default_rng(wl.seed), wl.lens, wl.batch)
+    inp = gen.make_inputs(wl, batch=b1 - b0, lens=full[b0:b1], canary=False)
+    nb = b1 - b0
+    if wl.cross:
+        cK = np.zeros((nb, wl.n_kv_heads, gen.padded_rows(gen.ENC_LEN), 64), inp.k_cache.dtype)
+        cV = np.zeros_like(cK)
+        oracle.seed(cK, inp.cross_k_tok)
+        oracle.seed(cV, inp.cross_v_tok)
+        clens = np.full(nb, gen.ENC_LEN, np.int32)
+    Kh, Vh = inp.k_cache, inp.v_cache
+    barrier.wait()
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        s = i % wl.steps
+        if s == 0:
+            lens = inp.lens.copy()
+        lens = oracle.append(Kh, Vh, inp.k_new[s], inp.v_new[s], lens)
+        oracle.attend(inp.q_self[s], Kh, Vh, lens)
+        if wl.cross:
+            oracle.attend(inp.q_cross[s], cK, cV, clens)
+    results.put(time.perf_counter() - t0)
+
+
+def cpu_baseline_all_cores(name, single_rate, workers, target_s=10.0):
+    """The same oracle on `workers` host cores: one process per core, each
+    running whole decode steps for its share of the sequences (the oracle is
+    per sequence, so the shares are independent).  Throughput = steps / the
+    slowest worker's time; started together at a barrier."""
+    import multiprocessing as mp
+    from kv_cached_decode_kvdec_amd import inputs as gen
+    wl = gen.WORKLOADS[name]
+    workers = max(1, min(workers, wl.batch))
+    n_steps = max(wl.steps, int(target_s * single_rate * workers * 0.8))
+    bounds = np.linspace(0, wl.batch, workers + 1).astype(int)
+    ctx = mp.get_context("spawn")            # fresh interpreters: no GPU state in the workers
+    barrier, results = ctx.Barrier(workers), ctx.Queue()
+    procs = [ctx.Process(target=_oracle_slice_worker,
+                         args=(name, int(bounds[i]), int(bounds[i + 1]), n_steps, barrier, results))
+             for i in range(workers)]
+    for p in procs:
+        p.start()
+    times = []
+    deadline = time.time() + 600
+    while len(times) < workers:
+        try:
+            times.append(results.get(timeout=1.0))
+        except Exception:                    # queue empty: check that no worker died
+            dead = [p.exitcode for p in procs if p.exitcode not in (None, 0)]
+            if dead or time.time() > deadline:
+                for p in procs:
+                    p.kill()
+                raise RuntimeError(f"oracle worker failed (exit codes {dead}) or timed out")
+    for p in procs:
+        p.join()
+    el = max(times)
+    return {"value": n_steps / el, "unit": "steps/s", "cores": workers, "kind": "oracle",
+            "sample": f"{n_steps} whole decode steps of {name}, the {wl.batch} sequences split "
+                      f"over {workers} processes (one per core), f64 C oracle, {el:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -505,6 +570,9 @@ def main():
                     help="comma list of extra workloads to report on stderr/JSON, or 'none'")
     ap.add_argument("--cold-steps", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-workers", type=int, default=16,
+                    help="host cores for the all-cores oracle baseline (capped by the CPU count; "
+                         "1 skips it)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay measurement")
     ap.add_argument("--variants", default="qwen2-0.5b+paged16,gqa+paged16,qwen2-0.5b+rope,"
@@ -622,6 +690,13 @@ def main():
         line["cpu_baseline"] = cpu_baseline(head)
         log(f"cpu baseline: {line['cpu_baseline']['value']:.3f} steps/s "
             f"({time.time() - t0:.0f}s incl. input generation)")
+        if args.cpu_workers > 1:
+            t0 = time.time()
+            workers = min(args.cpu_workers, os.cpu_count() or 1)
+            line["cpu_baseline_all_cores"] = cpu_baseline_all_cores(
+                head, line["cpu_baseline"]["value"], workers)
+            log(f"cpu baseline on {line['cpu_baseline_all_cores']['cores']} cores: "
+                f"{line['cpu_baseline_all_cores']['value']:.2f} steps/s ({time.time() - t0:.0f}s)")
     print(json.dumps(line), flush=True)
 
 
