@@ -199,11 +199,15 @@ class Bench:
             "effective_gbps": step_bytes / wall / 1e9,
             "attend_launches": len(att_ms),
             "attend_avg_us": 1e3 * float(np.mean(att_ms)),
-            "attend_us_p10_p50_p90": [round(1e3 * float(x), 2)
-                                      for x in np.percentile(att_ms, [10, 50, 90])],
+            # per call kind (with cross-attention the entries alternate self, cross)
+            "self_attend_us_p10_p50_p90": [round(1e3 * float(x), 2) for x in np.percentile(
+                att_ms[0::n_ev - 1], [10, 50, 90])],
             "attend_gbps": float(np.sum(att_bytes)) / (float(np.sum(att_ms)) * 1e-3) / 1e9,
             "attend_bytes_per_launch": float(np.mean(att_bytes)),
         }
+        if self.cross is not None:
+            res["cross_attend_us_p10_p50_p90"] = [round(1e3 * float(x), 2) for x in np.percentile(
+                att_ms[1::2], [10, 50, 90])]
         res["pct_of_hbm_peak"] = 100.0 * res["effective_gbps"] / HBM_PEAK_GBPS
         res["attend_frac"] = res["attend_gbps"] / HBM_PEAK_GBPS
         if cold_steps:
