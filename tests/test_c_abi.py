@@ -1,0 +1,28 @@
+"""The boundary from C: tests/c/abi_check.c, compiled as C99 with gcc against
+include/kvdec.h and linked to libkvdec.so, runs the argument checks that
+return before any device work (no GPU needed)."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from kv_cached_decode_kvdec_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not installed")
+def test_c99_program_links_and_runs(tmp_path):
+    lib_dir = os.path.dirname(B.LIB_PATH)
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail(f"{B.LIB_PATH} is missing: build it first")
+    exe = tmp_path / "abi_check"
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+           "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c", "abi_check.c"),
+           "-L", lib_dir, "-lkvdec", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)]
+    built = subprocess.run(cmd, capture_output=True, text=True)
+    assert built.returncode == 0, built.stderr
+    ran = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert ran.returncode == 0, ran.stdout + ran.stderr
+    assert ran.stdout.strip() == "0 failed"
