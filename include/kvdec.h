@@ -268,8 +268,10 @@ KVDEC_API int32_t kvdec_attend_cross(const kvdec_cache* cache, const float* q, i
  * allocation failure nothing changes).  The library keeps the page
  * allocator (a host-side free list) and host mirrors of the lengths and
  * block tables; the caller owns every device buffer.
- *   k_pages, v_pages : (device) [num_pages][n_kv_heads][page_rows][64] elements
- *                      of dtype: one (page, KV head) is a contiguous run of rows
+ *   k_pages, v_pages : (device) [n_kv_heads][num_pages][page_rows][64] elements
+ *                      of dtype, head-major: one page id covers every KV head,
+ *                      one (KV head, page) is a contiguous run of rows, and
+ *                      consecutive pages of one head are adjacent
  *   block_table      : (device) int32 [batch][max_pages_per_seq]; written by
  *                      the library's appends, never read past a sequence's pages
  *   lens             : (device) int32 [batch], all zero after create

@@ -189,7 +189,7 @@ class PagedKVCache:
         self.max_pages = int(max_pages_per_seq)
         self.dtype = dtype
         tdt = _TORCH_DTYPE[dtype]
-        shape = (self.num_pages, self.n_kv_heads, self.page_rows, B.HEAD_DIM)
+        shape = (self.n_kv_heads, self.num_pages, self.page_rows, B.HEAD_DIM)   # head-major pool
         self.k = torch.zeros(shape, dtype=tdt, device=device)
         self.v = torch.zeros(shape, dtype=tdt, device=device)
         self.table_dev = torch.full((self.batch, self.max_pages), -1, dtype=torch.int32,
@@ -238,8 +238,8 @@ class PagedKVCache:
             n = int(n)
             for i in range((n + P - 1) // P):
                 rows = min(P, n - i * P)
-                self.k[table[b][i], :, :rows] = k[b, :, i * P:i * P + rows]
-                self.v[table[b][i], :, :rows] = v[b, :, i * P:i * P + rows]
+                self.k[:, table[b][i], :rows] = k[b, :, i * P:i * P + rows]
+                self.v[:, table[b][i], :rows] = v[b, :, i * P:i * P + rows]
 
     def attend(self, q, scale=0.125, chunk_rows=0, out=None):
         Hq = q.shape[1]

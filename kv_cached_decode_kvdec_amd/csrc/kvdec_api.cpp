@@ -143,7 +143,7 @@ struct AttendView {
     std::vector<int32_t> rows;     // rows attended per sequence (host mirror)
     int64_t max_chunks;            // workspace sizing bound
     const int32_t* table = nullptr;
-    int32_t table_stride = 0, pshift = 0;
+    int32_t table_stride = 0, pshift = 0, num_pages = 0;
     // append fused into the attend launch
     const int32_t* fused_lens = nullptr;   // pre-append lengths (host mirror)
     bool fused_device = false;             // append fused, lengths from the device
@@ -218,6 +218,7 @@ int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, floa
     a.table = v.table;
     a.table_stride = v.table_stride;
     a.pshift = v.pshift;
+    a.num_pages = v.num_pages;
     a.fused_lens = v.fused_lens;
     a.fused_device = v.fused_device;
     if (v.fused_device) a.need_merge = true;   // the merge launch bumps the lengths
@@ -587,7 +588,7 @@ int32_t kvdec_paged_append(kvdec_paged* p, const void* k_new, const void* v_new,
         }
     const hipError_t e = kvdec::launch_paged_append(
         p->d.dtype, p->d.k_pages, p->d.v_pages, k_new, v_new, p->d.lens, p->d.block_table,
-        p->d.max_pages_per_seq, p->d.batch, p->d.n_kv_heads, p->pshift, fresh.data(),
+        p->d.max_pages_per_seq, p->d.batch, p->d.n_kv_heads, p->pshift, p->d.num_pages, fresh.data(),
         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
         for (int32_t b = p->d.batch - 1; b >= 0; --b)
@@ -729,6 +730,7 @@ int32_t kvdec_paged_attend(const kvdec_paged* p, const float* q, int32_t n_q_hea
     v.table = p->d.block_table;
     v.table_stride = p->d.max_pages_per_seq;
     v.pshift = p->pshift;
+    v.num_pages = p->d.num_pages;
     return attend_view(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
 }
 

@@ -47,6 +47,7 @@ struct AttendArgs {
     const int32_t* table = nullptr;
     int32_t table_stride = 0;
     int32_t pshift = 0;
+    int32_t num_pages = 0;      // pages in the pool (head-major pool)
     // append fused into the launch (fused_lens != nullptr): pre-append
     // lengths (host), new rows, the device lengths to bump, ring window
     const int32_t* fused_lens = nullptr;
@@ -74,7 +75,8 @@ hipError_t launch_append_rope(int dtype, void* k, void* v, const void* k_new, co
 hipError_t launch_paged_append(int dtype, void* k_pages, void* v_pages, const void* k_new,
                                const void* v_new, int32_t* lens, int32_t* table,
                                int32_t table_stride, int32_t batch, int32_t n_kv_heads,
-                               int32_t pshift, const int32_t* new_pages, hipStream_t s);
+                               int32_t pshift, int32_t num_pages, const int32_t* new_pages,
+                               hipStream_t s);
 hipError_t launch_paged_reserve(int32_t* table, int32_t table_stride, int32_t* lens, int32_t seq,
                                 const int32_t* pages, int32_t n_pages, int32_t len, hipStream_t s);
 hipError_t launch_seed(int dtype, void* k, void* v, const void* k_tok, const void* v_tok,

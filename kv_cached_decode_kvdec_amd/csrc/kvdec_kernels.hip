@@ -382,13 +382,17 @@ __device__ __forceinline__ void finish_block(const float (&sm_o)[WAVES][GROUP][k
 
 
 // Paged layout: row r of (sequence b, KV head g) lives in page
-// table[b * table_stride + (r >> pshift)], slot r & (2^pshift - 1); a page is
-// [n_kv_heads][2^pshift rows][64].  A workgroup stages the page ids of its
-// chunk in LDS once, then addresses rows from them.
+// table[b * table_stride + (r >> pshift)], slot r & (2^pshift - 1).  The pool
+// is head-major, [n_kv_heads][num_pages][2^pshift rows][64]: one page id
+// covers every KV head, and consecutive page ids of one head are adjacent,
+// so a sequence whose pages were taken in order reads each head as one
+// stream.  A workgroup stages the page ids of its chunk in LDS once, then
+// addresses rows from them.
 struct PageMap {
     const int32_t* table;   // device block table (nullptr: contiguous layout)
     int stride;             // entries per sequence
     int pshift;             // log2(rows per page)
+    int num_pages;          // pages in the pool
 };
 
 constexpr int kMaxChunkPages = KVDEC_MAX_CHUNK / 16 + 1;
@@ -413,7 +417,7 @@ __device__ __forceinline__ size_t row_offset(const PageMap& pm, const int* sm_pa
 {
     if constexpr (PAGED) {
         const int page = sm_pages[(r >> pm.pshift) - (row0 >> pm.pshift)];
-        const size_t rows = ((static_cast<size_t>(page) * Hkv + g) << pm.pshift) +
+        const size_t rows = ((static_cast<size_t>(g) * pm.num_pages + page) << pm.pshift) +
                             (r & ((1 << pm.pshift) - 1));
         return rows * RB;
     } else {
@@ -536,7 +540,7 @@ __global__ __launch_bounds__(256) void append_rope_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// paged append: a page pool [num_pages][n_kv_heads][2^pshift rows][64] and a
+// paged append: a page pool [n_kv_heads][num_pages][2^pshift rows][64] and a
 // block table per sequence (the paged cache of whisper-apr 0.3.3
 // decoder_generated.rs, `PagedDecoderKVCache`: page = position / page size,
 // slot = position % page size).  When a sequence's row lands at the start of
@@ -547,7 +551,7 @@ template <int ROW_BYTES>
 __global__ __launch_bounds__(256) void paged_append_kernel(
     char* __restrict__ Kp, char* __restrict__ Vp, const char* __restrict__ kn,
     const char* __restrict__ vn, int32_t* __restrict__ lens, int32_t* __restrict__ table,
-    int table_stride, int Hkv, int pshift, int b0, PageBlock new_pages)
+    int table_stride, int Hkv, int pshift, int num_pages, int b0, PageBlock new_pages)
 {
     constexpr int VPR = ROW_BYTES / 16;
     const int b = b0 + blockIdx.x;
@@ -571,7 +575,7 @@ __global__ __launch_bounds__(256) void paged_append_kernel(
         const int tt = isv ? t - n : t;
         const int g = tt / VPR, w = tt - g * VPR;
         const size_t hg = static_cast<size_t>(b) * Hkv + g;
-        const size_t row = ((static_cast<size_t>(page) * Hkv + g) << pshift) + slot;
+        const size_t row = ((static_cast<size_t>(g) * num_pages + page) << pshift) + slot;
         const uint4* src = reinterpret_cast<const uint4*>((isv ? vn : kn) + hg * ROW_BYTES) + w;
         uint4* dst = reinterpret_cast<uint4*>((isv ? Vp : Kp) + row * ROW_BYTES) + w;
         *dst = *src;
@@ -1190,7 +1194,8 @@ hipError_t launch_append_rope(int dtype, void* k, void* v, const void* k_new, co
 hipError_t launch_paged_append(int dtype, void* k_pages, void* v_pages, const void* k_new,
                                const void* v_new, int32_t* lens, int32_t* table,
                                int32_t table_stride, int32_t batch, int32_t n_kv_heads,
-                               int32_t pshift, const int32_t* new_pages, hipStream_t s)
+                               int32_t pshift, int32_t num_pages, const int32_t* new_pages,
+                               hipStream_t s)
 {
     for (int32_t b0 = 0; b0 < batch; b0 += kPagesPerLaunch) {
         const int32_t cnt = (batch - b0) < kPagesPerLaunch ? (batch - b0) : kPagesPerLaunch;
@@ -1201,12 +1206,12 @@ hipError_t launch_paged_append(int dtype, void* k_pages, void* v_pages, const vo
             hipLaunchKernelGGL(paged_append_kernel<256>, grid, block, 0, s,
                                static_cast<char*>(k_pages), static_cast<char*>(v_pages),
                                static_cast<const char*>(k_new), static_cast<const char*>(v_new),
-                               lens, table, table_stride, n_kv_heads, pshift, b0, blk);
+                               lens, table, table_stride, n_kv_heads, pshift, num_pages, b0, blk);
         else
             hipLaunchKernelGGL(paged_append_kernel<128>, grid, block, 0, s,
                                static_cast<char*>(k_pages), static_cast<char*>(v_pages),
                                static_cast<const char*>(k_new), static_cast<const char*>(v_new),
-                               lens, table, table_stride, n_kv_heads, pshift, b0, blk);
+                               lens, table, table_stride, n_kv_heads, pshift, num_pages, b0, blk);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1263,7 +1268,7 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
     char* ws = static_cast<char*>(a.ws);
     float* po = reinterpret_cast<float*>(ws + a.part.o_offset);
     float2* pml = reinterpret_cast<float2*>(ws + a.part.ml_offset);
-    const PageMap pm{a.table, a.table_stride, a.pshift};
+    const PageMap pm{a.table, a.table_stride, a.pshift, a.num_pages};
     LensSrc<LM> ls;
     if constexpr (LM == kLensDevice) {
         ls.lens = a.lens;

@@ -75,8 +75,8 @@ def test_paged_parity_and_pool_contents(dtype, Hq, Hkv, P):
     for b in range(Bsz):
         for r, (kr, vr) in enumerate(hist[b]):
             page, slot = table[b][r // P], r % P
-            assert kp[page, :, slot].tobytes() == kr.tobytes()
-            assert vp[page, :, slot].tobytes() == vr.tobytes()
+            assert kp[:, page, slot].tobytes() == kr.tobytes()
+            assert vp[:, page, slot].tobytes() == vr.tobytes()
 
 
 def test_paged_allocator_limits_change_nothing():
