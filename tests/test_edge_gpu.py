@@ -6,7 +6,9 @@
   in 32 groups of 64; most sequences fit one chunk, some span two);
 - the fused append at exactly its largest batch (512), where it still runs as
   one launch;
-- group 8 over a single KV head with a ragged batch, through the fused call.
+- group 8 over a single KV head with a ragged batch, through the fused call;
+- 48 KV heads (the launch grid's second dimension) in both kernel families;
+- two independent caches driven on two streams at once.
 """
 import sys
 
@@ -93,3 +95,66 @@ def test_fused_append_at_its_batch_limits(Bsz):
     assert to_host_bits(c.k).tobytes() == Kh.tobytes()
     assert to_host_bits(c.v).tobytes() == Vh.tobytes()
     assert c.lens() == ln.tolist() and c.lens_dev.cpu().tolist() == ln.tolist()
+
+
+def test_many_kv_heads():
+    """48 KV heads (grid y) with two query heads each, bf16 (MFMA) and f32 (VALU)."""
+    for dtype in ("bf16", "f32"):
+        rng = np.random.default_rng(84)
+        Bsz, Hkv, Hq = 3, 48, 96
+        lens = np.array([300, 0, 777], np.int32)
+        cap = gen.padded_rows(int(lens.max()) + 1)
+        K = _rows(rng, (Bsz, Hkv, cap, 64), dtype)
+        V = _rows(rng, (Bsz, Hkv, cap, 64), dtype)
+        q = rng.standard_normal((Bsz, Hq, 64), dtype=np.float32)
+        _log(f"{Hkv} KV heads, {dtype}")
+        c = KVCache(Bsz, Hkv, cap, dtype, lens=lens, k=to_device(K), v=to_device(V))
+        ref = oracle.attend(q, K, V, lens)
+        for T in (64, 0):
+            out = c.attend(to_device(q), chunk_rows=T)
+            torch.cuda.synchronize()
+            assert_attention_close(out.cpu().numpy(), ref, dtype, f"{dtype} Hkv={Hkv} T={T}")
+
+
+def test_independent_caches_on_two_streams():
+    """The library keeps no state outside its handles: two caches driven on two
+    streams at once (append + attend, fused and not) give the oracle's results."""
+    rng = np.random.default_rng(85)
+    setups = []
+    for dtype, Hkv, Hq, Bsz in (("f32", 4, 8, 7), ("bf16", 2, 8, 9)):
+        lens = rng.integers(50, 900, size=Bsz).astype(np.int32)
+        cap = gen.padded_rows(int(lens.max()) + 4)
+        K = _rows(rng, (Bsz, Hkv, cap, 64), dtype)
+        V = _rows(rng, (Bsz, Hkv, cap, 64), dtype)
+        setups.append(dict(dtype=dtype, Hkv=Hkv, Hq=Hq, B=Bsz, lens=lens, K=K, V=V, cap=cap))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    caches, refs, outs = [], [], []
+    for st, s in zip(streams, setups):
+        with torch.cuda.stream(st):
+            caches.append(KVCache(s["B"], s["Hkv"], s["cap"], s["dtype"], lens=s["lens"],
+                                  k=to_device(s["K"]), v=to_device(s["V"])))
+    torch.cuda.synchronize()
+    for step in range(3):
+        inputs = []
+        for s in setups:
+            kn = _rows(rng, (s["B"], s["Hkv"], 64), s["dtype"])
+            vn = _rows(rng, (s["B"], s["Hkv"], 64), s["dtype"])
+            q = rng.standard_normal((s["B"], s["Hq"], 64), dtype=np.float32)
+            inputs.append((kn, vn, q, to_device(kn), to_device(vn), to_device(q)))
+        torch.cuda.synchronize()
+        outs = []
+        for st, c, (kn, vn, q, dkn, dvn, dq) in zip(streams, caches, inputs):
+            with torch.cuda.stream(st):
+                if step % 2 == 0:
+                    outs.append(c.append_attend(dkn, dvn, dq, chunk_rows=64))
+                else:
+                    c.append(dkn, dvn)
+                    outs.append(c.attend(dq, chunk_rows=128))
+        torch.cuda.synchronize()
+        for s, out, (kn, vn, q, *_rest) in zip(setups, outs, inputs):
+            s["lens"] = oracle.append(s["K"], s["V"], kn, vn, s["lens"])
+            ref = oracle.attend(q, s["K"], s["V"], s["lens"])
+            assert_attention_close(out.cpu().numpy(), ref, s["dtype"], f"{s['dtype']} step {step}")
+    for s, c in zip(setups, caches):
+        assert to_host_bits(c.k).tobytes() == s["K"].tobytes()
+        assert c.lens() == s["lens"].tolist()
