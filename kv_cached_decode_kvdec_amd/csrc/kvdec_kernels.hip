@@ -1262,6 +1262,43 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kUnroll = 4;
 
+constexpr int kWideWaves = 16;
+
+// 16-wave workgroups of this VALU kernel resident at once on the device, or
+// -1 when fewer than two fit on a CU (occupancy query, once per
+// instantiation).
+template <int GROUP, bool PAGED, int LM>
+int wide_resident()
+{
+    static std::atomic<int> known{0};       // 0: not asked yet
+    int k = known.load(std::memory_order_relaxed);
+    if (k == 0) {
+        int per_cu = 0, dev = 0, cus = 0;
+        const bool ok =
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, reinterpret_cast<const void*>(&attend_kernel<4, GROUP, kWideWaves, kUnroll, PAGED, LM>),
+                kWideWaves * 64, 0) == hipSuccess &&
+            hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
+        k = (ok && per_cu >= 2 && cus > 0) ? per_cu * cus : -1;
+        known.store(k, std::memory_order_relaxed);
+    }
+    return k;
+}
+
+// The merge launch after an attend launch, when some sequence spans several chunks.
+template <int LM>
+hipError_t launch_merge(const AttendArgs& a, int group, const LensSrc<LM>& ls, float* po,
+                        float2* pml, hipStream_t s)
+{
+    if (!a.need_merge) return hipSuccess;
+    const int Hq = a.n_kv_heads * group;
+    const int waves = a.batch * Hq;
+    hipLaunchKernelGGL((merge_kernel<LM>), dim3((waves + 3) / 4), dim3(256), 0, s, ls, a.batch,
+                       Hq, a.chunk_rows, a.row_limit, po, pml, a.out);
+    return hipGetLastError();
+}
+
 template <int ESZ, int GROUP, bool PAGED, int LM>
 hipError_t attend_t(const AttendArgs& a, hipStream_t s)
 {
@@ -1287,6 +1324,24 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
         ls.f.window = a.window;
     }
     const dim3 grid(static_cast<unsigned>(a.n_chunks), a.n_kv_heads), block(kWaves * 64);
+    hipError_t e = hipSuccess;
+    if constexpr (ESZ == 4 && GROUP <= 2) {
+        // f32 with 1 or 2 query heads per KV head: chunks of >= 256 rows run
+        // on 16-wave workgroups (each wave one pass of 16 rows) where two of
+        // them fit on a CU and the grid fills at least four residency rounds
+        // of them (with fewer, the last partial round costs more than the
+        // wide workgroups gain: whisper-base's cross-attention, 1.5 rounds)
+        const int rw = wide_resident<GROUP, PAGED, LM>();
+        if (a.chunk_rows >= kWideWaves * kUnroll * Lay<4>::kRPI && rw > 0 &&
+            a.n_chunks * a.n_kv_heads >= 4 * static_cast<int64_t>(rw)) {
+            hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWideWaves, kUnroll, PAGED, LM>), grid,
+                               dim3(kWideWaves * 64), 0, s, a.q, static_cast<const char*>(a.k),
+                               static_cast<const char*>(a.v), ls, a.batch, a.n_kv_heads, a.cap_pad,
+                               a.row_limit, a.chunk_rows, a.qscale, a.out, po, pml, pm);
+            e = hipGetLastError();
+            return e != hipSuccess ? e : launch_merge<LM>(a, GROUP, ls, po, pml, s);
+        }
+    }
     if constexpr (ESZ == 2 && GROUP >= 2)
         hipLaunchKernelGGL((attend_gqa_mfma_kernel<GROUP, kWaves, PAGED, LM>), grid, block, 0, s,
                            a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v), ls,
@@ -1297,13 +1352,8 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
                            0, s, a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v),
                            ls, a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows,
                            a.qscale, a.out, po, pml, pm);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !a.need_merge) return e;
-    const int Hq = a.n_kv_heads * GROUP;
-    const int waves = a.batch * Hq;
-    hipLaunchKernelGGL((merge_kernel<LM>), dim3((waves + 3) / 4), dim3(256), 0, s, ls, a.batch,
-                       Hq, a.chunk_rows, a.row_limit, po, pml, a.out);
-    return hipGetLastError();
+    e = hipGetLastError();
+    return e != hipSuccess ? e : launch_merge<LM>(a, GROUP, ls, po, pml, s);
 }
 
 template <int ESZ, bool PAGED, int LM>

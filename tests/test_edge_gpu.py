@@ -8,7 +8,8 @@
   one launch;
 - group 8 over a single KV head with a ragged batch, through the fused call;
 - 48 KV heads (the launch grid's second dimension) in both kernel families;
-- two independent caches driven on two streams at once.
+- two independent caches driven on two streams at once;
+- f32 launches large enough for the 16-wave workgroups (plain, fused, paged).
 """
 import sys
 
@@ -19,7 +20,7 @@ import torch
 import oracle
 from kv_cached_decode_kvdec_amd import binding as B
 from kv_cached_decode_kvdec_amd import inputs as gen
-from kv_cached_decode_kvdec_amd.cache import KVCache, to_device, to_host_bits
+from kv_cached_decode_kvdec_amd.cache import KVCache, PagedKVCache, to_device, to_host_bits
 
 from helpers import assert_attention_close
 
@@ -158,3 +159,41 @@ def test_independent_caches_on_two_streams():
     for s, c in zip(setups, caches):
         assert to_host_bits(c.k).tobytes() == s["K"].tobytes()
         assert c.lens() == s["lens"].tolist()
+
+
+@pytest.mark.parametrize("mode", ["attend", "fused", "paged"])
+@pytest.mark.parametrize("group", [1, 2])
+def test_wide_workgroups(group, mode):
+    """f32 with 1 or 2 query heads per KV head and at least four residency
+    rounds of 256-row chunks runs on 16-wave workgroups."""
+    rng = np.random.default_rng(86 + group)
+    Bsz, Hkv = 64, 8
+    Hq = Hkv * group
+    lens = rng.integers(1000, 1500, size=Bsz).astype(np.int32)   # >= 4 chunks each: 2048+ workgroups
+    cap = gen.padded_rows(int(lens.max()) + 1)
+    K = _rows(rng, (Bsz, Hkv, cap, 64), "f32")
+    V = _rows(rng, (Bsz, Hkv, cap, 64), "f32")
+    q = rng.standard_normal((Bsz, Hq, 64), dtype=np.float32)
+    _log(f"wide workgroups: group {group}, {mode}")
+    if mode == "paged":
+        P = 32
+        maxp = cap // P
+        pc = PagedKVCache(Bsz, Hkv, P, num_pages=Bsz * maxp, max_pages_per_seq=maxp, dtype="f32")
+        pc.load_contiguous(to_device(K), to_device(V), lens)
+        out = pc.attend(to_device(q), chunk_rows=256)
+        ref = oracle.attend(q, K, V, lens)
+    elif mode == "attend":
+        c = KVCache(Bsz, Hkv, cap, "f32", lens=lens, k=to_device(K), v=to_device(V))
+        out = c.attend(to_device(q), chunk_rows=256)
+        ref = oracle.attend(q, K, V, lens)
+    else:
+        c = KVCache(Bsz, Hkv, cap, "f32", lens=lens, k=to_device(K), v=to_device(V))
+        kn = _rows(rng, (Bsz, Hkv, 64), "f32")
+        vn = _rows(rng, (Bsz, Hkv, 64), "f32")
+        out = c.append_attend(to_device(kn), to_device(vn), to_device(q), chunk_rows=256)
+        ln = oracle.append(K, V, kn, vn, lens)
+        ref = oracle.attend(q, K, V, ln)
+    torch.cuda.synchronize()
+    assert_attention_close(out.cpu().numpy(), ref, "f32", f"wide group {group} {mode}")
+    if mode == "fused":
+        assert to_host_bits(c.k).tobytes() == K.tobytes()
