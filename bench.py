@@ -301,7 +301,9 @@ def measured_traffic(workload):
 class VariantBench(Bench):
     """The same workload through one of the other cache forms:
       paged<P>    : paged pool with P-row pages (block table read per chunk),
-                    lengths rolled back each cycle with kvdec_paged_truncate;
+                    through kvdec_paged_append_attend (the append fused into
+                    the attend launch); lengths rolled back each cycle with
+                    kvdec_paged_truncate;
       rope        : kvdec_append_rope (key and query rotated at the position)
                     instead of a plain append, then kvdec_attend_self;
       window<W>   : sliding-window ring of W rows (attends the last W tokens),
@@ -362,7 +364,7 @@ class VariantBench(Bench):
         self.self_bytes, self.step_bytes = [], []
         for s in range(self.S):
             post = rows_attended(self.lens0 + s + 1)
-            fused_store = new_row_bytes(wl) if variant.startswith("window") else 0
+            fused_store = new_row_bytes(wl) if variant.startswith(("window", "paged")) else 0
             self.self_bytes.append(attend_bytes(wl, post) + fused_store)
             self.step_bytes.append(attend_bytes(wl, post) + 2 * new_row_bytes(wl))
         self.cross_bytes = 0
@@ -392,12 +394,10 @@ class VariantBench(Bench):
             if s == 0:
                 rc = lib.kvdec_paged_truncate(h, self.lens0_c, st)
                 assert rc == 0, lib.kvdec_last_error()
-            rc = lib.kvdec_paged_append(h, self.p_kn[s], self.p_vn[s], st)
-            assert rc == 0, lib.kvdec_last_error()
             if events is not None:
                 events[0].record()
-            rc = lib.kvdec_paged_attend(h, self.p_q[s], Hq, 0.125, 0, self.p_out, self.p_ws,
-                                        self.n_ws, st)
+            rc = lib.kvdec_paged_append_attend(h, self.p_kn[s], self.p_vn[s], self.p_q[s], Hq, 0.125,
+                                               0, self.p_out, self.p_ws, self.n_ws, st)
             assert rc == 0, lib.kvdec_last_error()
             if events is not None:
                 events[1].record()

@@ -66,6 +66,7 @@ typedef enum { KVDEC_F32 = 0, KVDEC_BF16 = 1 } kvdec_dtype;
 #define KVDEC_MAX_GROUP 8      /* query heads per KV head supported */
 #define KVDEC_REPLAY_AUTO (-1) /* kvdec_set_replay_mode: pick the chunk from current lengths */
 #define KVDEC_MAX_FUSED_BATCH 512 /* largest batch kvdec_append_attend runs as one launch */
+#define KVDEC_MAX_PAGED_FUSED_BATCH 256 /* largest batch kvdec_paged_append_attend runs as one launch */
 
 /* Opaque host-side handle: the cache description plus a host mirror of the
  * per-sequence lengths (used for validation and launch sizing, so no call
@@ -339,6 +340,26 @@ KVDEC_API size_t kvdec_paged_workspace_bytes(const kvdec_paged* paged, int32_t n
 KVDEC_API int32_t kvdec_paged_attend(const kvdec_paged* paged, const float* q, int32_t n_q_heads,
                            float scale, int32_t chunk_rows, float* out, void* ws, size_t ws_bytes,
                            void* stream);
+
+/*
+ * kvdec_paged_append then kvdec_paged_attend, as one call (the one-launch
+ * decode step of kvdec_append_attend for the paged layout): pages are taken
+ * exactly as kvdec_paged_append takes them, and output, pool rows, block
+ * table and lengths are bitwise those of the two calls.  Up to
+ * KVDEC_MAX_PAGED_FUSED_BATCH sequences run as one attend launch (plus the
+ * merge when a sequence spans several chunks): the pre-append lengths and
+ * each sequence's fresh page (if its new row starts one) go to the kernel by
+ * value, the workgroup holding the new row's slot stores it, and head 0's
+ * workgroup gives the block table the fresh page and bumps the length.
+ * Larger batches run the two calls.  Arguments as kvdec_paged_append and
+ * kvdec_paged_attend; every check runs before anything changes.  Errors:
+ * theirs (KVDEC_E_INVALID, KVDEC_E_SHAPE, KVDEC_E_OVERFLOW,
+ * KVDEC_E_WORKSPACE, KVDEC_E_HIP; a failed launch returns the pages taken).
+ */
+KVDEC_API int32_t kvdec_paged_append_attend(kvdec_paged* paged, const void* k_new, const void* v_new,
+                                            const float* q, int32_t n_q_heads, float scale,
+                                            int32_t chunk_rows, float* out, void* ws, size_t ws_bytes,
+                                            void* stream);
 
 /*
  * Replay mode, for decode steps captured once in a HIP graph and replayed

@@ -25,6 +25,7 @@ MIN_CHUNK = 64
 MAX_CHUNK = 4096
 MAX_GROUP = 8
 KVDEC_MAX_FUSED_BATCH = 512
+KVDEC_MAX_PAGED_FUSED_BATCH = 256
 
 EXPORTED = [
     "kvdec_padded_capacity", "kvdec_cache_create", "kvdec_cache_destroy", "kvdec_reset_lens",
@@ -36,6 +37,7 @@ EXPORTED = [
     "kvdec_paged_release", "kvdec_paged_reserve", "kvdec_paged_truncate",
     "kvdec_paged_get_lens", "kvdec_paged_get_table",
     "kvdec_paged_free_pages", "kvdec_paged_workspace_bytes", "kvdec_paged_attend",
+    "kvdec_paged_append_attend",
 ]
 
 
@@ -103,6 +105,8 @@ def load():
         "kvdec_paged_free_pages": (_i32, [_vp]),
         "kvdec_paged_workspace_bytes": (_sz, [_vp, _i32]),
         "kvdec_paged_attend": (_i32, [_vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz, _vp]),
+        "kvdec_paged_append_attend": (_i32, [_vp, _vp, _vp, _vp, _i32, ctypes.c_float, _i32, _vp,
+                                             _vp, _sz, _vp]),
         "kvdec_status_str": (ctypes.c_char_p, [_i32]),
         "kvdec_last_error": (ctypes.c_char_p, []),
     }
@@ -241,6 +245,13 @@ def kvdec_paged_attend(handle, q_ptr, n_q_heads, scale, chunk_rows, out_ptr, ws_
                        stream=None):
     _check(load().kvdec_paged_attend(handle, q_ptr, int(n_q_heads), float(scale), int(chunk_rows),
                                      out_ptr, ws_ptr, int(ws_bytes), stream), "kvdec_paged_attend")
+
+
+def kvdec_paged_append_attend(handle, k_new_ptr, v_new_ptr, q_ptr, n_q_heads, scale, chunk_rows,
+                              out_ptr, ws_ptr, ws_bytes, stream=None):
+    _check(load().kvdec_paged_append_attend(handle, k_new_ptr, v_new_ptr, q_ptr, int(n_q_heads),
+                                            float(scale), int(chunk_rows), out_ptr, ws_ptr,
+                                            int(ws_bytes), stream), "kvdec_paged_append_attend")
 
 
 def kvdec_append_attend(handle, k_new_ptr, v_new_ptr, q_ptr, n_q_heads, scale, chunk_rows, out_ptr,

@@ -241,16 +241,33 @@ class PagedKVCache:
                 self.k[:, table[b][i], :rows] = k[b, :, i * P:i * P + rows]
                 self.v[:, table[b][i], :rows] = v[b, :, i * P:i * P + rows]
 
+    def workspace(self, n_q_heads):
+        ws = self._ws.get(n_q_heads)
+        if ws is None:
+            ws = torch.empty(B.kvdec_paged_workspace_bytes(self.handle, n_q_heads), dtype=torch.uint8,
+                             device=self.k.device)
+            self._ws[n_q_heads] = ws
+        return ws
+
     def attend(self, q, scale=0.125, chunk_rows=0, out=None):
         Hq = q.shape[1]
         out = KVCache._q_out(self, q, out)
-        ws = self._ws.get(Hq)
-        if ws is None:
-            ws = torch.empty(B.kvdec_paged_workspace_bytes(self.handle, Hq), dtype=torch.uint8,
-                             device=self.k.device)
-            self._ws[Hq] = ws
+        ws = self.workspace(Hq)
         B.kvdec_paged_attend(self.handle, _ptr(q), Hq, scale, chunk_rows, _ptr(out), _ptr(ws),
                              ws.numel(), current_stream())
+        return out
+
+    def append_attend(self, k_new, v_new, q, scale=0.125, chunk_rows=0, out=None):
+        """kvdec_paged_append_attend: append the token, attend len + 1 rows."""
+        shape = (self.batch, self.n_kv_heads, B.HEAD_DIM)
+        for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+            if t.dtype != self.k.dtype or tuple(t.shape) != shape or not t.is_contiguous():
+                raise ValueError(f"{n} must be a contiguous {shape} {self.k.dtype} tensor")
+        Hq = q.shape[1]
+        out = KVCache._q_out(self, q, out)
+        ws = self.workspace(Hq)
+        B.kvdec_paged_append_attend(self.handle, _ptr(k_new), _ptr(v_new), _ptr(q), Hq, scale,
+                                    chunk_rows, _ptr(out), _ptr(ws), ws.numel(), current_stream())
         return out
 
     def close(self):

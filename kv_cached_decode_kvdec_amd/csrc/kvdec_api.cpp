@@ -144,6 +144,7 @@ struct AttendView {
     int64_t max_chunks;            // workspace sizing bound
     const int32_t* table = nullptr;
     int32_t table_stride = 0, pshift = 0, num_pages = 0;
+    const int32_t* fresh_pages = nullptr;  // paged fused append: page of a row that starts one
     // append fused into the attend launch
     const int32_t* fused_lens = nullptr;   // pre-append lengths (host mirror)
     bool fused_device = false;             // append fused, lengths from the device
@@ -219,6 +220,7 @@ int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, floa
     a.table_stride = v.table_stride;
     a.pshift = v.pshift;
     a.num_pages = v.num_pages;
+    a.fresh_pages = v.fresh_pages;
     a.fused_lens = v.fused_lens;
     a.fused_device = v.fused_device;
     if (v.fused_device) a.need_merge = true;   // the merge launch bumps the lengths
@@ -328,6 +330,79 @@ int32_t append_attend_from(kvdec_cache* c, const std::vector<int32_t>& pre, bool
     c->lens = pre;
     for (auto& l : c->lens) ++l;
     if (set_device) c->lens_known = true;     // the positions came from the caller
+    return KVDEC_OK;
+}
+
+}  // namespace
+
+namespace {
+
+AttendView paged_view_of(const kvdec_paged* p)
+{
+    const int64_t cap = static_cast<int64_t>(p->d.max_pages_per_seq) * p->d.page_rows;
+    AttendView v;
+    v.batch = p->d.batch;
+    v.n_kv_heads = p->d.n_kv_heads;
+    v.dtype = p->d.dtype;
+    v.cap_pad = 0;
+    v.row_limit = static_cast<int32_t>(cap);
+    v.replay_chunk = 0;
+    v.k = p->d.k_pages;
+    v.v = p->d.v_pages;
+    v.lens_dev = p->d.lens;
+    v.rows = p->lens;
+    v.max_chunks = p->d.batch * ((cap + KVDEC_MIN_CHUNK - 1) / KVDEC_MIN_CHUNK);
+    v.table = p->d.block_table;
+    v.table_stride = p->d.max_pages_per_seq;
+    v.pshift = p->pshift;
+    v.num_pages = p->d.num_pages;
+    return v;
+}
+
+// Pages for the sequences whose next row starts a page (sequence order,
+// lowest-numbered first), installed in the host mirror of the table;
+// fresh[b] = the page, or -1.  The caller has checked that enough are free.
+std::vector<int32_t> take_fresh_pages(kvdec_paged* p)
+{
+    const int32_t P = p->d.page_rows;
+    std::vector<int32_t> fresh(p->d.batch, -1);
+    for (int32_t b = 0; b < p->d.batch; ++b)
+        if (p->lens[b] % P == 0) {
+            fresh[b] = p->free_pages.back();
+            p->free_pages.pop_back();
+            p->table[static_cast<size_t>(b) * p->d.max_pages_per_seq + p->lens[b] / P] = fresh[b];
+        }
+    return fresh;
+}
+
+void return_fresh_pages(kvdec_paged* p, const std::vector<int32_t>& fresh)
+{
+    const int32_t P = p->d.page_rows;
+    for (int32_t b = p->d.batch - 1; b >= 0; --b)
+        if (fresh[b] >= 0) {
+            p->table[static_cast<size_t>(b) * p->d.max_pages_per_seq + p->lens[b] / P] = -1;
+            p->free_pages.push_back(fresh[b]);
+        }
+}
+
+// Capacity and pool checks of a paged append (nothing changes on failure).
+int32_t check_paged_append(const kvdec_paged* p, const void* k_new, const void* v_new)
+{
+    if (!p) return fail(KVDEC_E_INVALID, "paged cache handle is NULL");
+    if (!aligned16(k_new) || !aligned16(v_new))
+        return fail(KVDEC_E_INVALID, "k_new and v_new must be non-NULL, 16-byte aligned device pointers");
+    const int32_t P = p->d.page_rows;
+    const int64_t cap = static_cast<int64_t>(p->d.max_pages_per_seq) * P;
+    int32_t needed = 0;
+    for (int32_t b = 0; b < p->d.batch; ++b) {
+        if (p->lens[b] + 1 > cap)
+            return fail(KVDEC_E_OVERFLOW, "cache overflow: sequence %d holds %d + 1 > %lld", b,
+                        p->lens[b], static_cast<long long>(cap));
+        if (p->lens[b] % P == 0) ++needed;
+    }
+    if (needed > static_cast<int32_t>(p->free_pages.size()))
+        return fail(KVDEC_E_OVERFLOW, "page pool exhausted: %d new pages needed, %zu free", needed,
+                    p->free_pages.size());
     return KVDEC_OK;
 }
 
@@ -562,40 +637,17 @@ void kvdec_paged_destroy(kvdec_paged* p) { delete p; }
 int32_t kvdec_paged_append(kvdec_paged* p, const void* k_new, const void* v_new, void* stream)
 {
     g_err.clear();
-    if (!p) return fail(KVDEC_E_INVALID, "paged cache handle is NULL");
-    if (!aligned16(k_new) || !aligned16(v_new))
-        return fail(KVDEC_E_INVALID, "k_new and v_new must be non-NULL, 16-byte aligned device pointers");
-    const int32_t P = p->d.page_rows;
-    const int64_t cap = static_cast<int64_t>(p->d.max_pages_per_seq) * P;
-    int32_t needed = 0;
-    for (int32_t b = 0; b < p->d.batch; ++b) {
-        if (p->lens[b] + 1 > cap)
-            return fail(KVDEC_E_OVERFLOW, "cache overflow: sequence %d holds %d + 1 > %lld", b,
-                        p->lens[b], static_cast<long long>(cap));
-        if (p->lens[b] % P == 0) ++needed;
-    }
-    if (needed > static_cast<int32_t>(p->free_pages.size()))
-        return fail(KVDEC_E_OVERFLOW, "page pool exhausted: %d new pages needed, %zu free", needed,
-                    p->free_pages.size());
-    // take pages (sequence order), install them in the host mirror, launch;
-    // on a launch failure give everything back
-    std::vector<int32_t> fresh(p->d.batch, -1);
-    for (int32_t b = 0; b < p->d.batch; ++b)
-        if (p->lens[b] % P == 0) {
-            fresh[b] = p->free_pages.back();
-            p->free_pages.pop_back();
-            p->table[static_cast<size_t>(b) * p->d.max_pages_per_seq + p->lens[b] / P] = fresh[b];
-        }
+    const int32_t rc = check_paged_append(p, k_new, v_new);
+    if (rc) return rc;
+    // take pages, install them in the host mirror, launch; on a launch
+    // failure give everything back
+    const std::vector<int32_t> fresh = take_fresh_pages(p);
     const hipError_t e = kvdec::launch_paged_append(
         p->d.dtype, p->d.k_pages, p->d.v_pages, k_new, v_new, p->d.lens, p->d.block_table,
         p->d.max_pages_per_seq, p->d.batch, p->d.n_kv_heads, p->pshift, p->d.num_pages, fresh.data(),
         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
-        for (int32_t b = p->d.batch - 1; b >= 0; --b)
-            if (fresh[b] >= 0) {
-                p->table[static_cast<size_t>(b) * p->d.max_pages_per_seq + p->lens[b] / P] = -1;
-                p->free_pages.push_back(fresh[b]);
-            }
+        return_fresh_pages(p, fresh);
         return hip_fail(e, "paged append launch");
     }
     for (auto& l : p->lens) ++l;
@@ -714,24 +766,41 @@ int32_t kvdec_paged_attend(const kvdec_paged* p, const float* q, int32_t n_q_hea
 {
     g_err.clear();
     if (!p) return fail(KVDEC_E_INVALID, "paged cache handle is NULL");
-    const int64_t cap = static_cast<int64_t>(p->d.max_pages_per_seq) * p->d.page_rows;
-    AttendView v;
-    v.batch = p->d.batch;
-    v.n_kv_heads = p->d.n_kv_heads;
-    v.dtype = p->d.dtype;
-    v.cap_pad = 0;
-    v.row_limit = static_cast<int32_t>(cap);
-    v.replay_chunk = 0;
-    v.k = p->d.k_pages;
-    v.v = p->d.v_pages;
-    v.lens_dev = p->d.lens;
-    v.rows = p->lens;
-    v.max_chunks = p->d.batch * ((cap + KVDEC_MIN_CHUNK - 1) / KVDEC_MIN_CHUNK);
-    v.table = p->d.block_table;
-    v.table_stride = p->d.max_pages_per_seq;
-    v.pshift = p->pshift;
-    v.num_pages = p->d.num_pages;
-    return attend_view(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
+    return attend_view(paged_view_of(p), q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
+}
+
+int32_t kvdec_paged_append_attend(kvdec_paged* p, const void* k_new, const void* v_new,
+                                  const float* q, int32_t n_q_heads, float scale, int32_t chunk_rows,
+                                  float* out, void* ws, size_t ws_bytes, void* stream)
+{
+    g_err.clear();
+    int32_t rc = check_paged_append(p, k_new, v_new);
+    if (rc) return rc;
+    AttendView v = paged_view_of(p);
+    for (auto& r : v.rows) ++r;                  // rows attended after the append
+    rc = check_attend(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes);
+    if (rc) return rc;
+    if (p->d.batch > KVDEC_MAX_PAGED_FUSED_BATCH) {
+        // two launches: the paged append, then the attend over the new lengths
+        rc = kvdec_paged_append(p, k_new, v_new, stream);
+        if (rc) return rc;
+        return attend_view(paged_view_of(p), q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes,
+                           stream);
+    }
+    const std::vector<int32_t> pre = p->lens;
+    const std::vector<int32_t> fresh = take_fresh_pages(p);
+    v.fused_lens = pre.data();
+    v.fresh_pages = fresh.data();
+    v.k_new = k_new;
+    v.v_new = v_new;
+    v.lens_out = p->d.lens;
+    rc = attend_view(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
+    if (rc) {
+        return_fresh_pages(p, fresh);
+        return rc;
+    }
+    for (auto& l : p->lens) ++l;
+    return KVDEC_OK;
 }
 
 int32_t kvdec_append_attend(kvdec_cache* c, const void* k_new, const void* v_new, const float* q,

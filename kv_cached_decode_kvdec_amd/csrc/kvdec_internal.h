@@ -48,6 +48,9 @@ struct AttendArgs {
     int32_t table_stride = 0;
     int32_t pshift = 0;
     int32_t num_pages = 0;      // pages in the pool (head-major pool)
+    // paged fused append (with table and fused_lens): the page each sequence's
+    // new row starts, -1 where its page is already in the table
+    const int32_t* fresh_pages = nullptr;
     // append fused into the launch (fused_lens != nullptr): pre-append
     // lengths (host), new rows, the device lengths to bump, ring window
     const int32_t* fused_lens = nullptr;

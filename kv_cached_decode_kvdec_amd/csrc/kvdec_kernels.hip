@@ -42,6 +42,7 @@ namespace kvdec {
 namespace {
 
 constexpr int kMaxFusedBatch = KVDEC_MAX_FUSED_BATCH;
+constexpr int kMaxPagedFusedBatch = KVDEC_MAX_PAGED_FUSED_BATCH;
 constexpr float kNegBig = -1.0e30f;   // finite "no row seen yet" running max
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -220,6 +221,7 @@ struct Located {
 constexpr int kLensDevice = 0;
 constexpr int kLensHostFused = 1;
 constexpr int kLensDeviceFused = 2;
+constexpr int kLensPagedFused = 3;   // paged cache, append fused, lengths and fresh pages by value
 
 template <int LM>
 struct LensSrc;
@@ -246,6 +248,27 @@ template <>
 struct LensSrc<kLensHostFused> {
     int32_t v[kMaxFusedBatch];
     FusedRows f;
+    static constexpr int kPlus = 1;
+    __device__ __forceinline__ int get(int b) const { return v[b]; }
+    __device__ __forceinline__ int merge_get(int b) const { return v[b]; }
+};
+
+// the paged fused mode: the new rows go to the page pool through the block
+// table; a sequence whose new row starts a page brings that page's id
+struct PagedFusedRows {
+    const char* k_new;      // [B][Hkv][64] elements
+    const char* v_new;
+    char* K;                // page pools [Hkv][num_pages][page_rows][64]
+    char* V;
+    int32_t* lens_out;      // device lengths, bumped by one per sequence
+    int32_t* table_out;     // device block table, given the fresh pages
+};
+
+template <>
+struct LensSrc<kLensPagedFused> {
+    int32_t v[kMaxPagedFusedBatch];       // pre-append lengths (host mirror)
+    int32_t fresh[kMaxPagedFusedBatch];   // page for a row that starts a page, else -1
+    PagedFusedRows f;
     static constexpr int kPlus = 1;
     __device__ __forceinline__ int get(int b) const { return v[b]; }
     __device__ __forceinline__ int merge_get(int b) const { return v[b]; }
@@ -397,15 +420,53 @@ struct PageMap {
 
 constexpr int kMaxChunkPages = KVDEC_MAX_CHUNK / 16 + 1;
 
+// fresh_idx >= 0: table entry fresh_idx is being given page fresh_page by this
+// launch (the paged fused append); it is taken from there, not read.
 template <bool PAGED>
 __device__ __forceinline__ void stage_pages(const PageMap& pm, int b, int row0, int row_end,
-                                            int* sm_pages)
+                                            int* sm_pages, int fresh_idx = -1, int fresh_page = -1)
 {
     if constexpr (PAGED) {
         const int p0 = row0 >> pm.pshift;
         const int np = row_end > row0 ? ((row_end - 1) >> pm.pshift) - p0 + 1 : 0;
         for (int t = threadIdx.x; t < np; t += blockDim.x)
-            sm_pages[t] = pm.table[static_cast<size_t>(b) * pm.stride + p0 + t];
+            sm_pages[t] = p0 + t == fresh_idx ? fresh_page
+                                              : pm.table[static_cast<size_t>(b) * pm.stride + p0 + t];
+        __syncthreads();
+    }
+}
+
+// Paged fused append, in the attend workgroup of (sequence b, KV head g,
+// chunk c) that holds the new row's slot: store the new K/V row of head g at
+// its pool row, give the block table the fresh page (head 0), bump the
+// length (head 0), then a workgroup barrier before any wave reads the slot.
+// A fresh page starts at the new row, so no other chunk of the sequence
+// covers it, and every workgroup of this chunk took it from the arguments.
+template <int RB>
+__device__ __forceinline__ void fused_append_paged(const LensSrc<kLensPagedFused>& ls,
+                                                  const Located& loc, int g, int Hkv,
+                                                  const PageMap& pm, const int* sm_pages, int row0,
+                                                  int row_end)
+{
+    const int b = loc.b;
+    const int len0 = ls.v[b];
+    if (row0 <= len0 && len0 < row_end) {
+        const int page = sm_pages[(len0 >> pm.pshift) - (row0 >> pm.pshift)];
+        const size_t hg = static_cast<size_t>(b) * Hkv + g;
+        const size_t row = ((static_cast<size_t>(g) * pm.num_pages + page) << pm.pshift) +
+                           (len0 & ((1 << pm.pshift) - 1));
+        constexpr int VPR = RB / 16;
+        if (threadIdx.x < VPR)
+            reinterpret_cast<uint4*>(ls.f.K + row * RB)[threadIdx.x] =
+                reinterpret_cast<const uint4*>(ls.f.k_new + hg * RB)[threadIdx.x];
+        else if (threadIdx.x < 2 * VPR)
+            reinterpret_cast<uint4*>(ls.f.V + row * RB)[threadIdx.x - VPR] =
+                reinterpret_cast<const uint4*>(ls.f.v_new + hg * RB)[threadIdx.x - VPR];
+        if (g == 0 && threadIdx.x == 0) {
+            if (ls.fresh[b] >= 0)
+                ls.f.table_out[static_cast<size_t>(b) * pm.stride + (len0 >> pm.pshift)] = ls.fresh[b];
+            ls.f.lens_out[b] = len0 + 1;
+        }
         __syncthreads();
     }
 }
@@ -659,10 +720,17 @@ void attend_kernel(
     const int row_end = min(loc.len, row0 + T);
 
     __shared__ int sm_pages[PAGED ? kMaxChunkPages : 1];
-    stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages);
+    if constexpr (LM == kLensPagedFused)
+        stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages,
+                           ls.fresh[loc.b] >= 0 ? (ls.v[loc.b] >> pm.pshift) : -1, ls.fresh[loc.b]);
+    else
+        stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages);
     const char* Kb = K + part * 16;
     const char* Vb = V + part * 16;
-    if constexpr (LM != kLensDevice) fused_append<RB>(ls, loc, g, Hkv, cap_pad, row0, row_end);
+    if constexpr (LM == kLensPagedFused)
+        fused_append_paged<RB>(ls, loc, g, Hkv, pm, sm_pages, row0, row_end);
+    else if constexpr (LM != kLensDevice)
+        fused_append<RB>(ls, loc, g, Hkv, cap_pad, row0, row_end);
 
     // q for the GROUP heads sharing KV head g, this lane's dims.  It is not
     // waited for before the loop: the first rows' loads are issued first and
@@ -855,10 +923,17 @@ void attend_gqa_mfma_kernel(
     const int row_end = min(loc.len, row0 + T);
 
     __shared__ int sm_pages[PAGED ? kMaxChunkPages : 1];
-    stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages);
+    if constexpr (LM == kLensPagedFused)
+        stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages,
+                           ls.fresh[loc.b] >= 0 ? (ls.v[loc.b] >> pm.pshift) : -1, ls.fresh[loc.b]);
+    else
+        stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages);
     const char* Kb = K + 16 * (lane & 7); // + row offset, row = r0 + 8c + (lane >> 3)
     const char* Vb = V + 16 * (lane & 7);
-    if constexpr (LM != kLensDevice) fused_append<RB>(ls, loc, g, Hkv, cap_pad, row0, row_end);
+    if constexpr (LM == kLensPagedFused)
+        fused_append_paged<RB>(ls, loc, g, Hkv, pm, sm_pages, row0, row_end);
+    else if constexpr (LM != kLensDevice)
+        fused_append<RB>(ls, loc, g, Hkv, cap_pad, row0, row_end);
 
     // q loads, then the wave's first 32 rows, both in flight before either is
     // waited for.  The loop is software-pipelined: once a tile sits in LDS
@@ -1309,6 +1384,17 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
     LensSrc<LM> ls;
     if constexpr (LM == kLensDevice) {
         ls.lens = a.lens;
+    } else if constexpr (LM == kLensPagedFused) {
+        for (int b = 0; b < kMaxPagedFusedBatch; ++b) {
+            ls.v[b] = b < a.batch ? a.fused_lens[b] : 0;
+            ls.fresh[b] = b < a.batch ? a.fresh_pages[b] : -1;
+        }
+        ls.f.k_new = static_cast<const char*>(a.k_new);
+        ls.f.v_new = static_cast<const char*>(a.v_new);
+        ls.f.K = static_cast<char*>(const_cast<void*>(a.k));
+        ls.f.V = static_cast<char*>(const_cast<void*>(a.v));
+        ls.f.lens_out = a.lens_out;
+        ls.f.table_out = const_cast<int32_t*>(a.table);
     } else {
         if constexpr (LM == kLensHostFused) {
             for (int b = 0; b < kMaxFusedBatch; ++b) ls.v[b] = b < a.batch ? a.fused_lens[b] : 0;
@@ -1433,6 +1519,11 @@ int resident_attend_blocks(int dtype, int group)
 
 hipError_t launch_attend(int dtype, const AttendArgs& a, hipStream_t s)
 {
+    if (a.table && a.fresh_pages) {
+        if (a.batch > kMaxPagedFusedBatch || !a.fused_lens) return hipErrorInvalidValue;
+        return dtype == 0 ? attend_dispatch_group<4, true, kLensPagedFused>(a, s)
+                          : attend_dispatch_group<2, true, kLensPagedFused>(a, s);
+    }
     if (a.table)
         return dtype == 0 ? attend_dispatch_group<4, true, kLensDevice>(a, s)
                           : attend_dispatch_group<2, true, kLensDevice>(a, s);

@@ -38,6 +38,7 @@ def test_binding_constants_match_header():
     assert int(defs["KVDEC_MAX_CHUNK"]) == B.MAX_CHUNK
     assert int(defs["KVDEC_MAX_GROUP"]) == B.MAX_GROUP
     assert int(defs["KVDEC_MAX_FUSED_BATCH"]) == B.KVDEC_MAX_FUSED_BATCH
+    assert int(defs["KVDEC_MAX_PAGED_FUSED_BATCH"]) == B.KVDEC_MAX_PAGED_FUSED_BATCH
     for name in ("KVDEC_OK", "KVDEC_E_INVALID", "KVDEC_E_SHAPE", "KVDEC_E_OVERFLOW",
                  "KVDEC_E_STATIC", "KVDEC_E_WORKSPACE", "KVDEC_E_HIP", "KVDEC_F32", "KVDEC_BF16"):
         assert int(defs[name]) == getattr(B, name), name

@@ -4,10 +4,13 @@ Each case draws a K/V dtype, a query-head group (1..8), a batch, a length
 law (empty sequences, lengths on and next to 32-row tile and 64-row chunk
 boundaries, short, long and log-uniform mixes), a chunk size, a scale, an
 input magnitude and an entry point (plain attend, the fused append + attend
-for two steps, the fused call at explicit positions, or the paged layout),
+for two steps, the fused call at explicit positions, the paged layout, or the paged fused step for two
+steps),
 and compares the output with the oracle.  The fused cases also compare the
 cache contents and lengths bit for bit with the oracle's append.  A few
-cases use batches above the one-launch fused limit (512 sequences).  Ring
+cases use batches above the one-launch fused limits (512 sequences, 256
+for the paged form).  Paged fused cases also compare the pool rows reached
+through the block table with the oracle's rows bit for bit.  Ring
 cases (window == capacity) run the fused step, or the fused step at
 explicit positions, on a sliding-window cache whose lengths may exceed the
 window: the new row goes to slot len % W and the oracle attends the first
@@ -31,8 +34,8 @@ from helpers import assert_attention_close
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 112
-MODES = ["attend", "fused", "fused_at", "paged", "ring", "ring_at", "cross"]
+N_CASES = 128
+MODES = ["attend", "fused", "fused_at", "paged", "ring", "ring_at", "cross", "paged_fused"]
 
 
 def _draw_lens(rng, Bsz):
@@ -66,6 +69,9 @@ def _case(i):
     mode = MODES[i % len(MODES)]
     if i % 16 == 5 and mode in ("attend", "fused", "fused_at"):
         Bsz = int(rng.integers(513, 600))         # above the one-launch fused batch
+        lens = rng.integers(0, 40, size=Bsz)
+    elif mode == "paged_fused" and i % 3 == 0:
+        Bsz = int(rng.integers(257, 300))         # above the one-launch paged fused batch
         lens = rng.integers(0, 40, size=Bsz)
     else:
         Bsz = int(rng.integers(1, 25))
@@ -114,6 +120,35 @@ def test_random_case(i):
     K = _rows(rng, (Bsz, Hkv, cap_pad, 64), dtype, s)
     V = _rows(rng, (Bsz, Hkv, cap_pad, 64), dtype, s)
     what = f"case {i} ({mode} {dtype} B={Bsz} Hq={Hq} Hkv={Hkv} T={T})"
+
+    if mode == "paged_fused":
+        P = int(rng.choice([16, 32, 64, 128]))
+        max_pages = (cap + P - 1) // P
+        pc = PagedKVCache(Bsz, Hkv, P, num_pages=Bsz * max_pages + 3, max_pages_per_seq=max_pages,
+                          dtype=dtype)
+        pc.load_contiguous(to_device(K), to_device(V), lens)
+        Kh, Vh, ln = K.copy(), V.copy(), lens.copy()
+        for st in range(2):
+            kn = _rows(rng, (Bsz, Hkv, 64), dtype, s)
+            vn = _rows(rng, (Bsz, Hkv, 64), dtype, s)
+            q = (rng.standard_normal((Bsz, Hq, 64)) * s).astype(np.float32)
+            out = pc.append_attend(to_device(kn), to_device(vn), to_device(q), scale=scale,
+                                   chunk_rows=T)
+            torch.cuda.synchronize()
+            ln = oracle.append(Kh, Vh, kn, vn, ln)
+            assert_attention_close(out.cpu().numpy(), oracle.attend(q, Kh, Vh, ln, scale), dtype,
+                                   f"{what} P={P} step {st}")
+        assert pc.lens() == ln.tolist() and pc.lens_dev.cpu().tolist() == ln.tolist()
+        table, tdev = pc.table(), pc.table_dev.cpu().numpy()
+        kp, vp = to_host_bits(pc.k), to_host_bits(pc.v)
+        for b in range(Bsz):
+            n = (int(ln[b]) + P - 1) // P
+            assert tdev[b, :n].tolist() == table[b][:n]
+            for r in range(int(ln[b])):
+                page, slot = table[b][r // P], r % P
+                assert kp[:, page, slot].tobytes() == Kh[b, :, r].tobytes(), f"{what} K row {b},{r}"
+                assert vp[:, page, slot].tobytes() == Vh[b, :, r].tobytes(), f"{what} V row {b},{r}"
+        return
 
     if mode == "paged":
         P = int(rng.choice([16, 32, 64, 128]))
