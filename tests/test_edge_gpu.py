@@ -9,7 +9,8 @@
 - group 8 over a single KV head with a ragged batch, through the fused call;
 - 48 KV heads (the launch grid's second dimension) in both kernel families;
 - two independent caches driven on two streams at once;
-- f32 launches large enough for the 16-wave workgroups (plain, fused, paged).
+- f32 launches large enough for the 16-wave workgroups (plain, fused, paged,
+  paged fused).
 """
 import sys
 
@@ -161,7 +162,7 @@ def test_independent_caches_on_two_streams():
         assert c.lens() == s["lens"].tolist()
 
 
-@pytest.mark.parametrize("mode", ["attend", "fused", "paged"])
+@pytest.mark.parametrize("mode", ["attend", "fused", "paged", "paged_fused"])
 @pytest.mark.parametrize("group", [1, 2])
 def test_wide_workgroups(group, mode):
     """f32 with 1 or 2 query heads per KV head and at least four residency
@@ -175,13 +176,26 @@ def test_wide_workgroups(group, mode):
     V = _rows(rng, (Bsz, Hkv, cap, 64), "f32")
     q = rng.standard_normal((Bsz, Hq, 64), dtype=np.float32)
     _log(f"wide workgroups: group {group}, {mode}")
-    if mode == "paged":
+    if mode.startswith("paged"):
         P = 32
         maxp = cap // P
         pc = PagedKVCache(Bsz, Hkv, P, num_pages=Bsz * maxp, max_pages_per_seq=maxp, dtype="f32")
         pc.load_contiguous(to_device(K), to_device(V), lens)
-        out = pc.attend(to_device(q), chunk_rows=256)
-        ref = oracle.attend(q, K, V, lens)
+        if mode == "paged":
+            out = pc.attend(to_device(q), chunk_rows=256)
+            ref = oracle.attend(q, K, V, lens)
+        else:
+            kn = _rows(rng, (Bsz, Hkv, 64), "f32")
+            vn = _rows(rng, (Bsz, Hkv, 64), "f32")
+            out = pc.append_attend(to_device(kn), to_device(vn), to_device(q), chunk_rows=256)
+            ln = oracle.append(K, V, kn, vn, lens)
+            ref = oracle.attend(q, K, V, ln)
+            torch.cuda.synchronize()
+            table, kp = pc.table(), to_host_bits(pc.k)
+            for b in range(Bsz):            # the new rows, reached through the block table
+                r = int(lens[b])
+                assert kp[:, table[b][r // P], r % P].tobytes() == kn[b].tobytes()
+            assert pc.lens() == ln.tolist()
     elif mode == "attend":
         c = KVCache(Bsz, Hkv, cap, "f32", lens=lens, k=to_device(K), v=to_device(V))
         out = c.attend(to_device(q), chunk_rows=256)
