@@ -28,6 +28,7 @@ the step time as the difference between a pass of flush + step and a pass of
 the flush alone.
 """
 import argparse
+import gc
 import json
 import os
 import platform
@@ -251,6 +252,7 @@ class Bench:
         # one graph holds whole cycles, at least 32 steps, so the graph launch
         # itself is amortised
         per_graph = self.S * max(1, -(-32 // self.S))
+        gc.collect()          # no dead cycle holding device memory is freed mid-capture
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)

@@ -274,7 +274,10 @@ KVDEC_API int32_t kvdec_attend_cross(const kvdec_cache* cache, const float* q, i
  *                      one (KV head, page) is a contiguous run of rows, and
  *                      consecutive pages of one head are adjacent
  *   block_table      : (device) int32 [batch][max_pages_per_seq]; written by
- *                      the library's appends, never read past a sequence's pages
+ *                      the library only: -1 after create, page ids as pages
+ *                      are taken, -1 again as they return to the pool; read
+ *                      for the rows a sequence holds and, in replay mode, for
+ *                      the row an append stores
  *   lens             : (device) int32 [batch], all zero after create
  * ------------------------------------------------------------------------- */
 typedef struct kvdec_paged kvdec_paged;
@@ -295,8 +298,9 @@ typedef struct {
 } kvdec_paged_desc;
 
 /* Create a paged cache: every sequence empty, every page free; writes zero
- * lengths on `stream`.  Errors: KVDEC_E_INVALID, KVDEC_E_SHAPE (head_dim,
- * page_rows not a power of two in range). */
+ * lengths and a block table of -1 on `stream`.  Errors: KVDEC_E_INVALID,
+ * KVDEC_E_SHAPE (head_dim, page_rows not a power of two in range, block
+ * table or rows per sequence too large for int32 indices). */
 KVDEC_API int32_t kvdec_paged_create(const kvdec_paged_desc* desc, void* stream, kvdec_paged** out);
 KVDEC_API void kvdec_paged_destroy(kvdec_paged* paged);
 
@@ -308,8 +312,8 @@ KVDEC_API void kvdec_paged_destroy(kvdec_paged* paged);
  * launch (KVDEC_E_HIP) returns the pages taken. */
 KVDEC_API int32_t kvdec_paged_append(kvdec_paged* paged, const void* k_new, const void* v_new, void* stream);
 
-/* End sequence `seq`: its pages return to the pool and its length becomes 0
- * (written on `stream`). */
+/* End sequence `seq`: its pages return to the pool, their block table
+ * entries become -1 and its length becomes 0 (written on `stream`). */
 KVDEC_API int32_t kvdec_paged_release(kvdec_paged* paged, int32_t seq, void* stream);
 
 /* Give the empty sequence `seq` ceil(len / page_rows) free pages and the
@@ -320,10 +324,12 @@ KVDEC_API int32_t kvdec_paged_release(kvdec_paged* paged, int32_t seq, void* str
  * or too few free pages; nothing changes). */
 KVDEC_API int32_t kvdec_paged_reserve(kvdec_paged* paged, int32_t seq, int32_t len, void* stream);
 
-/* Shorten sequences to lens_host[batch] (each <= its current length): pages
- * past the new ends return to the pool, rows before them are kept -- rolling
- * back speculative tokens, or replaying a benchmark cycle.  Errors:
- * KVDEC_E_INVALID, KVDEC_E_SHAPE (a length outside [0, current]). */
+/* Shorten sequences to lens_host[batch] (each <= its current length; after
+ * replay mode, each <= the rows its pages hold): pages past the new ends
+ * return to the pool (block table entries -1), rows before them are kept --
+ * rolling back speculative tokens, replaying a benchmark cycle, or setting
+ * the lengths after replay mode.  Errors: KVDEC_E_INVALID, KVDEC_E_SHAPE (a
+ * length outside that range). */
 KVDEC_API int32_t kvdec_paged_truncate(kvdec_paged* paged, const int32_t* lens_host, void* stream);
 
 /* Host mirrors: lengths [batch], block table [batch][max_pages_per_seq]
@@ -360,6 +366,42 @@ KVDEC_API int32_t kvdec_paged_append_attend(kvdec_paged* paged, const void* k_ne
                                             const float* q, int32_t n_q_heads, float scale,
                                             int32_t chunk_rows, float* out, void* ws, size_t ws_bytes,
                                             void* stream);
+
+/*
+ * Replay mode for a paged cache: the paged decode step captured once in a
+ * HIP graph and replayed for consecutive tokens, as kvdec_set_replay_mode
+ * does for a contiguous cache ([WA-CUDA] `forward_decoder_token_gpu_stream`
+ * over the paged cache of [WA-DEC] `PagedDecoderKVCache`).  chunk_rows as
+ * for kvdec_set_replay_mode (> 0, KVDEC_REPLAY_AUTO, or 0 to leave).  In
+ * replay mode kvdec_paged_attend is launched for max_pages_per_seq *
+ * page_rows rows with the merge launch always made, kvdec_paged_append and
+ * kvdec_paged_append_attend read the lengths from the device (the latter as
+ * the two calls), and an append takes no page: every row's page must
+ * already be in the block table, put there by kvdec_paged_prepare (outside
+ * the graph) before the replays that append it.  An append whose row has no
+ * page leaves that sequence's row and length unchanged.  Pages returned to
+ * the pool (kvdec_paged_release, kvdec_paged_truncate) have their block
+ * table entries set to -1 on the device, so such a row never lands in
+ * another sequence's page.  The host mirror counts the prepared rows, which
+ * the replays may not all have appended, so leaving replay mode (0) makes
+ * calls that need the exact lengths (kvdec_paged_append, kvdec_paged_attend,
+ * kvdec_paged_append_attend, kvdec_paged_reserve, kvdec_paged_get_lens,
+ * entering replay mode again) fail with KVDEC_E_INVALID until
+ * kvdec_paged_truncate sets the lengths.
+ * Errors: KVDEC_E_INVALID (chunk_rows, or entering with unknown lengths).
+ */
+KVDEC_API int32_t kvdec_paged_set_replay_mode(kvdec_paged* paged, int32_t chunk_rows);
+
+/* In replay mode: give every sequence the pages for its next n_tokens rows
+ * (from the pool, in sequence order, lowest-numbered first, as
+ * kvdec_paged_append takes them), write them to the device block table on
+ * `stream`, and advance the host mirror by n_tokens per sequence -- the
+ * appends the next replays make.  Not capturable (it picks pages on the
+ * host); call it between replays.  Errors: KVDEC_E_INVALID (not in replay
+ * mode, n_tokens < 0), KVDEC_E_OVERFLOW (a sequence would exceed
+ * max_pages_per_seq * page_rows rows, or too few free pages; nothing
+ * changes), KVDEC_E_HIP (the pages are returned). */
+KVDEC_API int32_t kvdec_paged_prepare(kvdec_paged* paged, int32_t n_tokens, void* stream);
 
 /*
  * Replay mode, for decode steps captured once in a HIP graph and replayed

@@ -38,6 +38,8 @@ EXPORTED = [
     "kvdec_paged_get_lens", "kvdec_paged_get_table",
     "kvdec_paged_free_pages", "kvdec_paged_workspace_bytes", "kvdec_paged_attend",
     "kvdec_paged_append_attend",
+    "kvdec_paged_set_replay_mode",
+    "kvdec_paged_prepare",
 ]
 
 
@@ -107,6 +109,8 @@ def load():
         "kvdec_paged_attend": (_i32, [_vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz, _vp]),
         "kvdec_paged_append_attend": (_i32, [_vp, _vp, _vp, _vp, _i32, ctypes.c_float, _i32, _vp,
                                              _vp, _sz, _vp]),
+        "kvdec_paged_set_replay_mode": (_i32, [_vp, _i32]),
+        "kvdec_paged_prepare": (_i32, [_vp, _i32, _vp]),
         "kvdec_status_str": (ctypes.c_char_p, [_i32]),
         "kvdec_last_error": (ctypes.c_char_p, []),
     }
@@ -252,6 +256,14 @@ def kvdec_paged_append_attend(handle, k_new_ptr, v_new_ptr, q_ptr, n_q_heads, sc
     _check(load().kvdec_paged_append_attend(handle, k_new_ptr, v_new_ptr, q_ptr, int(n_q_heads),
                                             float(scale), int(chunk_rows), out_ptr, ws_ptr,
                                             int(ws_bytes), stream), "kvdec_paged_append_attend")
+
+
+def kvdec_paged_set_replay_mode(handle, chunk_rows):
+    _check(load().kvdec_paged_set_replay_mode(handle, int(chunk_rows)), "kvdec_paged_set_replay_mode")
+
+
+def kvdec_paged_prepare(handle, n_tokens, stream=None):
+    _check(load().kvdec_paged_prepare(handle, int(n_tokens), stream), "kvdec_paged_prepare")
 
 
 def kvdec_append_attend(handle, k_new_ptr, v_new_ptr, q_ptr, n_q_heads, scale, chunk_rows, out_ptr,

@@ -221,6 +221,14 @@ class PagedKVCache:
     def release(self, seq):
         B.kvdec_paged_release(self.handle, seq, current_stream())
 
+    def set_replay_mode(self, chunk_rows):
+        B.kvdec_paged_set_replay_mode(self.handle, chunk_rows)
+
+    def prepare(self, n_tokens=1):
+        """Replay mode: pages for every sequence's next n_tokens rows (call
+        between graph replays)."""
+        B.kvdec_paged_prepare(self.handle, n_tokens, current_stream())
+
     def reserve(self, seq, length):
         B.kvdec_paged_reserve(self.handle, seq, length, current_stream())
 

@@ -21,6 +21,12 @@ struct kvdec_paged {
     std::vector<int32_t> lens;        // host mirror of d.lens
     std::vector<int32_t> table;       // host mirror of d.block_table, -1: no page
     std::vector<int32_t> free_pages;  // pool pages not held by any sequence (a stack)
+    int32_t replay_chunk = 0;         // > 0: replay mode with this fixed chunk size
+    // In replay mode `lens` counts the rows given pages by kvdec_paged_prepare
+    // (an upper bound of the device lengths).  false after replay mode was
+    // left: calls that need the exact lengths fail until kvdec_paged_truncate
+    // sets them.
+    bool lens_known = true;
 };
 
 struct kvdec_cache {
@@ -346,7 +352,7 @@ AttendView paged_view_of(const kvdec_paged* p)
     v.dtype = p->d.dtype;
     v.cap_pad = 0;
     v.row_limit = static_cast<int32_t>(cap);
-    v.replay_chunk = 0;
+    v.replay_chunk = p->replay_chunk;
     v.k = p->d.k_pages;
     v.v = p->d.v_pages;
     v.lens_dev = p->d.lens;
@@ -385,12 +391,48 @@ void return_fresh_pages(kvdec_paged* p, const std::vector<int32_t>& fresh)
         }
 }
 
+// Calls outside replay mode size launches and take pages from the host
+// mirror, so they need it to match the device lengths.
+int32_t check_paged_mirror(const kvdec_paged* p)
+{
+    if (p->replay_chunk == 0 && !p->lens_known)
+        return fail(KVDEC_E_INVALID, "lengths unknown after leaving replay mode: set them with "
+                    "kvdec_paged_truncate first");
+    return KVDEC_OK;
+}
+
+// Return the pages of sequence b past its first `keep` to the pool (host
+// mirror), and collect their table entries, to be set to -1 on the device so
+// that a replay-mode append never finds a page another sequence now holds.
+void free_pages_past(kvdec_paged* p, int32_t b, int32_t keep, std::vector<int32_t>& cleared)
+{
+    const size_t base = static_cast<size_t>(b) * p->d.max_pages_per_seq;
+    const int32_t held = (p->lens[b] + p->d.page_rows - 1) / p->d.page_rows;
+    for (int32_t i = held - 1; i >= keep; --i) {
+        p->free_pages.push_back(p->table[base + i]);
+        p->table[base + i] = -1;
+        cleared.push_back(static_cast<int32_t>(base) + i);
+    }
+}
+
+hipError_t clear_entries(kvdec_paged* p, const std::vector<int32_t>& cleared, void* stream)
+{
+    const std::vector<int32_t> minus(cleared.size(), -1);
+    return kvdec::launch_table_write(p->d.block_table, cleared.data(), minus.data(),
+                                     static_cast<int32_t>(cleared.size()),
+                                     static_cast<hipStream_t>(stream));
+}
+
 // Capacity and pool checks of a paged append (nothing changes on failure).
+// In replay mode the pages were given ahead (kvdec_paged_prepare) and the
+// device drops a row that has none, so there is nothing to check here.
 int32_t check_paged_append(const kvdec_paged* p, const void* k_new, const void* v_new)
 {
     if (!p) return fail(KVDEC_E_INVALID, "paged cache handle is NULL");
     if (!aligned16(k_new) || !aligned16(v_new))
         return fail(KVDEC_E_INVALID, "k_new and v_new must be non-NULL, 16-byte aligned device pointers");
+    const int32_t rc = check_paged_mirror(p);
+    if (rc || p->replay_chunk > 0) return rc;
     const int32_t P = p->d.page_rows;
     const int64_t cap = static_cast<int64_t>(p->d.max_pages_per_seq) * P;
     int32_t needed = 0;
@@ -608,8 +650,9 @@ int32_t kvdec_paged_create(const kvdec_paged_desc* desc, void* stream, kvdec_pag
     if (d.page_rows < 16 || d.page_rows > KVDEC_MAX_CHUNK || (1 << pshift) != d.page_rows)
         return fail(KVDEC_E_SHAPE, "page_rows must be a power of two in [16, %d], got %d",
                     KVDEC_MAX_CHUNK, d.page_rows);
-    if (static_cast<int64_t>(d.max_pages_per_seq) * d.page_rows > INT32_MAX / 2)
-        return fail(KVDEC_E_SHAPE, "max_pages_per_seq * page_rows too large");
+    if (static_cast<int64_t>(d.max_pages_per_seq) * d.page_rows > INT32_MAX / 2 ||
+        static_cast<int64_t>(d.max_pages_per_seq) * d.batch > INT32_MAX)
+        return fail(KVDEC_E_SHAPE, "max_pages_per_seq * page_rows or * batch too large");
     if (d.reserved0 != 0) return fail(KVDEC_E_INVALID, "reserved0 must be 0");
     if (!aligned16(d.k_pages) || !aligned16(d.v_pages) || !aligned16(d.block_table) ||
         !aligned16(d.lens))
@@ -622,11 +665,14 @@ int32_t kvdec_paged_create(const kvdec_paged_desc* desc, void* stream, kvdec_pag
     p->table.assign(static_cast<size_t>(d.batch) * d.max_pages_per_seq, -1);
     p->free_pages.reserve(d.num_pages);
     for (int32_t i = d.num_pages - 1; i >= 0; --i) p->free_pages.push_back(i);   // pops 0, 1, 2, ...
-    const hipError_t e = kvdec::launch_set_lens(d.lens, p->lens.data(), d.batch,
-                                                static_cast<hipStream_t>(stream));
+    hipError_t e = kvdec::launch_set_lens(d.lens, p->lens.data(), d.batch,
+                                          static_cast<hipStream_t>(stream));
+    if (e == hipSuccess)
+        e = kvdec::launch_fill_i32(d.block_table, static_cast<int64_t>(d.batch) * d.max_pages_per_seq,
+                                   -1, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
         delete p;
-        return hip_fail(e, "set lengths");
+        return hip_fail(e, "set lengths and block table");
     }
     *out = p;
     return KVDEC_OK;
@@ -639,13 +685,22 @@ int32_t kvdec_paged_append(kvdec_paged* p, const void* k_new, const void* v_new,
     g_err.clear();
     const int32_t rc = check_paged_append(p, k_new, v_new);
     if (rc) return rc;
+    if (p->replay_chunk > 0) {
+        // pages were given ahead; the mirror already counts the prepared rows
+        const std::vector<int32_t> none(p->d.batch, -1);
+        const hipError_t e = kvdec::launch_paged_append(
+            p->d.dtype, p->d.k_pages, p->d.v_pages, k_new, v_new, p->d.lens, p->d.block_table,
+            p->d.max_pages_per_seq, p->d.batch, p->d.n_kv_heads, p->pshift, p->d.num_pages,
+            none.data(), true, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? KVDEC_OK : hip_fail(e, "paged append launch");
+    }
     // take pages, install them in the host mirror, launch; on a launch
     // failure give everything back
     const std::vector<int32_t> fresh = take_fresh_pages(p);
     const hipError_t e = kvdec::launch_paged_append(
         p->d.dtype, p->d.k_pages, p->d.v_pages, k_new, v_new, p->d.lens, p->d.block_table,
         p->d.max_pages_per_seq, p->d.batch, p->d.n_kv_heads, p->pshift, p->d.num_pages, fresh.data(),
-        static_cast<hipStream_t>(stream));
+        false, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
         return_fresh_pages(p, fresh);
         return hip_fail(e, "paged append launch");
@@ -664,14 +719,11 @@ int32_t kvdec_paged_release(kvdec_paged* p, int32_t seq, void* stream)
     const hipError_t e = kvdec::launch_set_lens(p->d.lens + seq, &zero, 1,
                                                 static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "set lengths");
-    const size_t base = static_cast<size_t>(seq) * p->d.max_pages_per_seq;
-    const int32_t held = (p->lens[seq] + p->d.page_rows - 1) / p->d.page_rows;
-    for (int32_t i = held - 1; i >= 0; --i) {
-        p->free_pages.push_back(p->table[base + i]);
-        p->table[base + i] = -1;
-    }
+    std::vector<int32_t> cleared;
+    free_pages_past(p, seq, 0, cleared);
     p->lens[seq] = 0;
-    return KVDEC_OK;
+    const hipError_t e2 = clear_entries(p, cleared, stream);
+    return e2 == hipSuccess ? KVDEC_OK : hip_fail(e2, "block table write");
 }
 
 int32_t kvdec_paged_reserve(kvdec_paged* p, int32_t seq, int32_t len, void* stream)
@@ -680,6 +732,8 @@ int32_t kvdec_paged_reserve(kvdec_paged* p, int32_t seq, int32_t len, void* stre
     if (!p) return fail(KVDEC_E_INVALID, "paged cache handle is NULL");
     if (seq < 0 || seq >= p->d.batch)
         return fail(KVDEC_E_INVALID, "sequence %d outside [0, %d)", seq, p->d.batch);
+    const int32_t rc = check_paged_mirror(p);
+    if (rc) return rc;
     if (p->lens[seq] != 0)
         return fail(KVDEC_E_INVALID, "sequence %d is not empty (%d rows)", seq, p->lens[seq]);
     const int64_t cap = static_cast<int64_t>(p->d.max_pages_per_seq) * p->d.page_rows;
@@ -711,31 +765,36 @@ int32_t kvdec_paged_truncate(kvdec_paged* p, const int32_t* lens_host, void* str
 {
     g_err.clear();
     if (!p || !lens_host) return fail(KVDEC_E_INVALID, "handle and lens_host must not be NULL");
-    for (int32_t b = 0; b < p->d.batch; ++b)
-        if (lens_host[b] < 0 || lens_host[b] > p->lens[b])
-            return fail(KVDEC_E_SHAPE, "new length %d of sequence %d outside [0, %d]", lens_host[b], b,
-                        p->lens[b]);
+    // a known length only shrinks; after replay mode a length may be
+    // anything the sequence's pages hold (replays may have appended more or
+    // fewer rows than were prepared)
+    const int32_t P = p->d.page_rows;
+    for (int32_t b = 0; b < p->d.batch; ++b) {
+        const int64_t limit = p->lens_known ? p->lens[b]
+                                            : static_cast<int64_t>((p->lens[b] + P - 1) / P) * P;
+        if (lens_host[b] < 0 || lens_host[b] > limit)
+            return fail(KVDEC_E_SHAPE, "new length %d of sequence %d outside [0, %lld]", lens_host[b],
+                        b, static_cast<long long>(limit));
+    }
     const hipError_t e = kvdec::launch_set_lens(p->d.lens, lens_host, p->d.batch,
                                                 static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "set lengths");
-    const int32_t P = p->d.page_rows;
+    std::vector<int32_t> cleared;
     for (int32_t b = 0; b < p->d.batch; ++b) {
-        const size_t base = static_cast<size_t>(b) * p->d.max_pages_per_seq;
-        const int32_t keep = (lens_host[b] + P - 1) / P;
-        const int32_t held = (p->lens[b] + P - 1) / P;
-        for (int32_t i = held - 1; i >= keep; --i) {
-            p->free_pages.push_back(p->table[base + i]);
-            p->table[base + i] = -1;
-        }
+        free_pages_past(p, b, (lens_host[b] + P - 1) / P, cleared);
         p->lens[b] = lens_host[b];
     }
-    return KVDEC_OK;
+    p->lens_known = true;
+    const hipError_t e2 = clear_entries(p, cleared, stream);
+    return e2 == hipSuccess ? KVDEC_OK : hip_fail(e2, "block table write");
 }
 
 int32_t kvdec_paged_get_lens(const kvdec_paged* p, int32_t* lens_out)
 {
     g_err.clear();
     if (!p || !lens_out) return fail(KVDEC_E_INVALID, "handle and lens_out must not be NULL");
+    const int32_t rc = check_paged_mirror(p);
+    if (rc) return rc;
     std::memcpy(lens_out, p->lens.data(), sizeof(int32_t) * p->lens.size());
     return KVDEC_OK;
 }
@@ -766,6 +825,8 @@ int32_t kvdec_paged_attend(const kvdec_paged* p, const float* q, int32_t n_q_hea
 {
     g_err.clear();
     if (!p) return fail(KVDEC_E_INVALID, "paged cache handle is NULL");
+    const int32_t rc = check_paged_mirror(p);
+    if (rc) return rc;
     return attend_view(paged_view_of(p), q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
 }
 
@@ -780,8 +841,9 @@ int32_t kvdec_paged_append_attend(kvdec_paged* p, const void* k_new, const void*
     for (auto& r : v.rows) ++r;                  // rows attended after the append
     rc = check_attend(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes);
     if (rc) return rc;
-    if (p->d.batch > KVDEC_MAX_PAGED_FUSED_BATCH) {
-        // two launches: the paged append, then the attend over the new lengths
+    if (p->d.batch > KVDEC_MAX_PAGED_FUSED_BATCH || p->replay_chunk > 0) {
+        // two launches: the paged append, then the attend over the new
+        // lengths (in replay mode both read the lengths from the device)
         rc = kvdec_paged_append(p, k_new, v_new, stream);
         if (rc) return rc;
         return attend_view(paged_view_of(p), q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes,
@@ -800,6 +862,79 @@ int32_t kvdec_paged_append_attend(kvdec_paged* p, const void* k_new, const void*
         return rc;
     }
     for (auto& l : p->lens) ++l;
+    return KVDEC_OK;
+}
+
+int32_t kvdec_paged_set_replay_mode(kvdec_paged* p, int32_t chunk_rows)
+{
+    g_err.clear();
+    if (!p) return fail(KVDEC_E_INVALID, "paged cache handle is NULL");
+    if (chunk_rows != 0 && chunk_rows != KVDEC_REPLAY_AUTO &&
+        (chunk_rows < KVDEC_MIN_CHUNK || chunk_rows > KVDEC_MAX_CHUNK || chunk_rows % 64 != 0))
+        return fail(KVDEC_E_INVALID, "chunk_rows %d must be 0, KVDEC_REPLAY_AUTO or a multiple of "
+                    "64 in [%d, %d]", chunk_rows, KVDEC_MIN_CHUNK, KVDEC_MAX_CHUNK);
+    if (chunk_rows != 0 && p->replay_chunk == 0) {
+        const int32_t rc = check_paged_mirror(p);   // prepare counts from exact lengths
+        if (rc) return rc;
+    }
+    if (chunk_rows == KVDEC_REPLAY_AUTO) {
+        p->replay_chunk = auto_chunk(p->lens, p->d.n_kv_heads, esz_of(p->d.dtype),
+                                     kvdec::resident_attend_blocks(p->d.dtype, 1));
+        return KVDEC_OK;
+    }
+    // leaving replay mode: the mirror counts prepared rows, which replays may
+    // not all have appended
+    if (chunk_rows == 0 && p->replay_chunk > 0) p->lens_known = false;
+    p->replay_chunk = chunk_rows;
+    return KVDEC_OK;
+}
+
+int32_t kvdec_paged_prepare(kvdec_paged* p, int32_t n_tokens, void* stream)
+{
+    g_err.clear();
+    if (!p) return fail(KVDEC_E_INVALID, "paged cache handle is NULL");
+    if (p->replay_chunk == 0)
+        return fail(KVDEC_E_INVALID, "kvdec_paged_prepare needs replay mode (outside it appends "
+                    "take their own pages)");
+    if (n_tokens < 0) return fail(KVDEC_E_INVALID, "n_tokens %d must be >= 0", n_tokens);
+    const int32_t P = p->d.page_rows;
+    const int64_t cap = static_cast<int64_t>(p->d.max_pages_per_seq) * P;
+    int64_t needed = 0;
+    for (int32_t b = 0; b < p->d.batch; ++b) {
+        const int64_t want = static_cast<int64_t>(p->lens[b]) + n_tokens;
+        if (want > cap)
+            return fail(KVDEC_E_OVERFLOW, "cache overflow: sequence %d holds %d + %d > %lld", b,
+                        p->lens[b], n_tokens, static_cast<long long>(cap));
+        needed += (want + P - 1) / P - (p->lens[b] + P - 1) / P;
+    }
+    if (needed > static_cast<int64_t>(p->free_pages.size()))
+        return fail(KVDEC_E_OVERFLOW, "page pool exhausted: %lld new pages needed, %zu free",
+                    static_cast<long long>(needed), p->free_pages.size());
+    // pages in sequence order, lowest-numbered first, as appends take them
+    std::vector<int32_t> idx, val;
+    for (int32_t b = 0; b < p->d.batch; ++b) {
+        const size_t base = static_cast<size_t>(b) * p->d.max_pages_per_seq;
+        const int32_t from = (p->lens[b] + P - 1) / P;
+        const int32_t to = static_cast<int32_t>((static_cast<int64_t>(p->lens[b]) + n_tokens + P - 1) / P);
+        for (int32_t i = from; i < to; ++i) {
+            const int32_t page = p->free_pages.back();
+            p->free_pages.pop_back();
+            p->table[base + i] = page;
+            idx.push_back(static_cast<int32_t>(base) + i);
+            val.push_back(page);
+        }
+    }
+    const hipError_t e = kvdec::launch_table_write(p->d.block_table, idx.data(), val.data(),
+                                                   static_cast<int32_t>(idx.size()),
+                                                   static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        for (size_t k = idx.size(); k-- > 0;) {
+            p->table[idx[k]] = -1;
+            p->free_pages.push_back(val[k]);
+        }
+        return hip_fail(e, "block table write");
+    }
+    for (auto& l : p->lens) l += n_tokens;
     return KVDEC_OK;
 }
 

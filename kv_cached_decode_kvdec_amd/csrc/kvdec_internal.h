@@ -67,6 +67,13 @@ struct PageBlock {
     int32_t v[kPagesPerLaunch];        // new page for each sequence of the slice, or -1
 };
 
+constexpr int kEntriesPerLaunch = 256; // block-table entries written by one table-write launch
+
+struct EntryBlock {
+    int32_t idx[kEntriesPerLaunch];    // flat index b * table_stride + page slot
+    int32_t val[kEntriesPerLaunch];    // page id, or -1
+};
+
 hipError_t launch_set_lens(int32_t* lens, const int32_t* host, int32_t n, hipStream_t s);
 hipError_t launch_append(int dtype, void* k, void* v, const void* k_new, const void* v_new,
                          int32_t* lens, int32_t batch, int32_t n_kv_heads, int32_t capacity,
@@ -79,9 +86,12 @@ hipError_t launch_paged_append(int dtype, void* k_pages, void* v_pages, const vo
                                const void* v_new, int32_t* lens, int32_t* table,
                                int32_t table_stride, int32_t batch, int32_t n_kv_heads,
                                int32_t pshift, int32_t num_pages, const int32_t* new_pages,
-                               hipStream_t s);
+                               bool from_table, hipStream_t s);
 hipError_t launch_paged_reserve(int32_t* table, int32_t table_stride, int32_t* lens, int32_t seq,
                                 const int32_t* pages, int32_t n_pages, int32_t len, hipStream_t s);
+hipError_t launch_table_write(int32_t* table, const int32_t* idx, const int32_t* val, int32_t n,
+                              hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 hipError_t launch_seed(int dtype, void* k, void* v, const void* k_tok, const void* v_tok,
                        int32_t batch, int32_t rows, int32_t n_kv_heads, int32_t cap_pad,
                        hipStream_t s);

@@ -606,30 +606,35 @@ __global__ __launch_bounds__(256) void append_rope_kernel(
 // decoder_generated.rs, `PagedDecoderKVCache`: page = position / page size,
 // slot = position % page size).  When a sequence's row lands at the start of
 // a page, the host has chosen a free page for it (passed by value); the
-// kernel installs it in the table before writing the row.
+// kernel installs it in the table before writing the row.  With from_table
+// (replay mode) every row's page comes from the table, where the host put it
+// ahead of the replays; a row whose entry holds no page is not written and
+// its sequence keeps its length.
 // ---------------------------------------------------------------------------
 template <int ROW_BYTES>
 __global__ __launch_bounds__(256) void paged_append_kernel(
     char* __restrict__ Kp, char* __restrict__ Vp, const char* __restrict__ kn,
     const char* __restrict__ vn, int32_t* __restrict__ lens, int32_t* __restrict__ table,
-    int table_stride, int Hkv, int pshift, int num_pages, int b0, PageBlock new_pages)
+    int table_stride, int Hkv, int pshift, int num_pages, int b0, PageBlock new_pages,
+    int from_table)
 {
     constexpr int VPR = ROW_BYTES / 16;
     const int b = b0 + blockIdx.x;
     const int len = lens[b];
     if (len < 0) return;
     const int pidx = len >> pshift;
-    if (pidx >= table_stride) return;                 // host already rejected this
+    if (pidx >= table_stride) return;                 // full: nothing written
     const int slot = len & ((1 << pshift) - 1);
     int32_t* entry = table + static_cast<size_t>(b) * table_stride + pidx;
     int page;
-    if (slot == 0) {
+    if (slot == 0 && !from_table) {
         page = new_pages.v[blockIdx.x];
         if (page < 0) return;                         // host already rejected this
         if (threadIdx.x == 0) *entry = page;
     } else {
         page = *entry;
     }
+    if (page < 0 || page >= num_pages) return;        // no page holds this row: nothing written
     const int n = Hkv * VPR;
     for (int t = threadIdx.x; t < 2 * n; t += blockDim.x) {
         const bool isv = t >= n;
@@ -654,6 +659,22 @@ __global__ void paged_reserve_kernel(int32_t* __restrict__ table, int32_t* __res
     const int t = threadIdx.x;
     if (t < n) table[first + t] = pages.v[t];
     if (t == 0 && len >= 0) lens[seq] = len;
+}
+
+// Fill n int32 values (a new paged cache's block table with -1).
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v)
+{
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        p[i] = v;
+}
+
+// Write block-table entries (flat indices and values carried by value):
+// pages given ahead of replays, and -1 where pages return to the pool.
+__global__ void table_write_kernel(int32_t* __restrict__ table, int n, EntryBlock e)
+{
+    const int t = threadIdx.x;
+    if (t < n) table[e.idx[t]] = e.val[t];
 }
 
 // ---------------------------------------------------------------------------
@@ -1270,7 +1291,7 @@ hipError_t launch_paged_append(int dtype, void* k_pages, void* v_pages, const vo
                                const void* v_new, int32_t* lens, int32_t* table,
                                int32_t table_stride, int32_t batch, int32_t n_kv_heads,
                                int32_t pshift, int32_t num_pages, const int32_t* new_pages,
-                               hipStream_t s)
+                               bool from_table, hipStream_t s)
 {
     for (int32_t b0 = 0; b0 < batch; b0 += kPagesPerLaunch) {
         const int32_t cnt = (batch - b0) < kPagesPerLaunch ? (batch - b0) : kPagesPerLaunch;
@@ -1281,12 +1302,14 @@ hipError_t launch_paged_append(int dtype, void* k_pages, void* v_pages, const vo
             hipLaunchKernelGGL(paged_append_kernel<256>, grid, block, 0, s,
                                static_cast<char*>(k_pages), static_cast<char*>(v_pages),
                                static_cast<const char*>(k_new), static_cast<const char*>(v_new),
-                               lens, table, table_stride, n_kv_heads, pshift, num_pages, b0, blk);
+                               lens, table, table_stride, n_kv_heads, pshift, num_pages, b0, blk,
+                               from_table ? 1 : 0);
         else
             hipLaunchKernelGGL(paged_append_kernel<128>, grid, block, 0, s,
                                static_cast<char*>(k_pages), static_cast<char*>(v_pages),
                                static_cast<const char*>(k_new), static_cast<const char*>(v_new),
-                               lens, table, table_stride, n_kv_heads, pshift, num_pages, b0, blk);
+                               lens, table, table_stride, n_kv_heads, pshift, num_pages, b0, blk,
+                               from_table ? 1 : 0);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1308,6 +1331,32 @@ hipError_t launch_paged_reserve(int32_t* table, int32_t table_stride, int32_t* l
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (n_pages == 0) break;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(static_cast<unsigned>(blocks < 1024 ? blocks : 1024)),
+                       dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_table_write(int32_t* table, const int32_t* idx, const int32_t* val, int32_t n,
+                              hipStream_t s)
+{
+    for (int32_t off = 0; off < n; off += kEntriesPerLaunch) {
+        const int32_t cnt = (n - off) < kEntriesPerLaunch ? (n - off) : kEntriesPerLaunch;
+        EntryBlock blk;
+        for (int32_t i = 0; i < kEntriesPerLaunch; ++i) {
+            blk.idx[i] = i < cnt ? idx[off + i] : 0;
+            blk.val[i] = i < cnt ? val[off + i] : 0;
+        }
+        hipLaunchKernelGGL(table_write_kernel, dim3(1), dim3(kEntriesPerLaunch), 0, s, table, cnt, blk);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }

@@ -1,14 +1,19 @@
 """A multi-layer decode step captured once in a HIP graph and replayed for
 consecutive tokens (replay mode), checked against the oracle after every
 replay, with eager library calls between replays; the step either appends
-and attends in two calls or through kvdec_append_attend."""
+and attends in two calls or through kvdec_append_attend.  The paged form
+is replayed the same way, with its pages given between replays
+(kvdec_paged_prepare)."""
+import gc
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from kv_cached_decode_kvdec_amd import inputs as gen
-from kv_cached_decode_kvdec_amd.cache import KVCache, to_device
+from kv_cached_decode_kvdec_amd import binding as B
+from kv_cached_decode_kvdec_amd.cache import KVCache, PagedKVCache, to_device, to_host_bits
 
 from helpers import assert_attention_close
 
@@ -18,6 +23,16 @@ pytestmark = pytest.mark.gpu
 def _rows(rng, shape, dtype):
     x = rng.standard_normal(shape, dtype=np.float32)
     return x if dtype == "f32" else gen.f32_to_bf16_bits(x)
+
+
+def _new_graph():
+    """A graph to capture into, after collecting dead Python cycles: a cycle
+    left by an earlier test (an exception info holding its frame, with that
+    test's graph and device tensors) must not be freed by the collector in
+    the middle of a capture, where freeing device memory is not allowed."""
+    gc.collect()
+    torch.cuda.synchronize()
+    return torch.cuda.CUDAGraph()
 
 
 @pytest.mark.parametrize("rchunk", [64, 256])
@@ -68,7 +83,7 @@ def test_graph_replayed_multilayer_step(dtype, Hq, Hkv, cross, window, fused, rc
         layers.append(lay)
     torch.cuda.synchronize()
 
-    g = torch.cuda.CUDAGraph()
+    g = _new_graph()
     with torch.cuda.graph(g):
         for lay in layers:
             if fused:   # replay mode: lengths read from and bumped on the device
@@ -165,7 +180,7 @@ def test_leaving_replay_mode_needs_lengths_again():
     st = KVCache(Bsz, Hkv, cap, "f32", static=True, lens=lens, k=to_device(K), v=to_device(V))
     c.set_replay_mode(64)
     st.set_replay_mode(64)
-    g = torch.cuda.CUDAGraph()
+    g = _new_graph()
     kn = to_device(_rows(rng, (Bsz, Hkv, 64), "f32"))
     vn = to_device(_rows(rng, (Bsz, Hkv, 64), "f32"))
     with torch.cuda.graph(g):
@@ -194,3 +209,151 @@ def test_leaving_replay_mode_needs_lengths_again():
         Vh[b, :, lens[b]:lens[b] + 4] = vh[b][:, None, :]
     assert_attention_close(out.cpu().numpy(), oracle.attend(q.cpu().numpy(), Kh, Vh, dev), "f32",
                            "after reset_lens")
+
+
+def _history(lay, lens, Bsz, Hkv):
+    cap = gen.padded_rows(int(lens.max()))
+    K = np.zeros((Bsz, Hkv, cap, 64), lay["hk"].dtype)
+    V = np.zeros_like(K)
+    for b in range(Bsz):
+        K[b, :, :lens[b]] = lay["hk"][b, :, :lens[b]]
+        V[b, :, :lens[b]] = lay["hv"][b, :, :lens[b]]
+    return K, V
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("dtype,Hq,Hkv,P,rchunk", [("f32", 4, 4, 16, 64), ("bf16", 16, 4, 16, 256),
+                                                   ("bf16", 8, 2, 32, 128)])
+def test_graph_replayed_paged_step(dtype, Hq, Hkv, P, rchunk, fused):
+    """Two paged layers captured once and replayed for 40 tokens that cross
+    page boundaries (sequences start empty, one row short of a page, and
+    mid-page), pages given by kvdec_paged_prepare between replays.  After
+    every replay: the oracle over each sequence's history, and an eager
+    attend equal to the replayed one.  At the end: the pool rows reached
+    through the block table are the appended rows bit for bit; leaving
+    replay mode makes the lengths unknown until kvdec_paged_truncate, and
+    the ordinary fused step then continues from them."""
+    rng = np.random.default_rng(17 + Hq + P)
+    L, Bsz, T = 2, 3, 40
+    start = np.array([0, P - 1, 37], np.int32)
+    total = int(start.max()) + T + 1
+    maxp = -(-total // P)
+    layers = []
+    for _ in range(L):
+        hk = _rows(rng, (Bsz, Hkv, gen.padded_rows(total), 64), dtype)
+        hv = _rows(rng, hk.shape, dtype)
+        pc = PagedKVCache(Bsz, Hkv, P, num_pages=Bsz * maxp, max_pages_per_seq=maxp, dtype=dtype)
+        pc.load_contiguous(to_device(hk), to_device(hv), start)
+        pc.set_replay_mode(rchunk)
+        pc.workspace(Hq)
+        layers.append(dict(hk=hk, hv=hv, pc=pc, kn=to_device(np.zeros((Bsz, Hkv, 64), hk.dtype)),
+                           vn=to_device(np.zeros((Bsz, Hkv, 64), hk.dtype)),
+                           q=torch.zeros(Bsz, Hq, 64, device="cuda"),
+                           out=torch.zeros(Bsz, Hq, 64, device="cuda")))
+    torch.cuda.synchronize()
+
+    g = _new_graph()
+    with torch.cuda.graph(g):
+        for lay in layers:
+            if fused:
+                lay["pc"].append_attend(lay["kn"], lay["vn"], lay["q"], out=lay["out"])
+            else:
+                lay["pc"].append(lay["kn"], lay["vn"])
+                lay["pc"].attend(lay["q"], out=lay["out"])
+
+    lens = start.copy()
+    for t in range(T):
+        qs = []
+        for lay in layers:
+            lay["pc"].prepare(1)                    # pages for the row this replay appends
+            kn = np.stack([lay["hk"][b, :, lens[b]] for b in range(Bsz)])
+            vn = np.stack([lay["hv"][b, :, lens[b]] for b in range(Bsz)])
+            lay["kn"].copy_(to_device(kn))
+            lay["vn"].copy_(to_device(vn))
+            q = rng.standard_normal((Bsz, Hq, 64), dtype=np.float32)
+            lay["q"].copy_(torch.from_numpy(q).cuda())
+            qs.append(q)
+        g.replay()
+        torch.cuda.synchronize()
+        lens = lens + 1
+        for l, lay in enumerate(layers):
+            K, V = _history(lay, lens, Bsz, Hkv)
+            assert_attention_close(lay["out"].cpu().numpy(), oracle.attend(qs[l], K, V, lens),
+                                   dtype, f"paged replay {t} layer {l}")
+            eager = lay["pc"].attend(lay["q"])
+            torch.cuda.synchronize()
+            assert torch.equal(eager, lay["out"])
+        assert layers[0]["pc"].lens_dev.cpu().tolist() == lens.tolist()
+        assert layers[0]["pc"].lens() == lens.tolist()     # the prepared rows, all appended
+
+    for lay in layers:
+        pc = lay["pc"]
+        table, tdev = pc.table(), pc.table_dev.cpu().numpy()
+        kp, vp = to_host_bits(pc.k), to_host_bits(pc.v)
+        for b in range(Bsz):
+            n = -(-int(lens[b]) // P)
+            assert tdev[b, :n].tolist() == table[b][:n]
+            assert (tdev[b, n:] == -1).all()
+            for r in range(int(lens[b])):
+                assert kp[:, table[b][r // P], r % P].tobytes() == lay["hk"][b, :, r].tobytes()
+                assert vp[:, table[b][r // P], r % P].tobytes() == lay["hv"][b, :, r].tobytes()
+        pc.set_replay_mode(0)
+        with pytest.raises(B.KvdecError) as e:
+            pc.lens()
+        assert e.value.code == B.KVDEC_E_INVALID
+        with pytest.raises(B.KvdecError) as e:
+            pc.attend(lay["q"])
+        assert e.value.code == B.KVDEC_E_INVALID
+        pc.truncate(lens)
+        assert pc.lens() == lens.tolist()
+
+    # the ordinary one-launch step continues from the lengths set again
+    for l, lay in enumerate(layers):
+        kn = np.stack([lay["hk"][b, :, lens[b]] for b in range(Bsz)])
+        vn = np.stack([lay["hv"][b, :, lens[b]] for b in range(Bsz)])
+        q = rng.standard_normal((Bsz, Hq, 64), dtype=np.float32)
+        out = lay["pc"].append_attend(to_device(kn), to_device(vn), to_device(q))
+        torch.cuda.synchronize()
+        K, V = _history(lay, lens + 1, Bsz, Hkv)
+        assert_attention_close(out.cpu().numpy(), oracle.attend(q, K, V, lens + 1), dtype,
+                               f"after replay mode, layer {l}")
+
+
+def test_paged_replay_rows_without_pages_are_dropped():
+    """In replay mode an append whose row has no page in the block table
+    (not prepared, or a page returned to the pool) writes nothing and keeps
+    that sequence's length; rows in held pages are appended.  Pages returned
+    to the pool leave -1 in the device table."""
+    rng = np.random.default_rng(23)
+    Bsz, Hkv, Hq, P = 3, 2, 4, 16
+    pc = PagedKVCache(Bsz, Hkv, P, num_pages=8, max_pages_per_seq=3, dtype="f32")
+    K = _rows(rng, (Bsz, Hkv, 64, 64), "f32")
+    pc.load_contiguous(to_device(K), to_device(K), np.array([16, 5, 20], np.int32))
+    assert pc.table_dev.cpu().numpy()[2, :2].min() >= 0
+    pc.release(2)                        # its two pages return to the pool
+    pc.set_replay_mode(64)
+    kn = to_device(_rows(rng, (Bsz, Hkv, 64), "f32"))
+    before = to_host_bits(pc.k).copy()
+    pc.append(kn, kn)                    # row 16 starts a page: none; row 5: held; row 0: none
+    torch.cuda.synchronize()
+    assert pc.lens_dev.cpu().tolist() == [16, 6, 0]
+    after = to_host_bits(pc.k)
+    page1 = pc.table()[1][0]
+    changed = np.argwhere((before != after).any(axis=-1))
+    assert {(int(g), int(p), int(r)) for g, p, r in changed} <= {(g, page1, 5) for g in range(Hkv)}
+    assert pc.table_dev.cpu().numpy()[2].tolist() == [-1, -1, -1]
+    with pytest.raises(B.KvdecError) as e:
+        pc.prepare(-1)
+    assert e.value.code == B.KVDEC_E_INVALID
+    with pytest.raises(B.KvdecError) as e:
+        pc.prepare(40)                   # 16 + 40 rows > 3 pages of 16
+    assert e.value.code == B.KVDEC_E_OVERFLOW
+    pc.prepare(1)                        # pages for rows 16 (sequence 0) and 0 (sequence 2)
+    pc.append(kn, kn)
+    torch.cuda.synchronize()
+    assert pc.lens_dev.cpu().tolist() == [17, 7, 1]
+    pc.set_replay_mode(0)
+    pc.truncate([17, 7, 1])              # sequence 1 ran one row past its prepared length
+    assert pc.lens() == [17, 7, 1]
+    with pytest.raises(B.KvdecError):
+        pc.prepare(1)                    # outside replay mode
