@@ -211,6 +211,7 @@ int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, floa
         const int64_t per_seq = (static_cast<int64_t>(a.row_limit) + a.chunk_rows - 1) / a.chunk_rows;
         a.n_chunks = static_cast<int64_t>(v.batch) * (per_seq > 0 ? per_seq : 1);
         a.need_merge = per_seq > 1;
+        a.replay = true;
     } else {
         a.chunk_rows = chunk_rows ? chunk_rows
                                   : auto_chunk(v.rows, v.n_kv_heads, esz_of(v.dtype),

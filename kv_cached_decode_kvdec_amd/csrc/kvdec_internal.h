@@ -39,6 +39,7 @@ struct AttendArgs {
     int32_t chunk_rows;     // rows per split-sequence chunk
     int64_t n_chunks;       // sum over sequences of max(1, ceil(len / chunk_rows))
     bool need_merge;        // some sequence spans more than one chunk
+    bool replay = false;    // capacity-sized grid (replay mode): surplus workgroups exit at once
     float qscale;           // scale * log2(e)
     float* out;
     void* ws;

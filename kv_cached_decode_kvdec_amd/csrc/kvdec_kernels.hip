@@ -1465,9 +1465,12 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
         // on 16-wave workgroups (each wave one pass of 16 rows) where two of
         // them fit on a CU and the grid fills at least four residency rounds
         // of them (with fewer, the last partial round costs more than the
-        // wide workgroups gain: whisper-base's cross-attention, 1.5 rounds)
+        // wide workgroups gain: whisper-base's cross-attention, 1.5 rounds).
+        // Not for capacity-sized replay grids: there a surplus workgroup
+        // launches and retires 16 waves for nothing (qwen2-0.5b replayed:
+        // 83.3 us per step on 16-wave, 80.1 on 4-wave workgroups).
         const int rw = wide_resident<GROUP, PAGED, LM>();
-        if (a.chunk_rows >= kWideWaves * kUnroll * Lay<4>::kRPI && rw > 0 &&
+        if (!a.replay && a.chunk_rows >= kWideWaves * kUnroll * Lay<4>::kRPI && rw > 0 &&
             a.n_chunks * a.n_kv_heads >= 4 * static_cast<int64_t>(rw)) {
             hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWideWaves, kUnroll, PAGED, LM>), grid,
                                dim3(kWideWaves * 64), 0, s, a.q, static_cast<const char*>(a.k),
