@@ -1,7 +1,12 @@
 // gfx950 kernels of the single-token KV-cached decode step.
 //
 //   append  : scatter one new K/V row per (sequence, KV head) to row lens[b]
-//             of the head-major cache, then lens[b] += 1 (pure byte copy).
+//             of the head-major cache, then lens[b] += 1 (pure byte copy);
+//             also fused into the attend launch (the workgroup whose chunk
+//             holds the new row stores it), and a RoPE form that rotates
+//             the key on the way.
+//   paged   : the same append through a block table into a head-major page
+//             pool, plus the small table writes of the host page allocator.
 //   seed    : token-major [B][rows][H*64] -> head-major [B][H][cap][64].
 //   attend  : split-sequence decode attention.  One workgroup owns one
 //             (sequence, chunk of rows, KV head) and all query heads that
@@ -17,10 +22,13 @@
 //             its partial (m, l, o[64]).
 //   merge   : log-sum-exp merge of the chunk partials of every
 //             (sequence, query head) whose length spans more than one chunk
-//             (a second launch, only when some sequence has several chunks:
-//             a last-block merge inside the attend kernel would need a
-//             device-scope release per workgroup, which on this chip writes
-//             back the XCD's L2 and serialises the chunks).
+//             (a second launch, only when some sequence has several chunks.
+//             A last-workgroup merge inside the attend kernel needs a
+//             device-scope hand-off per workgroup: with a release fence it
+//             writes back the XCD's L2 each time; with device-scope stores
+//             and a counter it holds every workgroup through a store wait
+//             and an atomic round trip, and needs counters that start at
+//             zero.  Both cost more than the launch on large grids.)
 //
 // Arithmetic follows the per-head decode of franken_ocr 0.8.0
 // decoder_qwen2.rs (`decode_attn_head`: scores scaled by 1/sqrt(d), max-shifted
