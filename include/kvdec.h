@@ -275,9 +275,9 @@ KVDEC_API int32_t kvdec_attend_cross(const kvdec_cache* cache, const float* q, i
  *                      consecutive pages of one head are adjacent
  *   block_table      : (device) int32 [batch][max_pages_per_seq]; written by
  *                      the library only: -1 after create, page ids as pages
- *                      are taken, -1 again as they return to the pool; read
- *                      for the rows a sequence holds and, in replay mode, for
- *                      the row an append stores
+ *                      are taken; read for the rows a sequence holds and, in
+ *                      replay mode, for the row an append stores (then every
+ *                      entry past a sequence's pages is -1)
  *   lens             : (device) int32 [batch], all zero after create
  * ------------------------------------------------------------------------- */
 typedef struct kvdec_paged kvdec_paged;
@@ -312,8 +312,8 @@ KVDEC_API void kvdec_paged_destroy(kvdec_paged* paged);
  * launch (KVDEC_E_HIP) returns the pages taken. */
 KVDEC_API int32_t kvdec_paged_append(kvdec_paged* paged, const void* k_new, const void* v_new, void* stream);
 
-/* End sequence `seq`: its pages return to the pool, their block table
- * entries become -1 and its length becomes 0 (written on `stream`). */
+/* End sequence `seq`: its pages return to the pool and its length becomes 0
+ * (written on `stream`; in replay mode its block table entries become -1). */
 KVDEC_API int32_t kvdec_paged_release(kvdec_paged* paged, int32_t seq, void* stream);
 
 /* Give the empty sequence `seq` ceil(len / page_rows) free pages and the
@@ -326,7 +326,8 @@ KVDEC_API int32_t kvdec_paged_reserve(kvdec_paged* paged, int32_t seq, int32_t l
 
 /* Shorten sequences to lens_host[batch] (each <= its current length; after
  * replay mode, each <= the rows its pages hold): pages past the new ends
- * return to the pool (block table entries -1), rows before them are kept --
+ * return to the pool (in replay mode their block table entries become -1),
+ * rows before them are kept --
  * rolling back speculative tokens, replaying a benchmark cycle, or setting
  * the lengths after replay mode.  Errors: KVDEC_E_INVALID, KVDEC_E_SHAPE (a
  * length outside that range). */
@@ -379,18 +380,20 @@ KVDEC_API int32_t kvdec_paged_append_attend(kvdec_paged* paged, const void* k_ne
  * the two calls), and an append takes no page: every row's page must
  * already be in the block table, put there by kvdec_paged_prepare (outside
  * the graph) before the replays that append it.  An append whose row has no
- * page leaves that sequence's row and length unchanged.  Pages returned to
- * the pool (kvdec_paged_release, kvdec_paged_truncate) have their block
- * table entries set to -1 on the device, so such a row never lands in
+ * page leaves that sequence's row and length unchanged.  Entering replay
+ * mode sets -1 on `stream` in every block table entry past a sequence's
+ * pages, and in replay mode pages returned to the pool (kvdec_paged_release,
+ * kvdec_paged_truncate) get -1 there too, so such a row never lands in
  * another sequence's page.  The host mirror counts the prepared rows, which
  * the replays may not all have appended, so leaving replay mode (0) makes
  * calls that need the exact lengths (kvdec_paged_append, kvdec_paged_attend,
  * kvdec_paged_append_attend, kvdec_paged_reserve, kvdec_paged_get_lens,
  * entering replay mode again) fail with KVDEC_E_INVALID until
  * kvdec_paged_truncate sets the lengths.
- * Errors: KVDEC_E_INVALID (chunk_rows, or entering with unknown lengths).
+ * Errors: KVDEC_E_INVALID (chunk_rows, or entering with unknown lengths),
+ * KVDEC_E_HIP.
  */
-KVDEC_API int32_t kvdec_paged_set_replay_mode(kvdec_paged* paged, int32_t chunk_rows);
+KVDEC_API int32_t kvdec_paged_set_replay_mode(kvdec_paged* paged, int32_t chunk_rows, void* stream);
 
 /* In replay mode: give every sequence the pages for its next n_tokens rows
  * (from the pool, in sequence order, lowest-numbered first, as

@@ -109,7 +109,7 @@ def load():
         "kvdec_paged_attend": (_i32, [_vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz, _vp]),
         "kvdec_paged_append_attend": (_i32, [_vp, _vp, _vp, _vp, _i32, ctypes.c_float, _i32, _vp,
                                              _vp, _sz, _vp]),
-        "kvdec_paged_set_replay_mode": (_i32, [_vp, _i32]),
+        "kvdec_paged_set_replay_mode": (_i32, [_vp, _i32, _vp]),
         "kvdec_paged_prepare": (_i32, [_vp, _i32, _vp]),
         "kvdec_status_str": (ctypes.c_char_p, [_i32]),
         "kvdec_last_error": (ctypes.c_char_p, []),
@@ -258,8 +258,9 @@ def kvdec_paged_append_attend(handle, k_new_ptr, v_new_ptr, q_ptr, n_q_heads, sc
                                             int(ws_bytes), stream), "kvdec_paged_append_attend")
 
 
-def kvdec_paged_set_replay_mode(handle, chunk_rows):
-    _check(load().kvdec_paged_set_replay_mode(handle, int(chunk_rows)), "kvdec_paged_set_replay_mode")
+def kvdec_paged_set_replay_mode(handle, chunk_rows, stream=None):
+    _check(load().kvdec_paged_set_replay_mode(handle, int(chunk_rows), stream),
+           "kvdec_paged_set_replay_mode")
 
 
 def kvdec_paged_prepare(handle, n_tokens, stream=None):

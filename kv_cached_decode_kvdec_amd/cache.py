@@ -222,7 +222,7 @@ class PagedKVCache:
         B.kvdec_paged_release(self.handle, seq, current_stream())
 
     def set_replay_mode(self, chunk_rows):
-        B.kvdec_paged_set_replay_mode(self.handle, chunk_rows)
+        B.kvdec_paged_set_replay_mode(self.handle, chunk_rows, current_stream())
 
     def prepare(self, n_tokens=1):
         """Replay mode: pages for every sequence's next n_tokens rows (call

@@ -403,8 +403,11 @@ int32_t check_paged_mirror(const kvdec_paged* p)
 }
 
 // Return the pages of sequence b past its first `keep` to the pool (host
-// mirror), and collect their table entries, to be set to -1 on the device so
-// that a replay-mode append never finds a page another sequence now holds.
+// mirror), and collect their table entries.  In replay mode they are set to
+// -1 on the device at once, so that an append that reads its page from the
+// table never finds one another sequence now holds; outside replay mode
+// nothing reads an entry past a sequence's pages, and entering replay mode
+// clears them all.
 void free_pages_past(kvdec_paged* p, int32_t b, int32_t keep, std::vector<int32_t>& cleared)
 {
     const size_t base = static_cast<size_t>(b) * p->d.max_pages_per_seq;
@@ -418,6 +421,7 @@ void free_pages_past(kvdec_paged* p, int32_t b, int32_t keep, std::vector<int32_
 
 hipError_t clear_entries(kvdec_paged* p, const std::vector<int32_t>& cleared, void* stream)
 {
+    if (p->replay_chunk == 0) return hipSuccess;
     const std::vector<int32_t> minus(cleared.size(), -1);
     return kvdec::launch_table_write(p->d.block_table, cleared.data(), minus.data(),
                                      static_cast<int32_t>(cleared.size()),
@@ -866,7 +870,7 @@ int32_t kvdec_paged_append_attend(kvdec_paged* p, const void* k_new, const void*
     return KVDEC_OK;
 }
 
-int32_t kvdec_paged_set_replay_mode(kvdec_paged* p, int32_t chunk_rows)
+int32_t kvdec_paged_set_replay_mode(kvdec_paged* p, int32_t chunk_rows, void* stream)
 {
     g_err.clear();
     if (!p) return fail(KVDEC_E_INVALID, "paged cache handle is NULL");
@@ -877,6 +881,14 @@ int32_t kvdec_paged_set_replay_mode(kvdec_paged* p, int32_t chunk_rows)
     if (chunk_rows != 0 && p->replay_chunk == 0) {
         const int32_t rc = check_paged_mirror(p);   // prepare counts from exact lengths
         if (rc) return rc;
+        // every entry past a sequence's pages becomes -1 on the device
+        std::vector<int32_t> held(p->d.batch);
+        for (int32_t b = 0; b < p->d.batch; ++b)
+            held[b] = (p->lens[b] + p->d.page_rows - 1) / p->d.page_rows;
+        const hipError_t e = kvdec::launch_table_clear_tail(p->d.block_table, p->d.max_pages_per_seq,
+                                                            held.data(), p->d.batch,
+                                                            static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail(e, "block table write");
     }
     if (chunk_rows == KVDEC_REPLAY_AUTO) {
         p->replay_chunk = auto_chunk(p->lens, p->d.n_kv_heads, esz_of(p->d.dtype),

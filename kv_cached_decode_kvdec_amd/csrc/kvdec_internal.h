@@ -93,6 +93,8 @@ hipError_t launch_paged_reserve(int32_t* table, int32_t table_stride, int32_t* l
 hipError_t launch_table_write(int32_t* table, const int32_t* idx, const int32_t* val, int32_t n,
                               hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+hipError_t launch_table_clear_tail(int32_t* table, int32_t table_stride, const int32_t* held,
+                                   int32_t batch, hipStream_t s);
 hipError_t launch_seed(int dtype, void* k, void* v, const void* k_tok, const void* v_tok,
                        int32_t batch, int32_t rows, int32_t n_kv_heads, int32_t cap_pad,
                        hipStream_t s);

@@ -677,6 +677,15 @@ __global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v)
         p[i] = v;
 }
 
+// Set -1 in every block-table entry past the first held[b] of each sequence
+// of a slice (entering replay mode).
+__global__ void table_clear_tail_kernel(int32_t* __restrict__ table, int stride, int b0,
+                                        LensBlock held)
+{
+    int32_t* row = table + static_cast<size_t>(b0 + blockIdx.x) * stride;
+    for (int i = held.v[blockIdx.x] + threadIdx.x; i < stride; i += blockDim.x) row[i] = -1;
+}
+
 // Write block-table entries (flat indices and values carried by value):
 // pages given ahead of replays, and -1 where pages return to the pool.
 __global__ void table_write_kernel(int32_t* __restrict__ table, int n, EntryBlock e)
@@ -1339,6 +1348,21 @@ hipError_t launch_paged_reserve(int32_t* table, int32_t table_stride, int32_t* l
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (n_pages == 0) break;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_table_clear_tail(int32_t* table, int32_t table_stride, const int32_t* held,
+                                   int32_t batch, hipStream_t s)
+{
+    for (int32_t b0 = 0; b0 < batch; b0 += kLensPerLaunch) {
+        const int32_t cnt = (batch - b0) < kLensPerLaunch ? (batch - b0) : kLensPerLaunch;
+        LensBlock blk;
+        for (int32_t i = 0; i < kLensPerLaunch; ++i) blk.v[i] = i < cnt ? held[b0 + i] : table_stride;
+        hipLaunchKernelGGL(table_clear_tail_kernel, dim3(cnt), dim3(64), 0, s, table, table_stride, b0,
+                           blk);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }

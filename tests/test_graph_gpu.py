@@ -322,8 +322,9 @@ def test_graph_replayed_paged_step(dtype, Hq, Hkv, P, rchunk, fused):
 def test_paged_replay_rows_without_pages_are_dropped():
     """In replay mode an append whose row has no page in the block table
     (not prepared, or a page returned to the pool) writes nothing and keeps
-    that sequence's length; rows in held pages are appended.  Pages returned
-    to the pool leave -1 in the device table."""
+    that sequence's length; rows in held pages are appended.  Entering replay
+    mode leaves -1 past every sequence's pages in the device table, and a
+    release in replay mode clears the released pages' entries."""
     rng = np.random.default_rng(23)
     Bsz, Hkv, Hq, P = 3, 2, 4, 16
     pc = PagedKVCache(Bsz, Hkv, P, num_pages=8, max_pages_per_seq=3, dtype="f32")
@@ -352,8 +353,16 @@ def test_paged_replay_rows_without_pages_are_dropped():
     pc.append(kn, kn)
     torch.cuda.synchronize()
     assert pc.lens_dev.cpu().tolist() == [17, 7, 1]
+    pc.release(0)                        # in replay mode: its entries become -1 at once
+    torch.cuda.synchronize()
+    assert pc.table_dev.cpu().numpy()[0].tolist() == [-1, -1, -1]
+    pc.append(kn, kn)                    # sequence 0 (row 0) has no page again
+    torch.cuda.synchronize()
+    assert pc.lens_dev.cpu().tolist() == [0, 8, 2]
     pc.set_replay_mode(0)
-    pc.truncate([17, 7, 1])              # sequence 1 ran one row past its prepared length
-    assert pc.lens() == [17, 7, 1]
+    with pytest.raises(B.KvdecError):
+        pc.truncate([0, 17, 2])          # more than sequence 1's page holds
+    pc.truncate([0, 8, 2])               # sequences 1 and 2 ran past their prepared lengths
+    assert pc.lens() == [0, 8, 2]
     with pytest.raises(B.KvdecError):
         pc.prepare(1)                    # outside replay mode
