@@ -377,10 +377,12 @@ KVDEC_API int32_t kvdec_paged_append_attend(kvdec_paged* paged, const void* k_ne
  * replay mode kvdec_paged_attend is launched for max_pages_per_seq *
  * page_rows rows with the merge launch always made, kvdec_paged_append and
  * kvdec_paged_append_attend read the lengths from the device (the latter as
- * the two calls), and an append takes no page: every row's page must
+ * one attend launch that stores the new rows, plus the merge launch, which
+ * bumps the lengths), and an append takes no page: every row's page must
  * already be in the block table, put there by kvdec_paged_prepare (outside
  * the graph) before the replays that append it.  An append whose row has no
- * page leaves that sequence's row and length unchanged.  Entering replay
+ * page leaves that sequence's row and length unchanged (and
+ * kvdec_paged_append_attend then attends the rows the sequence had).  Entering replay
  * mode sets -1 on `stream` in every block table entry past a sequence's
  * pages, and in replay mode pages returned to the pool (kvdec_paged_release,
  * kvdec_paged_truncate) get -1 there too, so such a row never lands in

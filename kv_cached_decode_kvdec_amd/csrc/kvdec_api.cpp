@@ -846,9 +846,19 @@ int32_t kvdec_paged_append_attend(kvdec_paged* p, const void* k_new, const void*
     for (auto& r : v.rows) ++r;                  // rows attended after the append
     rc = check_attend(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes);
     if (rc) return rc;
-    if (p->d.batch > KVDEC_MAX_PAGED_FUSED_BATCH || p->replay_chunk > 0) {
-        // two launches: the paged append, then the attend over the new
-        // lengths (in replay mode both read the lengths from the device)
+    if (p->replay_chunk > 0) {
+        // replay mode: the attend launch reads the pre-append lengths from the
+        // device and stores each new row in the page the table already holds
+        // for it; the merge launch bumps the lengths
+        AttendView r = paged_view_of(p);
+        r.fused_device = true;
+        r.k_new = k_new;
+        r.v_new = v_new;
+        r.lens_out = p->d.lens;
+        return attend_view(r, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes, stream);
+    }
+    if (p->d.batch > KVDEC_MAX_PAGED_FUSED_BATCH) {
+        // two launches: the paged append, then the attend over the new lengths
         rc = kvdec_paged_append(p, k_new, v_new, stream);
         if (rc) return rc;
         return attend_view(paged_view_of(p), q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes,

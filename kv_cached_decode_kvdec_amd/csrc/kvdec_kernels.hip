@@ -246,7 +246,7 @@ struct LensSrc<kLensDevice> {
 struct FusedRows {
     const char* k_new;      // [B][Hkv][64] elements
     const char* v_new;
-    char* K;                // contiguous cache, written at the new row's slot
+    char* K;                // contiguous cache (or page pools), written at the new row's slot
     char* V;
     int32_t* lens_out;      // device lengths, bumped by one per sequence
     int window;             // ring window, 0 for a linear cache
@@ -477,6 +477,41 @@ __device__ __forceinline__ void fused_append_paged(const LensSrc<kLensPagedFused
         }
         __syncthreads();
     }
+}
+
+// Paged cache, device-fused mode (replay): the new row's page comes from the
+// block table, where the host put it before the replay; the workgroup whose
+// chunk holds the slot stores the row there, then a workgroup barrier.  A
+// slot whose table entry holds no page is neither stored nor attended (the
+// chunk ends before it; the merge launch then leaves the length as it is).
+// Workgroup (chunk 0, head 0) snapshots the pre-append length for the merge.
+template <int RB>
+__device__ __forceinline__ void fused_append_paged_device(const LensSrc<kLensDeviceFused>& ls,
+                                                         const Located& loc, int g, int Hkv,
+                                                         const PageMap& pm, const int* sm_pages,
+                                                         int row0, int& row_end)
+{
+    const int b = loc.b;
+    const int len0 = ls.get(b);
+    if (row0 <= len0 && len0 < row_end) {
+        const int page = sm_pages[(len0 >> pm.pshift) - (row0 >> pm.pshift)];
+        if (page < 0 || page >= pm.num_pages) {
+            row_end = len0;
+        } else {
+            const size_t hg = static_cast<size_t>(b) * Hkv + g;
+            const size_t row = ((static_cast<size_t>(g) * pm.num_pages + page) << pm.pshift) +
+                               (len0 & ((1 << pm.pshift) - 1));
+            constexpr int VPR = RB / 16;
+            if (threadIdx.x < VPR)
+                reinterpret_cast<uint4*>(ls.f.K + row * RB)[threadIdx.x] =
+                    reinterpret_cast<const uint4*>(ls.f.k_new + hg * RB)[threadIdx.x];
+            else if (threadIdx.x < 2 * VPR)
+                reinterpret_cast<uint4*>(ls.f.V + row * RB)[threadIdx.x - VPR] =
+                    reinterpret_cast<const uint4*>(ls.f.v_new + hg * RB)[threadIdx.x - VPR];
+            __syncthreads();
+        }
+    }
+    if (loc.c == 0 && g == 0 && threadIdx.x == 0) ls.snap[b] = len0;
 }
 
 // Byte offset of row r of (sequence b, KV head g) from the pool / cache base.
@@ -755,7 +790,7 @@ void attend_kernel(
     Located loc;
     if (!locate<LM>(ls, B, T, row_limit, blockIdx.x, lane, loc)) return;
     const int row0 = loc.c * T;
-    const int row_end = min(loc.len, row0 + T);
+    int row_end = min(loc.len, row0 + T);   // lowered where a replayed row has no page
 
     __shared__ int sm_pages[PAGED ? kMaxChunkPages : 1];
     if constexpr (LM == kLensPagedFused)
@@ -767,6 +802,8 @@ void attend_kernel(
     const char* Vb = V + part * 16;
     if constexpr (LM == kLensPagedFused)
         fused_append_paged<RB>(ls, loc, g, Hkv, pm, sm_pages, row0, row_end);
+    else if constexpr (PAGED && LM == kLensDeviceFused)
+        fused_append_paged_device<RB>(ls, loc, g, Hkv, pm, sm_pages, row0, row_end);
     else if constexpr (LM != kLensDevice)
         fused_append<RB>(ls, loc, g, Hkv, cap_pad, row0, row_end);
 
@@ -958,7 +995,7 @@ void attend_gqa_mfma_kernel(
     Located loc;
     if (!locate<LM>(ls, B, T, row_limit, blockIdx.x, lane, loc)) return;
     const int row0 = loc.c * T;
-    const int row_end = min(loc.len, row0 + T);
+    int row_end = min(loc.len, row0 + T);   // lowered where a replayed row has no page
 
     __shared__ int sm_pages[PAGED ? kMaxChunkPages : 1];
     if constexpr (LM == kLensPagedFused)
@@ -970,6 +1007,8 @@ void attend_gqa_mfma_kernel(
     const char* Vb = V + 16 * (lane & 7);
     if constexpr (LM == kLensPagedFused)
         fused_append_paged<RB>(ls, loc, g, Hkv, pm, sm_pages, row0, row_end);
+    else if constexpr (PAGED && LM == kLensDeviceFused)
+        fused_append_paged_device<RB>(ls, loc, g, Hkv, pm, sm_pages, row0, row_end);
     else if constexpr (LM != kLensDevice)
         fused_append<RB>(ls, loc, g, Hkv, cap_pad, row0, row_end);
 
@@ -1165,7 +1204,7 @@ __global__ __launch_bounds__(256) void merge_kernel(LensSrc<LM> ls, int B, int H
                                                     int T, int row_limit,
                                                     const float* __restrict__ part_o,
                                                     const float2* __restrict__ part_ml,
-                                                    float* __restrict__ out)
+                                                    float* __restrict__ out, PageMap pm)
 {
     constexpr int plus = LensSrc<LM>::kPlus;
     const int lane = threadIdx.x & 63;
@@ -1183,7 +1222,10 @@ __global__ __launch_bounds__(256) void merge_kernel(LensSrc<LM> ls, int B, int H
     if constexpr (LM == kLensDeviceFused) {
         // the device-fused append's length bump (refused, like kvdec_append,
         // when a linear cache is full: row_limit is its capacity)
-        if (h == 0 && lane == 0 && (ls.f.window > 0 || len0 < row_limit)) ls.f.lens_out[b] = len0 + 1;
+        // (and, in a paged cache, when the new row had no page)
+        if (h == 0 && lane == 0 && (ls.f.window > 0 || len0 < row_limit) &&
+            (!pm.table || pm.table[static_cast<size_t>(b) * pm.stride + (len0 >> pm.pshift)] >= 0))
+            ls.f.lens_out[b] = len0 + 1;
     }
     const int nch = max(1, (min(max(len0 + plus, 0), row_limit) + T - 1) / T);
     if (nch == 1) return;     // finished by the attend kernel
@@ -1445,13 +1487,13 @@ int wide_resident()
 // The merge launch after an attend launch, when some sequence spans several chunks.
 template <int LM>
 hipError_t launch_merge(const AttendArgs& a, int group, const LensSrc<LM>& ls, float* po,
-                        float2* pml, hipStream_t s)
+                        float2* pml, const PageMap& pm, hipStream_t s)
 {
     if (!a.need_merge) return hipSuccess;
     const int Hq = a.n_kv_heads * group;
     const int waves = a.batch * Hq;
     hipLaunchKernelGGL((merge_kernel<LM>), dim3((waves + 3) / 4), dim3(256), 0, s, ls, a.batch,
-                       Hq, a.chunk_rows, a.row_limit, po, pml, a.out);
+                       Hq, a.chunk_rows, a.row_limit, po, pml, a.out, pm);
     return hipGetLastError();
 }
 
@@ -1509,7 +1551,7 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
                                static_cast<const char*>(a.v), ls, a.batch, a.n_kv_heads, a.cap_pad,
                                a.row_limit, a.chunk_rows, a.qscale, a.out, po, pml, pm);
             e = hipGetLastError();
-            return e != hipSuccess ? e : launch_merge<LM>(a, GROUP, ls, po, pml, s);
+            return e != hipSuccess ? e : launch_merge<LM>(a, GROUP, ls, po, pml, pm, s);
         }
     }
     if constexpr (ESZ == 2 && GROUP >= 2)
@@ -1523,7 +1565,7 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
                            ls, a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows,
                            a.qscale, a.out, po, pml, pm);
     e = hipGetLastError();
-    return e != hipSuccess ? e : launch_merge<LM>(a, GROUP, ls, po, pml, s);
+    return e != hipSuccess ? e : launch_merge<LM>(a, GROUP, ls, po, pml, pm, s);
 }
 
 template <int ESZ, bool PAGED, int LM>
@@ -1607,6 +1649,11 @@ hipError_t launch_attend(int dtype, const AttendArgs& a, hipStream_t s)
         if (a.batch > kMaxPagedFusedBatch || !a.fused_lens) return hipErrorInvalidValue;
         return dtype == 0 ? attend_dispatch_group<4, true, kLensPagedFused>(a, s)
                           : attend_dispatch_group<2, true, kLensPagedFused>(a, s);
+    }
+    if (a.table && a.fused_device) {
+        if (!a.need_merge) return hipErrorInvalidValue;   // the merge launch bumps the lengths
+        return dtype == 0 ? attend_dispatch_group<4, true, kLensDeviceFused>(a, s)
+                          : attend_dispatch_group<2, true, kLensDeviceFused>(a, s);
     }
     if (a.table)
         return dtype == 0 ? attend_dispatch_group<4, true, kLensDevice>(a, s)

@@ -366,3 +366,46 @@ def test_paged_replay_rows_without_pages_are_dropped():
     assert pc.lens() == [0, 8, 2]
     with pytest.raises(B.KvdecError):
         pc.prepare(1)                    # outside replay mode
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv", [("f32", 4, 2), ("bf16", 8, 2), ("bf16", 4, 4)])
+def test_paged_replay_fused_step_without_pages(dtype, Hq, Hkv):
+    """The one-launch paged step in replay mode (lengths from the device, the
+    new row stored in the page the table holds for it): a sequence whose new
+    row has no page keeps its length and attends the rows it had; the others
+    append and attend len + 1 rows.  Checked against the oracle, with the
+    pool bytes of every row compared."""
+    rng = np.random.default_rng(29 + Hq)
+    Bsz, P = 4, 16
+    lens = np.array([16, 5, 0, 70], np.int32)          # row 16 starts a page; 5 and 70 are mid-page
+    K = _rows(rng, (Bsz, Hkv, 128, 64), dtype)         # 64-row chunks: sequence 3 spans two
+    V = _rows(rng, (Bsz, Hkv, 128, 64), dtype)
+    pc = PagedKVCache(Bsz, Hkv, P, num_pages=40, max_pages_per_seq=8, dtype=dtype)
+    pc.load_contiguous(to_device(K), to_device(V), lens)
+    pc.set_replay_mode(64)
+    kn = _rows(rng, (Bsz, Hkv, 64), dtype)
+    vn = _rows(rng, (Bsz, Hkv, 64), dtype)
+    q = rng.standard_normal((Bsz, Hq, 64), dtype=np.float32)
+    out = pc.append_attend(to_device(kn), to_device(vn), to_device(q))
+    torch.cuda.synchronize()
+    stored = np.array([False, True, False, True])
+    new = lens + stored
+    Kh, Vh = K.copy(), V.copy()
+    for b in np.flatnonzero(stored):
+        Kh[b, :, lens[b]], Vh[b, :, lens[b]] = kn[b], vn[b]
+    assert pc.lens_dev.cpu().tolist() == new.tolist()
+    assert_attention_close(out.cpu().numpy(), oracle.attend(q, Kh, Vh, new), dtype, "paged replay fused")
+    table, kp, vp = pc.table(), to_host_bits(pc.k), to_host_bits(pc.v)
+    for b in range(Bsz):
+        for r in range(int(new[b])):
+            assert kp[:, table[b][r // P], r % P].tobytes() == Kh[b, :, r].tobytes()
+            assert vp[:, table[b][r // P], r % P].tobytes() == Vh[b, :, r].tobytes()
+    pc.prepare(1)                                      # now every next row has a page
+    q2 = rng.standard_normal((Bsz, Hq, 64), dtype=np.float32)
+    out2 = pc.append_attend(to_device(kn), to_device(vn), to_device(q2))
+    torch.cuda.synchronize()
+    for b in range(Bsz):
+        Kh[b, :, new[b]], Vh[b, :, new[b]] = kn[b], vn[b]
+    assert pc.lens_dev.cpu().tolist() == (new + 1).tolist()
+    assert_attention_close(out2.cpu().numpy(), oracle.attend(q2, Kh, Vh, new + 1), dtype,
+                           "paged replay fused, prepared")
