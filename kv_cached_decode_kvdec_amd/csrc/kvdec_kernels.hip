@@ -1200,7 +1200,7 @@ void attend_gqa_mfma_kernel(
 // short: lengths -> {(m, l), first 16 o rows} -> further batches of 16.
 // ---------------------------------------------------------------------------
 template <int LM>
-__global__ __launch_bounds__(256) void merge_kernel(LensSrc<LM> ls, int B, int Hq,
+__global__ __launch_bounds__(64) void merge_kernel(LensSrc<LM> ls, int B, int Hq,
                                                     int T, int row_limit,
                                                     const float* __restrict__ part_o,
                                                     const float2* __restrict__ part_ml,
@@ -1208,7 +1208,7 @@ __global__ __launch_bounds__(256) void merge_kernel(LensSrc<LM> ls, int B, int H
 {
     constexpr int plus = LensSrc<LM>::kPlus;
     const int lane = threadIdx.x & 63;
-    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int w = blockIdx.x;
     if (w >= B * Hq) return;
     const int b = w / Hq, h = w - b * Hq;
     // exclusive prefix of chunk counts over sequences < b, and this sequence's count
@@ -1492,7 +1492,9 @@ hipError_t launch_merge(const AttendArgs& a, int group, const LensSrc<LM>& ls, f
     if (!a.need_merge) return hipSuccess;
     const int Hq = a.n_kv_heads * group;
     const int waves = a.batch * Hq;
-    hipLaunchKernelGGL((merge_kernel<LM>), dim3((waves + 3) / 4), dim3(256), 0, s, ls, a.batch,
+    // one wave per workgroup: the waves spread over more CUs (whisper-base
+    // 27.3 -> 26.6 us per step against four-wave workgroups)
+    hipLaunchKernelGGL((merge_kernel<LM>), dim3(waves), dim3(64), 0, s, ls, a.batch,
                        Hq, a.chunk_rows, a.row_limit, po, pml, a.out, pm);
     return hipGetLastError();
 }
