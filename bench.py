@@ -249,6 +249,9 @@ class Bench:
         caches = [self.self_cache] + ([self.cross] if self.cross is not None else [])
         for c in caches:
             c.set_replay_mode(-1)
+            # every cycle restarts at the starting lengths, so each captured
+            # launch sees the lengths it was captured at: a one-token horizon
+            c.set_replay_horizon(1)
         # one graph holds whole cycles, at least 32 steps, so the graph launch
         # itself is amortised
         per_graph = self.S * max(1, -(-32 // self.S))
@@ -269,6 +272,7 @@ class Bench:
         wall = time.perf_counter() - t0
         for c in caches:
             c.set_replay_mode(0)
+            c.set_replay_horizon(0)
         n = reps * per_graph
         step_bytes = reps * (per_graph // self.S) * sum(self.step_bytes)
         return {"graph_ms_per_step": wall * 1e3 / n, "graph_steps_per_s": n / wall,

@@ -432,6 +432,20 @@ KVDEC_API int32_t kvdec_paged_prepare(kvdec_paged* paged, int32_t n_tokens, void
  */
 KVDEC_API int32_t kvdec_set_replay_mode(kvdec_cache* cache, int32_t chunk_rows);
 
+/* Replay grids sized per sequence instead of for the capacity: with
+ * tokens > 0, every attend launch made in replay mode covers, for each
+ * sequence, the rows the host mirror holds at the call plus `tokens` more
+ * (capped at the capacity or window) -- enough for a captured step replayed
+ * for `tokens` appends from the lengths at capture, with fewer surplus
+ * workgroups than a capacity-sized grid.  The mirror is what the calls made
+ * it (kvdec_reset_lens, kvdec_append_attend_at, or the appends made while
+ * capturing), not what replays did on the device.  A replay whose lengths
+ * have outgrown the grid writes NaN into the output rows of every sequence
+ * the grid no longer covers (and a fused append leaves their lengths as they
+ * are); re-capture, or reset the lengths, before that.  0 (the default)
+ * sizes for the capacity.  Errors: KVDEC_E_INVALID (tokens < 0). */
+KVDEC_API int32_t kvdec_set_replay_horizon(kvdec_cache* cache, int32_t tokens);
+
 /* Static description of a status code. */
 KVDEC_API const char* kvdec_status_str(int32_t status);
 

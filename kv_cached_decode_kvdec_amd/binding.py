@@ -32,6 +32,7 @@ EXPORTED = [
     "kvdec_get_lens", "kvdec_seed", "kvdec_append", "kvdec_append_rope", "kvdec_workspace_bytes",
     "kvdec_attend_self", "kvdec_attend_cross", "kvdec_append_attend", "kvdec_append_attend_at",
     "kvdec_set_replay_mode",
+    "kvdec_set_replay_horizon",
     "kvdec_status_str",
     "kvdec_last_error", "kvdec_paged_create", "kvdec_paged_destroy", "kvdec_paged_append",
     "kvdec_paged_release", "kvdec_paged_reserve", "kvdec_paged_truncate",
@@ -92,6 +93,7 @@ def load():
         "kvdec_attend_self": (_i32, [_vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz, _vp]),
         "kvdec_attend_cross": (_i32, [_vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz, _vp]),
         "kvdec_set_replay_mode": (_i32, [_vp, _i32]),
+        "kvdec_set_replay_horizon": (_i32, [_vp, _i32]),
         "kvdec_append_attend": (_i32, [_vp, _vp, _vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz,
                                        _vp]),
         "kvdec_append_attend_at": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float, _i32, _vp,
@@ -195,6 +197,10 @@ def kvdec_attend_cross(handle, q_ptr, n_q_heads, scale, chunk_rows, out_ptr, ws_
 
 def kvdec_set_replay_mode(handle, chunk_rows):
     _check(load().kvdec_set_replay_mode(handle, int(chunk_rows)), "kvdec_set_replay_mode")
+
+
+def kvdec_set_replay_horizon(handle, tokens):
+    _check(load().kvdec_set_replay_horizon(handle, int(tokens)), "kvdec_set_replay_horizon")
 
 
 def kvdec_paged_create(desc, stream=None):

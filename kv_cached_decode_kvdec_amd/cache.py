@@ -72,6 +72,9 @@ class KVCache:
     def set_replay_mode(self, chunk_rows):
         B.kvdec_set_replay_mode(self.handle, chunk_rows)
 
+    def set_replay_horizon(self, tokens):
+        B.kvdec_set_replay_horizon(self.handle, tokens)
+
     def close(self):
         if getattr(self, "handle", None):
             B.kvdec_cache_destroy(self.handle)

@@ -34,6 +34,7 @@ struct kvdec_cache {
     int32_t cap_pad;
     std::vector<int32_t> lens;   // host mirror of d.lens
     int32_t replay_chunk = 0;    // > 0: replay mode with this fixed chunk size
+    int32_t replay_horizon = 0;  // > 0: replay grids sized for the lengths + this many appends
     // false after replay mode was left on a dynamic cache: replays may have
     // advanced the device lengths, so the mirror is not used until the
     // caller sets the lengths again (kvdec_reset_lens, kvdec_seed,
@@ -143,6 +144,7 @@ int64_t max_chunks(const kvdec_cache* c)
 // contiguous and the paged layouts.
 struct AttendView {
     int32_t batch, n_kv_heads, dtype, cap_pad, row_limit, replay_chunk;
+    int32_t replay_horizon = 0;    // replay grids: rows + horizon per sequence, else the capacity
     const void* k;
     const void* v;
     const int32_t* lens_dev;
@@ -211,7 +213,18 @@ int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, floa
         const int64_t per_seq = (static_cast<int64_t>(a.row_limit) + a.chunk_rows - 1) / a.chunk_rows;
         a.n_chunks = static_cast<int64_t>(v.batch) * (per_seq > 0 ? per_seq : 1);
         a.need_merge = per_seq > 1;
-        a.replay = true;
+        a.replay = v.replay_horizon == 0;    // capacity-sized: surplus workgroups
+        if (v.replay_horizon > 0) {
+            // a horizon: each sequence sized for its rows now plus that many
+            // appends (the merge launch marks a sequence the grid no longer
+            // covers with NaN rows)
+            std::vector<int32_t> r(v.rows);
+            for (auto& x : r) {
+                const int64_t n = static_cast<int64_t>(x) + v.replay_horizon;
+                x = static_cast<int32_t>(n < a.row_limit ? n : a.row_limit);
+            }
+            a.n_chunks = chunks_for(r, a.chunk_rows);
+        }
     } else {
         a.chunk_rows = chunk_rows ? chunk_rows
                                   : auto_chunk(v.rows, v.n_kv_heads, esz_of(v.dtype),
@@ -249,6 +262,7 @@ AttendView view_of(const kvdec_cache* c)
     v.cap_pad = c->cap_pad;
     v.row_limit = c->d.window > 0 ? c->d.window : c->d.capacity;
     v.replay_chunk = c->replay_chunk;
+    v.replay_horizon = c->replay_horizon;
     v.k = c->d.k;
     v.v = c->d.v;
     v.lens_dev = c->d.lens;
@@ -634,6 +648,15 @@ int32_t kvdec_set_replay_mode(kvdec_cache* c, int32_t chunk_rows)
     // the mirror does not see (a static cache takes no appends)
     if (chunk_rows == 0 && c->replay_chunk > 0 && !c->d.is_static) c->lens_known = false;
     c->replay_chunk = chunk_rows;
+    return KVDEC_OK;
+}
+
+int32_t kvdec_set_replay_horizon(kvdec_cache* c, int32_t tokens)
+{
+    g_err.clear();
+    if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
+    if (tokens < 0) return fail(KVDEC_E_INVALID, "tokens %d must be >= 0", tokens);
+    c->replay_horizon = tokens;
     return KVDEC_OK;
 }
 

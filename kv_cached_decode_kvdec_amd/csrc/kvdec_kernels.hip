@@ -1204,7 +1204,8 @@ __global__ __launch_bounds__(64) void merge_kernel(LensSrc<LM> ls, int B, int Hq
                                                     int T, int row_limit,
                                                     const float* __restrict__ part_o,
                                                     const float2* __restrict__ part_ml,
-                                                    float* __restrict__ out, PageMap pm)
+                                                    float* __restrict__ out, PageMap pm,
+                                                    int n_grid)
 {
     constexpr int plus = LensSrc<LM>::kPlus;
     const int lane = threadIdx.x & 63;
@@ -1219,15 +1220,22 @@ __global__ __launch_bounds__(64) void merge_kernel(LensSrc<LM> ls, int B, int Hq
     }
     acc = wave_sum_int(acc);
     const int len0 = ls.merge_get(b);
+    const int nch = max(1, (min(max(len0 + plus, 0), row_limit) + T - 1) / T);
+    // a replay grid sized with a horizon that the lengths have outgrown ends
+    // before this sequence's last chunk: no length bump, NaN rows
+    const bool covered = acc + nch <= n_grid;
     if constexpr (LM == kLensDeviceFused) {
         // the device-fused append's length bump (refused, like kvdec_append,
         // when a linear cache is full: row_limit is its capacity)
         // (and, in a paged cache, when the new row had no page)
-        if (h == 0 && lane == 0 && (ls.f.window > 0 || len0 < row_limit) &&
+        if (covered && h == 0 && lane == 0 && (ls.f.window > 0 || len0 < row_limit) &&
             (!pm.table || pm.table[static_cast<size_t>(b) * pm.stride + (len0 >> pm.pshift)] >= 0))
             ls.f.lens_out[b] = len0 + 1;
     }
-    const int nch = max(1, (min(max(len0 + plus, 0), row_limit) + T - 1) / T);
+    if (!covered) {
+        out[static_cast<size_t>(w) * kHeadDim + lane] = __int_as_float(0x7fc00000);
+        return;
+    }
     if (nch == 1) return;     // finished by the attend kernel
     const size_t first = static_cast<size_t>(acc);
 
@@ -1495,7 +1503,8 @@ hipError_t launch_merge(const AttendArgs& a, int group, const LensSrc<LM>& ls, f
     // one wave per workgroup: the waves spread over more CUs (whisper-base
     // 27.3 -> 26.6 us per step against four-wave workgroups)
     hipLaunchKernelGGL((merge_kernel<LM>), dim3(waves), dim3(64), 0, s, ls, a.batch,
-                       Hq, a.chunk_rows, a.row_limit, po, pml, a.out, pm);
+                       Hq, a.chunk_rows, a.row_limit, po, pml, a.out, pm,
+                       static_cast<int>(a.n_chunks));
     return hipGetLastError();
 }
 

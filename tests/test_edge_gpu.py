@@ -10,7 +10,8 @@
 - 48 KV heads (the launch grid's second dimension) in both kernel families;
 - two independent caches driven on two streams at once;
 - f32 launches large enough for the 16-wave workgroups (plain, fused, paged,
-  paged fused).
+  paged fused, and the device-length fused step on a replay grid sized with
+  a horizon).
 """
 import sys
 
@@ -162,7 +163,7 @@ def test_independent_caches_on_two_streams():
         assert c.lens() == s["lens"].tolist()
 
 
-@pytest.mark.parametrize("mode", ["attend", "fused", "paged", "paged_fused"])
+@pytest.mark.parametrize("mode", ["attend", "fused", "paged", "paged_fused", "replay_fused"])
 @pytest.mark.parametrize("group", [1, 2])
 def test_wide_workgroups(group, mode):
     """f32 with 1 or 2 query heads per KV head and at least four residency
@@ -204,10 +205,14 @@ def test_wide_workgroups(group, mode):
         c = KVCache(Bsz, Hkv, cap, "f32", lens=lens, k=to_device(K), v=to_device(V))
         kn = _rows(rng, (Bsz, Hkv, 64), "f32")
         vn = _rows(rng, (Bsz, Hkv, 64), "f32")
+        if mode == "replay_fused":          # device-length fused step on a horizon-sized grid
+            c.set_replay_mode(256)
+            c.set_replay_horizon(1)
         out = c.append_attend(to_device(kn), to_device(vn), to_device(q), chunk_rows=256)
         ln = oracle.append(K, V, kn, vn, lens)
         ref = oracle.attend(q, K, V, ln)
     torch.cuda.synchronize()
     assert_attention_close(out.cpu().numpy(), ref, "f32", f"wide group {group} {mode}")
-    if mode == "fused":
+    if mode in ("fused", "replay_fused"):
         assert to_host_bits(c.k).tobytes() == K.tobytes()
+        assert c.lens_dev.cpu().tolist() == ln.tolist()

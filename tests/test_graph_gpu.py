@@ -409,3 +409,73 @@ def test_paged_replay_fused_step_without_pages(dtype, Hq, Hkv):
     assert pc.lens_dev.cpu().tolist() == (new + 1).tolist()
     assert_attention_close(out2.cpu().numpy(), oracle.attend(q2, Kh, Vh, new + 1), dtype,
                            "paged replay fused, prepared")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_replay_horizon_sizes_grids_per_sequence(fused):
+    """With a replay horizon the captured launches cover each sequence's rows
+    at capture plus the horizon, not the capacity: replays within it match
+    the oracle; the replay whose lengths outgrow the grid gives NaN rows for
+    the sequence past its end (and, fused, leaves that length) and correct
+    rows for the others; resetting the lengths makes the graph valid again."""
+    rng = np.random.default_rng(31 + fused)
+    Bsz, Hkv, Hq, cap, T, H = 3, 2, 4, 256, 64, 2
+    start = np.array([62, 10, 122], np.int32)
+    cp = gen.padded_rows(cap)
+    hk = _rows(rng, (Bsz, Hkv, cp, 64), "f32")
+    hv = _rows(rng, (Bsz, Hkv, cp, 64), "f32")
+    c = KVCache(Bsz, Hkv, cap, "f32", lens=start, k=to_device(hk), v=to_device(hv))
+    c.set_replay_mode(T)
+    c.set_replay_horizon(H)
+    c.workspace(Hq)
+    kn = to_device(np.zeros((Bsz, Hkv, 64), np.float32))
+    vn = to_device(np.zeros((Bsz, Hkv, 64), np.float32))
+    q = torch.zeros(Bsz, Hq, 64, device="cuda")
+    out = torch.zeros(Bsz, Hq, 64, device="cuda")
+    torch.cuda.synchronize()
+    g = _new_graph()
+    with torch.cuda.graph(g):
+        if fused:
+            c.append_attend(kn, vn, q, out=out)
+        else:
+            c.append(kn, vn)
+            c.attend(q, out=out)
+    # rows at capture: start + 1 (the captured append advanced the mirror)
+    grid = int(sum(-(-min(int(n) + 1 + H, cap) // T) for n in start))
+    K, V = hk.copy(), hv.copy()
+    lens = start.copy()
+    for t in range(7):
+        rows = np.stack([K[b, :, lens[b]] for b in range(Bsz)]), np.stack([V[b, :, lens[b]] for b in range(Bsz)])
+        kn.copy_(to_device(rows[0]))
+        vn.copy_(to_device(rows[1]))
+        qh = rng.standard_normal((Bsz, Hq, 64), dtype=np.float32)
+        q.copy_(torch.from_numpy(qh).cuda())
+        g.replay()
+        torch.cuda.synchronize()
+        n = lens + 1
+        covered = np.cumsum([-(-int(x) // T) for x in n]) <= grid
+        got = out.cpu().numpy()
+        ref = oracle.attend(qh, K, V, n.astype(np.int32))
+        for b in range(Bsz):
+            if covered[b]:
+                assert_attention_close(got[b:b + 1], ref[b:b + 1], "f32", f"replay {t} seq {b}")
+            else:
+                assert np.isnan(got[b]).all(), f"replay {t} seq {b}: outgrown grid must give NaN"
+        if fused:
+            lens = np.where(covered, n, lens)
+        else:
+            lens = n
+        assert c.lens_dev.cpu().tolist() == lens.tolist()
+        if t < 6:
+            assert covered.all()
+        else:
+            assert covered.tolist() == [True, True, False]
+    c.reset_lens(start)
+    qh = rng.standard_normal((Bsz, Hq, 64), dtype=np.float32)
+    q.copy_(torch.from_numpy(qh).cuda())
+    kn.copy_(to_device(np.stack([K[b, :, start[b]] for b in range(Bsz)])))
+    vn.copy_(to_device(np.stack([V[b, :, start[b]] for b in range(Bsz)])))
+    g.replay()
+    torch.cuda.synchronize()
+    assert_attention_close(out.cpu().numpy(), oracle.attend(qh, K, V, start + 1), "f32",
+                           "after resetting the lengths")
