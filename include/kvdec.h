@@ -397,6 +397,12 @@ KVDEC_API int32_t kvdec_paged_append_attend(kvdec_paged* paged, const void* k_ne
  */
 KVDEC_API int32_t kvdec_paged_set_replay_mode(kvdec_paged* paged, int32_t chunk_rows, void* stream);
 
+/* kvdec_set_replay_horizon for a paged cache: replay grids cover each
+ * sequence's mirrored rows (in replay mode, the rows prepared so far) plus
+ * `tokens`, capped at max_pages_per_seq * page_rows; 0 sizes for that cap.
+ * Errors: KVDEC_E_INVALID (tokens < 0). */
+KVDEC_API int32_t kvdec_paged_set_replay_horizon(kvdec_paged* paged, int32_t tokens);
+
 /* In replay mode: give every sequence the pages for its next n_tokens rows
  * (from the pool, in sequence order, lowest-numbered first, as
  * kvdec_paged_append takes them), write them to the device block table on

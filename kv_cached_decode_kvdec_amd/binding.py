@@ -41,6 +41,7 @@ EXPORTED = [
     "kvdec_paged_append_attend",
     "kvdec_paged_set_replay_mode",
     "kvdec_paged_prepare",
+    "kvdec_paged_set_replay_horizon",
 ]
 
 
@@ -113,6 +114,7 @@ def load():
                                              _vp, _sz, _vp]),
         "kvdec_paged_set_replay_mode": (_i32, [_vp, _i32, _vp]),
         "kvdec_paged_prepare": (_i32, [_vp, _i32, _vp]),
+        "kvdec_paged_set_replay_horizon": (_i32, [_vp, _i32]),
         "kvdec_status_str": (ctypes.c_char_p, [_i32]),
         "kvdec_last_error": (ctypes.c_char_p, []),
     }
@@ -271,6 +273,10 @@ def kvdec_paged_set_replay_mode(handle, chunk_rows, stream=None):
 
 def kvdec_paged_prepare(handle, n_tokens, stream=None):
     _check(load().kvdec_paged_prepare(handle, int(n_tokens), stream), "kvdec_paged_prepare")
+
+
+def kvdec_paged_set_replay_horizon(handle, tokens):
+    _check(load().kvdec_paged_set_replay_horizon(handle, int(tokens)), "kvdec_paged_set_replay_horizon")
 
 
 def kvdec_append_attend(handle, k_new_ptr, v_new_ptr, q_ptr, n_q_heads, scale, chunk_rows, out_ptr,

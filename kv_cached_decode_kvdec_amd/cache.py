@@ -227,6 +227,9 @@ class PagedKVCache:
     def set_replay_mode(self, chunk_rows):
         B.kvdec_paged_set_replay_mode(self.handle, chunk_rows, current_stream())
 
+    def set_replay_horizon(self, tokens):
+        B.kvdec_paged_set_replay_horizon(self.handle, tokens)
+
     def prepare(self, n_tokens=1):
         """Replay mode: pages for every sequence's next n_tokens rows (call
         between graph replays)."""

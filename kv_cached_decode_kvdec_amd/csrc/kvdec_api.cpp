@@ -22,6 +22,7 @@ struct kvdec_paged {
     std::vector<int32_t> table;       // host mirror of d.block_table, -1: no page
     std::vector<int32_t> free_pages;  // pool pages not held by any sequence (a stack)
     int32_t replay_chunk = 0;         // > 0: replay mode with this fixed chunk size
+    int32_t replay_horizon = 0;       // > 0: replay grids sized for the lengths + this many appends
     // In replay mode `lens` counts the rows given pages by kvdec_paged_prepare
     // (an upper bound of the device lengths).  false after replay mode was
     // left: calls that need the exact lengths fail until kvdec_paged_truncate
@@ -368,6 +369,7 @@ AttendView paged_view_of(const kvdec_paged* p)
     v.cap_pad = 0;
     v.row_limit = static_cast<int32_t>(cap);
     v.replay_chunk = p->replay_chunk;
+    v.replay_horizon = p->replay_horizon;
     v.k = p->d.k_pages;
     v.v = p->d.v_pages;
     v.lens_dev = p->d.lens;
@@ -932,6 +934,15 @@ int32_t kvdec_paged_set_replay_mode(kvdec_paged* p, int32_t chunk_rows, void* st
     // not all have appended
     if (chunk_rows == 0 && p->replay_chunk > 0) p->lens_known = false;
     p->replay_chunk = chunk_rows;
+    return KVDEC_OK;
+}
+
+int32_t kvdec_paged_set_replay_horizon(kvdec_paged* p, int32_t tokens)
+{
+    g_err.clear();
+    if (!p) return fail(KVDEC_E_INVALID, "paged cache handle is NULL");
+    if (tokens < 0) return fail(KVDEC_E_INVALID, "tokens %d must be >= 0", tokens);
+    p->replay_horizon = tokens;
     return KVDEC_OK;
 }
 

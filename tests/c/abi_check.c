@@ -79,6 +79,7 @@ int main(void)
     CHECK(kvdec_paged_workspace_bytes(NULL, 4) == 0);
     CHECK(kvdec_paged_set_replay_mode(NULL, 64, NULL) == KVDEC_E_INVALID);
     CHECK(kvdec_set_replay_horizon(NULL, 4) == KVDEC_E_INVALID);
+    CHECK(kvdec_paged_set_replay_horizon(NULL, 4) == KVDEC_E_INVALID);
     CHECK(kvdec_paged_prepare(NULL, 1, NULL) == KVDEC_E_INVALID);
 
     printf("%d failed\n", fails);

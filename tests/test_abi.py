@@ -131,4 +131,5 @@ def test_replay_mode_argument_checks():
     assert lib.kvdec_set_replay_mode(None, 64) == B.KVDEC_E_INVALID
     assert lib.kvdec_paged_set_replay_mode(None, 64, None) == B.KVDEC_E_INVALID
     assert lib.kvdec_set_replay_horizon(None, 4) == B.KVDEC_E_INVALID
+    assert lib.kvdec_paged_set_replay_horizon(None, 4) == B.KVDEC_E_INVALID
     assert lib.kvdec_paged_prepare(None, 1, None) == B.KVDEC_E_INVALID

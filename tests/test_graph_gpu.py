@@ -245,6 +245,8 @@ def test_graph_replayed_paged_step(dtype, Hq, Hkv, P, rchunk, fused):
         pc = PagedKVCache(Bsz, Hkv, P, num_pages=Bsz * maxp, max_pages_per_seq=maxp, dtype=dtype)
         pc.load_contiguous(to_device(hk), to_device(hv), start)
         pc.set_replay_mode(rchunk)
+        if P == 32:                                 # grids sized for the replays ahead
+            pc.set_replay_horizon(T + 1)
         pc.workspace(Hq)
         layers.append(dict(hk=hk, hv=hv, pc=pc, kn=to_device(np.zeros((Bsz, Hkv, 64), hk.dtype)),
                            vn=to_device(np.zeros((Bsz, Hkv, 64), hk.dtype)),
