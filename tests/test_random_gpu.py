@@ -4,8 +4,9 @@ Each case draws a K/V dtype, a query-head group (1..8), a batch, a length
 law (empty sequences, lengths on and next to 32-row tile and 64-row chunk
 boundaries, short, long and log-uniform mixes), a chunk size, a scale, an
 input magnitude and an entry point (plain attend, the fused append + attend
-for two steps, the fused call at explicit positions, the paged layout, or the paged fused step for two
-steps),
+for two steps, the fused call at explicit positions, the paged layout, the paged fused step for two
+steps, or the fused step in replay mode -- device lengths, capacity-sized
+or horizon-sized grids -- for two steps),
 and compares the output with the oracle.  The fused cases also compare the
 cache contents and lengths bit for bit with the oracle's append.  A few
 cases use batches above the one-launch fused limits (512 sequences, 256
@@ -34,8 +35,8 @@ from helpers import assert_attention_close
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 128
-MODES = ["attend", "fused", "fused_at", "paged", "ring", "ring_at", "cross", "paged_fused"]
+N_CASES = 144
+MODES = ["attend", "fused", "fused_at", "paged", "ring", "ring_at", "cross", "paged_fused", "replay"]
 
 
 def _draw_lens(rng, Bsz):
@@ -67,7 +68,7 @@ def _case(i):
     Hkv = int(rng.integers(1, 5))
     group = int(rng.integers(1, 9))
     mode = MODES[i % len(MODES)]
-    if i % 16 == 5 and mode in ("attend", "fused", "fused_at"):
+    if i % 16 == 5 and mode in ("attend", "fused", "fused_at", "replay"):
         Bsz = int(rng.integers(513, 600))         # above the one-launch fused batch
         lens = rng.integers(0, 40, size=Bsz)
     elif mode == "paged_fused" and i % 3 == 0:
@@ -197,13 +198,16 @@ def test_random_case(i):
         assert_attention_close(out.cpu().numpy(), oracle.attend(q, K, V, lens, scale), dtype, what)
         return
 
+    if mode == "replay":
+        c.set_replay_mode(int(rng.choice([64, 128, 256, -1])))
+        c.set_replay_horizon(int(rng.integers(0, 4)))
     Kh, Vh, ln = K.copy(), V.copy(), lens.copy()
-    steps = 2 if mode == "fused" else 1
+    steps = 2 if mode in ("fused", "replay") else 1
     for st in range(steps):
         kn = _rows(rng, (Bsz, Hkv, 64), dtype, s)
         vn = _rows(rng, (Bsz, Hkv, 64), dtype, s)
         q = (rng.standard_normal((Bsz, Hq, 64)) * s).astype(np.float32)
-        if mode == "fused":
+        if mode in ("fused", "replay"):
             out = c.append_attend(to_device(kn), to_device(vn), to_device(q), scale=scale, chunk_rows=T)
         else:
             pos = (rng.random(Bsz) * (ln + 1)).astype(np.int32)   # rewind to any position <= len
