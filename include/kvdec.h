@@ -375,18 +375,19 @@ KVDEC_API int32_t kvdec_paged_append_attend(kvdec_paged* paged, const void* k_ne
  * over the paged cache of [WA-DEC] `PagedDecoderKVCache`).  chunk_rows as
  * for kvdec_set_replay_mode (> 0, KVDEC_REPLAY_AUTO, or 0 to leave).  In
  * replay mode kvdec_paged_attend is launched for max_pages_per_seq *
- * page_rows rows with the merge launch always made, kvdec_paged_append and
+ * page_rows rows (or per sequence, kvdec_paged_set_replay_horizon) with the
+ * merge launch always made, kvdec_paged_append and
  * kvdec_paged_append_attend read the lengths from the device (the latter as
  * one attend launch that stores the new rows, plus the merge launch, which
  * bumps the lengths), and an append takes no page: every row's page must
  * already be in the block table, put there by kvdec_paged_prepare (outside
  * the graph) before the replays that append it.  An append whose row has no
  * page leaves that sequence's row and length unchanged (and
- * kvdec_paged_append_attend then attends the rows the sequence had).  Entering replay
- * mode sets -1 on `stream` in every block table entry past a sequence's
- * pages, and in replay mode pages returned to the pool (kvdec_paged_release,
- * kvdec_paged_truncate) get -1 there too, so such a row never lands in
- * another sequence's page.  The host mirror counts the prepared rows, which
+ * kvdec_paged_append_attend then attends the rows the sequence had).
+ * Entering replay mode sets -1 on `stream` in every block table entry past a
+ * sequence's pages, and in replay mode pages returned to the pool
+ * (kvdec_paged_release, kvdec_paged_truncate) get -1 there too, so such a
+ * row never lands in another sequence's page.  The host mirror counts the prepared rows, which
  * the replays may not all have appended, so leaving replay mode (0) makes
  * calls that need the exact lengths (kvdec_paged_append, kvdec_paged_attend,
  * kvdec_paged_append_attend, kvdec_paged_reserve, kvdec_paged_get_lens,
@@ -399,8 +400,9 @@ KVDEC_API int32_t kvdec_paged_set_replay_mode(kvdec_paged* paged, int32_t chunk_
 
 /* kvdec_set_replay_horizon for a paged cache: replay grids cover each
  * sequence's mirrored rows (in replay mode, the rows prepared so far) plus
- * `tokens`, capped at max_pages_per_seq * page_rows; 0 sizes for that cap.
- * Errors: KVDEC_E_INVALID (tokens < 0). */
+ * `tokens`, capped at max_pages_per_seq * page_rows, with NaN output rows
+ * for a sequence a replay has outgrown; 0 sizes for that cap.  Errors:
+ * KVDEC_E_INVALID (tokens < 0). */
 KVDEC_API int32_t kvdec_paged_set_replay_horizon(kvdec_paged* paged, int32_t tokens);
 
 /* In replay mode: give every sequence the pages for its next n_tokens rows
