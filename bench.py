@@ -688,6 +688,9 @@ def main():
         "graph_steps_per_s": round(h.get("graph_steps_per_s", 0.0), 2),
         "cold_pct_of_hbm_peak": round(h.get("cold_pct_of_hbm_peak", 0.0), 2),
         "copy_kernel_gbps": round(copy_gbps, 1),
+        # the step's effective rate against a plain device copy measured in the
+        # same run (a copy reads and writes, so a read-mostly step can exceed it)
+        "pct_of_copy_kernel": round(100.0 * h["effective_gbps"] / copy_gbps, 1) if copy_gbps > 0 else None,
         "roofline": {"bound": "hbm",
                      "kernel": kname or "attend kernel (one launch per attend call)",
                      "achieved": round(h["attend_gbps"], 1), "peak": HBM_PEAK_GBPS,
