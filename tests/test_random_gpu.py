@@ -5,8 +5,9 @@ law (empty sequences, lengths on and next to 32-row tile and 64-row chunk
 boundaries, short, long and log-uniform mixes), a chunk size, a scale, an
 input magnitude and an entry point (plain attend, the fused append + attend
 for two steps, the fused call at explicit positions, the paged layout, the paged fused step for two
-steps, or the fused step in replay mode -- device lengths, capacity-sized
-or horizon-sized grids -- for two steps),
+steps, the fused step in replay mode -- device lengths, capacity-sized
+or horizon-sized grids -- for two steps, or the paged fused step in replay
+mode with its pages given ahead, for two steps),
 and compares the output with the oracle.  The fused cases also compare the
 cache contents and lengths bit for bit with the oracle's append.  A few
 cases use batches above the one-launch fused limits (512 sequences, 256
@@ -35,8 +36,9 @@ from helpers import assert_attention_close
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 144
-MODES = ["attend", "fused", "fused_at", "paged", "ring", "ring_at", "cross", "paged_fused", "replay"]
+N_CASES = 160
+MODES = ["attend", "fused", "fused_at", "paged", "ring", "ring_at", "cross", "paged_fused", "replay",
+         "paged_replay"]
 
 
 def _draw_lens(rng, Bsz):
@@ -71,7 +73,7 @@ def _case(i):
     if i % 16 == 5 and mode in ("attend", "fused", "fused_at", "replay"):
         Bsz = int(rng.integers(513, 600))         # above the one-launch fused batch
         lens = rng.integers(0, 40, size=Bsz)
-    elif mode == "paged_fused" and i % 3 == 0:
+    elif mode in ("paged_fused", "paged_replay") and i % 3 == 0:
         Bsz = int(rng.integers(257, 300))         # above the one-launch paged fused batch
         lens = rng.integers(0, 40, size=Bsz)
     else:
@@ -122,14 +124,19 @@ def test_random_case(i):
     V = _rows(rng, (Bsz, Hkv, cap_pad, 64), dtype, s)
     what = f"case {i} ({mode} {dtype} B={Bsz} Hq={Hq} Hkv={Hkv} T={T})"
 
-    if mode == "paged_fused":
+    if mode in ("paged_fused", "paged_replay"):
         P = int(rng.choice([16, 32, 64, 128]))
         max_pages = (cap + P - 1) // P
         pc = PagedKVCache(Bsz, Hkv, P, num_pages=Bsz * max_pages + 3, max_pages_per_seq=max_pages,
                           dtype=dtype)
         pc.load_contiguous(to_device(K), to_device(V), lens)
+        if mode == "paged_replay":
+            pc.set_replay_mode(int(rng.choice([64, 128, 256, -1])))
+            pc.set_replay_horizon(int(rng.integers(0, 4)))
         Kh, Vh, ln = K.copy(), V.copy(), lens.copy()
         for st in range(2):
+            if mode == "paged_replay":
+                pc.prepare(1)
             kn = _rows(rng, (Bsz, Hkv, 64), dtype, s)
             vn = _rows(rng, (Bsz, Hkv, 64), dtype, s)
             q = (rng.standard_normal((Bsz, Hq, 64)) * s).astype(np.float32)
