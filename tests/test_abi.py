@@ -133,3 +133,18 @@ def test_replay_mode_argument_checks():
     assert lib.kvdec_set_replay_horizon(None, 4) == B.KVDEC_E_INVALID
     assert lib.kvdec_paged_set_replay_horizon(None, 4) == B.KVDEC_E_INVALID
     assert lib.kvdec_paged_prepare(None, 1, None) == B.KVDEC_E_INVALID
+
+
+def test_binding_signatures_match_header_arity():
+    """Every ctypes signature the binding sets has as many arguments as the
+    header's declaration (a missing stream or handle argument would shift
+    every later argument)."""
+    with open(os.path.join(ROOT, "include", "kvdec.h")) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    lib = B.load()
+    decls = re.findall(r"KVDEC_API\s+[^;]*?\b(kvdec_[a-z_]+)\s*\(([^)]*)\)\s*;", text)
+    assert len(decls) == len(B.EXPORTED)
+    for name, params in decls:
+        params = params.strip()
+        n = 0 if params in ("", "void") else params.count(",") + 1
+        assert len(getattr(lib, name).argtypes) == n, name
