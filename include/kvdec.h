@@ -19,8 +19,12 @@
  *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
  *     Work is enqueued asynchronously on it, in call order.
  *   - Device pointers must be non-NULL and 16-byte aligned.
- *   - Return value: KVDEC_OK or a kvdec_status error code.  On error nothing
- *     has been enqueued and no device or host state has changed;
+ *   - Return value: KVDEC_OK or a kvdec_status error code.  Every argument,
+ *     shape and capacity check runs before anything is enqueued: on any
+ *     error other than KVDEC_E_HIP nothing has been enqueued and no device
+ *     or host state has changed.  KVDEC_E_HIP means a launch was refused by
+ *     the runtime; launches the call made before it stay enqueued, and the
+ *     host mirrors describe what they do (calls where that matters say so).
  *     kvdec_last_error() describes the failure (thread-local string).
  *   - head_dim is 64.  K/V elements are IEEE binary32 (KVDEC_F32) or
  *     bfloat16 bit patterns (KVDEC_BF16); q and out are always binary32.
@@ -201,7 +205,12 @@ KVDEC_API size_t kvdec_workspace_bytes(const kvdec_cache* cache, int32_t n_q_hea
  * chunk_rows: rows per split-sequence chunk; 0 picks automatically, else a
  * multiple of 64 in [KVDEC_MIN_CHUNK, KVDEC_MAX_CHUNK].  For a given
  * chunk_rows the result for a sequence is bitwise independent of the other
- * sequences in the batch.  One kernel launch per call, plus a log-sum-exp
+ * sequences in the batch (and of the batch size), and bitwise the same
+ * through kvdec_attend_self, kvdec_append_attend and
+ * kvdec_append_attend_at; the one exception is replay mode without a
+ * horizon, whose capacity-sized grids may split a chunk's rows over waves
+ * differently from other launches (results within the tolerance, not
+ * bitwise equal to them).  One kernel launch per call, plus a log-sum-exp
  * merge launch when some sequence spans more than one chunk.
  * Errors: KVDEC_E_SHAPE (n_q_heads not a positive multiple of n_kv_heads, or
  * group > KVDEC_MAX_GROUP), KVDEC_E_STATIC, KVDEC_E_WORKSPACE, KVDEC_E_INVALID,
@@ -242,8 +251,11 @@ KVDEC_API int32_t kvdec_append_attend(kvdec_cache* cache, const void* k_new, con
  * one; afterwards it holds lens_host[b] + 1.  Where
  * kvdec_append_attend is one launch, the positions go to it by value and it
  * writes the device lengths, so the rewind costs no launch of its own;
- * otherwise the lengths are set on the device first.  Errors: those of the
- * two calls (a linear cache needs lens_host[b] < capacity).
+ * otherwise the lengths are set on the device first (a launch of its own),
+ * and if the attend launch is then refused (KVDEC_E_HIP) the lengths stay
+ * set to lens_host, on the device and in the host mirror alike, as after
+ * kvdec_reset_lens.  Errors: those of the two calls (a linear cache needs
+ * lens_host[b] < capacity).
  */
 KVDEC_API int32_t kvdec_append_attend_at(kvdec_cache* cache, const int32_t* lens_host,
                                          const void* k_new, const void* v_new, const float* q,

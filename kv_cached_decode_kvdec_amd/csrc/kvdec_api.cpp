@@ -226,12 +226,16 @@ int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, floa
             }
             a.n_chunks = chunks_for(r, a.chunk_rows);
         }
+        // the device lengths may grow up to the row limit between replays
+        a.one_chunk = per_seq <= 1 ? 1 : 0;
     } else {
         a.chunk_rows = chunk_rows ? chunk_rows
                                   : auto_chunk(v.rows, v.n_kv_heads, esz_of(v.dtype),
                                                kvdec::resident_attend_blocks(v.dtype, group));
         a.n_chunks = chunks_for(v.rows, a.chunk_rows);
         a.need_merge = a.n_chunks > v.batch;   // some sequence has more than one chunk
+        // the launch reads the lengths the grid was sized from
+        a.one_chunk = a.n_chunks == v.batch ? 1 : 0;
     }
     a.qscale = scale * 1.4426950408889634f;
     a.out = out;

@@ -39,6 +39,8 @@ struct AttendArgs {
     int32_t chunk_rows;     // rows per split-sequence chunk
     int64_t n_chunks;       // sum over sequences of max(1, ceil(len / chunk_rows))
     bool need_merge;        // some sequence spans more than one chunk
+    int32_t one_chunk = 0;  // 1: every sequence has exactly one chunk, whatever the
+                            // device lengths (grid index = sequence)
     bool replay = false;    // capacity-sized grid (replay mode): surplus workgroups exit at once
     float qscale;           // scale * log2(e)
     float* out;

@@ -205,11 +205,12 @@ __device__ __forceinline__ uint4 load16_stream(const char* p)
 // consecutive indices starting at the exclusive prefix sum (an empty
 // sequence keeps one chunk with no rows, which writes its zero row).  Done by one wave with a
 // 64-wide scan per group of 64 sequences; all lanes return the same values.
-// A grid of exactly B workgroups (along x) means every sequence has one
-// chunk (the launch sizes the grid as the sum of the chunk counts, each at
-// least 1, from the same lengths the kernel reads; in replay mode the grid
-// has B workgroups only when the row limit fits one chunk): then chunk blk
-// is sequence blk and no scan is needed.
+// When the host knows that every sequence has exactly one chunk (one_chunk:
+// outside replay mode the grid was sized from the same lengths the kernel
+// reads and has B workgroups; in replay mode the row limit fits one chunk),
+// chunk blk is sequence blk and no scan is needed.  The grid size alone does
+// not tell: a replay grid sized with a horizon can have B workgroups while
+// the device lengths have grown past one chunk.
 struct Located {
     int b, c, len, nch;
 };
@@ -309,9 +310,9 @@ __device__ __forceinline__ int wave_inclusive_sum(int x)
 
 template <int LM>
 __device__ __forceinline__ bool locate(const LensSrc<LM>& ls, int B, int T, int cap, int blk,
-                                       int lane, Located& r)
+                                       int lane, int one_chunk, Located& r)
 {
-    if (static_cast<int>(gridDim.x) == B) {
+    if (one_chunk) {
         const int ln = min(max(ls.get(blk) + LensSrc<LM>::kPlus, 0), cap);
         r.b = blk;
         r.c = 0;
@@ -774,7 +775,7 @@ template <int ESZ, int GROUP, int WAVES, int U, bool PAGED, int LM>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(valu_min_waves<ESZ, GROUP>())))
 void attend_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
-    LensSrc<LM> ls, int B, int Hkv, int cap_pad, int row_limit, int T,
+    LensSrc<LM> ls, int B, int Hkv, int cap_pad, int row_limit, int T, int one_chunk,
     float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
     PageMap pm)
 {
@@ -788,7 +789,7 @@ void attend_kernel(
     const int Hq = Hkv * GROUP;
 
     Located loc;
-    if (!locate<LM>(ls, B, T, row_limit, blockIdx.x, lane, loc)) return;
+    if (!locate<LM>(ls, B, T, row_limit, blockIdx.x, lane, one_chunk, loc)) return;
     const int row0 = loc.c * T;
     int row_end = min(loc.len, row0 + T);   // lowered where a replayed row has no page
 
@@ -971,7 +972,7 @@ template <int GROUP, int WAVES, bool PAGED, int LM>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void attend_gqa_mfma_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
-    LensSrc<LM> ls, int B, int Hkv, int cap_pad, int row_limit, int T,
+    LensSrc<LM> ls, int B, int Hkv, int cap_pad, int row_limit, int T, int one_chunk,
     float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
     PageMap pm)
 {
@@ -993,7 +994,7 @@ void attend_gqa_mfma_kernel(
     __shared__ __attribute__((aligned(16))) char sm_stage[WAVES * kStage];
 
     Located loc;
-    if (!locate<LM>(ls, B, T, row_limit, blockIdx.x, lane, loc)) return;
+    if (!locate<LM>(ls, B, T, row_limit, blockIdx.x, lane, one_chunk, loc)) return;
     const int row0 = loc.c * T;
     int row_end = min(loc.len, row0 + T);   // lowered where a replayed row has no page
 
@@ -1470,26 +1471,29 @@ constexpr int kUnroll = 4;
 
 constexpr int kWideWaves = 16;
 
-// 16-wave workgroups of this VALU kernel resident at once on the device, or
-// -1 when fewer than two fit on a CU (occupancy query, once per
-// instantiation).
-template <int GROUP, bool PAGED, int LM>
-int wide_resident()
+// Whether two 16-wave workgroups of the f32 VALU kernel for GROUP fit on a
+// CU (occupancy query of the plain contiguous instance, once).  The answer
+// depends on the kernel alone, never on the launch, so every call with the
+// same chunk size picks the same wave count: a sequence's rows are split
+// over waves and row slots the same way whatever else is in the batch, and
+// in the fused and unfused forms alike (the two wave counts sum a chunk's
+// rows in different orders, so they differ in the last bits).
+template <int GROUP>
+bool wide_fits()
 {
-    static std::atomic<int> known{0};       // 0: not asked yet
+    static std::atomic<int> known{0};       // 0: not asked yet, 1: fits, -1: does not
     int k = known.load(std::memory_order_relaxed);
     if (k == 0) {
-        int per_cu = 0, dev = 0, cus = 0;
+        int per_cu = 0;
         const bool ok =
             hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, reinterpret_cast<const void*>(&attend_kernel<4, GROUP, kWideWaves, kUnroll, PAGED, LM>),
-                kWideWaves * 64, 0) == hipSuccess &&
-            hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
-        k = (ok && per_cu >= 2 && cus > 0) ? per_cu * cus : -1;
+                &per_cu,
+                reinterpret_cast<const void*>(&attend_kernel<4, GROUP, kWideWaves, kUnroll, false, kLensDevice>),
+                kWideWaves * 64, 0) == hipSuccess;
+        k = (ok && per_cu >= 2) ? 1 : -1;
         known.store(k, std::memory_order_relaxed);
     }
-    return k;
+    return k > 0;
 }
 
 // The merge launch after an attend launch, when some sequence spans several chunks.
@@ -1547,20 +1551,17 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
     hipError_t e = hipSuccess;
     if constexpr (ESZ == 4 && GROUP <= 2) {
         // f32 with 1 or 2 query heads per KV head: chunks of >= 256 rows run
-        // on 16-wave workgroups (each wave one pass of 16 rows) where two of
-        // them fit on a CU and the grid fills at least four residency rounds
-        // of them (with fewer, the last partial round costs more than the
-        // wide workgroups gain: whisper-base's cross-attention, 1.5 rounds).
-        // Not for capacity-sized replay grids: there a surplus workgroup
+        // on 16-wave workgroups (each wave one pass of 16 rows per 256 rows)
+        // where two of them fit on a CU.  The choice depends on the chunk
+        // size and the kernel only (see wide_fits), not on the grid.  Not
+        // for capacity-sized replay grids: there a surplus workgroup
         // launches and retires 16 waves for nothing (qwen2-0.5b replayed:
         // 83.3 us per step on 16-wave, 80.1 on 4-wave workgroups).
-        const int rw = wide_resident<GROUP, PAGED, LM>();
-        if (!a.replay && a.chunk_rows >= kWideWaves * kUnroll * Lay<4>::kRPI && rw > 0 &&
-            a.n_chunks * a.n_kv_heads >= 4 * static_cast<int64_t>(rw)) {
+        if (!a.replay && a.chunk_rows >= kWideWaves * kUnroll * Lay<4>::kRPI && wide_fits<GROUP>()) {
             hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWideWaves, kUnroll, PAGED, LM>), grid,
                                dim3(kWideWaves * 64), 0, s, a.q, static_cast<const char*>(a.k),
                                static_cast<const char*>(a.v), ls, a.batch, a.n_kv_heads, a.cap_pad,
-                               a.row_limit, a.chunk_rows, a.qscale, a.out, po, pml, pm);
+                               a.row_limit, a.chunk_rows, a.one_chunk, a.qscale, a.out, po, pml, pm);
             e = hipGetLastError();
             return e != hipSuccess ? e : launch_merge<LM>(a, GROUP, ls, po, pml, pm, s);
         }
@@ -1568,13 +1569,13 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
     if constexpr (ESZ == 2 && GROUP >= 2)
         hipLaunchKernelGGL((attend_gqa_mfma_kernel<GROUP, kWaves, PAGED, LM>), grid, block, 0, s,
                            a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v), ls,
-                           a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows, a.qscale,
+                           a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows, a.one_chunk, a.qscale,
                            a.out, po, pml, pm);
     else
         hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWaves, kUnroll, PAGED, LM>), grid, block,
                            0, s, a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v),
                            ls, a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows,
-                           a.qscale, a.out, po, pml, pm);
+                           a.one_chunk, a.qscale, a.out, po, pml, pm);
     e = hipGetLastError();
     return e != hipSuccess ? e : launch_merge<LM>(a, GROUP, ls, po, pml, pm, s);
 }

@@ -116,31 +116,28 @@ def test_fused_ring(dtype, Hq, Hkv, W):
     assert to_host_bits(one.v).tobytes() == to_host_bits(two.v).tobytes()
 
 
-def test_fused_full_size_workloads():
-    """Every self-attention workload at its real shape, every step, sampled rows
-    against the oracle and the whole cache bit for bit."""
-    sample = {"whisper-tiny": None, "whisper-base": None, "whisper-large": [0, 31, 63],
-              "qwen2-0.5b": [0, 13, 31], "gqa": [0, 21, 42, 63]}
-    for name in gen.ORDER:
-        wl = gen.WORKLOADS[name]
-        _log(f"fused full {name}")
-        inp = gen.make_inputs(wl)
-        c = KVCache(len(inp.lens), wl.n_kv_heads, inp.cap, wl.dtype, lens=inp.lens,
-                    k=to_device(inp.k_cache), v=to_device(inp.v_cache))
-        Kh, Vh, lens = inp.k_cache.copy(), inp.v_cache.copy(), inp.lens.copy()
-        bs = np.arange(len(lens)) if sample[name] is None else np.asarray(sample[name])
-        for s in range(wl.steps):
-            out = c.append_attend(to_device(inp.k_new[s]), to_device(inp.v_new[s]),
-                                  to_device(inp.q_self[s]))
-            torch.cuda.synchronize()
-            lens = oracle.append(Kh, Vh, inp.k_new[s], inp.v_new[s], lens)
-            ref = oracle.attend(inp.q_self[s][bs], Kh[bs], Vh[bs], lens[bs])
-            assert_attention_close(out.cpu().numpy()[bs], ref, wl.dtype, f"{name} step {s}")
-        assert to_host_bits(c.k).tobytes() == Kh.tobytes()
-        assert to_host_bits(c.v).tobytes() == Vh.tobytes()
-        assert c.lens_dev.cpu().tolist() == lens.tolist()
-        del c
-        torch.cuda.empty_cache()
+@pytest.mark.parametrize("name", gen.ORDER)
+def test_fused_full_size_workloads(name):
+    """Every self-attention workload at its real shape and automatic chunk
+    size, every step, every sequence and head against the oracle, and the
+    whole cache bit for bit."""
+    wl = gen.WORKLOADS[name]
+    _log(f"fused full {name}")
+    inp = gen.make_inputs(wl)
+    c = KVCache(len(inp.lens), wl.n_kv_heads, inp.cap, wl.dtype, lens=inp.lens,
+                k=to_device(inp.k_cache), v=to_device(inp.v_cache))
+    Kh, Vh, lens = inp.k_cache.copy(), inp.v_cache.copy(), inp.lens.copy()
+    for s in range(wl.steps):
+        out = c.append_attend(to_device(inp.k_new[s]), to_device(inp.v_new[s]),
+                              to_device(inp.q_self[s]))
+        torch.cuda.synchronize()
+        lens = oracle.append(Kh, Vh, inp.k_new[s], inp.v_new[s], lens)
+        ref = oracle.attend(inp.q_self[s], Kh, Vh, lens)
+        assert_attention_close(out.cpu().numpy(), ref, wl.dtype, f"{name} step {s}")
+    assert to_host_bits(c.k).tobytes() == Kh.tobytes()
+    assert to_host_bits(c.v).tobytes() == Vh.tobytes()
+    assert c.lens_dev.cpu().tolist() == lens.tolist()
+    c.close()
 
 
 @pytest.mark.parametrize("mode", ["large-batch", "replay"])

@@ -481,3 +481,72 @@ def test_replay_horizon_sizes_grids_per_sequence(fused):
     torch.cuda.synchronize()
     assert_attention_close(out.cpu().numpy(), oracle.attend(qh, K, V, start + 1), "f32",
                            "after resetting the lengths")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_replay_horizon_one_chunk_grid_outgrown(fused):
+    """A horizon grid with exactly one workgroup per sequence (rows at capture
+    plus the horizon fit one chunk) while the capacity spans several chunks:
+    the launch must still find each workgroup's sequence from the device
+    lengths (the grid size says nothing about them).  Once sequence 0 grows
+    past one chunk the grid no longer reaches sequence 2: its output rows
+    are NaN and, fused, its row is not stored and its length stays; the
+    other sequences stay exact, sequence 0 over its two chunks included."""
+    rng = np.random.default_rng(41 + fused)
+    Bsz, Hkv, Hq, cap, T, H = 3, 2, 4, 256, 64, 2
+    start = np.array([60, 20, 30], np.int32)      # rows at capture: 61, 21, 31 (+2 fit 64)
+    cp = gen.padded_rows(cap)
+    hk = _rows(rng, (Bsz, Hkv, cp, 64), "f32")
+    hv = _rows(rng, (Bsz, Hkv, cp, 64), "f32")
+    c = KVCache(Bsz, Hkv, cap, "f32", lens=start, k=to_device(hk), v=to_device(hv))
+    c.set_replay_mode(T)
+    c.set_replay_horizon(H)
+    c.workspace(Hq)
+    kn = to_device(np.zeros((Bsz, Hkv, 64), np.float32))
+    vn = to_device(np.zeros((Bsz, Hkv, 64), np.float32))
+    q = torch.zeros(Bsz, Hq, 64, device="cuda")
+    out = torch.zeros(Bsz, Hq, 64, device="cuda")
+    torch.cuda.synchronize()
+    g = _new_graph()
+    with torch.cuda.graph(g):
+        if fused:
+            c.append_attend(kn, vn, q, out=out)
+        else:
+            c.append(kn, vn)
+            c.attend(q, out=out)
+    grid = Bsz                                     # one chunk per sequence at capture + H
+    K, V = hk.copy(), hv.copy()
+    lens = start.copy()
+    cache_k = to_host_bits(c.k)
+    seen_outgrown = False
+    for t in range(6):
+        new_k = _rows(rng, (Bsz, Hkv, 64), "f32")
+        new_v = _rows(rng, (Bsz, Hkv, 64), "f32")
+        kn.copy_(to_device(new_k))
+        vn.copy_(to_device(new_v))
+        qh = rng.standard_normal((Bsz, Hq, 64), dtype=np.float32)
+        q.copy_(torch.from_numpy(qh).cuda())
+        g.replay()
+        torch.cuda.synchronize()
+        n = lens + 1
+        covered = np.cumsum([-(-int(x) // T) for x in n]) <= grid
+        seen_outgrown |= not covered.all()
+        for b in range(Bsz):
+            if covered[b] or not fused:
+                K[b, :, lens[b]], V[b, :, lens[b]] = new_k[b], new_v[b]
+        got = out.cpu().numpy()
+        for b in range(Bsz):
+            if covered[b]:
+                ref = oracle.attend(qh[b:b + 1], K[b:b + 1], V[b:b + 1], n[b:b + 1].astype(np.int32))
+                assert_attention_close(got[b:b + 1], ref, "f32", f"replay {t} seq {b}")
+            else:
+                assert np.isnan(got[b]).all(), f"replay {t} seq {b}: outgrown grid must give NaN"
+        lens = np.where(covered, n, lens) if fused else n
+        assert c.lens_dev.cpu().tolist() == lens.tolist(), f"replay {t}"
+        if fused:
+            # the sequence the grid no longer reaches got no row: its cache is as it was
+            now_k = to_host_bits(c.k)
+            for b in np.flatnonzero(~covered):
+                assert now_k[b].tobytes() == cache_k[b].tobytes(), f"replay {t} seq {b} cache"
+            cache_k = now_k
+    assert seen_outgrown
