@@ -71,6 +71,7 @@ typedef enum { KVDEC_F32 = 0, KVDEC_BF16 = 1 } kvdec_dtype;
 #define KVDEC_REPLAY_AUTO (-1) /* kvdec_set_replay_mode: pick the chunk from current lengths */
 #define KVDEC_MAX_FUSED_BATCH 512 /* largest batch kvdec_append_attend runs as one launch */
 #define KVDEC_MAX_PAGED_FUSED_BATCH 256 /* largest batch kvdec_paged_append_attend runs as one launch */
+#define KVDEC_NOALLOC_SCRATCH_BYTES 16777216 /* device scratch of kvdec_append_attend_noalloc (16 MiB per GPU) */
 
 /* Opaque host-side handle: the cache description plus a host mirror of the
  * per-sequence lengths (used for validation and launch sizing, so no call
@@ -241,6 +242,33 @@ KVDEC_API int32_t kvdec_append_attend(kvdec_cache* cache, const void* k_new, con
                                       const float* q, int32_t n_q_heads, float scale,
                                       int32_t chunk_rows, float* out, void* ws, size_t ws_bytes,
                                       void* stream);
+
+/*
+ * kvdec_append_attend for callers that cannot allocate device memory or pass
+ * a workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same step, the same kernels and bitwise the
+ * same results, cache bytes and lengths, with the split-sequence partials
+ * held in the library's own device scratch instead of a workspace
+ * argument.  The call allocates and frees nothing.  The scratch is a
+ * static array of KVDEC_NOALLOC_SCRATCH_BYTES on each GPU the library runs
+ * on (held until the process ends); its address is looked up once per GPU,
+ * on the first call made with that GPU current.  A call needs
+ * 264 * n_q_heads * C + 4 * batch bytes of it (each part rounded up to 256
+ * bytes), where C is the number of chunks of the launch: the sum over
+ * sequences of max(1, ceil(rows / chunk_rows)) with rows = lens[b] + 1 (the
+ * window of a ring at most), or, in replay mode, the rows a sequence can
+ * reach (the capacity or the horizon).  Larger calls fail with
+ * KVDEC_E_WORKSPACE before anything is enqueued.  Every call on one GPU
+ * shares its scratch, and the scratch keeps only what the last call left:
+ * calls whose launches overlap on one GPU (other streams, other threads,
+ * other handles) race and must be ordered by the caller.  Arguments and
+ * other errors as kvdec_append_attend without ws / ws_bytes; KVDEC_E_HIP
+ * also when the scratch address cannot be found.
+ */
+KVDEC_API int32_t kvdec_append_attend_noalloc(kvdec_cache* cache, const void* k_new,
+                                              const void* v_new, const float* q,
+                                              int32_t n_q_heads, float scale, int32_t chunk_rows,
+                                              float* out, void* stream);
 
 /*
  * kvdec_reset_lens(lens_host) then kvdec_append_attend, as one call: the

@@ -26,6 +26,7 @@ MAX_CHUNK = 4096
 MAX_GROUP = 8
 KVDEC_MAX_FUSED_BATCH = 512
 KVDEC_MAX_PAGED_FUSED_BATCH = 256
+KVDEC_NOALLOC_SCRATCH_BYTES = 16777216
 
 EXPORTED = [
     "kvdec_padded_capacity", "kvdec_cache_create", "kvdec_cache_destroy", "kvdec_reset_lens",
@@ -42,6 +43,7 @@ EXPORTED = [
     "kvdec_paged_set_replay_mode",
     "kvdec_paged_prepare",
     "kvdec_paged_set_replay_horizon",
+    "kvdec_append_attend_noalloc",
 ]
 
 
@@ -99,6 +101,8 @@ def load():
                                        _vp]),
         "kvdec_append_attend_at": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float, _i32, _vp,
                                           _vp, _sz, _vp]),
+        "kvdec_append_attend_noalloc": (_i32, [_vp, _vp, _vp, _vp, _i32, ctypes.c_float, _i32, _vp,
+                                               _vp]),
         "kvdec_paged_create": (_i32, [ctypes.POINTER(PagedDesc), _vp, ctypes.POINTER(_vp)]),
         "kvdec_paged_destroy": (None, [_vp]),
         "kvdec_paged_append": (_i32, [_vp, _vp, _vp, _vp]),
@@ -294,3 +298,10 @@ def kvdec_append_attend_at(handle, lens_host, k_new_ptr, v_new_ptr, q_ptr, n_q_h
     _check(load().kvdec_append_attend_at(handle, lens_host, k_new_ptr, v_new_ptr, q_ptr,
                                          int(n_q_heads), float(scale), int(chunk_rows), out_ptr,
                                          ws_ptr, int(ws_bytes), stream), "kvdec_append_attend_at")
+
+
+def kvdec_append_attend_noalloc(handle, k_new_ptr, v_new_ptr, q_ptr, n_q_heads, scale, chunk_rows,
+                                out_ptr, stream=None):
+    _check(load().kvdec_append_attend_noalloc(handle, k_new_ptr, v_new_ptr, q_ptr, int(n_q_heads),
+                                              float(scale), int(chunk_rows), out_ptr, stream),
+           "kvdec_append_attend_noalloc")

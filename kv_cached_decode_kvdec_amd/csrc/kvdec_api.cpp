@@ -161,6 +161,9 @@ struct AttendView {
     const void* v_new = nullptr;
     int32_t* lens_out = nullptr;
     int32_t window = 0;
+    // the partials go to the library's device scratch, laid out for this
+    // launch's chunks, instead of the caller's workspace (ws is ignored)
+    bool use_scratch = false;
 };
 
 // Argument checks of an attend call; nothing is enqueued.
@@ -180,6 +183,7 @@ int32_t check_attend(const AttendView& v, const float* q, int32_t n_q_heads, flo
                             chunk_rows % 64 != 0))
         return fail(KVDEC_E_INVALID, "chunk_rows %d must be 0 or a multiple of 64 in [%d, %d]",
                     chunk_rows, KVDEC_MIN_CHUNK, KVDEC_MAX_CHUNK);
+    if (v.use_scratch) return KVDEC_OK;     // sized per launch in attend_view
     const kvdec::PartialLayout part = kvdec::partial_layout(v.max_chunks, n_q_heads, v.batch);
     if (!aligned16(ws) || ws_bytes < part.bytes)
         return fail(KVDEC_E_WORKSPACE, "workspace needs %zu bytes at a 16-byte aligned address, got %zu",
@@ -193,7 +197,7 @@ int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, floa
     const int32_t rc = check_attend(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes);
     if (rc) return rc;
     const int32_t group = n_q_heads / v.n_kv_heads;
-    const kvdec::PartialLayout part = kvdec::partial_layout(v.max_chunks, n_q_heads, v.batch);
+    kvdec::PartialLayout part = kvdec::partial_layout(v.max_chunks, n_q_heads, v.batch);
 
     kvdec::AttendArgs a;
     a.q = q;
@@ -236,6 +240,18 @@ int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, floa
         a.need_merge = a.n_chunks > v.batch;   // some sequence has more than one chunk
         // the launch reads the lengths the grid was sized from
         a.one_chunk = a.n_chunks == v.batch ? 1 : 0;
+    }
+    if (v.use_scratch) {
+        // the partial slots this launch writes (one per workgroup along x and
+        // query head) and the length snapshot, in the library's scratch
+        part = kvdec::partial_layout(a.n_chunks, n_q_heads, v.batch);
+        size_t avail = 0;
+        const hipError_t e = kvdec::scratch_device_ptr(&ws, &avail);
+        if (e != hipSuccess) return hip_fail(e, "device scratch address");
+        if (part.bytes > avail)
+            return fail(KVDEC_E_WORKSPACE, "this call needs %zu bytes of device scratch (%lld chunks x "
+                        "%d query heads); the library holds %zu", part.bytes,
+                        static_cast<long long>(a.n_chunks), n_q_heads, avail);
     }
     a.qscale = scale * 1.4426950408889634f;
     a.out = out;
@@ -324,9 +340,10 @@ namespace {
 int32_t append_attend_from(kvdec_cache* c, const std::vector<int32_t>& pre, bool set_device,
                            const void* k_new, const void* v_new, const float* q,
                            int32_t n_q_heads, float scale, int32_t chunk_rows, float* out,
-                           void* ws, size_t ws_bytes, void* stream)
+                           void* ws, size_t ws_bytes, void* stream, bool use_scratch = false)
 {
     AttendView v = view_of(c);
+    v.use_scratch = use_scratch;
     // rows attended after the append
     for (size_t b = 0; b < pre.size(); ++b) {
         const int64_t n = static_cast<int64_t>(pre[b]) + 1;
@@ -1009,6 +1026,18 @@ int32_t kvdec_append_attend(kvdec_cache* c, const void* k_new, const void* v_new
     const std::vector<int32_t> pre = c->lens;
     return append_attend_from(c, pre, false, k_new, v_new, q, n_q_heads, scale, chunk_rows, out,
                               ws, ws_bytes, stream);
+}
+
+int32_t kvdec_append_attend_noalloc(kvdec_cache* c, const void* k_new, const void* v_new,
+                                    const float* q, int32_t n_q_heads, float scale,
+                                    int32_t chunk_rows, float* out, void* stream)
+{
+    g_err.clear();
+    const int32_t rc = check_append(c, k_new, v_new);
+    if (rc) return rc;
+    const std::vector<int32_t> pre = c->lens;
+    return append_attend_from(c, pre, false, k_new, v_new, q, n_q_heads, scale, chunk_rows, out,
+                              nullptr, 0, stream, true);
 }
 
 int32_t kvdec_append_attend_at(kvdec_cache* c, const int32_t* lens_host, const void* k_new,

@@ -102,6 +102,11 @@ hipError_t launch_seed(int dtype, void* k, void* v, const void* k_tok, const voi
                        hipStream_t s);
 hipError_t launch_attend(int dtype, const AttendArgs& a, hipStream_t s);
 
+// Address of the library's device scratch on the current device (looked up
+// on the first call per device) and its size.  Used only by the entry point
+// that allocates nothing.
+hipError_t scratch_device_ptr(void** ptr, size_t* bytes);
+
 // Workgroups of the attend kernel for (dtype, group) that are resident on the
 // current device at once (occupancy x compute units); 0 if unknown.  Cached.
 int resident_attend_blocks(int dtype, int group);

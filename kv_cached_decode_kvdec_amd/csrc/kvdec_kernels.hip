@@ -41,6 +41,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/kvdec.h"
 #include "kvdec_internal.h"
@@ -1653,6 +1654,45 @@ int resident_attend_blocks(int dtype, int group)
     const int n = per_cu * cus;
     if (n > 0) slot.store(n, std::memory_order_relaxed);
     return n;
+}
+
+// ---------------------------------------------------------------------------
+// The library's own device scratch, for the entry point that allocates
+// nothing (kvdec_append_attend_noalloc): the split-sequence partials and the
+// length snapshot that the caller's workspace holds otherwise.  Each GPU the
+// library runs on holds one copy, at its own address, until the process
+// ends; every call on that GPU shares it (the partials need no initial
+// contents: each launch writes the slots it reads).  In host code `scratch`
+// names a host-side stand-in, never the device memory: the address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[KVDEC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t scratch_device_ptr(void** ptr, size_t* bytes)
+{
+    *ptr = nullptr;
+    *bytes = KVDEC_NOALLOC_SCRATCH_BYTES;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 hipError_t launch_attend(int dtype, const AttendArgs& a, hipStream_t s)

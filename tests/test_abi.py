@@ -39,6 +39,7 @@ def test_binding_constants_match_header():
     assert int(defs["KVDEC_MAX_GROUP"]) == B.MAX_GROUP
     assert int(defs["KVDEC_MAX_FUSED_BATCH"]) == B.KVDEC_MAX_FUSED_BATCH
     assert int(defs["KVDEC_MAX_PAGED_FUSED_BATCH"]) == B.KVDEC_MAX_PAGED_FUSED_BATCH
+    assert int(defs["KVDEC_NOALLOC_SCRATCH_BYTES"]) == B.KVDEC_NOALLOC_SCRATCH_BYTES
     for name in ("KVDEC_OK", "KVDEC_E_INVALID", "KVDEC_E_SHAPE", "KVDEC_E_OVERFLOW",
                  "KVDEC_E_STATIC", "KVDEC_E_WORKSPACE", "KVDEC_E_HIP", "KVDEC_F32", "KVDEC_BF16"):
         assert int(defs[name]) == getattr(B, name), name
@@ -114,6 +115,9 @@ def test_null_handle_calls_fail_cleanly():
     assert lib.kvdec_append(None, ctypes.c_void_p(16), ctypes.c_void_p(32), None) == B.KVDEC_E_INVALID
     assert lib.kvdec_attend_self(None, ctypes.c_void_p(16), 4, 0.125, 0, ctypes.c_void_p(32),
                                  ctypes.c_void_p(64), 1 << 20, None) == B.KVDEC_E_INVALID
+    assert lib.kvdec_append_attend_noalloc(None, ctypes.c_void_p(16), ctypes.c_void_p(32),
+                                           ctypes.c_void_p(48), 4, 0.125, 0, ctypes.c_void_p(64),
+                                           None) == B.KVDEC_E_INVALID
     assert lib.kvdec_workspace_bytes(None, 4) == 0
     assert lib.kvdec_reset_lens(None, None, None) == B.KVDEC_E_INVALID
     lib.kvdec_cache_destroy(None)
