@@ -244,6 +244,39 @@ KVDEC_API int32_t kvdec_append_attend(kvdec_cache* cache, const void* k_new, con
                                       void* stream);
 
 /*
+ * One decoder layer's whole attention step for an encoder-decoder model:
+ * kvdec_append_attend on the self cache, then kvdec_attend_cross on the
+ * static encoder cache, as one call -- the self-then-cross order of one
+ * decoder block in [CERA] `decode_step_into` and [WA-CUDA]
+ * `forward_decoder_block_gpu_stream`.  Both parts run in one attend launch
+ * (plus one log-sum-exp merge launch when a sequence of either part spans
+ * several chunks): the cross part's workgroups come first in the grid, the
+ * self part's, with the append fused in, after them.  Outputs, cache bytes
+ * and lengths are bitwise those of the two calls made with the chunk sizes
+ * the call used: chunk_self and chunk_cross where given, else each call's
+ * own automatic choice -- except that where the two parts would then run on
+ * workgroups of different shapes (f32 with 1-2 query heads per KV head, one
+ * chunk size >= 256 rows and the other smaller), an automatic part takes
+ * 128-row chunks so that both share the launch.  If both sizes were given
+ * and still differ in shape, the call makes the two calls instead.
+ *   self_cache  : dynamic cache, appended to (KVDEC_E_STATIC otherwise)
+ *   cross_cache : static cache of the same batch, n_kv_heads and dtype
+ *                 (KVDEC_E_STATIC if dynamic, KVDEC_E_SHAPE if they differ)
+ *   k_new, v_new, q_self, out_self : as kvdec_append_attend
+ *   q_cross, out_cross             : as kvdec_attend_cross (same n_q_heads)
+ *   ws : (device) workspace of ws_bytes >= kvdec_workspace_bytes(self_cache,
+ *        n_q_heads) + kvdec_workspace_bytes(cross_cache, n_q_heads)
+ * Every check of both calls runs before anything is enqueued.  Errors:
+ * those of the two calls.
+ */
+KVDEC_API int32_t kvdec_append_attend_cross(kvdec_cache* self_cache, const kvdec_cache* cross_cache,
+                                            const void* k_new, const void* v_new,
+                                            const float* q_self, const float* q_cross,
+                                            int32_t n_q_heads, float scale, int32_t chunk_self,
+                                            int32_t chunk_cross, float* out_self, float* out_cross,
+                                            void* ws, size_t ws_bytes, void* stream);
+
+/*
  * kvdec_append_attend for callers that cannot allocate device memory or pass
  * a workspace (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc): the same step, the same kernels and bitwise the

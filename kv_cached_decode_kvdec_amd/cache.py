@@ -156,6 +156,30 @@ class KVCache:
                               chunk_rows, _ptr(out), _ptr(ws), ws.numel(), current_stream())
         return out
 
+    def append_attend_cross(self, cross, k_new, v_new, q_self, q_cross, scale=0.125, chunk_self=0,
+                            chunk_cross=0, out_self=None, out_cross=None):
+        """One decoder layer's attention step: append + self-attend on this
+        cache and cross-attend over the static cache `cross`, as one call
+        (one attend launch).  Returns (out_self, out_cross)."""
+        shape = (self.batch, self.n_kv_heads, B.HEAD_DIM)
+        self._check_rows(k_new, shape, "k_new")
+        self._check_rows(v_new, shape, "v_new")
+        out_self = self._q_out(q_self, out_self)
+        out_cross = cross._q_out(q_cross, out_cross)
+        Hq = q_self.shape[1]
+        key = ("pair", cross.cap_pad, Hq)
+        ws = self._ws.get(key)
+        if ws is None:
+            nbytes = (B.kvdec_workspace_bytes(self.handle, Hq) +
+                      B.kvdec_workspace_bytes(cross.handle, Hq))
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=self.k.device)
+            self._ws[key] = ws
+        B.kvdec_append_attend_cross(self.handle, cross.handle, _ptr(k_new), _ptr(v_new), _ptr(q_self),
+                                    _ptr(q_cross), Hq, scale, chunk_self, chunk_cross,
+                                    _ptr(out_self), _ptr(out_cross), _ptr(ws), ws.numel(),
+                                    current_stream())
+        return out_self, out_cross
+
     def append_attend_at(self, lens, k_new, v_new, q, scale=0.125, chunk_rows=0, out=None):
         """Set the lengths to `lens` (the new token's positions), then append
         and attend, as one call."""

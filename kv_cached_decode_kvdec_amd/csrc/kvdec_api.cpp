@@ -191,18 +191,11 @@ int32_t check_attend(const AttendView& v, const float* q, int32_t n_q_heads, flo
     return KVDEC_OK;
 }
 
-int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, float scale,
-                    int32_t chunk_rows, float* out, void* ws, size_t ws_bytes, void* stream)
+// The chunk plan of an attend launch over view v: chunk size, grid size
+// along x, whether a merge launch follows, and whether every sequence has
+// exactly one chunk.
+void plan_chunks(const AttendView& v, int32_t group, int32_t chunk_rows, kvdec::AttendArgs& a)
 {
-    const int32_t rc = check_attend(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes);
-    if (rc) return rc;
-    const int32_t group = n_q_heads / v.n_kv_heads;
-    kvdec::PartialLayout part = kvdec::partial_layout(v.max_chunks, n_q_heads, v.batch);
-
-    kvdec::AttendArgs a;
-    a.q = q;
-    a.k = v.k;
-    a.v = v.v;
     a.lens = v.lens_dev;
     a.batch = v.batch;
     a.n_kv_heads = v.n_kv_heads;
@@ -241,18 +234,16 @@ int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, floa
         // the launch reads the lengths the grid was sized from
         a.one_chunk = a.n_chunks == v.batch ? 1 : 0;
     }
-    if (v.use_scratch) {
-        // the partial slots this launch writes (one per workgroup along x and
-        // query head) and the length snapshot, in the library's scratch
-        part = kvdec::partial_layout(a.n_chunks, n_q_heads, v.batch);
-        size_t avail = 0;
-        const hipError_t e = kvdec::scratch_device_ptr(&ws, &avail);
-        if (e != hipSuccess) return hip_fail(e, "device scratch address");
-        if (part.bytes > avail)
-            return fail(KVDEC_E_WORKSPACE, "this call needs %zu bytes of device scratch (%lld chunks x "
-                        "%d query heads); the library holds %zu", part.bytes,
-                        static_cast<long long>(a.n_chunks), n_q_heads, avail);
-    }
+}
+
+// Everything else of the launch over view v (the append fused into it, the
+// paged layout), after plan_chunks.
+void fill_args(const AttendView& v, const float* q, float scale, float* out, void* ws,
+               const kvdec::PartialLayout& part, kvdec::AttendArgs& a)
+{
+    a.q = q;
+    a.k = v.k;
+    a.v = v.v;
     a.qscale = scale * 1.4426950408889634f;
     a.out = out;
     a.ws = ws;
@@ -269,6 +260,30 @@ int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, floa
     a.v_new = v.v_new;
     a.lens_out = v.lens_out;
     a.window = v.window;
+}
+
+int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, float scale,
+                    int32_t chunk_rows, float* out, void* ws, size_t ws_bytes, void* stream)
+{
+    const int32_t rc = check_attend(v, q, n_q_heads, scale, chunk_rows, out, ws, ws_bytes);
+    if (rc) return rc;
+    const int32_t group = n_q_heads / v.n_kv_heads;
+    kvdec::PartialLayout part = kvdec::partial_layout(v.max_chunks, n_q_heads, v.batch);
+    kvdec::AttendArgs a;
+    plan_chunks(v, group, chunk_rows, a);
+    if (v.use_scratch) {
+        // the partial slots this launch writes (one per workgroup along x and
+        // query head) and the length snapshot, in the library's scratch
+        part = kvdec::partial_layout(a.n_chunks, n_q_heads, v.batch);
+        size_t avail = 0;
+        const hipError_t e = kvdec::scratch_device_ptr(&ws, &avail);
+        if (e != hipSuccess) return hip_fail(e, "device scratch address");
+        if (part.bytes > avail)
+            return fail(KVDEC_E_WORKSPACE, "this call needs %zu bytes of device scratch (%lld chunks x "
+                        "%d query heads); the library holds %zu", part.bytes,
+                        static_cast<long long>(a.n_chunks), n_q_heads, avail);
+    }
+    fill_args(v, q, scale, out, ws, part, a);
     const hipError_t e = kvdec::launch_attend(v.dtype, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "attend launch");
     return KVDEC_OK;
@@ -1026,6 +1041,93 @@ int32_t kvdec_append_attend(kvdec_cache* c, const void* k_new, const void* v_new
     const std::vector<int32_t> pre = c->lens;
     return append_attend_from(c, pre, false, k_new, v_new, q, n_q_heads, scale, chunk_rows, out,
                               ws, ws_bytes, stream);
+}
+
+int32_t kvdec_append_attend_cross(kvdec_cache* c, const kvdec_cache* x, const void* k_new,
+                                  const void* v_new, const float* q_self, const float* q_cross,
+                                  int32_t n_q_heads, float scale, int32_t chunk_self,
+                                  int32_t chunk_cross, float* out_self, float* out_cross, void* ws,
+                                  size_t ws_bytes, void* stream)
+{
+    g_err.clear();
+    int32_t rc = check_append(c, k_new, v_new);
+    if (rc) return rc;
+    if (!x) return fail(KVDEC_E_INVALID, "cross cache handle is NULL");
+    if (!x->d.is_static) return fail(KVDEC_E_STATIC, "the cross part needs a static (encoder) cache");
+    rc = check_mirror(x);
+    if (rc) return rc;
+    if (x->d.batch != c->d.batch || x->d.n_kv_heads != c->d.n_kv_heads || x->d.dtype != c->d.dtype)
+        return fail(KVDEC_E_SHAPE, "self and cross caches differ in batch (%d, %d), KV heads (%d, %d) "
+                    "or dtype (%d, %d)", c->d.batch, x->d.batch, c->d.n_kv_heads, x->d.n_kv_heads,
+                    c->d.dtype, x->d.dtype);
+    const std::vector<int32_t> pre = c->lens;
+    AttendView sv = view_of(c);
+    for (size_t b = 0; b < pre.size(); ++b) {        // rows attended after the append
+        const int64_t n = static_cast<int64_t>(pre[b]) + 1;
+        sv.rows[b] = static_cast<int32_t>(c->d.window > 0 && n > c->d.window ? c->d.window : n);
+    }
+    const AttendView xv = view_of(x);
+    rc = check_attend(sv, q_self, n_q_heads, scale, chunk_self, out_self, ws, ws_bytes);
+    if (rc) return rc;
+    rc = check_attend(xv, q_cross, n_q_heads, scale, chunk_cross, out_cross, ws, ws_bytes);
+    if (rc) return rc;
+    // one workspace holds both parts' partials
+    const kvdec::PartialLayout part =
+        kvdec::partial_layout(sv.max_chunks + xv.max_chunks, n_q_heads, c->d.batch);
+    if (ws_bytes < part.bytes)
+        return fail(KVDEC_E_WORKSPACE, "workspace needs %zu bytes for both parts (the sum of the two "
+                    "caches' kvdec_workspace_bytes is enough), got %zu", part.bytes, ws_bytes);
+    const int32_t group = n_q_heads / c->d.n_kv_heads;
+    kvdec::AttendArgs a, xa;
+    plan_chunks(sv, group, chunk_self, a);
+    plan_chunks(xv, group, chunk_cross, xa);
+    auto waves = [&](const kvdec::AttendArgs& p) {
+        return kvdec::attend_waves(c->d.dtype, group, p.chunk_rows, p.replay);
+    };
+    // An automatic chunk size gives way where the parts would need
+    // workgroups of different shapes: the automatic part drops to the
+    // largest chunk below 256 rows (4-wave workgroups).
+    for (int side = 0; side < 2 && waves(a) != waves(xa); ++side) {
+        const bool cross_side = side == 0;
+        if ((cross_side ? chunk_cross : chunk_self) != 0) continue;
+        kvdec::AttendArgs& p = cross_side ? xa : a;
+        if (waves(p) > 4 && p.chunk_rows >= 256)
+            plan_chunks(cross_side ? xv : sv, group, 128, p);
+    }
+    if (waves(a) != waves(xa)) {
+        // the two parts run on workgroups of different shapes at these chunk
+        // sizes: the two calls, in order (same results)
+        rc = append_attend_from(c, pre, false, k_new, v_new, q_self, n_q_heads, scale, chunk_self,
+                                out_self, ws, ws_bytes, stream);
+        if (rc) return rc;
+        return attend_view(xv, q_cross, n_q_heads, scale, chunk_cross, out_cross, ws, ws_bytes,
+                           stream);
+    }
+    if (c->d.batch > KVDEC_MAX_FUSED_BATCH || c->replay_chunk > 0)
+        sv.fused_device = true;        // lengths read from (and bumped on) the device
+    else
+        sv.fused_lens = pre.data();    // pre-append lengths by value
+    sv.k_new = k_new;
+    sv.v_new = v_new;
+    sv.lens_out = c->d.lens;
+    sv.window = c->d.window;
+    fill_args(sv, q_self, scale, out_self, ws, part, a);
+    a.x_blocks = xa.n_chunks;
+    a.x_q = q_cross;
+    a.x_k = x->d.k;
+    a.x_v = x->d.v;
+    a.x_lens = x->d.lens;
+    a.x_out = out_cross;
+    a.x_cap_pad = x->cap_pad;
+    a.x_row_limit = xa.row_limit;
+    a.x_chunk_rows = xa.chunk_rows;
+    a.x_one_chunk = xa.one_chunk;
+    a.need_merge = a.need_merge || xa.need_merge;
+    const hipError_t e = kvdec::launch_attend(c->d.dtype, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "attend launch");
+    c->lens = pre;
+    for (auto& l : c->lens) ++l;
+    return KVDEC_OK;
 }
 
 int32_t kvdec_append_attend_noalloc(kvdec_cache* c, const void* k_new, const void* v_new,

@@ -62,6 +62,20 @@ struct AttendArgs {
     const void* v_new = nullptr;
     int32_t* lens_out = nullptr;
     int32_t window = 0;
+    // cross-attention part of a one-launch decoder layer step (x_blocks > 0;
+    // contiguous caches, fused append modes only): a static cache attended in
+    // the same grid, whose x_blocks workgroups come first along x and whose
+    // partials take the first x_blocks slots of the workspace
+    int64_t x_blocks = 0;
+    const float* x_q = nullptr;
+    const void* x_k = nullptr;
+    const void* x_v = nullptr;
+    const int32_t* x_lens = nullptr;
+    float* x_out = nullptr;
+    int32_t x_cap_pad = 0;
+    int32_t x_row_limit = 0;
+    int32_t x_chunk_rows = 0;
+    int32_t x_one_chunk = 0;
 };
 
 constexpr int kPagesPerLaunch = 256;   // new-page ids carried by value in one paged append
@@ -106,6 +120,11 @@ hipError_t launch_attend(int dtype, const AttendArgs& a, hipStream_t s);
 // on the first call per device) and its size.  Used only by the entry point
 // that allocates nothing.
 hipError_t scratch_device_ptr(void** ptr, size_t* bytes);
+
+// Waves per workgroup the attend kernel for (dtype, group) runs with at this
+// chunk size (in capacity-sized replay grids when `replay`): a function of
+// these arguments only.  Both parts of a one-launch layer step must agree.
+int attend_waves(int dtype, int group, int chunk_rows, bool replay);
 
 // Workgroups of the attend kernel for (dtype, group) that are resident on the
 // current device at once (occupancy x compute units); 0 if unknown.  Cached.

@@ -430,6 +430,26 @@ struct PageMap {
 
 constexpr int kMaxChunkPages = KVDEC_MAX_CHUNK / 16 + 1;
 
+// The cross-attention part of a one-launch decoder layer step (self append +
+// attend and cross attend in one grid): its workgroups come first along x
+// (they read the longer rows: started first, they leave the shorter
+// self-attention workgroups to fill the tail); it reads a static cache with
+// lengths from the device, has its own chunk size, and writes its own
+// output.  Its chunk partials take the first n_blocks slots of the
+// workspace, the self part's the slots after them.
+struct CrossPart {
+    const float* q;         // [B][Hq][64]
+    const char* K;          // static cache [B][Hkv][cap_pad][64]
+    const char* V;
+    const int32_t* lens;    // device lengths of the static cache
+    float* out;             // [B][Hq][64]
+    int cap_pad;
+    int row_limit;
+    int T;                  // chunk rows
+    int one_chunk;          // every sequence has exactly one chunk
+    int n_blocks;           // workgroups of the part along x (0: no cross part)
+};
+
 // fresh_idx >= 0: table entry fresh_idx is being given page fresh_page by this
 // launch (the paged fused append); it is taken from there, not read.
 template <bool PAGED>
@@ -770,16 +790,17 @@ __global__ __launch_bounds__(256) void seed_kernel(char* __restrict__ K, char* _
 // Waves per SIMD the VALU kernel asks the compiler to fit (1: no request):
 // f32 groups 2 and 6 land one or two VGPRs past an occupancy step without it.
 template <int ESZ, int GROUP>
-constexpr int valu_min_waves() { return ESZ == 4 && GROUP == 2 ? 7 : ESZ == 4 && GROUP == 6 ? 4 : 1; }
+constexpr int valu_min_waves() { return ESZ == 4 && GROUP == 2 ? 7 : ESZ == 4 && GROUP == 6 ? 4 : ESZ == 2 && GROUP == 1 ? 7 : 1; }
 
-template <int ESZ, int GROUP, int WAVES, int U, bool PAGED, int LM>
+template <int ESZ, int GROUP, int WAVES, int U, bool PAGED, int LM, bool X2>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(valu_min_waves<ESZ, GROUP>())))
 void attend_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
     LensSrc<LM> ls, int B, int Hkv, int cap_pad, int row_limit, int T, int one_chunk,
     float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    PageMap pm)
+    PageMap pm, CrossPart xp)
 {
+    static_assert(!(X2 && PAGED), "the one-launch layer step reads contiguous caches");
     using L = Lay<ESZ>;
     constexpr int EPL = L::kEPL, LPR = L::kLPR, RPI = L::kRPI, RB = L::kRowBytes;
     const int lane = threadIdx.x & 63;
@@ -790,7 +811,21 @@ void attend_kernel(
     const int Hq = Hkv * GROUP;
 
     Located loc;
-    if (!locate<LM>(ls, B, T, row_limit, blockIdx.x, lane, one_chunk, loc)) return;
+    const bool in_cross = X2 && static_cast<int>(blockIdx.x) < xp.n_blocks;   // workgroup-uniform
+    if (in_cross) {
+        const LensSrc<kLensDevice> xs{xp.lens};
+        if (!locate<kLensDevice>(xs, B, xp.T, xp.row_limit, blockIdx.x, lane, xp.one_chunk, loc))
+            return;
+        q = xp.q;
+        K = xp.K;
+        V = xp.V;
+        out = xp.out;
+        cap_pad = xp.cap_pad;
+        T = xp.T;
+    } else {
+        const int blk = X2 ? static_cast<int>(blockIdx.x) - xp.n_blocks : static_cast<int>(blockIdx.x);
+        if (!locate<LM>(ls, B, T, row_limit, blk, lane, one_chunk, loc)) return;
+    }
     const int row0 = loc.c * T;
     int row_end = min(loc.len, row0 + T);   // lowered where a replayed row has no page
 
@@ -807,7 +842,7 @@ void attend_kernel(
     else if constexpr (PAGED && LM == kLensDeviceFused)
         fused_append_paged_device<RB>(ls, loc, g, Hkv, pm, sm_pages, row0, row_end);
     else if constexpr (LM != kLensDevice)
-        fused_append<RB>(ls, loc, g, Hkv, cap_pad, row0, row_end);
+        if (!in_cross) fused_append<RB>(ls, loc, g, Hkv, cap_pad, row0, row_end);
 
     // q for the GROUP heads sharing KV head g, this lane's dims.  It is not
     // waited for before the loop: the first rows' loads are issued first and
@@ -969,14 +1004,15 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 constexpr int kGqaLdsStride = 160;     // bytes per staged V row (conflict-free tr16 reads)
 constexpr int kGqaKStride = 144;       // bytes per staged K row (conflict-free 16-byte reads)
 
-template <int GROUP, int WAVES, bool PAGED, int LM>
+template <int GROUP, int WAVES, bool PAGED, int LM, bool X2>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void attend_gqa_mfma_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
     LensSrc<LM> ls, int B, int Hkv, int cap_pad, int row_limit, int T, int one_chunk,
     float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    PageMap pm)
+    PageMap pm, CrossPart xp)
 {
+    static_assert(!(X2 && PAGED), "the one-launch layer step reads contiguous caches");
     static_assert(GROUP >= 2 && GROUP <= 8, "MFMA path takes 2..8 query heads per KV head");
     constexpr int RB = 128;                // bf16 row bytes
     const int lane = threadIdx.x & 63;
@@ -995,7 +1031,21 @@ void attend_gqa_mfma_kernel(
     __shared__ __attribute__((aligned(16))) char sm_stage[WAVES * kStage];
 
     Located loc;
-    if (!locate<LM>(ls, B, T, row_limit, blockIdx.x, lane, one_chunk, loc)) return;
+    const bool in_cross = X2 && static_cast<int>(blockIdx.x) < xp.n_blocks;   // workgroup-uniform
+    if (in_cross) {
+        const LensSrc<kLensDevice> xs{xp.lens};
+        if (!locate<kLensDevice>(xs, B, xp.T, xp.row_limit, blockIdx.x, lane, xp.one_chunk, loc))
+            return;
+        q = xp.q;
+        K = xp.K;
+        V = xp.V;
+        out = xp.out;
+        cap_pad = xp.cap_pad;
+        T = xp.T;
+    } else {
+        const int blk = X2 ? static_cast<int>(blockIdx.x) - xp.n_blocks : static_cast<int>(blockIdx.x);
+        if (!locate<LM>(ls, B, T, row_limit, blk, lane, one_chunk, loc)) return;
+    }
     const int row0 = loc.c * T;
     int row_end = min(loc.len, row0 + T);   // lowered where a replayed row has no page
 
@@ -1012,7 +1062,7 @@ void attend_gqa_mfma_kernel(
     else if constexpr (PAGED && LM == kLensDeviceFused)
         fused_append_paged_device<RB>(ls, loc, g, Hkv, pm, sm_pages, row0, row_end);
     else if constexpr (LM != kLensDevice)
-        fused_append<RB>(ls, loc, g, Hkv, cap_pad, row0, row_end);
+        if (!in_cross) fused_append<RB>(ls, loc, g, Hkv, cap_pad, row0, row_end);
 
     // q loads, then the wave's first 32 rows, both in flight before either is
     // waited for.  The loop is software-pipelined: once a tile sits in LDS
@@ -1201,19 +1251,18 @@ void attend_gqa_mfma_kernel(
 // wave), so the loads are grouped to keep the chain of dependent round trips
 // short: lengths -> {(m, l), first 16 o rows} -> further batches of 16.
 // ---------------------------------------------------------------------------
+// One (sequence b, query head h) of one part of the grid: its chunks'
+// partials start at slot `base` + the exclusive prefix of the part's chunk
+// counts; n_grid is the number of workgroups the part was launched with.
 template <int LM>
-__global__ __launch_bounds__(64) void merge_kernel(LensSrc<LM> ls, int B, int Hq,
-                                                    int T, int row_limit,
-                                                    const float* __restrict__ part_o,
-                                                    const float2* __restrict__ part_ml,
-                                                    float* __restrict__ out, PageMap pm,
-                                                    int n_grid)
+__device__ __forceinline__ void merge_one(const LensSrc<LM>& ls, int B, int Hq, int T,
+                                          int row_limit, int b, int h, int lane, int base,
+                                          int n_grid, const float* __restrict__ part_o,
+                                          const float2* __restrict__ part_ml,
+                                          float* __restrict__ out, const PageMap& pm)
 {
     constexpr int plus = LensSrc<LM>::kPlus;
-    const int lane = threadIdx.x & 63;
-    const int w = blockIdx.x;
-    if (w >= B * Hq) return;
-    const int b = w / Hq, h = w - b * Hq;
+    const size_t w = static_cast<size_t>(b) * Hq + h;
     // exclusive prefix of chunk counts over sequences < b, and this sequence's count
     int acc = 0;
     for (int b0 = 0; b0 < b; b0 += 64) {
@@ -1235,11 +1284,11 @@ __global__ __launch_bounds__(64) void merge_kernel(LensSrc<LM> ls, int B, int Hq
             ls.f.lens_out[b] = len0 + 1;
     }
     if (!covered) {
-        out[static_cast<size_t>(w) * kHeadDim + lane] = __int_as_float(0x7fc00000);
+        out[w * kHeadDim + lane] = __int_as_float(0x7fc00000);
         return;
     }
     if (nch == 1) return;     // finished by the attend kernel
-    const size_t first = static_cast<size_t>(acc);
+    const size_t first = static_cast<size_t>(base) + static_cast<size_t>(acc);
 
     // Chunk c's (m, l) is read by lane c % 64; the o rows are read kBatch
     // chunks at a time, all loads of a batch in flight together, and the
@@ -1289,7 +1338,35 @@ __global__ __launch_bounds__(64) void merge_kernel(LensSrc<LM> ls, int B, int Hq
             }
         }
     }
-    out[static_cast<size_t>(w) * kHeadDim + lane] = (Lsum > 0.f) ? o / Lsum : 0.f;
+    out[w * kHeadDim + lane] = (Lsum > 0.f) ? o / Lsum : 0.f;
+}
+
+// One wave per (sequence, query head) of the launch's part(s): waves
+// [0, B*Hq) merge the self part (whose partials follow the cross part's in
+// a one-launch layer step), waves [B*Hq, 2*B*Hq) the cross part.
+template <int LM, bool X2>
+__global__ __launch_bounds__(64) void merge_kernel(LensSrc<LM> ls, int B, int Hq,
+                                                    int T, int row_limit,
+                                                    const float* __restrict__ part_o,
+                                                    const float2* __restrict__ part_ml,
+                                                    float* __restrict__ out, PageMap pm,
+                                                    int n_grid, CrossPart xp)
+{
+    const int lane = threadIdx.x & 63;
+    const int w = blockIdx.x;
+    if (X2 && w >= B * Hq) {
+        const int wx = w - B * Hq;
+        if (wx >= B * Hq) return;
+        const int b = wx / Hq, h = wx - b * Hq;
+        const LensSrc<kLensDevice> xs{xp.lens};
+        merge_one<kLensDevice>(xs, B, Hq, xp.T, xp.row_limit, b, h, lane, 0, xp.n_blocks, part_o,
+                               part_ml, xp.out, PageMap{nullptr, 0, 0, 0});
+        return;
+    }
+    if (w >= B * Hq) return;
+    const int b = w / Hq, h = w - b * Hq;
+    merge_one<LM>(ls, B, Hq, T, row_limit, b, h, lane, X2 ? xp.n_blocks : 0, n_grid, part_o, part_ml,
+                  out, pm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1489,7 +1566,8 @@ bool wide_fits()
         const bool ok =
             hipOccupancyMaxActiveBlocksPerMultiprocessor(
                 &per_cu,
-                reinterpret_cast<const void*>(&attend_kernel<4, GROUP, kWideWaves, kUnroll, false, kLensDevice>),
+                reinterpret_cast<const void*>(&attend_kernel<4, GROUP, kWideWaves, kUnroll, false,
+                                                             kLensDevice, false>),
                 kWideWaves * 64, 0) == hipSuccess;
         k = (ok && per_cu >= 2) ? 1 : -1;
         known.store(k, std::memory_order_relaxed);
@@ -1497,29 +1575,65 @@ bool wide_fits()
     return k > 0;
 }
 
-// The merge launch after an attend launch, when some sequence spans several chunks.
-template <int LM>
+// f32 with 1 or 2 query heads per KV head: chunks of >= 256 rows run on
+// 16-wave workgroups (each wave one pass of 16 rows per 256 rows) where two
+// of them fit on a CU.  The choice depends on the chunk size and the kernel
+// only (see wide_fits), not on the grid.  Not for capacity-sized replay
+// grids: there a surplus workgroup launches and retires 16 waves for nothing
+// (qwen2-0.5b replayed: 83.3 us per step on 16-wave, 80.1 on 4-wave
+// workgroups).
+template <int ESZ, int GROUP>
+bool use_wide(int chunk_rows, bool replay)
+{
+    if constexpr (ESZ == 4 && GROUP <= 2)
+        return !replay && chunk_rows >= kWideWaves * kUnroll * Lay<4>::kRPI && wide_fits<GROUP>();
+    else
+        return false;
+}
+
+CrossPart cross_part(const AttendArgs& a)
+{
+    CrossPart x{};
+    if (a.x_blocks > 0) {
+        x.q = a.x_q;
+        x.K = static_cast<const char*>(a.x_k);
+        x.V = static_cast<const char*>(a.x_v);
+        x.lens = a.x_lens;
+        x.out = a.x_out;
+        x.cap_pad = a.x_cap_pad;
+        x.row_limit = a.x_row_limit;
+        x.T = a.x_chunk_rows;
+        x.one_chunk = a.x_one_chunk;
+        x.n_blocks = static_cast<int>(a.x_blocks);
+    }
+    return x;
+}
+
+// The merge launch after an attend launch, when some sequence of some part
+// spans several chunks.
+template <int LM, bool X2>
 hipError_t launch_merge(const AttendArgs& a, int group, const LensSrc<LM>& ls, float* po,
-                        float2* pml, const PageMap& pm, hipStream_t s)
+                        float2* pml, const PageMap& pm, const CrossPart& xp, hipStream_t s)
 {
     if (!a.need_merge) return hipSuccess;
     const int Hq = a.n_kv_heads * group;
-    const int waves = a.batch * Hq;
+    const int waves = a.batch * Hq * (X2 ? 2 : 1);
     // one wave per workgroup: the waves spread over more CUs (whisper-base
     // 27.3 -> 26.6 us per step against four-wave workgroups)
-    hipLaunchKernelGGL((merge_kernel<LM>), dim3(waves), dim3(64), 0, s, ls, a.batch,
+    hipLaunchKernelGGL((merge_kernel<LM, X2>), dim3(waves), dim3(64), 0, s, ls, a.batch,
                        Hq, a.chunk_rows, a.row_limit, po, pml, a.out, pm,
-                       static_cast<int>(a.n_chunks));
+                       static_cast<int>(a.n_chunks), xp);
     return hipGetLastError();
 }
 
-template <int ESZ, int GROUP, bool PAGED, int LM>
+template <int ESZ, int GROUP, bool PAGED, int LM, bool X2>
 hipError_t attend_t(const AttendArgs& a, hipStream_t s)
 {
     char* ws = static_cast<char*>(a.ws);
     float* po = reinterpret_cast<float*>(ws + a.part.o_offset);
     float2* pml = reinterpret_cast<float2*>(ws + a.part.ml_offset);
     const PageMap pm{a.table, a.table_stride, a.pshift, a.num_pages};
+    const CrossPart xp = cross_part(a);
     LensSrc<LM> ls;
     if constexpr (LM == kLensDevice) {
         ls.lens = a.lens;
@@ -1548,56 +1662,71 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
         ls.f.lens_out = a.lens_out;
         ls.f.window = a.window;
     }
-    const dim3 grid(static_cast<unsigned>(a.n_chunks), a.n_kv_heads), block(kWaves * 64);
-    hipError_t e = hipSuccess;
-    if constexpr (ESZ == 4 && GROUP <= 2) {
-        // f32 with 1 or 2 query heads per KV head: chunks of >= 256 rows run
-        // on 16-wave workgroups (each wave one pass of 16 rows per 256 rows)
-        // where two of them fit on a CU.  The choice depends on the chunk
-        // size and the kernel only (see wide_fits), not on the grid.  Not
-        // for capacity-sized replay grids: there a surplus workgroup
-        // launches and retires 16 waves for nothing (qwen2-0.5b replayed:
-        // 83.3 us per step on 16-wave, 80.1 on 4-wave workgroups).
-        if (!a.replay && a.chunk_rows >= kWideWaves * kUnroll * Lay<4>::kRPI && wide_fits<GROUP>()) {
-            hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWideWaves, kUnroll, PAGED, LM>), grid,
+    const dim3 grid(static_cast<unsigned>(a.n_chunks + a.x_blocks), a.n_kv_heads), block(kWaves * 64);
+    if (use_wide<ESZ, GROUP>(a.chunk_rows, a.replay)) {
+        if constexpr (ESZ == 4 && GROUP <= 2)
+            hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWideWaves, kUnroll, PAGED, LM, X2>), grid,
                                dim3(kWideWaves * 64), 0, s, a.q, static_cast<const char*>(a.k),
                                static_cast<const char*>(a.v), ls, a.batch, a.n_kv_heads, a.cap_pad,
-                               a.row_limit, a.chunk_rows, a.one_chunk, a.qscale, a.out, po, pml, pm);
-            e = hipGetLastError();
-            return e != hipSuccess ? e : launch_merge<LM>(a, GROUP, ls, po, pml, pm, s);
-        }
-    }
-    if constexpr (ESZ == 2 && GROUP >= 2)
-        hipLaunchKernelGGL((attend_gqa_mfma_kernel<GROUP, kWaves, PAGED, LM>), grid, block, 0, s,
+                               a.row_limit, a.chunk_rows, a.one_chunk, a.qscale, a.out, po, pml, pm,
+                               xp);
+    } else if constexpr (ESZ == 2 && GROUP >= 2) {
+        hipLaunchKernelGGL((attend_gqa_mfma_kernel<GROUP, kWaves, PAGED, LM, X2>), grid, block, 0, s,
                            a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v), ls,
-                           a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows, a.one_chunk, a.qscale,
-                           a.out, po, pml, pm);
-    else
-        hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWaves, kUnroll, PAGED, LM>), grid, block,
+                           a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows, a.one_chunk,
+                           a.qscale, a.out, po, pml, pm, xp);
+    } else {
+        hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWaves, kUnroll, PAGED, LM, X2>), grid, block,
                            0, s, a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v),
                            ls, a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows,
-                           a.one_chunk, a.qscale, a.out, po, pml, pm);
-    e = hipGetLastError();
-    return e != hipSuccess ? e : launch_merge<LM>(a, GROUP, ls, po, pml, pm, s);
+                           a.one_chunk, a.qscale, a.out, po, pml, pm, xp);
+    }
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : launch_merge<LM, X2>(a, GROUP, ls, po, pml, pm, xp, s);
+}
+
+template <int ESZ, int GROUP, bool PAGED, int LM>
+hipError_t attend_x(const AttendArgs& a, hipStream_t s)
+{
+    if constexpr (!PAGED && (LM == kLensHostFused || LM == kLensDeviceFused)) {
+        if (a.x_blocks > 0) return attend_t<ESZ, GROUP, PAGED, LM, true>(a, s);
+    }
+    if (a.x_blocks > 0) return hipErrorInvalidValue;    // no cross part in this mode
+    return attend_t<ESZ, GROUP, PAGED, LM, false>(a, s);
 }
 
 template <int ESZ, bool PAGED, int LM>
 hipError_t attend_dispatch_group(const AttendArgs& a, hipStream_t s)
 {
     switch (a.group) {
-        case 1: return attend_t<ESZ, 1, PAGED, LM>(a, s);
-        case 2: return attend_t<ESZ, 2, PAGED, LM>(a, s);
-        case 3: return attend_t<ESZ, 3, PAGED, LM>(a, s);
-        case 4: return attend_t<ESZ, 4, PAGED, LM>(a, s);
-        case 5: return attend_t<ESZ, 5, PAGED, LM>(a, s);
-        case 6: return attend_t<ESZ, 6, PAGED, LM>(a, s);
-        case 7: return attend_t<ESZ, 7, PAGED, LM>(a, s);
-        case 8: return attend_t<ESZ, 8, PAGED, LM>(a, s);
+        case 1: return attend_x<ESZ, 1, PAGED, LM>(a, s);
+        case 2: return attend_x<ESZ, 2, PAGED, LM>(a, s);
+        case 3: return attend_x<ESZ, 3, PAGED, LM>(a, s);
+        case 4: return attend_x<ESZ, 4, PAGED, LM>(a, s);
+        case 5: return attend_x<ESZ, 5, PAGED, LM>(a, s);
+        case 6: return attend_x<ESZ, 6, PAGED, LM>(a, s);
+        case 7: return attend_x<ESZ, 7, PAGED, LM>(a, s);
+        case 8: return attend_x<ESZ, 8, PAGED, LM>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
+template <int ESZ>
+int waves_for(int group, int chunk_rows, bool replay)
+{
+    switch (group) {
+        case 1: return use_wide<ESZ, 1>(chunk_rows, replay) ? kWideWaves : kWaves;
+        case 2: return use_wide<ESZ, 2>(chunk_rows, replay) ? kWideWaves : kWaves;
+        default: return kWaves;
+    }
+}
+
 }  // namespace
+
+int attend_waves(int dtype, int group, int chunk_rows, bool replay)
+{
+    return dtype == 0 ? waves_for<4>(group, chunk_rows, replay) : waves_for<2>(group, chunk_rows, replay);
+}
 
 namespace {
 
@@ -1607,26 +1736,26 @@ const void* attend_kernel_ptr(int group, int* block)
     *block = kWaves * 64;
     if constexpr (ESZ == 2) {
         switch (group) {
-            case 1: return reinterpret_cast<const void*>(&attend_kernel<2, 1, kWaves, kUnroll, false, kLensDevice>);
-            case 2: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<2, kWaves, false, kLensDevice>);
-            case 3: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<3, kWaves, false, kLensDevice>);
-            case 4: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<4, kWaves, false, kLensDevice>);
-            case 5: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<5, kWaves, false, kLensDevice>);
-            case 6: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<6, kWaves, false, kLensDevice>);
-            case 7: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<7, kWaves, false, kLensDevice>);
-            case 8: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<8, kWaves, false, kLensDevice>);
+            case 1: return reinterpret_cast<const void*>(&attend_kernel<2, 1, kWaves, kUnroll, false, kLensDevice, false>);
+            case 2: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<2, kWaves, false, kLensDevice, false>);
+            case 3: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<3, kWaves, false, kLensDevice, false>);
+            case 4: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<4, kWaves, false, kLensDevice, false>);
+            case 5: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<5, kWaves, false, kLensDevice, false>);
+            case 6: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<6, kWaves, false, kLensDevice, false>);
+            case 7: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<7, kWaves, false, kLensDevice, false>);
+            case 8: return reinterpret_cast<const void*>(&attend_gqa_mfma_kernel<8, kWaves, false, kLensDevice, false>);
             default: return nullptr;
         }
     } else {
         switch (group) {
-            case 1: return reinterpret_cast<const void*>(&attend_kernel<4, 1, kWaves, kUnroll, false, kLensDevice>);
-            case 2: return reinterpret_cast<const void*>(&attend_kernel<4, 2, kWaves, kUnroll, false, kLensDevice>);
-            case 3: return reinterpret_cast<const void*>(&attend_kernel<4, 3, kWaves, kUnroll, false, kLensDevice>);
-            case 4: return reinterpret_cast<const void*>(&attend_kernel<4, 4, kWaves, kUnroll, false, kLensDevice>);
-            case 5: return reinterpret_cast<const void*>(&attend_kernel<4, 5, kWaves, kUnroll, false, kLensDevice>);
-            case 6: return reinterpret_cast<const void*>(&attend_kernel<4, 6, kWaves, kUnroll, false, kLensDevice>);
-            case 7: return reinterpret_cast<const void*>(&attend_kernel<4, 7, kWaves, kUnroll, false, kLensDevice>);
-            case 8: return reinterpret_cast<const void*>(&attend_kernel<4, 8, kWaves, kUnroll, false, kLensDevice>);
+            case 1: return reinterpret_cast<const void*>(&attend_kernel<4, 1, kWaves, kUnroll, false, kLensDevice, false>);
+            case 2: return reinterpret_cast<const void*>(&attend_kernel<4, 2, kWaves, kUnroll, false, kLensDevice, false>);
+            case 3: return reinterpret_cast<const void*>(&attend_kernel<4, 3, kWaves, kUnroll, false, kLensDevice, false>);
+            case 4: return reinterpret_cast<const void*>(&attend_kernel<4, 4, kWaves, kUnroll, false, kLensDevice, false>);
+            case 5: return reinterpret_cast<const void*>(&attend_kernel<4, 5, kWaves, kUnroll, false, kLensDevice, false>);
+            case 6: return reinterpret_cast<const void*>(&attend_kernel<4, 6, kWaves, kUnroll, false, kLensDevice, false>);
+            case 7: return reinterpret_cast<const void*>(&attend_kernel<4, 7, kWaves, kUnroll, false, kLensDevice, false>);
+            case 8: return reinterpret_cast<const void*>(&attend_kernel<4, 8, kWaves, kUnroll, false, kLensDevice, false>);
             default: return nullptr;
         }
     }
