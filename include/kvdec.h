@@ -245,8 +245,9 @@ KVDEC_API int32_t kvdec_append_attend(kvdec_cache* cache, const void* k_new, con
 
 /*
  * One decoder layer's whole attention step for an encoder-decoder model:
- * kvdec_append_attend on the self cache, then kvdec_attend_cross on the
- * static encoder cache, as one call -- the self-then-cross order of one
+ * kvdec_append_attend (or kvdec_append_attend_at) on the self cache, then
+ * kvdec_attend_cross on the static encoder cache, as one call -- the
+ * self-then-cross order of one
  * decoder block in [CERA] `decode_step_into` and [WA-CUDA]
  * `forward_decoder_block_gpu_stream`.  Both parts run in one attend launch
  * (plus one log-sum-exp merge launch when a sequence of either part spans
@@ -262,6 +263,10 @@ KVDEC_API int32_t kvdec_append_attend(kvdec_cache* cache, const void* k_new, con
  *   self_cache  : dynamic cache, appended to (KVDEC_E_STATIC otherwise)
  *   cross_cache : static cache of the same batch, n_kv_heads and dtype
  *                 (KVDEC_E_STATIC if dynamic, KVDEC_E_SHAPE if they differ)
+ *   lens_host   : (host) NULL, or int32[batch] positions: the self part is
+ *                 then kvdec_append_attend_at(lens_host) instead (the step
+ *                 at explicit positions, a rewind included, with no launch
+ *                 of its own where the step is one launch)
  *   k_new, v_new, q_self, out_self : as kvdec_append_attend
  *   q_cross, out_cross             : as kvdec_attend_cross (same n_q_heads)
  *   ws : (device) workspace of ws_bytes >= kvdec_workspace_bytes(self_cache,
@@ -270,7 +275,8 @@ KVDEC_API int32_t kvdec_append_attend(kvdec_cache* cache, const void* k_new, con
  * those of the two calls.
  */
 KVDEC_API int32_t kvdec_append_attend_cross(kvdec_cache* self_cache, const kvdec_cache* cross_cache,
-                                            const void* k_new, const void* v_new,
+                                            const int32_t* lens_host, const void* k_new,
+                                            const void* v_new,
                                             const float* q_self, const float* q_cross,
                                             int32_t n_q_heads, float scale, int32_t chunk_self,
                                             int32_t chunk_cross, float* out_self, float* out_cross,

@@ -104,8 +104,8 @@ def load():
                                           _vp, _sz, _vp]),
         "kvdec_append_attend_noalloc": (_i32, [_vp, _vp, _vp, _vp, _i32, ctypes.c_float, _i32, _vp,
                                                _vp]),
-        "kvdec_append_attend_cross": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float, _i32,
-                                             _i32, _vp, _vp, _vp, _sz, _vp]),
+        "kvdec_append_attend_cross": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float,
+                                             _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
         "kvdec_paged_create": (_i32, [ctypes.POINTER(PagedDesc), _vp, ctypes.POINTER(_vp)]),
         "kvdec_paged_destroy": (None, [_vp]),
         "kvdec_paged_append": (_i32, [_vp, _vp, _vp, _vp]),
@@ -310,10 +310,13 @@ def kvdec_append_attend_noalloc(handle, k_new_ptr, v_new_ptr, q_ptr, n_q_heads, 
            "kvdec_append_attend_noalloc")
 
 
-def kvdec_append_attend_cross(self_handle, cross_handle, k_new_ptr, v_new_ptr, q_self_ptr,
+def kvdec_append_attend_cross(self_handle, cross_handle, lens_host, k_new_ptr, v_new_ptr, q_self_ptr,
                               q_cross_ptr, n_q_heads, scale, chunk_self, chunk_cross, out_self_ptr,
                               out_cross_ptr, ws_ptr, ws_bytes, stream=None):
-    _check(load().kvdec_append_attend_cross(self_handle, cross_handle, k_new_ptr, v_new_ptr,
+    """lens_host: None, a sequence of ints or a ctypes int32 array (host)."""
+    if lens_host is not None and not isinstance(lens_host, ctypes.Array):
+        lens_host = (ctypes.c_int32 * len(lens_host))(*[int(x) for x in lens_host])
+    _check(load().kvdec_append_attend_cross(self_handle, cross_handle, lens_host, k_new_ptr, v_new_ptr,
                                             q_self_ptr, q_cross_ptr, int(n_q_heads), float(scale),
                                             int(chunk_self), int(chunk_cross), out_self_ptr,
                                             out_cross_ptr, ws_ptr, int(ws_bytes), stream),

@@ -157,10 +157,15 @@ class KVCache:
         return out
 
     def append_attend_cross(self, cross, k_new, v_new, q_self, q_cross, scale=0.125, chunk_self=0,
-                            chunk_cross=0, out_self=None, out_cross=None):
+                            chunk_cross=0, out_self=None, out_cross=None, lens=None):
         """One decoder layer's attention step: append + self-attend on this
-        cache and cross-attend over the static cache `cross`, as one call
-        (one attend launch).  Returns (out_self, out_cross)."""
+        cache (at positions `lens` when given) and cross-attend over the
+        static cache `cross`, as one call (one attend launch).  Returns
+        (out_self, out_cross)."""
+        if lens is not None:
+            lens = [int(x) for x in lens]
+            if len(lens) != self.batch:
+                raise ValueError(f"lens must hold {self.batch} positions")
         shape = (self.batch, self.n_kv_heads, B.HEAD_DIM)
         self._check_rows(k_new, shape, "k_new")
         self._check_rows(v_new, shape, "v_new")
@@ -174,7 +179,7 @@ class KVCache:
                       B.kvdec_workspace_bytes(cross.handle, Hq))
             ws = torch.empty(nbytes, dtype=torch.uint8, device=self.k.device)
             self._ws[key] = ws
-        B.kvdec_append_attend_cross(self.handle, cross.handle, _ptr(k_new), _ptr(v_new), _ptr(q_self),
+        B.kvdec_append_attend_cross(self.handle, cross.handle, lens, _ptr(k_new), _ptr(v_new), _ptr(q_self),
                                     _ptr(q_cross), Hq, scale, chunk_self, chunk_cross,
                                     _ptr(out_self), _ptr(out_cross), _ptr(ws), ws.numel(),
                                     current_stream())

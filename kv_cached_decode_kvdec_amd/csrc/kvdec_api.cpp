@@ -344,6 +344,28 @@ int32_t check_append(const kvdec_cache* c, const void* k_new, const void* v_new)
     return KVDEC_OK;
 }
 
+// Checks of an append at explicit positions lens_host (kvdec_append_attend_at
+// and the layer step given positions); the positions go to `pre`.
+int32_t check_positions(const kvdec_cache* c, const int32_t* lens_host, const void* k_new,
+                        const void* v_new, std::vector<int32_t>& pre)
+{
+    if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
+    const int32_t rc = check_lens(lens_host, c->d.batch, c->d.capacity, c->d.window);
+    if (rc) return rc;
+    pre.assign(lens_host, lens_host + c->d.batch);
+    for (int32_t b = 0; b < c->d.batch; ++b) {
+        if (c->d.window == 0 && pre[b] >= c->d.capacity)
+            return fail(KVDEC_E_OVERFLOW, "cache overflow: sequence %d at position %d, capacity %d",
+                        b, pre[b], c->d.capacity);
+        if (pre[b] == INT32_MAX)
+            return fail(KVDEC_E_OVERFLOW, "token count of sequence %d would overflow int32", b);
+    }
+    if (c->d.is_static) return fail(KVDEC_E_STATIC, "append on a static (encoder) cache");
+    if (!aligned16(k_new) || !aligned16(v_new))
+        return fail(KVDEC_E_INVALID, "k_new and v_new must be non-NULL, 16-byte aligned device pointers");
+    return KVDEC_OK;
+}
+
 }  // namespace
 
 namespace {
@@ -1043,15 +1065,20 @@ int32_t kvdec_append_attend(kvdec_cache* c, const void* k_new, const void* v_new
                               ws, ws_bytes, stream);
 }
 
-int32_t kvdec_append_attend_cross(kvdec_cache* c, const kvdec_cache* x, const void* k_new,
-                                  const void* v_new, const float* q_self, const float* q_cross,
-                                  int32_t n_q_heads, float scale, int32_t chunk_self,
-                                  int32_t chunk_cross, float* out_self, float* out_cross, void* ws,
-                                  size_t ws_bytes, void* stream)
+int32_t kvdec_append_attend_cross(kvdec_cache* c, const kvdec_cache* x, const int32_t* lens_host,
+                                  const void* k_new, const void* v_new, const float* q_self,
+                                  const float* q_cross, int32_t n_q_heads, float scale,
+                                  int32_t chunk_self, int32_t chunk_cross, float* out_self,
+                                  float* out_cross, void* ws, size_t ws_bytes, void* stream)
 {
     g_err.clear();
-    int32_t rc = check_append(c, k_new, v_new);
+    // the token's positions: the host mirror, or given (then also set)
+    std::vector<int32_t> pre;
+    const bool set_device = lens_host != nullptr;
+    int32_t rc = set_device ? check_positions(c, lens_host, k_new, v_new, pre)
+                            : check_append(c, k_new, v_new);
     if (rc) return rc;
+    if (!set_device) pre = c->lens;
     if (!x) return fail(KVDEC_E_INVALID, "cross cache handle is NULL");
     if (!x->d.is_static) return fail(KVDEC_E_STATIC, "the cross part needs a static (encoder) cache");
     rc = check_mirror(x);
@@ -1060,7 +1087,6 @@ int32_t kvdec_append_attend_cross(kvdec_cache* c, const kvdec_cache* x, const vo
         return fail(KVDEC_E_SHAPE, "self and cross caches differ in batch (%d, %d), KV heads (%d, %d) "
                     "or dtype (%d, %d)", c->d.batch, x->d.batch, c->d.n_kv_heads, x->d.n_kv_heads,
                     c->d.dtype, x->d.dtype);
-    const std::vector<int32_t> pre = c->lens;
     AttendView sv = view_of(c);
     for (size_t b = 0; b < pre.size(); ++b) {        // rows attended after the append
         const int64_t n = static_cast<int64_t>(pre[b]) + 1;
@@ -1097,16 +1123,25 @@ int32_t kvdec_append_attend_cross(kvdec_cache* c, const kvdec_cache* x, const vo
     if (waves(a) != waves(xa)) {
         // the two parts run on workgroups of different shapes at these chunk
         // sizes: the two calls, in order (same results)
-        rc = append_attend_from(c, pre, false, k_new, v_new, q_self, n_q_heads, scale, chunk_self,
-                                out_self, ws, ws_bytes, stream);
+        rc = append_attend_from(c, pre, set_device, k_new, v_new, q_self, n_q_heads, scale,
+                                chunk_self, out_self, ws, ws_bytes, stream);
         if (rc) return rc;
         return attend_view(xv, q_cross, n_q_heads, scale, chunk_cross, out_cross, ws, ws_bytes,
                            stream);
     }
-    if (c->d.batch > KVDEC_MAX_FUSED_BATCH || c->replay_chunk > 0)
-        sv.fused_device = true;        // lengths read from (and bumped on) the device
-    else
-        sv.fused_lens = pre.data();    // pre-append lengths by value
+    if (c->d.batch > KVDEC_MAX_FUSED_BATCH || c->replay_chunk > 0) {
+        // lengths read from (and bumped on) the device
+        if (set_device) {
+            const hipError_t e = kvdec::launch_set_lens(c->d.lens, pre.data(), c->d.batch,
+                                                        static_cast<hipStream_t>(stream));
+            if (e != hipSuccess) return hip_fail(e, "set lengths");
+            c->lens = pre;             // mirror and device agree even if the attend launch fails
+            c->lens_known = true;
+        }
+        sv.fused_device = true;
+    } else {
+        sv.fused_lens = pre.data();    // pre-append lengths by value; the launch writes the lengths
+    }
     sv.k_new = k_new;
     sv.v_new = v_new;
     sv.lens_out = c->d.lens;
@@ -1127,6 +1162,7 @@ int32_t kvdec_append_attend_cross(kvdec_cache* c, const kvdec_cache* x, const vo
     if (e != hipSuccess) return hip_fail(e, "attend launch");
     c->lens = pre;
     for (auto& l : c->lens) ++l;
+    if (set_device) c->lens_known = true;     // the positions came from the caller
     return KVDEC_OK;
 }
 
@@ -1148,20 +1184,9 @@ int32_t kvdec_append_attend_at(kvdec_cache* c, const int32_t* lens_host, const v
                                void* stream)
 {
     g_err.clear();
-    if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
-    int32_t rc = check_lens(lens_host, c->d.batch, c->d.capacity, c->d.window);
+    std::vector<int32_t> pre;
+    const int32_t rc = check_positions(c, lens_host, k_new, v_new, pre);
     if (rc) return rc;
-    std::vector<int32_t> pre(lens_host, lens_host + c->d.batch);
-    for (int32_t b = 0; b < c->d.batch; ++b) {
-        if (c->d.window == 0 && pre[b] >= c->d.capacity)
-            return fail(KVDEC_E_OVERFLOW, "cache overflow: sequence %d at position %d, capacity %d",
-                        b, pre[b], c->d.capacity);
-        if (pre[b] == INT32_MAX)
-            return fail(KVDEC_E_OVERFLOW, "token count of sequence %d would overflow int32", b);
-    }
-    if (c->d.is_static) return fail(KVDEC_E_STATIC, "append on a static (encoder) cache");
-    if (!aligned16(k_new) || !aligned16(v_new))
-        return fail(KVDEC_E_INVALID, "k_new and v_new must be non-NULL, 16-byte aligned device pointers");
     return append_attend_from(c, pre, true, k_new, v_new, q, n_q_heads, scale, chunk_rows, out, ws,
                               ws_bytes, stream);
 }

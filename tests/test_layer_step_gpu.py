@@ -185,16 +185,48 @@ def test_layer_step_errors_enqueue_nothing():
     out = torch.empty_like(q)
     p = lambda t: ctypes.c_void_p(t.data_ptr())
     with pytest.raises(B.KvdecError) as e:
-        B.kvdec_append_attend_cross(ok.handle, cross.handle, p(kn), p(kn), p(q), p(q), H, 0.125, 0, 0,
-                                    p(out), p(out), p(small), small.numel())
+        B.kvdec_append_attend_cross(ok.handle, cross.handle, None, p(kn), p(kn), p(q), p(q), H, 0.125,
+                                    0, 0, p(out), p(out), p(small), small.numel())
     assert e.value.code == B.KVDEC_E_WORKSPACE
     # the workspace of the self cache alone is not enough for both parts
     need_self = B.kvdec_workspace_bytes(ok.handle, H)
     ws = torch.empty(need_self, dtype=torch.uint8, device="cuda")
     with pytest.raises(B.KvdecError) as e:
-        B.kvdec_append_attend_cross(ok.handle, cross.handle, p(kn), p(kn), p(q), p(q), H, 0.125, 0, 0,
-                                    p(out), p(out), p(ws), ws.numel())
+        B.kvdec_append_attend_cross(ok.handle, cross.handle, None, p(kn), p(kn), p(q), p(q), H, 0.125,
+                                    0, 0, p(out), p(out), p(ws), ws.numel())
     assert e.value.code == B.KVDEC_E_WORKSPACE
     torch.cuda.synchronize()
     assert self_c.lens() == [3, 8] and ok.lens() == [3, 4]
     assert ok.lens_dev.cpu().tolist() == [3, 4] and torch.all(ok.k == 0)
+
+
+@pytest.mark.parametrize("mode", ["one-launch", "replay", "large-batch"])
+def test_layer_step_at_positions(mode):
+    """Positions given (lens): bitwise kvdec_append_attend_at followed by
+    kvdec_attend_cross, a rewind included; the lengths end at positions + 1."""
+    Bsz = B.KVDEC_MAX_FUSED_BATCH + 2 if mode == "large-batch" else 5
+    wl = gen.Workload("layer-at", Bsz, 8, 8, "bf16", "uniform:10:300", 3, True, seed=221)
+    inp = gen.make_inputs(wl, batch=Bsz, steps=3, enc_len=200, seed=222)
+    L = Layer(inp)
+    if mode == "replay":
+        L.one.set_replay_mode(64)
+        L.two.set_replay_mode(64)
+    rng = np.random.default_rng(223)
+    pos = inp.lens.copy()
+    for s in range(3):
+        if s == 2:
+            pos = np.maximum(pos - rng.integers(0, 10, size=Bsz).astype(np.int32), 0)
+        kn, vn = to_device(inp.k_new[s]), to_device(inp.v_new[s])
+        qs, qx = to_device(inp.q_self[s]), to_device(inp.q_cross[s])
+        got_s, got_x = L.one.append_attend_cross(L.cross, kn, vn, qs, qx, lens=pos)
+        ref_s = L.two.append_attend_at(pos, kn, vn, qs)
+        ref_x = L.cross.attend(qx)
+        torch.cuda.synchronize()
+        assert got_s.cpu().numpy().tobytes() == ref_s.cpu().numpy().tobytes(), f"{mode} step {s}"
+        assert got_x.cpu().numpy().tobytes() == ref_x.cpu().numpy().tobytes(), f"{mode} step {s}"
+        pos = oracle.append(L.Kh, L.Vh, inp.k_new[s], inp.v_new[s], pos)
+        bs = np.arange(0, Bsz, max(1, Bsz // 8))
+        ref = oracle.attend(inp.q_self[s][bs], L.Kh[bs], L.Vh[bs], pos[bs])
+        assert_attention_close(got_s.cpu().numpy()[bs], ref, "bf16", f"{mode} step {s}")
+    assert L.one.lens() == pos.tolist() and L.one.lens_dev.cpu().tolist() == pos.tolist()
+    assert to_host_bits(L.one.k).tobytes() == to_host_bits(L.two.k).tobytes()
