@@ -557,6 +557,34 @@ def copy_bandwidth(torch, nbytes=2 << 30, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def read_probe(torch, nbytes=2 << 30, reps=4, blocks=8192):
+    """The nontemporal 16-byte streaming read of libkvdec_probe.so over a
+    buffer of known size (one launch reads it once): the calibration of
+    FETCH_SIZE for the attend kernels' K/V load form."""
+    import ctypes
+    path = os.path.join(ROOT, "kv_cached_decode_kvdec_amd", "libkvdec_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.kvdec_probe_stream_read.restype = ctypes.c_int
+    lib.kvdec_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_void_p]
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    run = lambda: lib.kvdec_probe_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes,
+                                              ctypes.c_void_p(sink.data_ptr()), blocks, st)
+    assert run() == 0
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        assert run() == 0
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, sink
+    return nbytes / (ms * 1e-3) / 1e9, nbytes
+
+
 def cpu_baseline(name, target_s=12.0):
     """The f64 oracle, as it stands, timed on whole decode steps of the workload.
 
@@ -717,6 +745,9 @@ def main():
                     help="how a step calls the library (see the module docstring)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the plain copy kernel (for counter calibration)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="only run the nontemporal 16-byte streaming read of a 2 GiB buffer "
+                         "(the attend kernels' load form, for counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -736,6 +767,11 @@ def main():
     if args.copy_probe:
         gbps = copy_bandwidth(torch, reps=4)
         log(f"copy probe: {gbps:.0f} GB/s")
+        return
+    if args.read_probe:
+        gbps, nbytes = read_probe(torch)
+        log(f"read probe: {nbytes} bytes per launch, {gbps:.0f} GB/s")
+        print(json.dumps({"read_probe_bytes_per_launch": nbytes, "read_probe_gbps": round(gbps, 1)}))
         return
 
     head = args.workload

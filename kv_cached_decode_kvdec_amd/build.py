@@ -14,6 +14,9 @@ CSRC = os.path.join(HERE, "csrc")
 SOURCES = [os.path.join(CSRC, "kvdec_kernels.hip"), os.path.join(CSRC, "kvdec_api.cpp")]
 HEADERS = [os.path.join(CSRC, "kvdec_internal.h"), os.path.join(ROOT, "include", "kvdec.h")]
 LIB = os.path.join(HERE, "libkvdec.so")
+# counter-calibration probe for bench.py (not part of the decode library)
+PROBE_SOURCES = [os.path.join(CSRC, "read_probe.hip")]
+PROBE_LIB = os.path.join(HERE, "libkvdec_probe.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -24,23 +27,30 @@ def _stale():
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(p) > t for p in SOURCES + HEADERS)
+    if not os.path.exists(PROBE_LIB):
+        return True
+    return any(os.path.getmtime(p) > t for p in SOURCES + HEADERS + PROBE_SOURCES)
 
 
-def build(force: bool = True, verbose: bool = False) -> str:
-    if not force and not _stale():
-        return LIB
-    tmp = LIB + ".tmp"
+def _hipcc(out, sources, verbose):
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-fvisibility=hidden",
            "-Wall", "-Wno-unused-command-line-argument", *DEVICE_FLAGS,
-           "-I", os.path.join(ROOT, "include"), "-o", tmp, *SOURCES]
+           "-I", os.path.join(ROOT, "include"), "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr[-6000:]}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    if not force and not _stale():
+        return LIB
+    _hipcc(LIB, SOURCES, verbose)
+    _hipcc(PROBE_LIB, PROBE_SOURCES, verbose)
     return LIB
 
 
