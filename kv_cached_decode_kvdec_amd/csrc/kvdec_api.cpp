@@ -233,7 +233,34 @@ void plan_chunks(const AttendView& v, int32_t group, int32_t chunk_rows, kvdec::
         a.need_merge = a.n_chunks > v.batch;   // some sequence has more than one chunk
         // the launch reads the lengths the grid was sized from
         a.one_chunk = a.n_chunks == v.batch ? 1 : 0;
+        // equal lengths: the launch needs to read none of them to find its chunk
+        bool equal = true;
+        for (int32_t r : v.rows) equal = equal && r == v.rows[0];
+        a.uniform = equal && !v.rows.empty() ? v.rows[0] : -1;
     }
+}
+
+// The merge launch planned on the host: an entry for every sequence that
+// `rows` and chunk size T split over several chunks, whose partials start
+// at base_slot + the prefix of the chunk counts.  False (and the device-side
+// merge is used) when there are more than the plan holds.
+bool plan_merge(const std::vector<int32_t>& rows, int32_t T, int64_t base_slot, bool cross,
+                kvdec::MergePlanHost& mp)
+{
+    int64_t slot = base_slot;
+    for (size_t b = 0; b < rows.size(); ++b) {
+        const int64_t n = (static_cast<int64_t>(rows[b]) + T - 1) / T;
+        const int64_t nch = n > 0 ? n : 1;
+        if (nch > 1) {
+            if (mp.n >= kvdec::kMaxMergeEntries || nch >= (1 << 24) || slot > INT32_MAX) return false;
+            mp.plan.first[mp.n] = static_cast<int32_t>(slot);
+            mp.plan.b[mp.n] = static_cast<int32_t>(b);
+            mp.plan.nch[mp.n] = static_cast<int32_t>(nch) | (cross ? (1 << 24) : 0);
+            ++mp.n;
+        }
+        slot += nch;
+    }
+    return true;
 }
 
 // Everything else of the launch over view v (the append fused into it, the
@@ -284,6 +311,11 @@ int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, floa
                         static_cast<long long>(a.n_chunks), n_q_heads, avail);
     }
     fill_args(v, q, scale, out, ws, part, a);
+    // outside replay mode the host holds every length the launch reads
+    kvdec::MergePlanHost mp;
+    if (v.replay_chunk == 0 && !v.fused_device && a.need_merge &&
+        plan_merge(v.rows, a.chunk_rows, 0, false, mp))
+        a.merge_plan = &mp;
     const hipError_t e = kvdec::launch_attend(v.dtype, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "attend launch");
     return KVDEC_OK;
@@ -1157,7 +1189,13 @@ int32_t kvdec_append_attend_cross(kvdec_cache* c, const kvdec_cache* x, const in
     a.x_row_limit = xa.row_limit;
     a.x_chunk_rows = xa.chunk_rows;
     a.x_one_chunk = xa.one_chunk;
+    a.x_uniform = xa.uniform;
     a.need_merge = a.need_merge || xa.need_merge;
+    kvdec::MergePlanHost mp;
+    if (c->replay_chunk == 0 && x->replay_chunk == 0 && !sv.fused_device && a.need_merge &&
+        plan_merge(xv.rows, xa.chunk_rows, 0, true, mp) &&
+        plan_merge(sv.rows, a.chunk_rows, xa.n_chunks, false, mp))
+        a.merge_plan = &mp;
     const hipError_t e = kvdec::launch_attend(c->d.dtype, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "attend launch");
     c->lens = pre;

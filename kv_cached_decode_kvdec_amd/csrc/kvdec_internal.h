@@ -26,6 +26,22 @@ struct PartialLayout {
 
 PartialLayout partial_layout(int64_t max_chunks, int32_t n_q_heads, int32_t batch);
 
+// The merge launch planned on the host (outside replay mode, where the host
+// holds every sequence's length): one entry per sequence split over several
+// chunks, by value.
+constexpr int kMaxMergeEntries = 160;
+
+struct MergePlan {
+    int32_t first[kMaxMergeEntries];   // workspace slot of the sequence's first chunk
+    int32_t b[kMaxMergeEntries];       // sequence
+    int32_t nch[kMaxMergeEntries];     // chunk count; bit 24 set: the cross part's output
+};
+
+struct MergePlanHost {
+    MergePlan plan;
+    int n = 0;
+};
+
 struct AttendArgs {
     const float* q;
     const void* k;
@@ -41,6 +57,8 @@ struct AttendArgs {
     bool need_merge;        // some sequence spans more than one chunk
     int32_t one_chunk = 0;  // 1: every sequence has exactly one chunk, whatever the
                             // device lengths (grid index = sequence)
+    int32_t uniform = -1;   // >= 0: every sequence attends this many rows, known on the
+                            // host (the launch reads no length to find its chunk)
     bool replay = false;    // capacity-sized grid (replay mode): surplus workgroups exit at once
     float qscale;           // scale * log2(e)
     float* out;
@@ -76,6 +94,10 @@ struct AttendArgs {
     int32_t x_row_limit = 0;
     int32_t x_chunk_rows = 0;
     int32_t x_one_chunk = 0;
+    int32_t x_uniform = -1;
+    // the merge planned on the host (nullptr: the merge finds the chunks
+    // from the lengths on the device)
+    const MergePlanHost* merge_plan = nullptr;
 };
 
 constexpr int kPagesPerLaunch = 256;   // new-page ids carried by value in one paged append

@@ -242,6 +242,11 @@ struct LensSrc<kLensDevice> {
     static constexpr int kPlus = 0;
     __device__ __forceinline__ int get(int b) const { return lens[b]; }
     __device__ __forceinline__ int merge_get(int b) const { return lens[b]; }
+    // the length of sequence b0 + lane (0 past the batch), one per lane
+    __device__ __forceinline__ int lanes(int b0, int lane, int B) const
+    {
+        return b0 + lane < B ? lens[b0 + lane] : 0;
+    }
 };
 
 // the new rows and the cache they are stored into (fused modes)
@@ -261,6 +266,10 @@ struct LensSrc<kLensHostFused> {
     static constexpr int kPlus = 1;
     __device__ __forceinline__ int get(int b) const { return v[b]; }
     __device__ __forceinline__ int merge_get(int b) const { return v[b]; }
+    __device__ __forceinline__ int lanes(int b0, int lane, int B) const
+    {
+        return b0 + lane < B ? v[b0 + lane] : 0;
+    }
 };
 
 // the paged fused mode: the new rows go to the page pool through the block
@@ -282,6 +291,10 @@ struct LensSrc<kLensPagedFused> {
     static constexpr int kPlus = 1;
     __device__ __forceinline__ int get(int b) const { return v[b]; }
     __device__ __forceinline__ int merge_get(int b) const { return v[b]; }
+    __device__ __forceinline__ int lanes(int b0, int lane, int B) const
+    {
+        return b0 + lane < B ? v[b0 + lane] : 0;
+    }
 };
 
 template <>
@@ -292,6 +305,10 @@ struct LensSrc<kLensDeviceFused> {
     static constexpr int kPlus = 1;
     __device__ __forceinline__ int get(int b) const { return lens[b]; }
     __device__ __forceinline__ int merge_get(int b) const { return snap[b]; }
+    __device__ __forceinline__ int lanes(int b0, int lane, int B) const
+    {
+        return b0 + lane < B ? lens[b0 + lane] : 0;
+    }
 };
 
 // Inclusive prefix sum over the 64 lanes of a wave, without LDS: a
@@ -311,8 +328,18 @@ __device__ __forceinline__ int wave_inclusive_sum(int x)
 
 template <int LM>
 __device__ __forceinline__ bool locate(const LensSrc<LM>& ls, int B, int T, int cap, int blk,
-                                       int lane, int one_chunk, Located& r)
+                                       int lane, int one_chunk, int uniform, Located& r)
 {
+    if (uniform >= 0) {
+        // every sequence attends `uniform` rows (known on the host): no
+        // length is read
+        const int nch = max(1, (uniform + T - 1) / T);
+        r.b = blk / nch;
+        r.c = blk - r.b * nch;
+        r.len = uniform;
+        r.nch = nch;
+        return r.b < B;
+    }
     if (one_chunk) {
         const int ln = min(max(ls.get(blk) + LensSrc<LM>::kPlus, 0), cap);
         r.b = blk;
@@ -324,7 +351,7 @@ __device__ __forceinline__ bool locate(const LensSrc<LM>& ls, int B, int T, int 
     int base = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
         const int bi = b0 + lane;
-        const int ln = bi < B ? min(max(ls.get(bi) + LensSrc<LM>::kPlus, 0), cap) : 0;
+        const int ln = bi < B ? min(max(ls.lanes(b0, lane, B) + LensSrc<LM>::kPlus, 0), cap) : 0;
         const int cnt = bi < B ? max(1, (ln + T - 1) / T) : 0;
         const int incl = wave_inclusive_sum(cnt);
         // lane values read with readlane are wave-uniform (scalar registers),
@@ -447,6 +474,7 @@ struct CrossPart {
     int row_limit;
     int T;                  // chunk rows
     int one_chunk;          // every sequence has exactly one chunk
+    int uniform;            // rows every sequence attends, when the host knows them; else -1
     int n_blocks;           // chunks of the part (0: no cross part)
 };
 
@@ -834,7 +862,7 @@ template <int ESZ, int GROUP, int WAVES, int U, bool PAGED, int LM, bool X2>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(valu_min_waves<ESZ, GROUP>())))
 void attend_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
-    LensSrc<LM> ls, int B, int Hkv, int cap_pad, int row_limit, int T, int one_chunk,
+    LensSrc<LM> ls, int B, int Hkv, int cap_pad, int row_limit, int T, int one_chunk, int uniform,
     float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
     PageMap pm, CrossPart xp)
 {
@@ -853,7 +881,8 @@ void attend_kernel(
     const bool in_cross = pos.in_cross;     // workgroup-uniform
     if (in_cross) {
         const LensSrc<kLensDevice> xs{xp.lens};
-        if (!locate<kLensDevice>(xs, B, xp.T, xp.row_limit, pos.blk, lane, xp.one_chunk, loc))
+        if (!locate<kLensDevice>(xs, B, xp.T, xp.row_limit, pos.blk, lane, xp.one_chunk, xp.uniform,
+                                 loc))
             return;
         q = xp.q;
         K = xp.K;
@@ -862,7 +891,7 @@ void attend_kernel(
         cap_pad = xp.cap_pad;
         T = xp.T;
     } else {
-        if (!locate<LM>(ls, B, T, row_limit, pos.blk, lane, one_chunk, loc)) return;
+        if (!locate<LM>(ls, B, T, row_limit, pos.blk, lane, one_chunk, uniform, loc)) return;
     }
     const int row0 = loc.c * T;
     int row_end = min(loc.len, row0 + T);   // lowered where a replayed row has no page
@@ -1047,7 +1076,7 @@ template <int GROUP, int WAVES, bool PAGED, int LM, bool X2>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void attend_gqa_mfma_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
-    LensSrc<LM> ls, int B, int Hkv, int cap_pad, int row_limit, int T, int one_chunk,
+    LensSrc<LM> ls, int B, int Hkv, int cap_pad, int row_limit, int T, int one_chunk, int uniform,
     float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
     PageMap pm, CrossPart xp)
 {
@@ -1074,7 +1103,8 @@ void attend_gqa_mfma_kernel(
     const bool in_cross = pos.in_cross;     // workgroup-uniform
     if (in_cross) {
         const LensSrc<kLensDevice> xs{xp.lens};
-        if (!locate<kLensDevice>(xs, B, xp.T, xp.row_limit, pos.blk, lane, xp.one_chunk, loc))
+        if (!locate<kLensDevice>(xs, B, xp.T, xp.row_limit, pos.blk, lane, xp.one_chunk, xp.uniform,
+                                 loc))
             return;
         q = xp.q;
         K = xp.K;
@@ -1083,7 +1113,7 @@ void attend_gqa_mfma_kernel(
         cap_pad = xp.cap_pad;
         T = xp.T;
     } else {
-        if (!locate<LM>(ls, B, T, row_limit, pos.blk, lane, one_chunk, loc)) return;
+        if (!locate<LM>(ls, B, T, row_limit, pos.blk, lane, one_chunk, uniform, loc)) return;
     }
     const int row0 = loc.c * T;
     int row_end = min(loc.len, row0 + T);   // lowered where a replayed row has no page
@@ -1291,6 +1321,11 @@ void attend_gqa_mfma_kernel(
 // wave), so the loads are grouped to keep the chain of dependent round trips
 // short: lengths -> {(m, l), first 16 o rows} -> further batches of 16.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void merge_core(size_t first, int nch, int Hq, int h, int lane,
+                                           const float* __restrict__ part_o,
+                                           const float2* __restrict__ part_ml,
+                                           float* __restrict__ out_row);
+
 // One (sequence b, query head h) of one part of the grid: its chunks'
 // partials start at slot `base` + the exclusive prefix of the part's chunk
 // counts; n_grid is the number of workgroups the part was launched with.
@@ -1328,8 +1363,17 @@ __device__ __forceinline__ void merge_one(const LensSrc<LM>& ls, int B, int Hq, 
         return;
     }
     if (nch == 1) return;     // finished by the attend kernel
-    const size_t first = static_cast<size_t>(base) + static_cast<size_t>(acc);
+    merge_core(static_cast<size_t>(base) + static_cast<size_t>(acc), nch, Hq, h, lane, part_o,
+               part_ml, out + w * kHeadDim);
+}
 
+// The merge of one (sequence, query head) whose nch chunk partials start at
+// slot `first`, into the output row out_row[64].
+__device__ __forceinline__ void merge_core(size_t first, int nch, int Hq, int h, int lane,
+                                           const float* __restrict__ part_o,
+                                           const float2* __restrict__ part_ml,
+                                           float* __restrict__ out_row)
+{
     // Chunk c's (m, l) is read by lane c % 64; the o rows are read kBatch
     // chunks at a time, all loads of a batch in flight together, and the
     // first batch is issued with the (m, l) loads (it does not need M).
@@ -1378,7 +1422,7 @@ __device__ __forceinline__ void merge_one(const LensSrc<LM>& ls, int B, int Hq, 
             }
         }
     }
-    out[w * kHeadDim + lane] = (Lsum > 0.f) ? o / Lsum : 0.f;
+    out_row[lane] = (Lsum > 0.f) ? o / Lsum : 0.f;
 }
 
 // One wave per (sequence, query head) of the launch's part(s): waves
@@ -1407,6 +1451,27 @@ __global__ __launch_bounds__(64) void merge_kernel(LensSrc<LM> ls, int B, int Hq
     const int b = w / Hq, h = w - b * Hq;
     merge_one<LM>(ls, B, Hq, T, row_limit, b, h, lane, X2 ? xp.n_blocks : 0, n_grid, part_o, part_ml,
                   out, pm);
+}
+
+// The merge where the host knows every sequence's chunk count (outside
+// replay mode the grids are sized from lengths the host holds): one wave per
+// (split sequence, query head), the sequence's first partial slot and chunk
+// count given by value, so no wave reads a length or scans the other
+// sequences' chunk counts, and no wave is launched for a sequence that the
+// attend launch finished in place.
+__global__ __launch_bounds__(64) void merge_planned_kernel(MergePlan plan, int Hq,
+                                                           const float* __restrict__ part_o,
+                                                           const float2* __restrict__ part_ml,
+                                                           float* __restrict__ out,
+                                                           float* __restrict__ out_x)
+{
+    const int lane = threadIdx.x & 63;
+    const int e = static_cast<int>(blockIdx.x) / Hq;
+    const int h = static_cast<int>(blockIdx.x) - e * Hq;
+    const int nch = plan.nch[e] & 0xFFFFFF;
+    float* o = (plan.nch[e] >> 24) ? out_x : out;
+    merge_core(static_cast<size_t>(plan.first[e]), nch, Hq, h, lane, part_o, part_ml,
+               o + (static_cast<size_t>(plan.b[e]) * Hq + h) * kHeadDim);
 }
 
 // ---------------------------------------------------------------------------
@@ -1644,6 +1709,7 @@ CrossPart cross_part(const AttendArgs& a)
         x.row_limit = a.x_row_limit;
         x.T = a.x_chunk_rows;
         x.one_chunk = a.x_one_chunk;
+        x.uniform = a.x_uniform;
         x.n_blocks = static_cast<int>(a.x_blocks);
     }
     return x;
@@ -1657,6 +1723,13 @@ hipError_t launch_merge(const AttendArgs& a, int group, const LensSrc<LM>& ls, f
 {
     if (!a.need_merge) return hipSuccess;
     const int Hq = a.n_kv_heads * group;
+    if (a.merge_plan) {
+        // the host planned it: only the split sequences, their slots by value
+        if (a.merge_plan->n == 0) return hipSuccess;
+        hipLaunchKernelGGL(merge_planned_kernel, dim3(a.merge_plan->n * Hq), dim3(64), 0, s,
+                           a.merge_plan->plan, Hq, po, pml, a.out, a.x_out);
+        return hipGetLastError();
+    }
     const int waves = a.batch * Hq * (X2 ? 2 : 1);
     // one wave per workgroup: the waves spread over more CUs (whisper-base
     // 27.3 -> 26.6 us per step against four-wave workgroups)
@@ -1711,18 +1784,18 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
             hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWideWaves, kUnroll, PAGED, LM, X2>), grid,
                                dim3(kWideWaves * 64), 0, s, a.q, static_cast<const char*>(a.k),
                                static_cast<const char*>(a.v), ls, a.batch, a.n_kv_heads, a.cap_pad,
-                               a.row_limit, a.chunk_rows, a.one_chunk, a.qscale, a.out, po, pml, pm,
-                               xp);
+                               a.row_limit, a.chunk_rows, a.one_chunk, a.uniform, a.qscale, a.out,
+                               po, pml, pm, xp);
     } else if constexpr (ESZ == 2 && GROUP >= 2) {
         hipLaunchKernelGGL((attend_gqa_mfma_kernel<GROUP, kWaves, PAGED, LM, X2>), grid, block, 0, s,
                            a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v), ls,
                            a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows, a.one_chunk,
-                           a.qscale, a.out, po, pml, pm, xp);
+                           a.uniform, a.qscale, a.out, po, pml, pm, xp);
     } else {
         hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWaves, kUnroll, PAGED, LM, X2>), grid, block,
                            0, s, a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v),
                            ls, a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows,
-                           a.one_chunk, a.qscale, a.out, po, pml, pm, xp);
+                           a.one_chunk, a.uniform, a.qscale, a.out, po, pml, pm, xp);
     }
     const hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : launch_merge<LM, X2>(a, GROUP, ls, po, pml, pm, xp, s);
