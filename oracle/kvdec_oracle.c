@@ -251,6 +251,50 @@ int kvdec_oracle_append(void* cacheK, void* cacheV, const void* k_new, const voi
 }
 
 /*
+ * Append with a sliding window that keeps an overlap, the streaming cache of
+ * [WA-DEC] `StreamingKVCache` (`append_with_slide`, `slide_window`): when the
+ * new row would take a sequence past `window` rows, the sequence first keeps
+ * only its last `overlap` rows (rows len - overlap .. len - 1 become rows
+ * 0 .. overlap - 1; the overlap is at most half the window, as the page's
+ * constructor caps it) and its length becomes `overlap`; then the row is
+ * appended as kvdec_oracle_append does.  `window` <= cap; slid[b] (may be
+ * NULL) is set to 1 where sequence b slid, else 0.
+ */
+int kvdec_oracle_append_slide(void* cacheK, void* cacheV, const void* k_new, const void* v_new,
+                              int64_t esz, int64_t B, int64_t Hkv, int64_t D, int64_t cap,
+                              int64_t window, int64_t overlap, int32_t* lens, int32_t* slid)
+{
+    if (esz <= 0 || B < 0 || Hkv <= 0 || D <= 0 || window < 1 || window > cap || overlap < 0)
+        return ORACLE_E_SHAPE;
+    const int64_t keep = overlap < window / 2 ? overlap : window / 2;
+    for (int64_t b = 0; b < B; ++b)
+        if (lens[b] < 0 || lens[b] > window) return ORACLE_E_SHAPE;
+    const size_t row = (size_t)(D * esz);
+    for (int64_t b = 0; b < B; ++b) {
+        int slide = (int64_t)lens[b] + 1 > window;
+        if (slide) {
+            const int64_t keep_from = lens[b] - keep;
+            for (int64_t g = 0; g < Hkv; ++g) {
+                char* k = (char*)cacheK + (size_t)((b * Hkv + g) * cap * D * esz);
+                char* v = (char*)cacheV + (size_t)((b * Hkv + g) * cap * D * esz);
+                memmove(k, k + (size_t)keep_from * row, (size_t)keep * row);
+                memmove(v, v + (size_t)keep_from * row, (size_t)keep * row);
+            }
+            lens[b] = (int32_t)keep;
+        }
+        if (slid) slid[b] = slide;
+        for (int64_t g = 0; g < Hkv; ++g) {
+            size_t dst = (size_t)(((b * Hkv + g) * cap + lens[b]) * D * esz);
+            size_t src = (size_t)((b * Hkv + g) * D * esz);
+            memcpy((char*)cacheK + dst, (const char*)k_new + src, row);
+            memcpy((char*)cacheV + dst, (const char*)v_new + src, row);
+        }
+        lens[b] += 1;
+    }
+    return ORACLE_OK;
+}
+
+/*
  * Token-major -> head-major import: the interleaved-to-head-first permute of
  * [WA-CUDA] `populate_cross_kv_caches_gpu` (`interleaved_to_head_first`),
  * [L, H*D] -> [H, L, D] per sequence, written into the padded cache.

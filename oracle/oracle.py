@@ -34,9 +34,12 @@ def load():
                                                     ctypes.c_double, _vp]
         lib.kvdec_oracle_append.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp]
         lib.kvdec_oracle_seed.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64]
+        lib.kvdec_oracle_append_slide.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                                  _i64, _i64, _vp, _vp]
         lib.kvdec_oracle_rope.argtypes = [_vp, _i64, _i64, _vp, ctypes.c_double, _vp]
         for f in (lib.kvdec_oracle_attend, lib.kvdec_oracle_prefill_causal,
-                  lib.kvdec_oracle_append, lib.kvdec_oracle_seed, lib.kvdec_oracle_rope):
+                  lib.kvdec_oracle_append, lib.kvdec_oracle_seed, lib.kvdec_oracle_rope,
+                  lib.kvdec_oracle_append_slide):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -108,6 +111,25 @@ def append(Kc, Vc, k_new, v_new, lens):
     if rc != 0:
         raise ValueError(f"oracle append rejected the arguments (code {rc})")
     return lens
+
+
+def append_slide(Kc, Vc, k_new, v_new, lens, window, overlap):
+    """In-place append with a sliding window keeping `overlap` rows (at most
+    window // 2) on numpy caches [B,Hkv,cap,D]; returns (new lens, slid
+    flags), both int32."""
+    if not (Kc.flags.c_contiguous and Vc.flags.c_contiguous):
+        raise ValueError("caches must be C-contiguous")
+    k_new = np.ascontiguousarray(k_new, dtype=Kc.dtype)
+    v_new = np.ascontiguousarray(v_new, dtype=Kc.dtype)
+    lens = np.array(lens, dtype=np.int32, copy=True)
+    B, Hkv, cap, D = Kc.shape
+    slid = np.zeros(B, dtype=np.int32)
+    rc = load().kvdec_oracle_append_slide(_ptr(Kc), _ptr(Vc), _ptr(k_new), _ptr(v_new),
+                                          Kc.dtype.itemsize, B, Hkv, D, cap, int(window),
+                                          int(overlap), _ptr(lens), _ptr(slid))
+    if rc != 0:
+        raise ValueError(f"oracle append_slide rejected the arguments (code {rc})")
+    return lens, slid
 
 
 def seed(dst, src):

@@ -411,3 +411,42 @@ def test_oracle_rope_closed_forms():
     s1 = oracle.rope(q[None], [50], 1e6)[0] @ oracle.rope(k[None], [20], 1e6)[0]
     s2 = oracle.rope(q[None], [4050], 1e6)[0] @ oracle.rope(k[None], [4020], 1e6)[0]
     assert abs(s1 - s2) < 1e-10
+
+
+@pytest.mark.parametrize("window,overlap", [(10, 3), (10, 8), (7, 0), (16, 16)])
+def test_append_slide_follows_the_streaming_cache_rule(window, overlap):
+    """oracle.append_slide against a literal list model of whisper-apr 0.3.3
+    decoder_generated.rs `StreamingKVCache`: the overlap is capped at half
+    the window (constructor); before an append that would exceed the window,
+    only the last `overlap` tokens are kept (`slide_window`: keep_from =
+    seq_len - overlap), then the token is appended (`append_with_slide`).
+    Each token's rows carry its identity, so the cached order is checked."""
+    B, Hkv, D = 3, 2, 64
+    cap = window + 5
+    keep = min(overlap, window // 2)
+    K = np.full((B, Hkv, cap, D), np.nan, np.float32)
+    V = np.full_like(K, np.nan)
+    start = [0, window - 1, window]
+    lists = [list(range(n)) for n in start]
+    row = lambda b, t, g, s: np.float32(s * (b * 100000 + t * 10 + g))
+    for b, n in enumerate(start):
+        for t in range(n):
+            for g in range(Hkv):
+                K[b, g, t], V[b, g, t] = row(b, t, g, 1), row(b, t, g, -1)
+    lens = np.array(start, np.int32)
+    for step in range(3 * window):
+        tok = [n + step for n in start]
+        kn = np.stack([[np.full(D, row(b, tok[b], g, 1)) for g in range(Hkv)] for b in range(B)])
+        vn = np.stack([[np.full(D, row(b, tok[b], g, -1)) for g in range(Hkv)] for b in range(B)])
+        lens, slid = oracle.append_slide(K, V, kn, vn, lens, window, overlap)
+        for b in range(B):
+            fired = len(lists[b]) + 1 > window
+            if fired:
+                lists[b] = lists[b][len(lists[b]) - keep:]
+            lists[b].append(tok[b])
+            assert slid[b] == int(fired)
+            assert lens[b] == len(lists[b]) <= window
+            for i, t in enumerate(lists[b]):
+                for g in range(Hkv):
+                    assert np.all(K[b, g, i] == row(b, t, g, 1)), (step, b, i)
+                    assert np.all(V[b, g, i] == row(b, t, g, -1)), (step, b, i)
