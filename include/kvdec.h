@@ -163,6 +163,28 @@ KVDEC_API int32_t kvdec_seed(kvdec_cache* cache, const void* k_tok, const void* 
 KVDEC_API int32_t kvdec_append(kvdec_cache* cache, const void* k_new, const void* v_new, void* stream);
 
 /*
+ * Append with a sliding window that keeps an overlap: the streaming cache of
+ * [WA-DEC] `StreamingKVCache` (`append_with_slide`, `slide_window`) on a
+ * linear cache whose capacity is the window.  For every sequence b whose new
+ * row would pass the capacity (lens[b] + 1 > capacity), the cache first
+ * keeps only its last keep = min(overlap, capacity / 2) rows -- rows
+ * lens[b] - keep .. lens[b] - 1 move to rows 0 .. keep - 1 (the page caps
+ * the overlap at half the window) -- and lens[b] becomes keep; then the row
+ * is appended as kvdec_append does.  Other sequences append normally.
+ * Attention then reads the kept rows and the new one.  The decision is
+ * taken on the device from the device lengths (so the call is capturable
+ * in replay mode too), and mirrored on the host.
+ *   k_new, v_new : as kvdec_append
+ *   overlap      : rows to keep when a sequence slides, >= 0
+ *   slid_out     : (host) NULL, or int32[batch]: 1 where the sequence slid, else
+ *                  0 (from the host mirror)
+ * Errors: KVDEC_E_STATIC (static cache), KVDEC_E_INVALID (a ring cache,
+ * overlap < 0, pointers, unknown lengths after replay mode).
+ */
+KVDEC_API int32_t kvdec_append_slide(kvdec_cache* cache, const void* k_new, const void* v_new,
+                                     int32_t overlap, int32_t* slid_out, void* stream);
+
+/*
  * Append with rotary position embedding: like kvdec_append, but k_new holds
  * the un-rotated keys; each is rotated at its token's position (the
  * sequence's length before this append) before it is stored, and, when q is

@@ -45,6 +45,7 @@ EXPORTED = [
     "kvdec_paged_set_replay_horizon",
     "kvdec_append_attend_noalloc",
     "kvdec_append_attend_cross",
+    "kvdec_append_slide",
 ]
 
 
@@ -93,6 +94,7 @@ def load():
         "kvdec_seed": (_i32, [_vp, _vp, _vp, _i32, _vp]),
         "kvdec_append": (_i32, [_vp, _vp, _vp, _vp]),
         "kvdec_append_rope": (_i32, [_vp, _vp, _vp, ctypes.c_float, _vp, _vp, _i32, _vp]),
+        "kvdec_append_slide": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp]),
         "kvdec_workspace_bytes": (_sz, [_vp, _i32]),
         "kvdec_attend_self": (_i32, [_vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz, _vp]),
         "kvdec_attend_cross": (_i32, [_vp, _vp, _i32, ctypes.c_float, _i32, _vp, _vp, _sz, _vp]),
@@ -321,3 +323,11 @@ def kvdec_append_attend_cross(self_handle, cross_handle, lens_host, k_new_ptr, v
                                             int(chunk_self), int(chunk_cross), out_self_ptr,
                                             out_cross_ptr, ws_ptr, int(ws_bytes), stream),
            "kvdec_append_attend_cross")
+
+
+def kvdec_append_slide(handle, k_new_ptr, v_new_ptr, overlap, batch, stream=None):
+    """Returns the per-sequence slid flags (host mirror)."""
+    slid = (ctypes.c_int32 * batch)()
+    _check(load().kvdec_append_slide(handle, k_new_ptr, v_new_ptr, int(overlap), slid, stream),
+           "kvdec_append_slide")
+    return list(slid)

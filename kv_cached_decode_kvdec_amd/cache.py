@@ -106,6 +106,16 @@ class KVCache:
         self._check_rows(v_new, shape, "v_new")
         B.kvdec_append(self.handle, _ptr(k_new), _ptr(v_new), current_stream())
 
+    def append_slide(self, k_new, v_new, overlap):
+        """Append; a full sequence first keeps only its last min(overlap,
+        capacity // 2) rows (the streaming cache's slide).  Returns the
+        per-sequence slid flags."""
+        shape = (self.batch, self.n_kv_heads, B.HEAD_DIM)
+        self._check_rows(k_new, shape, "k_new")
+        self._check_rows(v_new, shape, "v_new")
+        return B.kvdec_append_slide(self.handle, _ptr(k_new), _ptr(v_new), overlap, self.batch,
+                                    current_stream())
+
     def append_rope(self, k_new, v_new, theta, q=None, q_rot=None):
         """Append un-rotated keys, rotating them (and q into q_rot) at each
         sequence's current position.  Returns q_rot (or None)."""

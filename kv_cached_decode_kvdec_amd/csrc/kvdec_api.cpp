@@ -671,6 +671,34 @@ int32_t kvdec_append(kvdec_cache* c, const void* k_new, const void* v_new, void*
     return KVDEC_OK;
 }
 
+int32_t kvdec_append_slide(kvdec_cache* c, const void* k_new, const void* v_new, int32_t overlap,
+                           int32_t* slid_out, void* stream)
+{
+    g_err.clear();
+    if (!c) return fail(KVDEC_E_INVALID, "cache handle is NULL");
+    if (c->d.is_static) return fail(KVDEC_E_STATIC, "append on a static (encoder) cache");
+    if (c->d.window != 0)
+        return fail(KVDEC_E_INVALID, "a sliding-window ring already keeps the last window rows; "
+                    "kvdec_append_slide needs a linear cache");
+    if (overlap < 0) return fail(KVDEC_E_INVALID, "overlap %d must be >= 0", overlap);
+    const int32_t rc = check_mirror(c);
+    if (rc) return rc;
+    if (!aligned16(k_new) || !aligned16(v_new))
+        return fail(KVDEC_E_INVALID, "k_new and v_new must be non-NULL, 16-byte aligned device pointers");
+    const int32_t keep = overlap < c->d.capacity / 2 ? overlap : c->d.capacity / 2;
+    const hipError_t e = kvdec::launch_append_slide(c->d.dtype, c->d.k, c->d.v, k_new, v_new, c->d.lens,
+                                                    c->d.batch, c->d.n_kv_heads, c->d.capacity,
+                                                    c->cap_pad, keep, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+    for (int32_t b = 0; b < c->d.batch; ++b) {
+        const bool slide = c->lens[b] + 1 > c->d.capacity;
+        if (slide) c->lens[b] = keep;
+        if (slid_out) slid_out[b] = slide ? 1 : 0;
+        ++c->lens[b];
+    }
+    return KVDEC_OK;
+}
+
 int32_t kvdec_append_rope(kvdec_cache* c, const void* k_new, const void* v_new, float theta,
                           const float* q, float* q_rot, int32_t n_q_heads, void* stream)
 {

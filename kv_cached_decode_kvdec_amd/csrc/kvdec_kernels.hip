@@ -662,6 +662,58 @@ __global__ __launch_bounds__(256) void append_kernel(char* __restrict__ K, char*
 }
 
 // ---------------------------------------------------------------------------
+// append with a sliding window that keeps an overlap (the streaming cache of
+// whisper-apr 0.3.3 decoder_generated.rs, `StreamingKVCache`): a sequence
+// whose new row would pass the capacity first keeps only its last `keep`
+// rows, moved to rows 0 .. keep - 1 (keep <= capacity / 2, so the source rows
+// capacity - keep .. capacity - 1 and the destination rows never overlap),
+// and restarts at length `keep`; then the row is appended.  The decision is
+// taken on the device from the length there, so it also holds in replay
+// mode.
+// ---------------------------------------------------------------------------
+template <int ROW_BYTES>
+__global__ __launch_bounds__(256) void append_slide_kernel(char* __restrict__ K, char* __restrict__ V,
+                                                           const char* __restrict__ kn,
+                                                           const char* __restrict__ vn,
+                                                           int32_t* __restrict__ lens, int Hkv,
+                                                           int capacity, int cap_pad, int keep)
+{
+    constexpr int VPR = ROW_BYTES / 16;
+    const int b = blockIdx.x;
+    int len = lens[b];
+    if (len < 0 || len > capacity) return;
+    if (len + 1 > capacity) {
+        const int from = len - keep;
+        const int per_head = keep * VPR;
+        const int n = Hkv * per_head;
+        for (int t = threadIdx.x; t < 2 * n; t += blockDim.x) {
+            const bool isv = t >= n;
+            const int tt = isv ? t - n : t;
+            const int g = tt / per_head, rem = tt - g * per_head;
+            const int r = rem / VPR, w = rem - r * VPR;
+            char* base = (isv ? V : K) + (static_cast<size_t>(b) * Hkv + g) * cap_pad * ROW_BYTES;
+            reinterpret_cast<uint4*>(base + static_cast<size_t>(r) * ROW_BYTES)[w] =
+                reinterpret_cast<const uint4*>(base + static_cast<size_t>(from + r) * ROW_BYTES)[w];
+        }
+        // every moved row is read before the new row (at row `keep`, which may
+        // be the first source row) is written
+        __syncthreads();
+        len = keep;
+    }
+    const int n = Hkv * VPR;
+    for (int t = threadIdx.x; t < 2 * n; t += blockDim.x) {
+        const bool isv = t >= n;
+        const int tt = isv ? t - n : t;
+        const int g = tt / VPR, w = tt - g * VPR;
+        const size_t hg = static_cast<size_t>(b) * Hkv + g;
+        reinterpret_cast<uint4*>((isv ? V : K) + (hg * cap_pad + len) * ROW_BYTES)[w] =
+            reinterpret_cast<const uint4*>((isv ? vn : kn) + hg * ROW_BYTES)[w];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) lens[b] = len + 1;
+}
+
+// ---------------------------------------------------------------------------
 // append with rotary position embedding: the new key (and optionally the
 // query) of every sequence is rotated at the token's position (= its length
 // before the append) before the key is stored -- the RoPE-then-append order
@@ -1516,6 +1568,22 @@ hipError_t launch_append(int dtype, void* k, void* v, const void* k_new, const v
         hipLaunchKernelGGL(append_kernel<128>, grid, block, 0, s, static_cast<char*>(k),
                            static_cast<char*>(v), static_cast<const char*>(k_new),
                            static_cast<const char*>(v_new), lens, n_kv_heads, capacity, cap_pad, window);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_slide(int dtype, void* k, void* v, const void* k_new, const void* v_new,
+                               int32_t* lens, int32_t batch, int32_t n_kv_heads, int32_t capacity,
+                               int32_t cap_pad, int32_t keep, hipStream_t s)
+{
+    const dim3 grid(batch), block(256);
+    if (dtype == 0)
+        hipLaunchKernelGGL(append_slide_kernel<256>, grid, block, 0, s, static_cast<char*>(k),
+                           static_cast<char*>(v), static_cast<const char*>(k_new),
+                           static_cast<const char*>(v_new), lens, n_kv_heads, capacity, cap_pad, keep);
+    else
+        hipLaunchKernelGGL(append_slide_kernel<128>, grid, block, 0, s, static_cast<char*>(k),
+                           static_cast<char*>(v), static_cast<const char*>(k_new),
+                           static_cast<const char*>(v_new), lens, n_kv_heads, capacity, cap_pad, keep);
     return hipGetLastError();
 }
 
