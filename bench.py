@@ -196,7 +196,7 @@ class Bench:
     def _mean_bytes(self, seq, n):
         return sum(seq[i % self.S] for i in range(n)) / n
 
-    def run(self, steps, warmup, cold=True):
+    def run(self, steps, warmup, cold=True, window_ms=MIN_WINDOW_MS):
         torch = self.torch
         Ev = lambda: torch.cuda.Event(enable_timing=True)
         for i in range(warmup):
@@ -217,7 +217,7 @@ class Bench:
         # windows of W back-to-back steps (whole cycles), an event pair each
         W = self.S * max(1, math.ceil(16 / self.S))
         est_ms = max(res["ms_per_step"], 1e-4)
-        n_win = max(16, math.ceil(MIN_WINDOW_STEPS / W), math.ceil(MIN_WINDOW_MS / (W * est_ms)))
+        n_win = max(16, math.ceil(MIN_WINDOW_STEPS / W), math.ceil(window_ms / (W * est_ms)))
         evs = [Ev() for _ in range(n_win + 1)]
         torch.cuda.synchronize()
         evs[0].record()
@@ -729,6 +729,9 @@ def main():
     ap.add_argument("--per-workload", default="all",
                     help="comma list of extra workloads to report on stderr/JSON, or 'none'")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold (flushed) per-step timing")
+    ap.add_argument("--window-ms", type=float, default=MIN_WINDOW_MS,
+                    help="least GPU time the windowed timing covers per workload (profiled runs "
+                         "use less)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-workers", type=int, default=16,
                     help="host cores for the all-cores oracle baseline (capped by the CPU count; "
@@ -784,11 +787,11 @@ def main():
         wl = gen.WORKLOADS[name]
         bench = Bench(name, torch, gen, Bd, KVCache, to_device, form=args.form)
         if name == head:
-            res = bench.run(args.steps, args.warmup, cold=not args.no_cold)
+            res = bench.run(args.steps, args.warmup, cold=not args.no_cold, window_ms=args.window_ms)
         else:
             # at least 256 steps, whatever --steps is
             K = max(args.steps, MIN_WINDOW_STEPS, wl.steps)
-            res = bench.run(K, max(args.warmup, 16), cold=not args.no_cold)
+            res = bench.run(K, max(args.warmup, 16), cold=not args.no_cold, window_ms=args.window_ms)
         if not args.no_graph:
             res.update(bench.run_graph(max(args.steps, MIN_WINDOW_STEPS)))
         bench.close()
@@ -817,7 +820,8 @@ def main():
         name, variant = spec.split("+")
         vb = VariantBench(name, variant, torch, gen, Bd, KVCache, to_device)
         wl = gen.WORKLOADS[name]
-        res = vb.run(max(args.steps, MIN_WINDOW_STEPS, wl.steps), max(args.warmup, 16), cold=False)
+        res = vb.run(max(args.steps, MIN_WINDOW_STEPS, wl.steps), max(args.warmup, 16), cold=False,
+                     window_ms=args.window_ms)
         vb.close()
         del vb
         torch.cuda.empty_cache()
