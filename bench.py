@@ -29,8 +29,9 @@ workload:
             (at least 256 steps and 50 ms in all): median, p10 and p90 of
             the time per step over the windows -- one event pair per window,
             so the markers' own cost is spread over its steps;
-  per-step  an event pair around each single step, warm (back to back) and
-            cold (a 1 GiB buffer written before every step evicts the
+  per-step  an event pair around each single step, warm (after a ~50 us GPU
+            spin, so the host has queued the step before its first event)
+            and cold (a 1 GiB buffer written before every step evicts the
             Infinity Cache): median, p10, p90 over at least 128 steps; both
             carry one marker pair per step, so they compare like with like;
   roofline  the dominant launch's algorithmic bytes over its time per launch
@@ -238,8 +239,18 @@ class Bench:
         # launch, plus a merge launch where a sequence spans several chunks)
         res["launch_bytes"] = self._mean_bytes(self.launch_bytes, W)
 
-        # per-step event pairs: warm (back to back), then cold (flush before each)
+        # per-step event pairs: warm, then cold (flush before each).  Before
+        # every warm step the GPU idles ~50 us (a spin kernel) so that the
+        # host has the step's launches queued when its first event fires: the
+        # pair then times the GPU, not the host's launch rate (the cold
+        # steps get that from the flush).
         n_ev = self.S * max(1, math.ceil(MIN_EVENT_STEPS / self.S))
+        a0, b0 = Ev(), Ev()
+        a0.record()
+        torch.cuda._sleep(1 << 20)
+        b0.record()
+        torch.cuda.synchronize()
+        spin = int((1 << 20) * 50.0 / max(1e3 * a0.elapsed_time(b0), 1.0))
 
         def per_step(flush):
             a = [Ev() for _ in range(n_ev)]
@@ -248,6 +259,8 @@ class Bench:
             for i in range(n_ev):
                 if flush is not None:
                     flush.zero_()
+                else:
+                    torch.cuda._sleep(spin)
                 a[i].record()
                 self.step(i)
                 b[i].record()
