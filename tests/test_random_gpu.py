@@ -19,7 +19,13 @@ window: the new row goes to slot len % W and the oracle attends the first
 min(len + 1, W) rows of the ring buffer (attention does not depend on row
 order).  Cross cases seed a static cache from token-major encoder rows
 (kvdec_seed) and attend it with grouped query heads; the seeded bytes are
-compared with the oracle's head-first permute.
+compared with the oracle's head-first permute.  Layer cases run one
+decoder layer's step in one launch (kvdec_append_attend_cross: the fused
+self step and cross-attention over a seeded static cache, each part at its
+own drawn chunk size, sometimes at explicit positions or in replay mode)
+for two steps.  Slide cases append with the streaming cache's slide
+(kvdec_append_slide) on a small linear cache for several steps, so that
+sequences slide, and compare the cache bytes with the oracle's.
 """
 import sys
 
@@ -36,9 +42,9 @@ from helpers import assert_attention_close
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 160
+N_CASES = 192
 MODES = ["attend", "fused", "fused_at", "paged", "ring", "ring_at", "cross", "paged_fused", "replay",
-         "paged_replay"]
+         "paged_replay", "layer", "slide"]
 
 
 def _draw_lens(rng, Bsz):
@@ -113,6 +119,73 @@ def test_random_case(i):
         kd, vd = to_host_bits(c.k), to_host_bits(c.v)
         assert kd[:, :, :rows].tobytes() == K[:, :, :rows].tobytes()
         assert vd[:, :, :rows].tobytes() == V[:, :, :rows].tobytes()
+        return
+    if mode == "layer":
+        rows = int(rng.integers(1, 1600))         # encoder rows
+        ktok = _rows(rng, (Bsz, rows, Hkv * 64), dtype, s)
+        vtok = _rows(rng, (Bsz, rows, Hkv * 64), dtype, s)
+        cross = KVCache(Bsz, Hkv, rows, dtype, static=True, lens=[0] * Bsz)
+        cross.seed(to_device(ktok), to_device(vtok))
+        cK = np.zeros((Bsz, Hkv, gen.padded_rows(rows), 64), ktok.dtype)
+        cV = np.zeros_like(cK)
+        oracle.seed(cK, ktok)
+        oracle.seed(cV, vtok)
+        cap = int(lens.max(initial=0)) + 3
+        K = _rows(rng, (Bsz, Hkv, gen.padded_rows(cap), 64), dtype, s)
+        V = _rows(rng, (Bsz, Hkv, gen.padded_rows(cap), 64), dtype, s)
+        c = KVCache(Bsz, Hkv, cap, dtype, lens=lens, k=to_device(K), v=to_device(V))
+        Tx = int(rng.choice([0, 64, 128, 256, 512, 2048]))
+        sub = int(rng.integers(0, 3))             # 0: mirror, 1: positions, 2: replay mode
+        if sub == 2:
+            c.set_replay_mode(int(rng.choice([64, 128, 256, -1])))
+        what = f"case {i} (layer {dtype} B={Bsz} Hq={Hq} Hkv={Hkv} T={T}/{Tx} rows={rows} sub={sub})"
+        Kh, Vh, ln = K.copy(), V.copy(), lens.copy()
+        for st in range(2):
+            kn = _rows(rng, (Bsz, Hkv, 64), dtype, s)
+            vn = _rows(rng, (Bsz, Hkv, 64), dtype, s)
+            q = (rng.standard_normal((Bsz, Hq, 64)) * s).astype(np.float32)
+            qx = (rng.standard_normal((Bsz, Hq, 64)) * s).astype(np.float32)
+            pos = None
+            if sub == 1:
+                pos = (rng.random(Bsz) * (ln + 1)).astype(np.int32)
+                ln = pos
+            out, outx = c.append_attend_cross(cross, to_device(kn), to_device(vn), to_device(q),
+                                              to_device(qx), scale=scale, chunk_self=T,
+                                              chunk_cross=Tx, lens=pos)
+            torch.cuda.synchronize()
+            ln = oracle.append(Kh, Vh, kn, vn, ln)
+            assert_attention_close(out.cpu().numpy(), oracle.attend(q, Kh, Vh, ln, scale), dtype,
+                                   f"{what} self step {st}")
+            n = np.full(Bsz, rows, np.int32)
+            assert_attention_close(outx.cpu().numpy(), oracle.attend(qx, cK, cV, n, scale), dtype,
+                                   f"{what} cross step {st}")
+        assert c.lens_dev.cpu().tolist() == ln.tolist()
+        assert to_host_bits(c.k).tobytes() == Kh.tobytes()
+        assert to_host_bits(c.v).tobytes() == Vh.tobytes()
+        return
+    if mode == "slide":
+        W = int(rng.integers(2, 200))             # the window: a small linear cache
+        overlap = int(rng.integers(0, W + 2))
+        lens = np.minimum(lens, W).astype(np.int32)
+        cp = gen.padded_rows(W)
+        K = _rows(rng, (Bsz, Hkv, cp, 64), dtype, s)
+        V = _rows(rng, (Bsz, Hkv, cp, 64), dtype, s)
+        c = KVCache(Bsz, Hkv, W, dtype, lens=lens, k=to_device(K), v=to_device(V))
+        what = f"case {i} (slide {dtype} B={Bsz} Hq={Hq} Hkv={Hkv} T={T} W={W} overlap={overlap})"
+        Kh, Vh, ln = K.copy(), V.copy(), lens.copy()
+        for st in range(int(rng.integers(1, 2 * W + 3)) if W < 60 else 3):
+            kn = _rows(rng, (Bsz, Hkv, 64), dtype, s)
+            vn = _rows(rng, (Bsz, Hkv, 64), dtype, s)
+            slid = c.append_slide(to_device(kn), to_device(vn), overlap)
+            ln, ref_slid = oracle.append_slide(Kh, Vh, kn, vn, ln, W, overlap)
+            assert slid == ref_slid.tolist(), f"{what} step {st}"
+        q = (rng.standard_normal((Bsz, Hq, 64)) * s).astype(np.float32)
+        out = c.attend(to_device(q), scale=scale, chunk_rows=T)
+        torch.cuda.synchronize()
+        assert_attention_close(out.cpu().numpy(), oracle.attend(q, Kh, Vh, ln, scale), dtype, what)
+        assert c.lens() == ln.tolist() and c.lens_dev.cpu().tolist() == ln.tolist()
+        assert to_host_bits(c.k).tobytes() == Kh.tobytes()
+        assert to_host_bits(c.v).tobytes() == Vh.tobytes()
         return
     if mode.startswith("ring"):
         cap = int(rng.integers(40, 700))          # the window; lengths may exceed it
