@@ -6,11 +6,15 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
+#include <queue>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "kvdec_internal.h"
@@ -289,6 +293,61 @@ void fill_args(const AttendView& v, const float* q, float scale, float* out, voi
     a.window = v.window;
 }
 
+// The placement of a host-fused launch's chunks on the CUs (see
+// kvdec::Placement): only where the launch is one residency round of
+// four-wave workgroups with ragged chunks, the CU count is a multiple of
+// the KV heads, and every position class gets at least two chunks.  A
+// chunk's weight is its rows plus a fixed per-workgroup cost; the heaviest
+// go first, each into the least-loaded class that has a position left
+// (ties to the lower class and the earlier chunk, so the plan is a function
+// of the lengths alone).
+constexpr int64_t kPlaceFixedRows = 32;
+
+bool plan_placement(const AttendView& v, int32_t group, const kvdec::AttendArgs& a,
+                    kvdec::Placement& pl)
+{
+    if (a.uniform >= 0 || a.x_blocks > 0 || v.table) return false;
+    if (kvdec::attend_waves(v.dtype, group, a.chunk_rows, false) != 4) return false;
+    const int32_t Hkv = v.n_kv_heads;
+    const int cus = kvdec::device_cus();
+    if (cus <= 0 || cus % Hkv != 0) return false;
+    const int64_t classes = cus / Hkv;
+    const int64_t P = a.n_chunks;
+    const int64_t per = (P + classes - 1) / classes;
+    const int64_t npos = per * classes;
+    if (per < 2 || npos > kvdec::kMaxPlaced || npos >= kvdec::kNoChunk ||
+        npos * Hkv > kvdec::resident_attend_blocks(v.dtype, group))
+        return false;
+    // chunk weights in chunk order (sequence by sequence, as the kernels number them)
+    const int64_t T = a.chunk_rows;
+    std::vector<std::pair<int64_t, int32_t>> w;
+    w.reserve(static_cast<size_t>(P));
+    for (int32_t r : v.rows) {
+        const int64_t n = r > 0 ? r : 0;
+        const int64_t nch = n > 0 ? (n + T - 1) / T : 1;
+        for (int64_t c = 0; c < nch; ++c) {
+            const int64_t rows = std::min(n, (c + 1) * T) - c * T;
+            w.emplace_back(-(rows + kPlaceFixedRows), static_cast<int32_t>(w.size()));
+        }
+    }
+    if (static_cast<int64_t>(w.size()) != P) return false;
+    std::sort(w.begin(), w.end());
+    using Load = std::pair<int64_t, int32_t>;      // (load, class)
+    std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+    for (int32_t k = 0; k < classes; ++k) heap.emplace(0, k);
+    std::vector<int32_t> filled(static_cast<size_t>(classes), 0);
+    for (int64_t p = 0; p < npos; ++p) pl.pos[p] = kvdec::kNoChunk;
+    for (const auto& item : w) {
+        const Load top = heap.top();
+        heap.pop();
+        const int32_t k = top.second;
+        pl.pos[k + classes * filled[k]] = static_cast<uint16_t>(item.second);
+        if (++filled[k] < per) heap.emplace(top.first - item.first, k);
+    }
+    pl.n = static_cast<int32_t>(npos);
+    return true;
+}
+
 int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, float scale,
                     int32_t chunk_rows, float* out, void* ws, size_t ws_bytes, void* stream)
 {
@@ -316,6 +375,8 @@ int32_t attend_view(const AttendView& v, const float* q, int32_t n_q_heads, floa
     if (v.replay_chunk == 0 && !v.fused_device && a.need_merge &&
         plan_merge(v.rows, a.chunk_rows, 0, false, mp))
         a.merge_plan = &mp;
+    kvdec::Placement pl;
+    if (v.fused_lens && v.replay_chunk == 0 && plan_placement(v, group, a, pl)) a.placement = &pl;
     const hipError_t e = kvdec::launch_attend(v.dtype, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "attend launch");
     return KVDEC_OK;

@@ -42,6 +42,25 @@ struct MergePlanHost {
     int n = 0;
 };
 
+// Placement of the chunks of a one-round host-fused launch on the device's
+// compute units.  The hardware hands the workgroups of a launch that fits
+// one residency round out in order of their linear id, round robin over the
+// XCDs and then over each XCD's CUs, so ids that agree modulo the CU count
+// run on one CU.  With the grid laid out (KV head, position), a position's
+// heads cover n_kv_heads consecutive ids, and positions that agree modulo
+// cus / n_kv_heads share their CUs: the host puts the chunks into those
+// position classes so that every CU gets about the same rows (largest
+// first, each into the least-loaded class).  pos[p] is the chunk at
+// position p, kNoChunk an empty position.  Results do not depend on it: a
+// chunk's arithmetic and its partial slot are the same wherever it runs.
+constexpr int kMaxPlaced = 512;
+constexpr uint16_t kNoChunk = 0xFFFF;
+
+struct Placement {
+    uint16_t pos[kMaxPlaced];
+    int32_t n = 0;              // positions (0: the grid is (chunk, KV head) in chunk order)
+};
+
 struct AttendArgs {
     const float* q;
     const void* k;
@@ -98,6 +117,9 @@ struct AttendArgs {
     // the merge planned on the host (nullptr: the merge finds the chunks
     // from the lengths on the device)
     const MergePlanHost* merge_plan = nullptr;
+    // host-fused launches only: the chunks' placement on the CUs (nullptr or
+    // n == 0: chunk order)
+    const Placement* placement = nullptr;
 };
 
 constexpr int kPagesPerLaunch = 256;   // new-page ids carried by value in one paged append
@@ -154,5 +176,8 @@ int attend_waves(int dtype, int group, int chunk_rows, bool replay);
 // Workgroups of the attend kernel for (dtype, group) that are resident on the
 // current device at once (occupancy x compute units); 0 if unknown.  Cached.
 int resident_attend_blocks(int dtype, int group);
+
+// Compute units of the current device (0 if unknown); cached per device.
+int device_cus();
 
 }  // namespace kvdec

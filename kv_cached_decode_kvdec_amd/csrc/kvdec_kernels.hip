@@ -263,6 +263,8 @@ template <>
 struct LensSrc<kLensHostFused> {
     int32_t v[kMaxFusedBatch];
     FusedRows f;
+    uint16_t place[kMaxPlaced];   // chunk at each position (see Placement)
+    int32_t n_place;              // 0: grid (chunk, KV head) in chunk order
     static constexpr int kPlus = 1;
     __device__ __forceinline__ int get(int b) const { return v[b]; }
     __device__ __forceinline__ int merge_get(int b) const { return v[b]; }
@@ -514,6 +516,24 @@ __device__ __forceinline__ BlockPos block_pos(const CrossPart& xp, int Hkv)
         p.slot = p.blk;
     }
     return p;
+}
+
+// A host-fused launch with a placement runs on a (KV head, position) grid:
+// the workgroup takes the chunk the host put at its position (false: an
+// empty position, the workgroup has nothing to do).
+template <int LM, bool X2>
+__device__ __forceinline__ bool placed(const LensSrc<LM>& ls, BlockPos& p)
+{
+    if constexpr (LM == kLensHostFused && !X2) {
+        if (ls.n_place > 0) {
+            const int e = ls.place[blockIdx.y];
+            if (e == kNoChunk) return false;
+            p.g = static_cast<int>(blockIdx.x);
+            p.blk = e;
+            p.slot = e;
+        }
+    }
+    return true;
 }
 
 // fresh_idx >= 0: table entry fresh_idx is being given page fresh_page by this
@@ -925,7 +945,8 @@ void attend_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane / LPR;
     const int part = lane - sub * LPR;
-    const BlockPos pos = block_pos<X2>(xp, Hkv);
+    BlockPos pos = block_pos<X2>(xp, Hkv);
+    if (!placed<LM, X2>(ls, pos)) return;
     const int g = pos.g;
     const int Hq = Hkv * GROUP;
 
@@ -1140,7 +1161,8 @@ void attend_gqa_mfma_kernel(
     const int i = lane & 15;
     const int G = lane >> 4;
     const int hl = i % GROUP;              // head whose scores this lane holds
-    const BlockPos pos = block_pos<X2>(xp, Hkv);
+    BlockPos pos = block_pos<X2>(xp, Hkv);
+    if (!placed<LM, X2>(ls, pos)) return;
     const int g = pos.g;
     const int Hq = Hkv * GROUP;
 
@@ -1178,12 +1200,41 @@ void attend_gqa_mfma_kernel(
         stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages);
     const char* Kb = K + 16 * (lane & 7); // + row offset, row = r0 + 8c + (lane >> 3)
     const char* Vb = V + 16 * (lane & 7);
-    if constexpr (LM == kLensPagedFused)
+    // Fused append into a contiguous cache: the workgroup whose chunk holds
+    // the new token's slot reads that row from k_new / v_new wherever its
+    // tiles cover it (no load of this launch reads the slot from the cache),
+    // so its tile loads need not wait for the row to be stored; threads
+    // 0..15 copy the row into the cache once those loads are issued.
+    int slot_row = -1;                      // wave-uniform; -1: no slot in this chunk
+    const char* Kn = nullptr;
+    const char* Vn = nullptr;
+    char* app_dst = nullptr;
+    uint4 app_row{};
+    if constexpr (LM == kLensPagedFused) {
         fused_append_paged<RB>(ls, loc, g, Hkv, pm, sm_pages, row0, row_end);
-    else if constexpr (PAGED && LM == kLensDeviceFused)
+    } else if constexpr (PAGED && LM == kLensDeviceFused) {
         fused_append_paged_device<RB>(ls, loc, g, Hkv, pm, sm_pages, row0, row_end);
-    else if constexpr (LM != kLensDevice)
-        if (!in_cross) fused_append<RB>(ls, loc, g, Hkv, cap_pad, row0, row_end);
+    } else if constexpr (LM != kLensDevice) {
+        if (!in_cross) {
+            const int len0 = ls.get(loc.b);
+            const int slot = ls.f.window > 0 ? len0 % ls.f.window : len0;
+            if (row0 <= slot && slot < row_end) {
+                slot_row = slot;
+                const size_t hg = static_cast<size_t>(loc.b) * Hkv + g;
+                Kn = ls.f.k_new + hg * RB + 16 * (lane & 7);
+                Vn = ls.f.v_new + hg * RB + 16 * (lane & 7);
+                if (threadIdx.x < 16) {
+                    const bool isv = threadIdx.x >= 8;
+                    app_row = *reinterpret_cast<const uint4*>(isv ? Vn : Kn);
+                    app_dst = (isv ? ls.f.V : ls.f.K) + (hg * cap_pad + slot) * RB + 16 * (lane & 7);
+                }
+                if constexpr (LM == kLensHostFused)
+                    if (g == 0 && threadIdx.x == 0) ls.f.lens_out[loc.b] = len0 + 1;
+            }
+            if constexpr (LM == kLensDeviceFused)
+                if (loc.c == 0 && g == 0 && threadIdx.x == 0) ls.snap[loc.b] = len0;
+        }
+    }
 
     // q loads, then the wave's first 32 rows, both in flight before either is
     // waited for.  The loop is software-pipelined: once a tile sits in LDS
@@ -1200,7 +1251,7 @@ void attend_gqa_mfma_kernel(
     }
     uint4 kw[4], vr[4];
     auto load_tile = [&](int r0) {
-        if (!PAGED && r0 + 32 <= row_end) {
+        if (!PAGED && r0 + 32 <= row_end && (slot_row < r0 || slot_row >= r0 + 32)) {
             // whole tile inside the chunk (wave-uniform): rows r0 + 8c + lane/8
             // are 1 KB apart, no clamping
             const size_t off = row_offset<false, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0,
@@ -1211,19 +1262,41 @@ void attend_gqa_mfma_kernel(
                 vr[c] = load16_stream(Vb + off + 8 * RB * c);
             }
         } else {
-            // last tile: rows past the end repeat the last row (its weight is
-            // zero, and the V row is finite)
+            // last tile (or the one holding the new row's slot): rows past
+            // the end repeat the last row (its weight is zero, and the V row
+            // is finite)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int r = min(r0 + 8 * c + (lane >> 3), row_end - 1);
                 const size_t off = row_offset<PAGED, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0, r);
-                kw[c] = load16_stream(Kb + off);
-                vr[c] = load16_stream(Vb + off);
+                const bool fresh = r == slot_row;
+                kw[c] = load16_stream(fresh ? Kn : Kb + off);
+                vr[c] = load16_stream(fresh ? Vn : Vb + off);
             }
         }
     };
     int r0 = row0 + wave * 32;
-    if (r0 < row_end) load_tile(r0);
+    if constexpr (PAGED) {
+        if (r0 < row_end) load_tile(r0);
+    } else {
+        // The first tile is requested by every wave on one path (rows
+        // clamped to the chunk's last row, or to row 0 of the stream for an
+        // empty one; a wave with no rows discards what it read), so that
+        // the wait for q below is a wait for the q loads alone rather than
+        // for every load of the branches it joins.
+        const int rmax = max(row_end - 1, 0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int r = min(r0 + 8 * c + (lane >> 3), rmax);
+            const size_t off = row_offset<false, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0, r);
+            const bool fresh = r == slot_row;
+            kw[c] = load16_stream(fresh ? Kn : Kb + off);
+            vr[c] = load16_stream(fresh ? Vn : Vb + off);
+        }
+        // keep the scheduler from moving these loads behind the wait for q
+        __builtin_amdgcn_sched_barrier(0);
+        if (app_dst) *reinterpret_cast<uint4*>(app_dst) = app_row;
+    }
 
     // B operand of the score MFMA: column i is head i % GROUP; k-slot 8G+e of
     // instruction t is dim 32t + 8G + e.
@@ -1832,6 +1905,8 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
     } else {
         if constexpr (LM == kLensHostFused) {
             for (int b = 0; b < kMaxFusedBatch; ++b) ls.v[b] = b < a.batch ? a.fused_lens[b] : 0;
+            ls.n_place = !X2 && a.placement ? a.placement->n : 0;
+            for (int i = 0; i < ls.n_place; ++i) ls.place[i] = a.placement->pos[i];
         } else {
             ls.lens = a.lens;
             ls.snap = reinterpret_cast<int32_t*>(ws + a.part.snap_offset);
@@ -1844,8 +1919,11 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
         ls.f.window = a.window;
     }
     // with a cross part: one dimension, every cross workgroup first (see block_pos)
+    int n_place = 0;
+    if constexpr (LM == kLensHostFused) n_place = ls.n_place;
     const dim3 grid = X2 ? dim3(static_cast<unsigned>((a.n_chunks + a.x_blocks) * a.n_kv_heads))
-                         : dim3(static_cast<unsigned>(a.n_chunks), a.n_kv_heads);
+                    : n_place > 0 ? dim3(a.n_kv_heads, static_cast<unsigned>(n_place))
+                                  : dim3(static_cast<unsigned>(a.n_chunks), a.n_kv_heads);
     const dim3 block(kWaves * 64);
     if (use_wide<ESZ, GROUP>(a.chunk_rows, a.replay)) {
         if constexpr (ESZ == 4 && GROUP <= 2)
@@ -1949,6 +2027,18 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_resident[kMaxDevices][2][KVDEC_MAX_GROUP + 1];
 
 }  // namespace
+
+int device_cus()
+{
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (n > 0) cached[dev].store(n, std::memory_order_relaxed);
+    return n > 0 ? n : 0;
+}
 
 int resident_attend_blocks(int dtype, int group)
 {
