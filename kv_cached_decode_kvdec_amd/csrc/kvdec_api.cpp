@@ -315,19 +315,27 @@ bool plan_placement(const AttendView& v, int32_t group, const kvdec::AttendArgs&
     const int64_t P = a.n_chunks;
     const int64_t per = (P + classes - 1) / classes;
     const int64_t npos = per * classes;
-    if (per < 2 || npos > kvdec::kMaxPlaced || npos >= kvdec::kNoChunk ||
+    if (per < 2 || npos > kvdec::kMaxPlaced ||
         npos * Hkv > kvdec::resident_attend_blocks(v.dtype, group))
         return false;
-    // chunk weights in chunk order (sequence by sequence, as the kernels number them)
+    // chunk weights and entries in chunk order (sequence by sequence, as the
+    // kernels number them; a chunk's partial slot is its index in this order)
     const int64_t T = a.chunk_rows;
+    if (v.batch > 512) return false;
     std::vector<std::pair<int64_t, int32_t>> w;
+    std::vector<uint32_t> entry;
     w.reserve(static_cast<size_t>(P));
-    for (int32_t r : v.rows) {
-        const int64_t n = r > 0 ? r : 0;
+    entry.reserve(static_cast<size_t>(P));
+    for (int32_t b = 0; b < v.batch; ++b) {
+        const int64_t n = std::min<int64_t>(std::max<int32_t>(v.rows[b], 0), v.row_limit);
         const int64_t nch = n > 0 ? (n + T - 1) / T : 1;
+        if (nch > 128 || static_cast<int64_t>(w.size()) + nch > P) return false;
         for (int64_t c = 0; c < nch; ++c) {
             const int64_t rows = std::min(n, (c + 1) * T) - c * T;
             w.emplace_back(-(rows + kPlaceFixedRows), static_cast<int32_t>(w.size()));
+            entry.push_back(kvdec::place_entry(static_cast<uint32_t>(b), static_cast<uint32_t>(c),
+                                               static_cast<uint32_t>(nch),
+                                               static_cast<uint32_t>(entry.size())));
         }
     }
     if (static_cast<int64_t>(w.size()) != P) return false;
@@ -341,7 +349,7 @@ bool plan_placement(const AttendView& v, int32_t group, const kvdec::AttendArgs&
         const Load top = heap.top();
         heap.pop();
         const int32_t k = top.second;
-        pl.pos[k + classes * filled[k]] = static_cast<uint16_t>(item.second);
+        pl.pos[k + classes * filled[k]] = entry[static_cast<size_t>(item.second)];
         if (++filled[k] < per) heap.emplace(top.first - item.first, k);
     }
     pl.n = static_cast<int32_t>(npos);

@@ -50,14 +50,25 @@ struct MergePlanHost {
 // heads cover n_kv_heads consecutive ids, and positions that agree modulo
 // cus / n_kv_heads share their CUs: the host puts the chunks into those
 // position classes so that every CU gets about the same rows (largest
-// first, each into the least-loaded class).  pos[p] is the chunk at
-// position p, kNoChunk an empty position.  Results do not depend on it: a
-// chunk's arithmetic and its partial slot are the same wherever it runs.
-constexpr int kMaxPlaced = 512;
-constexpr uint16_t kNoChunk = 0xFFFF;
+// first, each into the least-loaded class).  pos[p] describes the chunk at
+// position p (place_entry), kNoChunk an empty position: its sequence, its
+// index in the sequence, the sequence's chunk count and its partial slot,
+// so a placed workgroup finds its rows without reading the lengths through
+// the vector memory path (where its request would queue behind the tile
+// loads of the workgroups that started before it on the same CU).  Results
+// do not depend on the placement: a chunk's arithmetic and its partial
+// slot are the same wherever it runs.
+constexpr int kMaxPlaced = 256;
+constexpr uint32_t kNoChunk = 0xFFFFFFFFu;
+
+// sequence b < 512, chunk c < 128 of nch < 256, partial slot < 256
+constexpr uint32_t place_entry(uint32_t b, uint32_t c, uint32_t nch, uint32_t slot)
+{
+    return b | (c << 9) | (nch << 16) | (slot << 24);
+}
 
 struct Placement {
-    uint16_t pos[kMaxPlaced];
+    uint32_t pos[kMaxPlaced];
     int32_t n = 0;              // positions (0: the grid is (chunk, KV head) in chunk order)
 };
 

@@ -263,7 +263,7 @@ template <>
 struct LensSrc<kLensHostFused> {
     int32_t v[kMaxFusedBatch];
     FusedRows f;
-    uint16_t place[kMaxPlaced];   // chunk at each position (see Placement)
+    uint32_t place[kMaxPlaced];   // chunk at each position (see Placement)
     int32_t n_place;              // 0: grid (chunk, KV head) in chunk order
     static constexpr int kPlus = 1;
     __device__ __forceinline__ int get(int b) const { return v[b]; }
@@ -407,6 +407,74 @@ __device__ __forceinline__ void fused_append(const LensSrc<LM>& ls, const Locate
         if (loc.c == 0 && g == 0 && threadIdx.x == 0) ls.snap[b] = len0;
 }
 
+// Fused append into a contiguous cache, inside the attend workgroup of
+// (sequence b, KV head g, chunk c) whose rows [row0, row_end) hold the new
+// token's slot.  No barrier: every load of this launch that would read the
+// slot row reads the new row from k_new / v_new instead (kn / vn, plus the
+// lane's byte offset in the row), so no load waits for the row to be stored,
+// and threads 0 .. 2 * RB / 16 - 1 copy the row into the cache (store(),
+// called once the workgroup's first loads are issued).  No other workgroup
+// reads the slot.  Host-fused: the slot's head-0 workgroup also bumps the
+// length.  Device-fused: workgroup (c 0, head 0) snapshots the pre-append
+// length for the merge launch, which bumps it.  (A full linear cache puts
+// the slot at row `capacity`, past every chunk: no copy, and the merge
+// leaves the length as it is.)
+template <int RB>
+struct FreshRow {
+    int row = -1;               // the slot, if this chunk holds it (wave-uniform), else -1
+    const char* kn;             // the new K / V row (wave-uniform; the cache base while row < 0)
+    const char* vn;
+    char* dst = nullptr;        // the copying thread's 16 bytes of the slot
+    uint4 val{};
+    __device__ __forceinline__ FreshRow(const char* K, const char* V) : kn(K), vn(V) {}
+    __device__ __forceinline__ void store() const
+    {
+        if (dst) *reinterpret_cast<uint4*>(dst) = val;
+    }
+    // the address a load of row r reads: the new row (at byte `piece` of
+    // it) for the slot, the cache address otherwise
+    __device__ __forceinline__ const char* pick_k(int r, int piece, const char* cache) const
+    {
+        return r == row ? kn + piece : cache;
+    }
+    __device__ __forceinline__ const char* pick_v(int r, int piece, const char* cache) const
+    {
+        return r == row ? vn + piece : cache;
+    }
+};
+
+template <int RB, int LM>
+__device__ __forceinline__ FreshRow<RB> fresh_row(const LensSrc<LM>& ls, const Located& loc, int g,
+                                                  int Hkv, int cap_pad, int row0, int row_end)
+{
+    FreshRow<RB> fr(ls.f.K, ls.f.V);
+    const int b = loc.b;
+    const int len0 = ls.get(b);
+    const int slot = ls.f.window > 0 ? len0 % ls.f.window : len0;
+    if (row0 <= slot && slot < row_end) {
+        constexpr int VPR = RB / 16;
+        const size_t hg = static_cast<size_t>(b) * Hkv + g;
+        const char* k_new = ls.f.k_new + hg * RB;
+        const char* v_new = ls.f.v_new + hg * RB;
+        fr.row = slot;
+        fr.kn = k_new;
+        fr.vn = v_new;
+        if (threadIdx.x < 2 * VPR) {
+            const bool isv = threadIdx.x >= VPR;
+            const int w = isv ? threadIdx.x - VPR : threadIdx.x;
+            char* K = ls.f.K;
+            char* V = ls.f.V;
+            fr.val = *reinterpret_cast<const uint4*>((isv ? v_new : k_new) + 16 * w);
+            fr.dst = (isv ? V : K) + (hg * cap_pad + slot) * RB + 16 * w;
+        }
+        if constexpr (LM == kLensHostFused)
+            if (g == 0 && threadIdx.x == 0) ls.f.lens_out[b] = len0 + 1;
+    }
+    if constexpr (LM == kLensDeviceFused)
+        if (loc.c == 0 && g == 0 && threadIdx.x == 0) ls.snap[b] = len0;
+    return fr;
+}
+
 // Combine the WAVES per-wave states of a workgroup (staged in LDS) and
 // write either the normalised output row (sequence fits one chunk) or the
 // chunk partial (m, l, o[64]) for the merge launch.
@@ -519,21 +587,29 @@ __device__ __forceinline__ BlockPos block_pos(const CrossPart& xp, int Hkv)
 }
 
 // A host-fused launch with a placement runs on a (KV head, position) grid:
-// the workgroup takes the chunk the host put at its position (false: an
-// empty position, the workgroup has nothing to do).
+// the workgroup takes the chunk the host put at its position, with its
+// sequence, index and chunk count from the entry and the sequence's length
+// from the by-value lengths (scalar reads only).  Returns 1 with loc
+// filled, 0 where the launch has no placement (locate finds the chunk), -1
+// for an empty position (the workgroup has nothing to do).
 template <int LM, bool X2>
-__device__ __forceinline__ bool placed(const LensSrc<LM>& ls, BlockPos& p)
+__device__ __forceinline__ int placed(const LensSrc<LM>& ls, int cap, BlockPos& p, Located& loc)
 {
     if constexpr (LM == kLensHostFused && !X2) {
         if (ls.n_place > 0) {
-            const int e = ls.place[blockIdx.y];
-            if (e == kNoChunk) return false;
+            const uint32_t e = ls.place[blockIdx.y];
+            if (e == kNoChunk) return -1;
             p.g = static_cast<int>(blockIdx.x);
-            p.blk = e;
-            p.slot = e;
+            p.blk = static_cast<int>(e >> 24);
+            p.slot = p.blk;
+            loc.b = static_cast<int>(e & 511u);
+            loc.c = static_cast<int>((e >> 9) & 127u);
+            loc.nch = static_cast<int>((e >> 16) & 255u);
+            loc.len = min(max(ls.v[loc.b] + LensSrc<LM>::kPlus, 0), cap);
+            return 1;
         }
     }
-    return true;
+    return 0;
 }
 
 // fresh_idx >= 0: table entry fresh_idx is being given page fresh_page by this
@@ -946,11 +1022,12 @@ void attend_kernel(
     const int sub = lane / LPR;
     const int part = lane - sub * LPR;
     BlockPos pos = block_pos<X2>(xp, Hkv);
-    if (!placed<LM, X2>(ls, pos)) return;
+    Located loc;
+    const int is_placed = placed<LM, X2>(ls, row_limit, pos, loc);
+    if (is_placed < 0) return;
     const int g = pos.g;
     const int Hq = Hkv * GROUP;
 
-    Located loc;
     const bool in_cross = pos.in_cross;     // workgroup-uniform
     if (in_cross) {
         const LensSrc<kLensDevice> xs{xp.lens};
@@ -964,7 +1041,8 @@ void attend_kernel(
         cap_pad = xp.cap_pad;
         T = xp.T;
     } else {
-        if (!locate<LM>(ls, B, T, row_limit, pos.blk, lane, one_chunk, uniform, loc)) return;
+        if (!is_placed && !locate<LM>(ls, B, T, row_limit, pos.blk, lane, one_chunk, uniform, loc))
+            return;
     }
     const int row0 = loc.c * T;
     int row_end = min(loc.len, row0 + T);   // lowered where a replayed row has no page
@@ -1162,7 +1240,9 @@ void attend_gqa_mfma_kernel(
     const int G = lane >> 4;
     const int hl = i % GROUP;              // head whose scores this lane holds
     BlockPos pos = block_pos<X2>(xp, Hkv);
-    if (!placed<LM, X2>(ls, pos)) return;
+    Located loc;
+    const int is_placed = placed<LM, X2>(ls, row_limit, pos, loc);
+    if (is_placed < 0) return;
     const int g = pos.g;
     const int Hq = Hkv * GROUP;
 
@@ -1173,7 +1253,6 @@ void attend_gqa_mfma_kernel(
                   "merge area must fit in the staging LDS");
     __shared__ __attribute__((aligned(16))) char sm_stage[WAVES * kStage];
 
-    Located loc;
     const bool in_cross = pos.in_cross;     // workgroup-uniform
     if (in_cross) {
         const LensSrc<kLensDevice> xs{xp.lens};
@@ -1187,7 +1266,8 @@ void attend_gqa_mfma_kernel(
         cap_pad = xp.cap_pad;
         T = xp.T;
     } else {
-        if (!locate<LM>(ls, B, T, row_limit, pos.blk, lane, one_chunk, uniform, loc)) return;
+        if (!is_placed && !locate<LM>(ls, B, T, row_limit, pos.blk, lane, one_chunk, uniform, loc))
+            return;
     }
     const int row0 = loc.c * T;
     int row_end = min(loc.len, row0 + T);   // lowered where a replayed row has no page
@@ -1200,40 +1280,13 @@ void attend_gqa_mfma_kernel(
         stage_pages<PAGED>(pm, loc.b, row0, row_end, sm_pages);
     const char* Kb = K + 16 * (lane & 7); // + row offset, row = r0 + 8c + (lane >> 3)
     const char* Vb = V + 16 * (lane & 7);
-    // Fused append into a contiguous cache: the workgroup whose chunk holds
-    // the new token's slot reads that row from k_new / v_new wherever its
-    // tiles cover it (no load of this launch reads the slot from the cache),
-    // so its tile loads need not wait for the row to be stored; threads
-    // 0..15 copy the row into the cache once those loads are issued.
-    int slot_row = -1;                      // wave-uniform; -1: no slot in this chunk
-    const char* Kn = nullptr;
-    const char* Vn = nullptr;
-    char* app_dst = nullptr;
-    uint4 app_row{};
+    FreshRow<RB> fr(K, V);
     if constexpr (LM == kLensPagedFused) {
         fused_append_paged<RB>(ls, loc, g, Hkv, pm, sm_pages, row0, row_end);
     } else if constexpr (PAGED && LM == kLensDeviceFused) {
         fused_append_paged_device<RB>(ls, loc, g, Hkv, pm, sm_pages, row0, row_end);
     } else if constexpr (LM != kLensDevice) {
-        if (!in_cross) {
-            const int len0 = ls.get(loc.b);
-            const int slot = ls.f.window > 0 ? len0 % ls.f.window : len0;
-            if (row0 <= slot && slot < row_end) {
-                slot_row = slot;
-                const size_t hg = static_cast<size_t>(loc.b) * Hkv + g;
-                Kn = ls.f.k_new + hg * RB + 16 * (lane & 7);
-                Vn = ls.f.v_new + hg * RB + 16 * (lane & 7);
-                if (threadIdx.x < 16) {
-                    const bool isv = threadIdx.x >= 8;
-                    app_row = *reinterpret_cast<const uint4*>(isv ? Vn : Kn);
-                    app_dst = (isv ? ls.f.V : ls.f.K) + (hg * cap_pad + slot) * RB + 16 * (lane & 7);
-                }
-                if constexpr (LM == kLensHostFused)
-                    if (g == 0 && threadIdx.x == 0) ls.f.lens_out[loc.b] = len0 + 1;
-            }
-            if constexpr (LM == kLensDeviceFused)
-                if (loc.c == 0 && g == 0 && threadIdx.x == 0) ls.snap[loc.b] = len0;
-        }
+        if (!in_cross) fr = fresh_row<RB>(ls, loc, g, Hkv, cap_pad, row0, row_end);
     }
 
     // q loads, then the wave's first 32 rows, both in flight before either is
@@ -1251,7 +1304,7 @@ void attend_gqa_mfma_kernel(
     }
     uint4 kw[4], vr[4];
     auto load_tile = [&](int r0) {
-        if (!PAGED && r0 + 32 <= row_end && (slot_row < r0 || slot_row >= r0 + 32)) {
+        if (!PAGED && r0 + 32 <= row_end && (fr.row < r0 || fr.row >= r0 + 32)) {
             // whole tile inside the chunk (wave-uniform): rows r0 + 8c + lane/8
             // are 1 KB apart, no clamping
             const size_t off = row_offset<false, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0,
@@ -1269,9 +1322,8 @@ void attend_gqa_mfma_kernel(
             for (int c = 0; c < 4; ++c) {
                 const int r = min(r0 + 8 * c + (lane >> 3), row_end - 1);
                 const size_t off = row_offset<PAGED, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0, r);
-                const bool fresh = r == slot_row;
-                kw[c] = load16_stream(fresh ? Kn : Kb + off);
-                vr[c] = load16_stream(fresh ? Vn : Vb + off);
+                kw[c] = load16_stream(fr.pick_k(r, 16 * (lane & 7), Kb + off));
+                vr[c] = load16_stream(fr.pick_v(r, 16 * (lane & 7), Vb + off));
             }
         }
     };
@@ -1289,13 +1341,12 @@ void attend_gqa_mfma_kernel(
         for (int c = 0; c < 4; ++c) {
             const int r = min(r0 + 8 * c + (lane >> 3), rmax);
             const size_t off = row_offset<false, RB>(pm, sm_pages, loc.b, g, Hkv, cap_pad, row0, r);
-            const bool fresh = r == slot_row;
-            kw[c] = load16_stream(fresh ? Kn : Kb + off);
-            vr[c] = load16_stream(fresh ? Vn : Vb + off);
+            kw[c] = load16_stream(fr.pick_k(r, 16 * (lane & 7), Kb + off));
+            vr[c] = load16_stream(fr.pick_v(r, 16 * (lane & 7), Vb + off));
         }
         // keep the scheduler from moving these loads behind the wait for q
         __builtin_amdgcn_sched_barrier(0);
-        if (app_dst) *reinterpret_cast<uint4*>(app_dst) = app_row;
+        fr.store();
     }
 
     // B operand of the score MFMA: column i is head i % GROUP; k-slot 8G+e of
