@@ -294,9 +294,10 @@ void fill_args(const AttendView& v, const float* q, float scale, float* out, voi
 }
 
 // The placement of a host-fused launch's chunks on the CUs (see
-// kvdec::Placement): only where the launch is one residency round of
-// four-wave workgroups with ragged chunks, the CU count is a multiple of
-// the KV heads, and every position class gets at least two chunks.  A
+// kvdec::Placement): only for the MFMA kernel (bf16, grouped heads), where
+// the launch is one residency round with ragged chunks, the CU count is a
+// multiple of the KV heads, and every position class gets at least two
+// chunks.  A
 // chunk's weight is its rows plus a fixed per-workgroup cost; the heaviest
 // go first, each into the least-loaded class that has a position left
 // (ties to the lower class and the earlier chunk, so the plan is a function
@@ -306,8 +307,9 @@ constexpr int64_t kPlaceFixedRows = 32;
 bool plan_placement(const AttendView& v, int32_t group, const kvdec::AttendArgs& a,
                     kvdec::Placement& pl)
 {
-    if (a.uniform >= 0 || a.x_blocks > 0 || v.table) return false;
-    if (kvdec::attend_waves(v.dtype, group, a.chunk_rows, false) != 4) return false;
+    // the MFMA kernel (bf16, grouped heads) takes a placement
+    if (v.dtype != KVDEC_BF16 || group < 2 || a.uniform >= 0 || a.x_blocks > 0 || v.table)
+        return false;
     const int32_t Hkv = v.n_kv_heads;
     const int cus = kvdec::device_cus();
     if (cus <= 0 || cus % Hkv != 0) return false;

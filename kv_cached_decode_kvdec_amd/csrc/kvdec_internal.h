@@ -42,11 +42,11 @@ struct MergePlanHost {
     int n = 0;
 };
 
-// Placement of the chunks of a one-round host-fused launch on the device's
-// compute units.  The hardware hands the workgroups of a launch that fits
-// one residency round out in order of their linear id, round robin over the
-// XCDs and then over each XCD's CUs, so ids that agree modulo the CU count
-// run on one CU.  With the grid laid out (KV head, position), a position's
+// Placement of the chunks of a one-round host-fused launch of the MFMA
+// kernel (bf16 K/V, grouped query heads) on the device's compute units.
+// The hardware hands the workgroups of a launch that fits one residency
+// round out in order of their linear id, round robin over the XCDs and then
+// over each XCD's CUs, so ids that agree modulo the CU count run on one CU.  With the grid laid out (KV head, position), a position's
 // heads cover n_kv_heads consecutive ids, and positions that agree modulo
 // cus / n_kv_heads share their CUs: the host puts the chunks into those
 // position classes so that every CU gets about the same rows (largest
@@ -128,8 +128,8 @@ struct AttendArgs {
     // the merge planned on the host (nullptr: the merge finds the chunks
     // from the lengths on the device)
     const MergePlanHost* merge_plan = nullptr;
-    // host-fused launches only: the chunks' placement on the CUs (nullptr or
-    // n == 0: chunk order)
+    // host-fused launches of the MFMA kernel only: the chunks' placement on
+    // the CUs (nullptr or n == 0: chunk order)
     const Placement* placement = nullptr;
 };
 

@@ -263,8 +263,6 @@ template <>
 struct LensSrc<kLensHostFused> {
     int32_t v[kMaxFusedBatch];
     FusedRows f;
-    uint32_t place[kMaxPlaced];   // chunk at each position (see Placement)
-    int32_t n_place;              // 0: grid (chunk, KV head) in chunk order
     static constexpr int kPlus = 1;
     __device__ __forceinline__ int get(int b) const { return v[b]; }
     __device__ __forceinline__ int merge_get(int b) const { return v[b]; }
@@ -586,18 +584,19 @@ __device__ __forceinline__ BlockPos block_pos(const CrossPart& xp, int Hkv)
     return p;
 }
 
-// A host-fused launch with a placement runs on a (KV head, position) grid:
-// the workgroup takes the chunk the host put at its position, with its
-// sequence, index and chunk count from the entry and the sequence's length
-// from the by-value lengths (scalar reads only).  Returns 1 with loc
-// filled, 0 where the launch has no placement (locate finds the chunk), -1
-// for an empty position (the workgroup has nothing to do).
+// A host-fused launch of the MFMA kernel with a placement runs on a
+// (KV head, position) grid: the workgroup takes the chunk the host put at
+// its position, with its sequence, index and chunk count from the entry and
+// the sequence's length from the by-value lengths (scalar reads only).
+// Returns 1 with loc filled, 0 where the launch has no placement (locate
+// finds the chunk), -1 for an empty position (nothing to do).
 template <int LM, bool X2>
-__device__ __forceinline__ int placed(const LensSrc<LM>& ls, int cap, BlockPos& p, Located& loc)
+__device__ __forceinline__ int placed(const Placement& pl, const LensSrc<LM>& ls, int cap,
+                                      BlockPos& p, Located& loc)
 {
     if constexpr (LM == kLensHostFused && !X2) {
-        if (ls.n_place > 0) {
-            const uint32_t e = ls.place[blockIdx.y];
+        if (pl.n > 0) {
+            const uint32_t e = pl.pos[blockIdx.y];
             if (e == kNoChunk) return -1;
             p.g = static_cast<int>(blockIdx.x);
             p.blk = static_cast<int>(e >> 24);
@@ -1021,13 +1020,11 @@ void attend_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane / LPR;
     const int part = lane - sub * LPR;
-    BlockPos pos = block_pos<X2>(xp, Hkv);
-    Located loc;
-    const int is_placed = placed<LM, X2>(ls, row_limit, pos, loc);
-    if (is_placed < 0) return;
+    const BlockPos pos = block_pos<X2>(xp, Hkv);
     const int g = pos.g;
     const int Hq = Hkv * GROUP;
 
+    Located loc;
     const bool in_cross = pos.in_cross;     // workgroup-uniform
     if (in_cross) {
         const LensSrc<kLensDevice> xs{xp.lens};
@@ -1041,8 +1038,7 @@ void attend_kernel(
         cap_pad = xp.cap_pad;
         T = xp.T;
     } else {
-        if (!is_placed && !locate<LM>(ls, B, T, row_limit, pos.blk, lane, one_chunk, uniform, loc))
-            return;
+        if (!locate<LM>(ls, B, T, row_limit, pos.blk, lane, one_chunk, uniform, loc)) return;
     }
     const int row0 = loc.c * T;
     int row_end = min(loc.len, row0 + T);   // lowered where a replayed row has no page
@@ -1229,7 +1225,7 @@ void attend_gqa_mfma_kernel(
     const float* __restrict__ q, const char* __restrict__ K, const char* __restrict__ V,
     LensSrc<LM> ls, int B, int Hkv, int cap_pad, int row_limit, int T, int one_chunk, int uniform,
     float qscale, float* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    PageMap pm, CrossPart xp)
+    PageMap pm, CrossPart xp, Placement pl)
 {
     static_assert(!(X2 && PAGED), "the one-launch layer step reads contiguous caches");
     static_assert(GROUP >= 2 && GROUP <= 8, "MFMA path takes 2..8 query heads per KV head");
@@ -1241,7 +1237,7 @@ void attend_gqa_mfma_kernel(
     const int hl = i % GROUP;              // head whose scores this lane holds
     BlockPos pos = block_pos<X2>(xp, Hkv);
     Located loc;
-    const int is_placed = placed<LM, X2>(ls, row_limit, pos, loc);
+    const int is_placed = placed<LM, X2>(pl, ls, row_limit, pos, loc);
     if (is_placed < 0) return;
     const int g = pos.g;
     const int Hq = Hkv * GROUP;
@@ -1956,8 +1952,6 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
     } else {
         if constexpr (LM == kLensHostFused) {
             for (int b = 0; b < kMaxFusedBatch; ++b) ls.v[b] = b < a.batch ? a.fused_lens[b] : 0;
-            ls.n_place = !X2 && a.placement ? a.placement->n : 0;
-            for (int i = 0; i < ls.n_place; ++i) ls.place[i] = a.placement->pos[i];
         } else {
             ls.lens = a.lens;
             ls.snap = reinterpret_cast<int32_t*>(ws + a.part.snap_offset);
@@ -1970,11 +1964,18 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
         ls.f.window = a.window;
     }
     // with a cross part: one dimension, every cross workgroup first (see block_pos)
-    int n_place = 0;
-    if constexpr (LM == kLensHostFused) n_place = ls.n_place;
+    // a placement (host-fused launches of the MFMA kernel): (KV head, position) grid
+    Placement pl;
+    pl.n = 0;
+    if constexpr (LM == kLensHostFused && !X2 && ESZ == 2 && GROUP >= 2) {
+        if (a.placement && a.placement->n > 0) {
+            pl.n = a.placement->n;
+            for (int i = 0; i < pl.n; ++i) pl.pos[i] = a.placement->pos[i];
+        }
+    }
     const dim3 grid = X2 ? dim3(static_cast<unsigned>((a.n_chunks + a.x_blocks) * a.n_kv_heads))
-                    : n_place > 0 ? dim3(a.n_kv_heads, static_cast<unsigned>(n_place))
-                                  : dim3(static_cast<unsigned>(a.n_chunks), a.n_kv_heads);
+                    : pl.n > 0 ? dim3(a.n_kv_heads, static_cast<unsigned>(pl.n))
+                               : dim3(static_cast<unsigned>(a.n_chunks), a.n_kv_heads);
     const dim3 block(kWaves * 64);
     if (use_wide<ESZ, GROUP>(a.chunk_rows, a.replay)) {
         if constexpr (ESZ == 4 && GROUP <= 2)
@@ -1987,7 +1988,7 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
         hipLaunchKernelGGL((attend_gqa_mfma_kernel<GROUP, kWaves, PAGED, LM, X2>), grid, block, 0, s,
                            a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v), ls,
                            a.batch, a.n_kv_heads, a.cap_pad, a.row_limit, a.chunk_rows, a.one_chunk,
-                           a.uniform, a.qscale, a.out, po, pml, pm, xp);
+                           a.uniform, a.qscale, a.out, po, pml, pm, xp, pl);
     } else {
         hipLaunchKernelGGL((attend_kernel<ESZ, GROUP, kWaves, kUnroll, PAGED, LM, X2>), grid, block,
                            0, s, a.q, static_cast<const char*>(a.k), static_cast<const char*>(a.v),

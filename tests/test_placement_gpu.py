@@ -1,16 +1,16 @@
-"""Chunk placement on the CUs (host-fused launches), through the C ABI.
+"""Chunk placement on the CUs (host-fused MFMA launches), through the C ABI.
 
-A host-fused launch (kvdec_append_attend) whose chunks fit one residency
-round of four-wave workgroups, with ragged lengths and more chunks than the
-device has CU classes (cus / n_kv_heads), runs its chunks on a
-(KV head, position) grid in an order the host picks to balance the rows per
-CU, some positions empty.  The order must change nothing: the output must
-equal kvdec_append + kvdec_attend_self (chunk order, no placement) bit for
-bit, at the same chunk size, step after step, the cache and lengths must
-equal kvdec_append's, and the output must match the f64 oracle.  On a
-256-CU MI355X every case below is placed: MFMA grouped heads (64 classes),
-f32 and bf16 single-head VALU kernels (64 and 32 classes), and a ring whose
-new rows land inside the window (the slot row read from k_new / v_new).
+A host-fused launch (kvdec_append_attend) of the MFMA kernel (bf16 K/V,
+grouped query heads) whose chunks fit one residency round, with ragged
+lengths and more chunks than the device has CU classes (cus / n_kv_heads),
+runs its chunks on a (KV head, position) grid in an order the host picks to
+balance the rows per CU, some positions empty.  The order must change
+nothing: the output must equal kvdec_append + kvdec_attend_self (chunk
+order, no placement) bit for bit, at the same chunk size, step after step,
+the cache and lengths must equal kvdec_append's, and the output must match
+the f64 oracle.  On a 256-CU MI355X every case below is placed: groups of
+4 (64 and 128 classes) and 3 (32 classes), and a ring whose new rows land
+inside the window (the slot row read from k_new / v_new).
 """
 import sys
 
@@ -32,8 +32,8 @@ def _log(msg):
 
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,B,max_len,chunk", [("bf16", 16, 4, 40, 1500, 256),
-                                                          ("f32", 4, 4, 40, 600, 64),
-                                                          ("bf16", 8, 8, 24, 400, 64)])
+                                                          ("bf16", 8, 2, 40, 1500, 256),
+                                                          ("bf16", 24, 8, 24, 400, 64)])
 def test_placed_fused_equals_chunk_order(dtype, Hq, Hkv, B, max_len, chunk):
     rng = np.random.default_rng(900 + B + Hkv)
     lens = rng.integers(0, max_len, B).astype(np.int32)
