@@ -25,7 +25,11 @@ self step and cross-attention over a seeded static cache, each part at its
 own drawn chunk size, sometimes at explicit positions or in replay mode)
 for two steps.  Slide cases append with the streaming cache's slide
 (kvdec_append_slide) on a small linear cache for several steps, so that
-sequences slide, and compare the cache bytes with the oracle's.
+sequences slide, and compare the cache bytes with the oracle's.  Placed
+cases draw bf16 grouped-head batches whose chunk count puts the fused
+step's MFMA launch on the CU-balanced placement (more chunks than the
+device has CU classes, one residency round) and compare it bit for bit
+with append + attend in chunk order, and with the oracle, for two steps.
 """
 import sys
 
@@ -42,9 +46,9 @@ from helpers import assert_attention_close
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 192
+N_CASES = 208
 MODES = ["attend", "fused", "fused_at", "paged", "ring", "ring_at", "cross", "paged_fused", "replay",
-         "paged_replay", "layer", "slide"]
+         "paged_replay", "layer", "slide", "placed"]
 
 
 def _draw_lens(rng, Bsz):
@@ -162,6 +166,9 @@ def test_random_case(i):
         assert c.lens_dev.cpu().tolist() == ln.tolist()
         assert to_host_bits(c.k).tobytes() == Kh.tobytes()
         assert to_host_bits(c.v).tobytes() == Vh.tobytes()
+        return
+    if mode == "placed":
+        _placed_case(i, rng, scale, s)
         return
     if mode == "slide":
         W = int(rng.integers(2, 200))             # the window: a small linear cache
@@ -303,3 +310,48 @@ def test_random_case(i):
     # touch keep their bits too (the whole buffer is compared)
     assert to_host_bits(c.k).tobytes() == Kh.tobytes()
     assert to_host_bits(c.v).tobytes() == Vh.tobytes()
+
+
+def _placed_case(i, rng, scale, s):
+    """A bf16 grouped-head batch whose chunks the fused step places on the
+    CUs: per-sequence chunk counts are drawn first so that the total lies
+    between the CU classes (cus / n_kv_heads) and what one residency round
+    of the MFMA kernel (4 workgroups per CU) and the 256-position table
+    hold; ragged lengths inside each sequence's last chunk."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    Hkv = int(rng.choice([2, 4, 8]))
+    group = int(rng.integers(2, 9))
+    Hq = Hkv * group
+    T = int(rng.choice([64, 128, 256]))
+    classes = cus // Hkv
+    hi = min(256, 4 * cus // Hkv)
+    P = int(rng.integers(classes + 1, hi + 1))
+    Bsz = int(rng.integers(8, min(64, P) + 1))
+    k = 1 + rng.multinomial(P - Bsz, np.ones(Bsz) / Bsz)   # chunks per sequence, >= 1
+    rows = ((k - 1) * T + rng.integers(1, T + 1, size=Bsz)).astype(np.int32)
+    lens = (rows - 1).astype(np.int32)                      # pre-append: the step attends `rows`
+    cap = int(lens.max()) + 3
+    cap_pad = gen.padded_rows(cap)
+    K = _rows(rng, (Bsz, Hkv, cap_pad, 64), "bf16", s)
+    V = _rows(rng, (Bsz, Hkv, cap_pad, 64), "bf16", s)
+    what = f"case {i} (placed bf16 B={Bsz} Hq={Hq} Hkv={Hkv} T={T} chunks={P})"
+    print(what, file=sys.stderr, flush=True)
+    mk = lambda: KVCache(Bsz, Hkv, cap, "bf16", lens=lens, k=to_device(K), v=to_device(V))
+    two, one = mk(), mk()
+    Kh, Vh, ln = K.copy(), V.copy(), lens.copy()
+    for st in range(2):
+        kn = _rows(rng, (Bsz, Hkv, 64), "bf16", s)
+        vn = _rows(rng, (Bsz, Hkv, 64), "bf16", s)
+        q = (rng.standard_normal((Bsz, Hq, 64)) * s).astype(np.float32)
+        two.append(to_device(kn), to_device(vn))
+        ref_dev = two.attend(to_device(q), scale=scale, chunk_rows=T)
+        got = one.append_attend(to_device(kn), to_device(vn), to_device(q), scale=scale,
+                                chunk_rows=T)
+        torch.cuda.synchronize()
+        assert got.cpu().numpy().tobytes() == ref_dev.cpu().numpy().tobytes(), f"{what} step {st}"
+        ln = oracle.append(Kh, Vh, kn, vn, ln)
+        assert_attention_close(got.cpu().numpy(), oracle.attend(q, Kh, Vh, ln, scale), "bf16",
+                               f"{what} step {st}")
+    assert one.lens() == ln.tolist() and one.lens_dev.cpu().tolist() == ln.tolist()
+    assert to_host_bits(one.k).tobytes() == Kh.tobytes()
+    assert to_host_bits(one.v).tobytes() == Vh.tobytes()
