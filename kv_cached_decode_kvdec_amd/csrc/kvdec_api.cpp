@@ -308,8 +308,7 @@ bool plan_placement(const AttendView& v, int32_t group, const kvdec::AttendArgs&
                     kvdec::Placement& pl)
 {
     // the MFMA kernel (bf16, grouped heads) takes a placement
-    if (v.dtype != KVDEC_BF16 || group < 2 || a.uniform >= 0 || a.x_blocks > 0 || v.table)
-        return false;
+    if (v.dtype != KVDEC_BF16 || group < 2 || a.uniform >= 0 || a.x_blocks > 0) return false;
     const int32_t Hkv = v.n_kv_heads;
     const int cus = kvdec::device_cus();
     if (cus <= 0 || cus % Hkv != 0) return false;

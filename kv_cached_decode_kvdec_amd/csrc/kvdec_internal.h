@@ -43,7 +43,8 @@ struct MergePlanHost {
 };
 
 // Placement of the chunks of a one-round host-fused launch of the MFMA
-// kernel (bf16 K/V, grouped query heads) on the device's compute units.
+// kernel (bf16 K/V, grouped query heads; contiguous or paged cache) on the
+// device's compute units.
 // The hardware hands the workgroups of a launch that fits one residency
 // round out in order of their linear id, round robin over the XCDs and then
 // over each XCD's CUs, so ids that agree modulo the CU count run on one CU.  With the grid laid out (KV head, position), a position's

@@ -584,8 +584,8 @@ __device__ __forceinline__ BlockPos block_pos(const CrossPart& xp, int Hkv)
     return p;
 }
 
-// A host-fused launch of the MFMA kernel with a placement runs on a
-// (KV head, position) grid: the workgroup takes the chunk the host put at
+// A host-fused launch of the MFMA kernel (contiguous or paged) with a
+// placement runs on a (KV head, position) grid: the workgroup takes the chunk the host put at
 // its position, with its sequence, index and chunk count from the entry and
 // the sequence's length from the by-value lengths (scalar reads only).
 // Returns 1 with loc filled, 0 where the launch has no placement (locate
@@ -594,7 +594,7 @@ template <int LM, bool X2>
 __device__ __forceinline__ int placed(const Placement& pl, const LensSrc<LM>& ls, int cap,
                                       BlockPos& p, Located& loc)
 {
-    if constexpr (LM == kLensHostFused && !X2) {
+    if constexpr ((LM == kLensHostFused || LM == kLensPagedFused) && !X2) {
         if (pl.n > 0) {
             const uint32_t e = pl.pos[blockIdx.y];
             if (e == kNoChunk) return -1;
@@ -1967,7 +1967,8 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
     // a placement (host-fused launches of the MFMA kernel): (KV head, position) grid
     Placement pl;
     pl.n = 0;
-    if constexpr (LM == kLensHostFused && !X2 && ESZ == 2 && GROUP >= 2) {
+    if constexpr ((LM == kLensHostFused || LM == kLensPagedFused) && !X2 && ESZ == 2 &&
+                  GROUP >= 2) {
         if (a.placement && a.placement->n > 0) {
             pl.n = a.placement->n;
             for (int i = 0; i < pl.n; ++i) pl.pos[i] = a.placement->pos[i];

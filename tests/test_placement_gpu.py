@@ -9,8 +9,10 @@ nothing: the output must equal kvdec_append + kvdec_attend_self (chunk
 order, no placement) bit for bit, at the same chunk size, step after step,
 the cache and lengths must equal kvdec_append's, and the output must match
 the f64 oracle.  On a 256-CU MI355X every case below is placed: groups of
-4 (64 and 128 classes) and 3 (32 classes), and a ring whose new rows land
-inside the window (the slot row read from k_new / v_new).
+4 (64 and 128 classes) and 3 (32 classes), a ring whose new rows land
+inside the window (the slot row read from k_new / v_new), and the paged
+fused step (kvdec_paged_append_attend against kvdec_paged_append +
+kvdec_paged_attend, pool bytes included).
 """
 import sys
 
@@ -20,7 +22,7 @@ import torch
 
 import oracle
 from kv_cached_decode_kvdec_amd import inputs as gen
-from kv_cached_decode_kvdec_amd.cache import KVCache, to_device, to_host_bits
+from kv_cached_decode_kvdec_amd.cache import KVCache, PagedKVCache, to_device, to_host_bits
 
 from helpers import assert_attention_close
 
@@ -100,3 +102,38 @@ def test_placed_fused_ring():
     assert to_host_bits(one.k).tobytes() == to_host_bits(two.k).tobytes()
     assert to_host_bits(one.v).tobytes() == to_host_bits(two.v).tobytes()
     assert one.lens() == lens.tolist() and one.lens_dev.cpu().tolist() == lens.tolist()
+
+
+@pytest.mark.parametrize("P", [16, 64])
+def test_placed_paged_fused(P):
+    """The paged fused step (pages of P rows, fresh pages taken by the launch)."""
+    rng = np.random.default_rng(951 + P)
+    B, Hq, Hkv, chunk = 40, 16, 4, 256
+    lens = rng.integers(0, 1500, B).astype(np.int32)
+    lens[:3] = [0, P - 1, P]                    # the new row opens a page, ends one
+    wl = gen.Workload("placed-paged", B, Hq, Hkv, "bf16", "const:1", 2, False, seed=961 + P)
+    inp = gen.make_inputs(wl, batch=B, lens=lens, steps=2)
+    maxp = -(-inp.cap // P)
+    pages = int(sum(-(-(int(n) + 2) // P) for n in lens)) + B
+    _log(f"placed paged P={P}")
+
+    def mk():
+        pc = PagedKVCache(B, Hkv, P, num_pages=pages, max_pages_per_seq=maxp, dtype="bf16")
+        pc.load_contiguous(to_device(inp.k_cache), to_device(inp.v_cache), lens)
+        return pc
+
+    two, one = mk(), mk()
+    Kh, Vh, lh = inp.k_cache.copy(), inp.v_cache.copy(), inp.lens.copy()
+    for s in range(2):
+        kn, vn, q = to_device(inp.k_new[s]), to_device(inp.v_new[s]), to_device(inp.q_self[s])
+        two.append(kn, vn)
+        ref_dev = two.attend(q, chunk_rows=chunk)
+        got = one.append_attend(kn, vn, q, chunk_rows=chunk)
+        torch.cuda.synchronize()
+        assert got.cpu().numpy().tobytes() == ref_dev.cpu().numpy().tobytes(), f"paged step {s}"
+        lh = oracle.append(Kh, Vh, inp.k_new[s], inp.v_new[s], lh)
+        assert_attention_close(got.cpu().numpy(), oracle.attend(inp.q_self[s], Kh, Vh, lh), "bf16",
+                               f"placed paged step {s}")
+    assert one.lens() == lh.tolist() and one.table() == two.table()
+    assert to_host_bits(one.k).tobytes() == to_host_bits(two.k).tobytes()
+    assert to_host_bits(one.v).tobytes() == to_host_bits(two.v).tobytes()
