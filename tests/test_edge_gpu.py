@@ -11,7 +11,10 @@
 - two independent caches driven on two streams at once;
 - f32 launches large enough for the 16-wave workgroups (plain, fused, paged,
   paged fused, and the device-length fused step on a replay grid sized with
-  a horizon).
+  a horizon);
+- ragged batches of 60,000 and 70,000 one- and two-row sequences: the grid
+  of a ragged launch puts the KV heads along x and the chunks along y, up to
+  y's limit of 65,535; past it the chunks go back along x.
 """
 import sys
 
@@ -216,3 +219,24 @@ def test_wide_workgroups(group, mode):
     if mode in ("fused", "replay_fused"):
         assert to_host_bits(c.k).tobytes() == K.tobytes()
         assert c.lens_dev.cpu().tolist() == ln.tolist()
+
+
+@pytest.mark.parametrize("dtype,Hq,Bsz", [("bf16", 2, 60_000), ("bf16", 2, 70_000),
+                                         ("f32", 1, 70_000)])
+def test_chunk_count_around_the_grid_y_limit(dtype, Hq, Bsz):
+    rng = np.random.default_rng(85)
+    Hkv = 1
+    lens = rng.integers(1, 3, size=Bsz).astype(np.int32)       # ragged: 1 or 2 rows
+    cap = gen.padded_rows(2)
+    shape = (Bsz, Hkv, cap, 64)
+    K = np.zeros(shape, np.float32 if dtype == "f32" else np.uint16)
+    V = np.zeros_like(K)
+    K[:, :, :2] = _rows(rng, (Bsz, Hkv, 2, 64), dtype)
+    V[:, :, :2] = _rows(rng, (Bsz, Hkv, 2, 64), dtype)
+    q = rng.standard_normal((Bsz, Hq, 64), dtype=np.float32)
+    _log(f"{Bsz} ragged sequences, {dtype}, chunk 64 -> {Bsz} chunks")
+    c = KVCache(Bsz, Hkv, cap, dtype, lens=lens, k=to_device(K), v=to_device(V))
+    out = c.attend(to_device(q), chunk_rows=64)
+    torch.cuda.synchronize()
+    assert_attention_close(out.cpu().numpy(), oracle.attend(q, K, V, lens), dtype,
+                           f"{dtype} B={Bsz}")
