@@ -548,15 +548,16 @@ struct CrossPart {
 
 // Where an attend workgroup sits: its part, KV head, chunk index within the
 // part's grid, and the workspace slot of its partials.  Without a cross part
-// the grid is (chunks, KV heads) where every sequence attends the same rows
-// and (KV heads, chunks) otherwise: the hardware hands workgroups to the 8
+// the grid is (KV heads, chunks) for ragged lengths in a contiguous cache
+// and (chunks, KV heads) otherwise: the hardware hands workgroups to the 8
 // XCDs by linear id modulo 8, and with the heads innermost each XCD gets
 // an equal share of every chunk of ragged lengths (qwen2-0.5b 73.4 -> 72.0
-// us per step; equal-length launches were slower that way, whisper-large as
-// two calls 100.3 -> 101.9 us).  With a cross part it is one-dimensional, every
-// cross workgroup (all heads) before every self workgroup, so that the
-// longer cross work is dispatched first and the shorter self work fills
-// the tail: the Whisper-large step takes 96.4 us this way, against 100.8 us
+// us per step); equal-length launches and the paged pool (whose heads lie
+// far apart) were slower that way (whisper-large as two calls 100.3 ->
+// 101.9 us, qwen2-0.5b with 16-row pages 75.7 -> 76.7 us).  With a cross
+// part it is one-dimensional, every cross workgroup (all heads) before every
+// self workgroup, so that the longer cross work is dispatched first and the
+// shorter self work fills the tail: the Whisper-large step takes 96.4 us this way, against 100.8 us
 // as two launches, 103.5 us with the parts ordered along x within each head
 // (which mixes them through the whole launch) and 111.8 us alternating them
 // block by block.  Within the cross part the KV head runs fastest: every
@@ -1039,7 +1040,7 @@ void attend_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane / LPR;
     const int part = lane - sub * LPR;
-    const BlockPos pos = block_pos<X2>(xp, Hkv, uniform);
+    const BlockPos pos = block_pos<X2>(xp, Hkv, PAGED ? 0 : uniform);
     const int g = pos.g;
     const int Hq = Hkv * GROUP;
 
@@ -1254,7 +1255,7 @@ void attend_gqa_mfma_kernel(
     const int i = lane & 15;
     const int G = lane >> 4;
     const int hl = i % GROUP;              // head whose scores this lane holds
-    BlockPos pos = block_pos<X2>(xp, Hkv, uniform);
+    BlockPos pos = block_pos<X2>(xp, Hkv, PAGED ? 0 : uniform);
     Located loc;
     const int is_placed = placed<LM, X2>(pl, ls, row_limit, pos, loc);
     if (is_placed < 0) return;
@@ -1995,7 +1996,7 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t s)
     }
     const dim3 grid = X2 ? dim3(static_cast<unsigned>((a.n_chunks + a.x_blocks) * a.n_kv_heads))
                     : pl.n > 0 ? dim3(a.n_kv_heads, static_cast<unsigned>(pl.n))
-                    : a.uniform < 0 && a.n_chunks <= 65535
+                    : !PAGED && a.uniform < 0 && a.n_chunks <= 65535
                           ? dim3(a.n_kv_heads, static_cast<unsigned>(a.n_chunks))
                           : dim3(static_cast<unsigned>(a.n_chunks), a.n_kv_heads);
     const dim3 block(kWaves * 64);
