@@ -117,15 +117,31 @@ int64_t chunks_for(const std::vector<int32_t>& lens, int32_t T)
 //    sequences need the R/4 floor (whisper-base self: 64 rows).
 constexpr int32_t kChunkBytes = 128 * 1024;
 
+// Whether a grid of P chunks (per KV head) can run on the CU-balanced
+// placement of the MFMA kernel (plan_placement): the CUs split evenly into
+// one class per KV head, at least two chunks per class, at most kMaxPlaced
+// positions, and the whole grid resident at once.
+bool placeable(int64_t P, int32_t n_kv_heads, int64_t resident)
+{
+    const int cus = kvdec::device_cus();
+    if (cus <= 0 || n_kv_heads <= 0 || cus % n_kv_heads != 0) return false;
+    const int64_t classes = cus / n_kv_heads;
+    const int64_t per = (P + classes - 1) / classes;
+    const int64_t npos = per * classes;
+    return per >= 2 && npos <= kvdec::kMaxPlaced && npos * n_kv_heads <= resident;
+}
+
 int32_t auto_chunk(const std::vector<int32_t>& lens, int32_t n_kv_heads, int32_t esz,
-                   int64_t resident)
+                   int64_t resident, int32_t group = 1)
 {
     if (resident <= 0) resident = 2048;
     int64_t total = 0;
     int32_t longest = 0;
+    bool equal = true;
     for (int32_t l : lens) {
         total += l;
         longest = l > longest ? l : longest;
+        equal = equal && l == lens[0];
     }
     const int64_t pairs = static_cast<int64_t>(lens.size()) * n_kv_heads;
     if (2 * pairs >= resident && longest <= KVDEC_MAX_CHUNK &&
@@ -137,6 +153,17 @@ int32_t auto_chunk(const std::vector<int32_t>& lens, int32_t n_kv_heads, int32_t
     int32_t T = kChunkBytes / (2 * KVDEC_HEAD_DIM * esz);
     const int64_t min_blocks = resident / 4;
     while (T > KVDEC_MIN_CHUNK && chunks_for(lens, T) * n_kv_heads < min_blocks) T >>= 1;
+    // Grids the MFMA kernel runs placed (bf16, grouped query heads, ragged
+    // lengths): the smallest chunk, in steps of 64 rows down to half the
+    // size above, whose grid still fits one placed residency round; the
+    // finer split balances the rows per CU better (gqa, 64 sequences of
+    // 16..8192 rows: 20.3 us per step at 448 rows against 20.6 at 512; at
+    // 384 the grid needs a second round and takes 22.5).
+    if (esz == 2 && group >= 2 && !equal && placeable(chunks_for(lens, T), n_kv_heads, resident)) {
+        const int32_t floor_rows = T / 2 > KVDEC_MIN_CHUNK ? T / 2 : KVDEC_MIN_CHUNK;
+        while (T - 64 >= floor_rows && placeable(chunks_for(lens, T - 64), n_kv_heads, resident))
+            T -= 64;
+    }
     return T;
 }
 
@@ -232,7 +259,7 @@ void plan_chunks(const AttendView& v, int32_t group, int32_t chunk_rows, kvdec::
     } else {
         a.chunk_rows = chunk_rows ? chunk_rows
                                   : auto_chunk(v.rows, v.n_kv_heads, esz_of(v.dtype),
-                                               kvdec::resident_attend_blocks(v.dtype, group));
+                                               kvdec::resident_attend_blocks(v.dtype, group), group);
         a.n_chunks = chunks_for(v.rows, a.chunk_rows);
         a.need_merge = a.n_chunks > v.batch;   // some sequence has more than one chunk
         // the launch reads the lengths the grid was sized from
@@ -310,15 +337,11 @@ bool plan_placement(const AttendView& v, int32_t group, const kvdec::AttendArgs&
     // the MFMA kernel (bf16, grouped heads) takes a placement
     if (v.dtype != KVDEC_BF16 || group < 2 || a.uniform >= 0 || a.x_blocks > 0) return false;
     const int32_t Hkv = v.n_kv_heads;
-    const int cus = kvdec::device_cus();
-    if (cus <= 0 || cus % Hkv != 0) return false;
-    const int64_t classes = cus / Hkv;
     const int64_t P = a.n_chunks;
+    if (!placeable(P, Hkv, kvdec::resident_attend_blocks(v.dtype, group))) return false;
+    const int64_t classes = kvdec::device_cus() / Hkv;
     const int64_t per = (P + classes - 1) / classes;
     const int64_t npos = per * classes;
-    if (per < 2 || npos > kvdec::kMaxPlaced ||
-        npos * Hkv > kvdec::resident_attend_blocks(v.dtype, group))
-        return false;
     // chunk weights and entries in chunk order (sequence by sequence, as the
     // kernels number them; a chunk's partial slot is its index in this order)
     const int64_t T = a.chunk_rows;

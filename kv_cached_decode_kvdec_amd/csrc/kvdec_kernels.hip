@@ -53,7 +53,6 @@ namespace {
 constexpr int kMaxFusedBatch = KVDEC_MAX_FUSED_BATCH;
 constexpr int kMaxPagedFusedBatch = KVDEC_MAX_PAGED_FUSED_BATCH;
 constexpr float kNegBig = -1.0e30f;   // finite "no row seen yet" running max
-constexpr float kLog2e = 1.4426950408889634f;
 
 template <int ESZ>
 struct Lay {
