@@ -1271,7 +1271,7 @@ int32_t kvdec_append_attend_cross(kvdec_cache* c, const kvdec_cache* x, const in
         if ((cross_side ? chunk_cross : chunk_self) != 0) continue;
         kvdec::AttendArgs& p = cross_side ? xa : a;
         if (waves(p) > 4 && p.chunk_rows >= 256)
-            plan_chunks(cross_side ? xv : sv, group, 128, p);
+            plan_chunks(cross_side ? xv : sv, group, 192, p);
     }
     if (waves(a) != waves(xa)) {
         // the two parts run on workgroups of different shapes at these chunk
