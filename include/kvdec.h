@@ -280,7 +280,7 @@ KVDEC_API int32_t kvdec_append_attend(kvdec_cache* cache, const void* k_new, con
  * own automatic choice -- except that where the two parts would then run on
  * workgroups of different shapes (f32 with 1-2 query heads per KV head, one
  * chunk size >= 256 rows and the other smaller), an automatic part takes
- * 128-row chunks so that both share the launch.  If both sizes were given
+ * 192-row chunks so that both share the launch.  If both sizes were given
  * and still differ in shape, the call makes the two calls instead.
  *   self_cache  : dynamic cache, appended to (KVDEC_E_STATIC otherwise)
  *   cross_cache : static cache of the same batch, n_kv_heads and dtype
