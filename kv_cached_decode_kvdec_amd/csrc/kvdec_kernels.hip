@@ -1308,14 +1308,19 @@ void attend_gqa_mfma_kernel(
     // waited for.  The loop is software-pipelined: once a tile sits in LDS
     // its registers take the next tile's loads, which overlap the MFMA and
     // softmax work on the current one.
-    float4 qraw[2][2];
+    // The group's q rows (GROUP x 64 floats, contiguous) come in with one
+    // 16-byte load per lane per 64 float4s; the MFMA operand layout below
+    // then takes each lane's 16 floats from the lanes that hold them
+    // (ds_bpermute).  Loading the operand layout directly would move each
+    // float4 four times per wave through the CU's in-order vector memory
+    // path, whose time the K/V stream shares.
+    constexpr int QN = (16 * GROUP + 63) / 64;     // float4 loads per lane
+    float4 qw[QN];
     {
-        const float* qp = q + (static_cast<size_t>(loc.b) * Hq + g * GROUP + hl) * kHeadDim + 8 * G;
+        const float4* qg =
+            reinterpret_cast<const float4*>(q + (static_cast<size_t>(loc.b) * Hq + g * GROUP) * kHeadDim);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            qraw[t][0] = *reinterpret_cast<const float4*>(qp + 32 * t);
-            qraw[t][1] = *reinterpret_cast<const float4*>(qp + 32 * t + 4);
-        }
+        for (int k = 0; k < QN; ++k) qw[k] = qg[min(64 * k + lane, 16 * GROUP - 1)];
     }
     uint4 kw[4], vr[4];
     auto load_tile = [&](int r0) {
@@ -1365,7 +1370,29 @@ void attend_gqa_mfma_kernel(
     }
 
     // B operand of the score MFMA: column i is head i % GROUP; k-slot 8G+e of
-    // instruction t is dim 32t + 8G + e.
+    // instruction t is dim 32t + 8G + e, i.e. float4s 16 hl + 8t + 2G and the
+    // next of the group's q, held by lane (that index) % 64 of load (index) / 64.
+    float4 qraw[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int F = 16 * hl + 8 * t + 2 * G + u;
+            const int src = (F & 63) << 2;
+            float x[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float v = 0.f;
+#pragma unroll
+                for (int k = 0; k < QN; ++k) {
+                    const float w = __int_as_float(__builtin_amdgcn_ds_bpermute(
+                        src, __float_as_int(c == 0 ? qw[k].x : c == 1 ? qw[k].y : c == 2 ? qw[k].z : qw[k].w)));
+                    v = (F >> 6) == k ? w : v;
+                }
+                x[c] = v;
+            }
+            qraw[t][u] = make_float4(x[0], x[1], x[2], x[3]);
+        }
     bf16x8 qb_hi[2], qb_lo[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
