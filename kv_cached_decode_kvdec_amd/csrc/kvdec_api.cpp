@@ -132,7 +132,7 @@ bool placeable(int64_t P, int32_t n_kv_heads, int64_t resident)
 }
 
 int32_t auto_chunk(const std::vector<int32_t>& lens, int32_t n_kv_heads, int32_t esz,
-                   int64_t resident, int32_t group = 1)
+                   int64_t resident, int32_t group = 1, bool paged = false)
 {
     if (resident <= 0) resident = 2048;
     int64_t total = 0;
@@ -154,12 +154,15 @@ int32_t auto_chunk(const std::vector<int32_t>& lens, int32_t n_kv_heads, int32_t
     const int64_t min_blocks = resident / 4;
     while (T > KVDEC_MIN_CHUNK && chunks_for(lens, T) * n_kv_heads < min_blocks) T >>= 1;
     // Grids the MFMA kernel runs placed (bf16, grouped query heads, ragged
-    // lengths): the smallest chunk, in steps of 64 rows down to half the
-    // size above, whose grid still fits one placed residency round; the
-    // finer split balances the rows per CU better (gqa, 64 sequences of
-    // 16..8192 rows: 20.3 us per step at 448 rows against 20.6 at 512; at
-    // 384 the grid needs a second round and takes 22.5).
-    if (esz == 2 && group >= 2 && !equal && placeable(chunks_for(lens, T), n_kv_heads, resident)) {
+    // lengths, contiguous cache): the smallest chunk, in steps of 64 rows
+    // down to half the size above, whose grid still fits one placed
+    // residency round; the finer split balances the rows per CU better
+    // (gqa, 64 sequences of 16..8192 rows: 19.75 us per step at 448 rows
+    // against 20.05 at 512; at 384 the grid needs a second round and takes
+    // 22.5).  Through a page pool the same split was slower (16-row pages:
+    // 20.7 against 20.1 us), so paged grids keep the size above.
+    if (esz == 2 && group >= 2 && !equal && !paged &&
+        placeable(chunks_for(lens, T), n_kv_heads, resident)) {
         const int32_t floor_rows = T / 2 > KVDEC_MIN_CHUNK ? T / 2 : KVDEC_MIN_CHUNK;
         while (T - 64 >= floor_rows && placeable(chunks_for(lens, T - 64), n_kv_heads, resident))
             T -= 64;
@@ -259,7 +262,8 @@ void plan_chunks(const AttendView& v, int32_t group, int32_t chunk_rows, kvdec::
     } else {
         a.chunk_rows = chunk_rows ? chunk_rows
                                   : auto_chunk(v.rows, v.n_kv_heads, esz_of(v.dtype),
-                                               kvdec::resident_attend_blocks(v.dtype, group), group);
+                                               kvdec::resident_attend_blocks(v.dtype, group), group,
+                                               v.table != nullptr);
         a.n_chunks = chunks_for(v.rows, a.chunk_rows);
         a.need_merge = a.n_chunks > v.batch;   // some sequence has more than one chunk
         // the launch reads the lengths the grid was sized from
